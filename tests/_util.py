@@ -1,0 +1,28 @@
+"""Comparison helpers shared by the GPU parity tests."""
+
+import numpy as np
+
+TOL = 1e-2  # max|gpu - oracle| / rms(oracle) on hidden states and logits
+
+
+def rel_err(gpu, ref):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(r * r))
+    return float(np.max(np.abs(g - r)) / (rms if rms > 0 else 1.0))
+
+
+def top1_checked(gpu_tok, ref_logits, margin_frac=1e-2):
+    """True/False if the oracle's top-2 gap exceeds margin_frac * rms(logits) (then the GPU token
+    must equal the oracle's argmax); None for a near-tie (not compared)."""
+    lg = np.asarray(ref_logits, dtype=np.float64)
+    order = np.argsort(-lg, kind="stable")
+    gap = lg[order[0]] - lg[order[1]]
+    if gap <= margin_frac * np.sqrt(np.mean(lg * lg)):
+        return None
+    return int(gpu_tok) == int(np.flatnonzero(lg == lg.max())[0])
+
+
+def f32(x):
+    """tau as the library sees it (fp32)."""
+    return float(np.float32(x))

@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every symbol include/river.h declares, and rejects bad
+arguments before touching the GPU (host-only calls; no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from token_level_early_amd import configs, river
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "river.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(river_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = river.load()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama3.2-1b-shape", "llama3.1-8b-shape"])
+def test_kv_layout_is_one_backbone_sized_cache(name):
+    c = configs.model_cfg(configs.ALL[name])
+    Tmax = 1000
+    d = river.kv_layout(river.make_config(c, Tmax))
+    assert list(d.dims) == [c["L"], 2, 1, c["Hkv"], Tmax, c["D"]]
+    assert d.strides[5] == 1 and d.strides[4] == c["D"] and d.strides[0] == 2 * c["Hkv"] * Tmax * c["D"]
+    # exactly one KV set of the backbone's size: L * 2 * B * Hkv * Tmax * D fp16
+    assert d.total_bytes == c["L"] * 2 * c["Hkv"] * Tmax * c["D"] * 2
+
+
+def test_river_buffer_covers_int4_copy():
+    c = configs.model_cfg(configs.LLAMA_8B)
+    rb, sb = river.workspace_bytes(river.make_config(c, 2400, 2048))
+    P_l = 218_103_808
+    assert c["L"] * (P_l // 2 + 2 * P_l // c["group"]) <= rb <= 1.01 * c["L"] * (P_l // 2 + 2 * P_l // c["group"])
+    assert sb > 0
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("n_kv_heads", 3, "multiple of n_kv_heads"),
+    ("head_dim", 96, "head_dim"),
+    ("group", 48, "group"),
+    ("max_prefill", 5000, "max_prefill"),
+    ("entry_layer", 0, "entry_layer"),
+    ("entry_layer", 33, "entry_layer"),
+    ("d_model", 4100, "d_model"),
+    ("max_batch", 3, "max_batch"),
+    ("rms_eps", 0.0, "rms_eps"),
+])
+def test_bad_config_rejected(field, value, msg):
+    c = configs.model_cfg(configs.LLAMA_8B)
+    cfg = river.make_config(c, 2400, 2048)
+    setattr(cfg, field, value)
+    with pytest.raises(river.RiverError) as e:
+        river.kv_layout(cfg)
+    assert e.value.code == river.RIVER_EINVAL and msg in str(e.value)
+
+
+def test_init_rejects_null_arguments_before_any_device_work():
+    lib = river.load()
+    c = configs.model_cfg(configs.TINY)
+    cfg = river.make_config(c, 128)
+    ctx = ctypes.c_void_p()
+    rc = lib.river_init(ctypes.byref(cfg), None, None, None, None, None, ctypes.byref(ctx))
+    assert rc == river.RIVER_EINVAL and lib.river_last_error()
+    w = river.Weights()
+    rc = lib.river_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(1), ctypes.c_void_p(1),
+                        ctypes.c_void_p(1), None, ctypes.byref(ctx))
+    assert rc == river.RIVER_EINVAL
+    assert lib.river_destroy(None) == river.RIVER_OK
+    assert lib.river_decode_step(None, None, None, 0.5, None, None, None, None, None) == river.RIVER_EINVAL
+    assert lib.river_prefill(None, None, 1, 0, 0.5, None, None, None, None, None) == river.RIVER_EINVAL

@@ -1,0 +1,167 @@
+"""GPU parity on the tiny decoder (4 layers, d=256): the HIP path through the C ABI against the
+CPU oracle, element by element."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import river_oracle as O
+from token_level_early_amd import configs, river, synth
+from tests._util import TOL, f32, rel_err, top1_checked
+
+pytestmark = pytest.mark.gpu
+
+TINY = configs.model_cfg(configs.TINY)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.weights(TINY, seed=0, device="cuda")
+    return w, synth.to_numpy(w), O.RiverOracle(TINY, synth.to_numpy(w))
+
+
+def test_quantizer_export_bit_exact(tiny):
+    w, wn, orc = tiny
+    rv = river.River(TINY, w, max_seq=16)
+    for layer in range(TINY["L"]):
+        for which, m in enumerate(river.MATS):
+            packed, scales = rv.export_river(layer, which)
+            q, s = orc.qcodes[layer][m]
+            want_p = O.pack_nibbles(q)
+            assert torch.equal(packed.cpu(), torch.from_numpy(want_p)), (layer, m)
+            assert np.array_equal(scales.cpu().numpy().view(np.uint16), s.view(np.uint16)), (layer, m)
+    rv.close()
+
+
+def _compare_step(rv, r, o, P, s, tag):
+    hs = rv.hidden()[:, 0].float().cpu().numpy()
+    assert rel_err(hs, o["hs"][:, 0]) <= TOL, (tag, s, rel_err(hs, o["hs"][:, 0]))
+    lg = r["logits"][0].cpu().numpy()
+    assert rel_err(lg, o["logits"][0]) <= TOL, (tag, s)
+    ok = top1_checked(int(r["tokens"][0]), o["logits"][0])
+    assert ok is not False, (tag, s, int(r["tokens"][0]), int(np.argmax(o["logits"][0])))
+    assert int(r["exit_layer"][0]) == int(o["exit_layer"][0]), (tag, s)
+
+
+def _kv_compare(rv, kvo, upto):
+    kv = rv.kv_view().float().cpu().numpy()
+    for l in range(TINY["L"]):
+        for j, ref in ((0, kvo.K), (1, kvo.V)):
+            g = kv[l, j, 0, :, :upto]
+            assert rel_err(g, ref[l, 0, :, :upto]) <= TOL, (l, j)
+    # every slot [0, upto) written on the GPU, nothing beyond
+    written = np.abs(kv[:, :, 0]).sum(axis=(1, 2, 4)) > 0  # [L][Tmax]
+    assert written[:, :upto].all() and not written[:, upto:].any()
+
+
+@pytest.mark.parametrize("mode", ["forced2", "tau"])
+def test_tiny_prefill_and_decode_match_oracle(tiny, mode):
+    w, wn, orc = tiny
+    cfg = configs.TINY
+    P, S = cfg["prompt"], cfg["steps"]
+    Tmax = P + S + 8
+    rv = river.River(TINY, w, max_seq=Tmax, max_prefill=P)
+    toks = synth.prompt(TINY, 1, P, seed=0, device="cuda")
+    kvo = orc.new_kv(1, Tmax)
+    tau = f32(cfg["tau"])
+    if mode == "forced2":
+        pre = rv.prefill(toks, prefill_exit=TINY["L"], logits=True)
+        opre = orc.prefill(kvo, toks.cpu().numpy(), prefill_exit=TINY["L"])
+    else:
+        pre = rv.prefill(toks, prefill_exit=0, tau=tau, logits=True, min_sim=True)
+        ge = pre["seq_exit"].cpu().numpy()
+        opre = orc.prefill(kvo, toks.cpu().numpy(), tau=tau, gpu_seq_exit=ge)
+        assert int(ge[0]) == int(opre["seq_exit"][0])
+    torch.cuda.synchronize()
+    assert rel_err(pre["logits"][0].cpu().numpy(), opre["logits"][0]) <= TOL
+    assert top1_checked(int(pre["tokens"][0]), opre["logits"][0]) is not False
+    _kv_compare(rv, kvo, P)
+    cur = pre["tokens"]
+    exits = []
+    for s in range(S):
+        if mode == "forced2":
+            fe = torch.tensor([cfg["forced_exit"]], dtype=torch.int32, device="cuda")
+            r = rv.decode_step(cur, forced_exit=fe, logits=True)
+            o = orc.decode_step(kvo, cur.cpu().numpy(), forced_exit=[cfg["forced_exit"]])
+        else:
+            r = rv.decode_step(cur, tau=tau, logits=True, sim=True)
+            ge = r["exit_layer"].cpu().numpy()
+            o = orc.decode_step(kvo, cur.cpu().numpy(), tau=tau, gpu_exit=ge)
+            sim = r["sim"][0].cpu().numpy()
+            osim = o["sim"][0]
+            assert np.array_equal(np.isnan(sim), np.isnan(osim)), s
+            fin = ~np.isnan(osim)
+            assert np.allclose(sim[fin], osim[fin], atol=2e-3), s
+        _compare_step(rv, r, o, P, s, mode)
+        exits.append(int(r["exit_layer"][0]))
+        cur = r["tokens"]
+    _kv_compare(rv, kvo, P + S)
+    assert rv.positions() == [P + S]
+    assert rv.device_status() == river.RIVER_OK
+    if mode == "forced2":
+        assert set(exits) == {2}
+    rv.close()
+
+
+def test_tau_extremes(tiny):
+    w, wn, orc = tiny
+    rv = river.River(TINY, w, max_seq=64)
+    toks = synth.prompt(TINY, 1, 8, seed=1, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=TINY["L"])
+    cur = pre["tokens"]
+    r = rv.decode_step(cur, tau=1.5)
+    assert int(r["exit_layer"][0]) == TINY["L"]
+    r = rv.decode_step(r["tokens"], tau=-1.5)
+    assert int(r["exit_layer"][0]) == TINY["entry"]
+    rv.close()
+
+
+def test_forced_exit_out_of_range_flags_device_error(tiny):
+    w, wn, orc = tiny
+    rv = river.River(TINY, w, max_seq=64)
+    toks = synth.prompt(TINY, 1, 8, seed=1, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=TINY["L"])
+    fe = torch.tensor([TINY["L"] + 5], dtype=torch.int32, device="cuda")
+    r = rv.decode_step(pre["tokens"], forced_exit=fe)
+    assert rv.device_status() == river.RIVER_EDEVICE
+    assert int(r["exit_layer"][0]) == TINY["L"]  # treated as no exit
+    assert rv.device_status() == river.RIVER_OK  # cleared
+    rv.close()
+
+
+def test_position_overflow_is_rejected_on_host(tiny):
+    w, wn, orc = tiny
+    rv = river.River(TINY, w, max_seq=10, max_prefill=10)
+    toks = synth.prompt(TINY, 1, 10, seed=1, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=TINY["L"])
+    with pytest.raises(river.RiverError) as e:
+        rv.decode_step(pre["tokens"], tau=0.5)
+    assert e.value.code == river.RIVER_ERANGE
+    rv.close()
+
+
+def test_multi_step_matches_single_steps(tiny):
+    w, wn, orc = tiny
+    S = 6
+    sched = torch.tensor([[1], [2], [3], [4], [2], [1]], dtype=torch.int32, device="cuda")
+    outs = []
+    for multi in (False, True):
+        rv = river.River(TINY, w, max_seq=64)
+        toks = synth.prompt(TINY, 1, 16, seed=2, device="cuda")
+        pre = rv.prefill(toks, prefill_exit=TINY["L"])
+        if multi:
+            ex = torch.empty(S, 1, dtype=torch.int32, device="cuda")
+            t = rv.decode_steps(pre["tokens"], sched=sched, exit_layer=ex)
+            outs.append((t.cpu().numpy().ravel(), ex.cpu().numpy().ravel(), rv.kv_view().cpu()))
+        else:
+            cur, tt, ee = pre["tokens"], [], []
+            for s in range(S):
+                r = rv.decode_step(cur, forced_exit=sched[s])
+                tt.append(int(r["tokens"][0]))
+                ee.append(int(r["exit_layer"][0]))
+                cur = r["tokens"]
+            outs.append((np.array(tt), np.array(ee), rv.kv_view().cpu()))
+        rv.close()
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1]) and list(outs[0][1]) == [1, 2, 3, 4, 2, 1]
+    assert torch.equal(outs[0][2], outs[1][2])  # deterministic, bit-identical cache

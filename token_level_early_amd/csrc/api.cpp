@@ -1,0 +1,555 @@
+// C ABI of the early-exit decode library: argument checks, buffer layouts, river build,
+// prefill and decode drivers (HIP-graph replay of the static per-step launch sequence).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/river.h"
+#include "params.hpp"
+
+// kernels (decode.hip, quant.hip, prefill.hip)
+hipError_t river_decode_layers(const DecodeArgs& a, hipStream_t st);
+hipError_t river_launch_gemv(const DecodeArgs& a, int op, int layer, hipStream_t st);
+hipError_t river_launch_begin(const DecodeArgs& a, hipStream_t st);
+int river_gemv_max_wg(const Dims& dm);
+hipError_t river_launch_quantize(const f16* W, int N, int K, int group, uint8_t* out, f16* scales,
+                                 hipStream_t st);
+hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K, int group,
+                               uint8_t* packed, uint16_t* scales, hipStream_t st);
+hipError_t river_launch_rope_table(float2* tab, int Tmax, int D, double theta, hipStream_t st);
+hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st);
+
+hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const LayerDev* host_layers,
+                                int forced, float tau, hipStream_t st);
+
+
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return RIVER_EHIP;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+int check_cfg(const river_config* c) {
+  if (!c) return fail(RIVER_EINVAL, "cfg is NULL");
+  if (c->n_layers < 1) return fail(RIVER_EINVAL, "n_layers must be >= 1");
+  if (c->d_model < 8 || c->d_model % 8) return fail(RIVER_EINVAL, "d_model must be a positive multiple of 8");
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+    return fail(RIVER_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RIVER_EINVAL, "n_heads/n_kv_heads must be 1, 2, 4 or 8");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(RIVER_EINVAL, "head_dim must be 64 or 128");
+  if (c->d_ffn < 8 || c->d_ffn % 8) return fail(RIVER_EINVAL, "d_ffn must be a positive multiple of 8");
+  if (c->vocab < 1) return fail(RIVER_EINVAL, "vocab must be >= 1");
+  if (c->group != 32 && c->group != 64 && c->group != 128) return fail(RIVER_EINVAL, "group must be 32, 64 or 128");
+  const int hd = c->n_heads * c->head_dim;
+  if (c->d_model > 16384 || hd > 16384 || c->d_ffn > 16384)
+    return fail(RIVER_EINVAL, "d_model, n_heads*head_dim and d_ffn must be <= 16384");
+  if (c->max_batch != 1)
+    return fail(RIVER_EINVAL, "max_batch must be 1 (batched decode is not built yet)");
+  if (c->max_seq < 1) return fail(RIVER_EINVAL, "max_seq must be >= 1");
+  if (c->max_prefill < 1 || c->max_prefill > c->max_seq)
+    return fail(RIVER_EINVAL, "max_prefill must be in [1, max_seq]");
+  if (c->entry_layer < 1 || c->entry_layer > c->n_layers)
+    return fail(RIVER_EINVAL, "entry_layer must be in [1, n_layers]");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(RIVER_EINVAL, "rms_eps and rope_theta must be > 0");
+  if (c->tied_embeddings != 0 && c->tied_embeddings != 1) return fail(RIVER_EINVAL, "tied_embeddings must be 0 or 1");
+  return RIVER_OK;
+}
+
+Dims make_dims(const river_config* c) {
+  Dims d{};
+  d.L = c->n_layers;
+  d.d = c->d_model;
+  d.H = c->n_heads;
+  d.Hkv = c->n_kv_heads;
+  d.D = c->head_dim;
+  d.F = c->d_ffn;
+  d.V = c->vocab;
+  d.group = c->group;
+  d.B = c->max_batch;
+  d.Tmax = c->max_seq;
+  d.entry = c->entry_layer;
+  d.tied = c->tied_embeddings;
+  d.max_prefill = c->max_prefill;
+  d.eps = c->rms_eps;
+  d.theta = c->rope_theta;
+  d.hd = c->n_heads * c->head_dim;
+  d.nqkv = d.hd + 2 * c->n_kv_heads * c->head_dim;
+  return d;
+}
+
+int attn_smax(const Dims& d) {
+  int s = 512 / (d.B * d.Hkv);
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return s;
+}
+
+// ---- river buffer layout: per layer qkv, o, gu, down (packed), then their scales
+struct RiverLayout {
+  uint64_t off_p[4], off_s[4];
+  uint64_t layer_bytes;
+  int N[4], K[4];
+};
+
+RiverLayout river_layout(const Dims& d) {
+  RiverLayout r{};
+  const int N[4] = {d.nqkv, d.d, 2 * d.F, d.d};
+  const int K[4] = {d.d, d.hd, d.d, d.F};
+  uint64_t off = 0;
+  for (int i = 0; i < 4; ++i) {
+    r.N[i] = N[i];
+    r.K[i] = K[i];
+    r.off_p[i] = off;
+    off = align256(off + (uint64_t)N[i] * w4_row_bytes(K[i]));
+  }
+  for (int i = 0; i < 4; ++i) {
+    r.off_s[i] = off;
+    off = align256(off + (uint64_t)N[i] * w4_row_scales(K[i], d.group) * 2);
+  }
+  r.layer_bytes = off;
+  return r;
+}
+
+// ---- scratch layout
+struct ScratchLayout {
+  uint64_t hs, hmid, q, o, a2, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
+      layers, rope;
+  uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
+      pf_minsim;
+  uint64_t total;
+  int smax;
+  int ncnt;
+};
+
+ScratchLayout scratch_layout(const Dims& d) {
+  ScratchLayout s{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const uint64_t B = d.B;
+  s.smax = attn_smax(d);
+  s.ncnt = CNT_ATTN + d.B * d.Hkv;
+  s.hs = take((d.L + 1) * B * d.d * 2);
+  s.hmid = take(d.L * B * d.d * 2);
+  s.q = take(B * d.hd * 2);
+  s.o = take(B * d.hd * 2);
+  s.a2 = take(B * d.F * 2);
+  s.inv_attn = take((d.L + 1) * B * 4);
+  s.inv_mlp = take(d.L * B * 4);
+  s.route = take((d.L + 2) * B * 4);
+  s.pos = take(B * 4);
+  s.step = take(4);
+  s.err = take(4);
+  s.red = take((uint64_t)kMaxRed * 4 * 8);
+  s.cnt = take((uint64_t)s.ncnt * 4);
+  s.pml = take(B * d.H * s.smax * 2 * 4);
+  s.pacc = take(B * d.H * s.smax * d.D * 4);
+  s.amax = take(B * 8);
+  s.layers = take((uint64_t)d.L * sizeof(LayerDev));
+  s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
+  const uint64_t M = B * d.max_prefill;
+  const uint64_t wide = (uint64_t)(d.d > d.hd ? d.d : d.hd);
+  s.pf_hin = take(M * wide * 2);
+  s.pf_hout = take(M * wide * 2);
+  s.pf_hmid = take(M * wide * 2);
+  s.pf_act = take(M * wide * 2);
+  s.pf_qkv = take(M * d.nqkv * 2);
+  s.pf_gu = take(M * 2 * d.F * 2);
+  s.pf_a2 = take(M * d.F * 2);
+  s.pf_cos = take(M * 8);
+  s.pf_route = take(B * 4);
+  s.pf_exit = take(B * 4);
+  s.pf_minsim = take(B * d.L * 4);
+  s.total = off;
+  return s;
+}
+
+}  // namespace
+
+struct river_ctx {
+  river_config cfg;
+  Dims dm;
+  RiverLayout rl;
+  ScratchLayout sl;
+  char* kv;
+  char* river;
+  char* scratch;
+  std::vector<LayerDev> layers;  // host copy of the device table
+  const f16* embed;
+  const f16* lm_head;
+  const f16* final_norm;
+  std::vector<int32_t> pos_host;
+  hipStream_t cap_stream;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  bool graph_valid;
+  DecodeArgs graph_key;
+  bool use_graph;
+};
+
+static DecodeArgs base_args(const river_ctx* c) {
+  DecodeArgs a{};
+  const ScratchLayout& s = c->sl;
+  char* sc = c->scratch;
+  a.dm = c->dm;
+  a.layers = (const LayerDev*)(sc + s.layers);
+  a.embed = c->embed;
+  a.lm_head = c->lm_head;
+  a.final_norm = c->final_norm;
+  a.kv = (f16*)c->kv;
+  a.rope = (const float2*)(sc + s.rope);
+  a.hs = (f16*)(sc + s.hs);
+  a.hmid = (f16*)(sc + s.hmid);
+  a.q = (f16*)(sc + s.q);
+  a.o = (f16*)(sc + s.o);
+  a.a2 = (f16*)(sc + s.a2);
+  a.inv_attn = (float*)(sc + s.inv_attn);
+  a.inv_mlp = (float*)(sc + s.inv_mlp);
+  a.route = (int*)(sc + s.route);
+  a.pos = (int*)(sc + s.pos);
+  a.step = (int*)(sc + s.step);
+  a.err = (int*)(sc + s.err);
+  a.red = (double*)(sc + s.red);
+  a.cnt = (int*)(sc + s.cnt);
+  a.pml = (float*)(sc + s.pml);
+  a.pacc = (float*)(sc + s.pacc);
+  a.amax = (unsigned long long*)(sc + s.amax);
+  a.attn_smax = s.smax;
+  return a;
+}
+
+extern "C" {
+
+const char* river_last_error(void) { return g_err.c_str(); }
+
+int river_kv_layout(const river_config* cfg, river_kv_desc* out) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!out) return fail(RIVER_EINVAL, "out is NULL");
+  const int64_t dims[6] = {cfg->n_layers, 2, cfg->max_batch, cfg->n_kv_heads, cfg->max_seq, cfg->head_dim};
+  int64_t stride = 1;
+  for (int i = 5; i >= 0; --i) {
+    out->dims[i] = dims[i];
+    out->strides[i] = stride;
+    stride *= dims[i];
+  }
+  out->elem_bytes = 2;
+  out->total_bytes = (uint64_t)stride * 2;
+  return RIVER_OK;
+}
+
+int river_workspace_bytes(const river_config* cfg, uint64_t* river_bytes, uint64_t* scratch_bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!river_bytes || !scratch_bytes) return fail(RIVER_EINVAL, "output pointer is NULL");
+  const Dims d = make_dims(cfg);
+  *river_bytes = river_layout(d).layer_bytes * (uint64_t)d.L;
+  *scratch_bytes = scratch_layout(d).total;
+  return RIVER_OK;
+}
+
+int river_init(const river_config* cfg, const river_weights* w, void* kv, void* river_buf,
+               void* scratch, void* stream, river_ctx** out) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!w || !kv || !river_buf || !scratch || !out) return fail(RIVER_EINVAL, "NULL argument");
+  if (!w->embed || !w->final_norm || !w->layers) return fail(RIVER_EINVAL, "NULL weight pointer");
+  if (!cfg->tied_embeddings && !w->lm_head) return fail(RIVER_EINVAL, "lm_head is NULL but embeddings are not tied");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const river_layer_weights& lw = w->layers[l];
+    if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.mlp_norm || !lw.w_gate ||
+        !lw.w_up || !lw.w_down)
+      return fail(RIVER_EINVAL, "NULL weight pointer in layer " + std::to_string(l));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  river_ctx* c = new (std::nothrow) river_ctx();
+  if (!c) return fail(RIVER_ENOMEM, "host allocation failed");
+  c->cfg = *cfg;
+  c->dm = make_dims(cfg);
+  c->rl = river_layout(c->dm);
+  c->sl = scratch_layout(c->dm);
+  c->kv = (char*)kv;
+  c->river = (char*)river_buf;
+  c->scratch = (char*)scratch;
+  c->embed = (const f16*)w->embed;
+  c->lm_head = (const f16*)(cfg->tied_embeddings ? w->embed : w->lm_head);
+  c->final_norm = (const f16*)w->final_norm;
+  c->pos_host.assign(cfg->max_batch, 0);
+  c->graph_valid = false;
+  c->graph = nullptr;
+  c->exec = nullptr;
+  const char* ng = getenv("RIVER_NO_GRAPH");
+  c->use_graph = !(ng && ng[0] == '1');
+  hipError_t e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipStreamCreateWithFlags");
+  }
+  const Dims& d = c->dm;
+  c->layers.resize(d.L);
+  for (int l = 0; l < d.L; ++l) {
+    const river_layer_weights& lw = w->layers[l];
+    LayerDev& ld = c->layers[l];
+    ld.attn_norm = (const f16*)lw.attn_norm;
+    ld.wq = (const f16*)lw.wq;
+    ld.wk = (const f16*)lw.wk;
+    ld.wv = (const f16*)lw.wv;
+    ld.wo = (const f16*)lw.wo;
+    ld.mlp_norm = (const f16*)lw.mlp_norm;
+    ld.wg = (const f16*)lw.w_gate;
+    ld.wu = (const f16*)lw.w_up;
+    ld.wd = (const f16*)lw.w_down;
+    char* base = c->river + (uint64_t)l * c->rl.layer_bytes;
+    ld.r_qkv = (const uint8_t*)(base + c->rl.off_p[0]);
+    ld.r_o = (const uint8_t*)(base + c->rl.off_p[1]);
+    ld.r_gu = (const uint8_t*)(base + c->rl.off_p[2]);
+    ld.r_d = (const uint8_t*)(base + c->rl.off_p[3]);
+    ld.s_qkv = (const f16*)(base + c->rl.off_s[0]);
+    ld.s_o = (const f16*)(base + c->rl.off_s[1]);
+    ld.s_gu = (const f16*)(base + c->rl.off_s[2]);
+    ld.s_d = (const f16*)(base + c->rl.off_s[3]);
+    // quantise the seven matrices into the river copy
+    struct Job {
+      const void* W;
+      int N, K, m, row0;
+    } jobs[7] = {{lw.wq, d.hd, d.d, 0, 0},
+                 {lw.wk, d.Hkv * d.D, d.d, 0, d.hd},
+                 {lw.wv, d.Hkv * d.D, d.d, 0, d.hd + d.Hkv * d.D},
+                 {lw.wo, d.d, d.hd, 1, 0},
+                 {lw.w_gate, d.F, d.d, 2, 0},
+                 {lw.w_up, d.F, d.d, 2, d.F},
+                 {lw.w_down, d.d, d.F, 3, 0}};
+    for (const Job& j : jobs) {
+      uint8_t* p = (uint8_t*)(base + c->rl.off_p[j.m]) + (uint64_t)j.row0 * w4_row_bytes(j.K);
+      f16* s = (f16*)(base + c->rl.off_s[j.m]) + (uint64_t)j.row0 * w4_row_scales(j.K, d.group);
+      e = river_launch_quantize((const f16*)j.W, j.N, j.K, d.group, p, s, st);
+      if (e != hipSuccess) {
+        river_destroy(c);
+        return hip_fail(e, "quantize launch");
+      }
+    }
+  }
+  DecodeArgs a = base_args(c);
+  // device state: clear everything that must start at zero, the layer table, the RoPE table
+  if ((e = river_launch_fill(c->scratch + c->sl.route, (uint64_t)(d.L + 2) * d.B * 4, 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.pos, 256 * 3, 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.cnt, align256((uint64_t)c->sl.ncnt * 4), 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)d.B * 8), 0, st)) ||
+      (e = river_launch_rope_table((float2*)a.rope, d.Tmax, d.D, (double)d.theta, st))) {
+    river_destroy(c);
+    return hip_fail(e, "init kernels");
+  }
+  e = hipMemcpyAsync(c->scratch + c->sl.layers, c->layers.data(), sizeof(LayerDev) * d.L,
+                     hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host table must outlive the copy
+  if (e != hipSuccess) {
+    river_destroy(c);
+    return hip_fail(e, "layer table upload");
+  }
+  *out = c;
+  return RIVER_OK;
+}
+
+int river_destroy(river_ctx* c) {
+  if (!c) return RIVER_OK;
+  (void)hipDeviceSynchronize();
+  if (c->exec) (void)hipGraphExecDestroy(c->exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  delete c;
+  return RIVER_OK;
+}
+
+int river_positions(const river_ctx* c, int32_t* pos) {
+  if (!c || !pos) return fail(RIVER_EINVAL, "NULL argument");
+  for (size_t i = 0; i < c->pos_host.size(); ++i) pos[i] = c->pos_host[i];
+  return RIVER_OK;
+}
+
+int river_device_status(river_ctx* c, void* stream) {
+  if (!c) return fail(RIVER_EINVAL, "ctx is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  int v = 0;
+  hipError_t e = hipMemcpyAsync(&v, c->scratch + c->sl.err, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "device status read");
+  if (v) {
+    (void)river_launch_fill(c->scratch + c->sl.err, 4, 0, st);
+    (void)hipStreamSynchronize(st);
+    return fail(RIVER_EDEVICE, "device error word " + std::to_string(v) +
+                                   " (1: token id out of range, 2: forced exit out of range)");
+  }
+  return RIVER_OK;
+}
+
+int river_prefill(river_ctx* c, const int32_t* tokens, int32_t P, int32_t prefill_exit, float tau,
+                  int32_t* next_tok, float* logits, int32_t* seq_exit, float* min_sim, void* stream) {
+  if (!c || !tokens || !next_tok) return fail(RIVER_EINVAL, "NULL argument");
+  const Dims& d = c->dm;
+  if (P < 1 || P > d.max_prefill || P > d.Tmax) return fail(RIVER_ERANGE, "P out of range");
+  if (prefill_exit != 0 && (prefill_exit < d.entry || prefill_exit > d.L))
+    return fail(RIVER_ERANGE, "prefill_exit must be 0 or in [entry_layer, n_layers]");
+  if (prefill_exit == 0 && std::isnan(tau)) return fail(RIVER_EINVAL, "tau is NaN");
+  hipStream_t st = (hipStream_t)stream;
+  char* sc = c->scratch;
+  const ScratchLayout& s = c->sl;
+  PfArgs p{};
+  p.dm = d;
+  p.M = d.B * P;
+  p.P = P;
+  p.tokens = tokens;
+  p.embed = c->embed;
+  p.hin = (f16*)(sc + s.pf_hin);
+  p.hout = (f16*)(sc + s.pf_hout);
+  p.hmid = (f16*)(sc + s.pf_hmid);
+  p.act = (f16*)(sc + s.pf_act);
+  p.qkv = (f16*)(sc + s.pf_qkv);
+  p.gu = (f16*)(sc + s.pf_gu);
+  p.a2 = (f16*)(sc + s.pf_a2);
+  p.cosv = (double*)(sc + s.pf_cos);
+  p.seq_route = (int*)(sc + s.pf_route);
+  p.seq_exit = (int*)(sc + s.pf_exit);
+  p.min_sim = min_sim;
+  p.err = (int*)(sc + s.err);
+  p.kv = (f16*)c->kv;
+  p.rope = (const float2*)(sc + s.rope);
+  DecodeArgs a = base_args(c);
+  a.tok_out = next_tok;
+  a.logits = logits;
+  hipError_t e = river_launch_prefill(p, a, c->layers.data(), prefill_exit, tau, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  e = river_launch_gemv(a, OP_LM, d.L + 1, st);
+  if (e != hipSuccess) return hip_fail(e, "prefill LM head launch");
+  if (seq_exit) {
+    e = hipMemcpyAsync(seq_exit, p.seq_exit, (size_t)d.B * 4, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "seq_exit copy");
+  }
+  for (auto& v : c->pos_host) v = P;
+  return RIVER_OK;
+}
+
+static bool same_key(const DecodeArgs& x, const DecodeArgs& y) {
+  return x.tok_in == y.tok_in && x.sched == y.sched && x.tok_out == y.tok_out &&
+         x.exit_out == y.exit_out && x.sim_out == y.sim_out && x.logits == y.logits &&
+         std::memcmp(&x.tau, &y.tau, sizeof(float)) == 0;
+}
+
+static int run_steps(river_ctx* c, const DecodeArgs& a, int S, hipStream_t st) {
+  hipError_t e = river_launch_begin(a, st);
+  if (e != hipSuccess) return hip_fail(e, "begin launch");
+  if (!c->use_graph) {
+    for (int i = 0; i < S; ++i)
+      if ((e = river_decode_layers(a, st)) != hipSuccess) return hip_fail(e, "decode launch");
+    return RIVER_OK;
+  }
+  if (!c->graph_valid || !same_key(a, c->graph_key)) {
+    if (c->exec) (void)hipGraphExecDestroy(c->exec);
+    if (c->graph) (void)hipGraphDestroy(c->graph);
+    c->exec = nullptr;
+    c->graph = nullptr;
+    c->graph_valid = false;
+    e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+    hipError_t le = river_decode_layers(a, c->cap_stream);
+    e = hipStreamEndCapture(c->cap_stream, &c->graph);
+    if (le != hipSuccess) return hip_fail(le, "decode capture");
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+    c->graph_key = a;
+    c->graph_valid = true;
+  }
+  for (int i = 0; i < S; ++i)
+    if ((e = hipGraphLaunch(c->exec, st)) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return RIVER_OK;
+}
+
+int river_decode_steps(river_ctx* c, const int32_t* tok_in, const int32_t* sched, int32_t S,
+                       float tau, int32_t* tok_out, int32_t* exit_layer, float* sim, void* stream) {
+  if (!c || !tok_in || !tok_out) return fail(RIVER_EINVAL, "NULL argument");
+  if (S < 1) return fail(RIVER_EINVAL, "S must be >= 1");
+  if (!sched && std::isnan(tau)) return fail(RIVER_EINVAL, "tau is NaN");
+  for (int32_t p : c->pos_host)
+    if ((int64_t)p + S > c->dm.Tmax) return fail(RIVER_ERANGE, "position would pass max_seq");
+  DecodeArgs a = base_args(c);
+  a.tok_in = tok_in;
+  a.sched = sched;
+  a.tok_out = tok_out;
+  a.exit_out = exit_layer;
+  a.sim_out = sim;
+  a.logits = nullptr;
+  a.tau = sched ? 0.f : tau;
+  int rc = run_steps(c, a, S, (hipStream_t)stream);
+  if (rc) return rc;
+  for (auto& v : c->pos_host) v += S;
+  return RIVER_OK;
+}
+
+int river_decode_step(river_ctx* c, const int32_t* tok_in, const int32_t* forced_exit, float tau,
+                      int32_t* tok_out, float* logits, int32_t* exit_layer, float* sim, void* stream) {
+  if (!c || !tok_in || !tok_out) return fail(RIVER_EINVAL, "NULL argument");
+  if (!forced_exit && std::isnan(tau)) return fail(RIVER_EINVAL, "tau is NaN");
+  for (int32_t p : c->pos_host)
+    if ((int64_t)p + 1 > c->dm.Tmax) return fail(RIVER_ERANGE, "position would pass max_seq");
+  DecodeArgs a = base_args(c);
+  a.tok_in = tok_in;
+  a.sched = forced_exit;
+  a.tok_out = tok_out;
+  a.exit_out = exit_layer;
+  a.sim_out = sim;
+  a.logits = logits;
+  a.tau = forced_exit ? 0.f : tau;
+  int rc = run_steps(c, a, 1, (hipStream_t)stream);
+  if (rc) return rc;
+  for (auto& v : c->pos_host) v += 1;
+  return RIVER_OK;
+}
+
+int river_export_river(river_ctx* c, int32_t layer, int32_t which, uint8_t* packed, uint16_t* scales,
+                       void* stream) {
+  if (!c || !packed || !scales) return fail(RIVER_EINVAL, "NULL argument");
+  const Dims& d = c->dm;
+  if (layer < 0 || layer >= d.L) return fail(RIVER_ERANGE, "layer out of range");
+  if (which < 0 || which > 6) return fail(RIVER_EINVAL, "which must be in [0, 6]");
+  const int mat[7] = {0, 0, 0, 1, 2, 2, 3};
+  const int row0[7] = {0, d.hd, d.hd + d.Hkv * d.D, 0, 0, d.F, 0};
+  const int Ns[7] = {d.hd, d.Hkv * d.D, d.Hkv * d.D, d.d, d.F, d.F, d.d};
+  const int m = mat[which];
+  const int K = c->rl.K[m];
+  const char* base = c->river + (uint64_t)layer * c->rl.layer_bytes;
+  const uint8_t* p = (const uint8_t*)(base + c->rl.off_p[m]) + (uint64_t)row0[which] * w4_row_bytes(K);
+  const f16* s = (const f16*)(base + c->rl.off_s[m]) + (uint64_t)row0[which] * w4_row_scales(K, d.group);
+  hipError_t e = river_launch_export(p, s, Ns[which], K, d.group, packed, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export launch");
+  return RIVER_OK;
+}
+
+int river_debug_hidden(river_ctx* c, void* dst, void* stream) {
+  if (!c || !dst) return fail(RIVER_EINVAL, "NULL argument");
+  const Dims& d = c->dm;
+  hipError_t e = hipMemcpyAsync(dst, c->scratch + c->sl.hs, (size_t)(d.L + 1) * d.B * d.d * 2,
+                                hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hidden copy");
+  return RIVER_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Device helpers shared by the decode, prefill and quantiser kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+#define RIVER_DEV __device__ __forceinline__
+
+static constexpr int kWave = 64;
+static constexpr int kBlock = 256;  // every kernel uses 4 waves per workgroup
+
+// ---------------------------------------------------------------------------------------
+// Weight-stream geometry. One "chunk" is what a wave reads of one matrix row with one
+// 16-byte load per lane: 512 fp16 elements, or 2048 int4 elements (1 KiB either way).
+// ---------------------------------------------------------------------------------------
+static constexpr int kChunkF16 = 512;
+static constexpr int kChunkW4 = 2048;
+
+// Row stride (bytes) of the device int4 layout: ceil(K / 2048) chunks of 1 KiB.
+__host__ __device__ inline int64_t w4_row_bytes(int K) {
+  return (int64_t)((K + kChunkW4 - 1) / kChunkW4) * 1024;
+}
+// Scales per row of the device int4 layout (groups covering the padded row).
+__host__ __device__ inline int64_t w4_row_scales(int K, int group) {
+  return (int64_t)((K + kChunkW4 - 1) / kChunkW4) * (kChunkW4 / group);
+}
+
+// ---------------------------------------------------------------------------------------
+// Bit casts, fp16 conversions
+// ---------------------------------------------------------------------------------------
+RIVER_DEV h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+RIVER_DEV uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+RIVER_DEV float h2f(f16 x) { return (float)x; }
+RIVER_DEV f16 f2h(float x) { return (f16)x; }  // round to nearest even
+
+// fp32 dot of two fp16 pairs accumulated into c (v_dot2_f32_f16)
+RIVER_DEV float dot2(h2 a, h2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+
+// ---------------------------------------------------------------------------------------
+// int4 unpack. A dword holds 8 offset-binary nibbles u_m (element m in bits 4m..4m+3).
+// OR-ing a nibble into the mantissa of fp16 1024.0 (0x6400) gives 1024 + u exactly; a
+// nibble in bits 4..7 of a half gives 1024 + 16u. Subtracting the bias leaves q = u - 8
+// exactly in fp16. Output pairs: (q0,q4), (q1,q5), (q2,q6), (q3,q7).
+// ---------------------------------------------------------------------------------------
+RIVER_DEV void unpack8(uint32_t w, h2& p0, h2& p1, h2& p2, h2& p3) {
+  const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+  const uint32_t w8 = w >> 8;
+  const h2 b0 = as_h2((w & lo) | magic);
+  const h2 b1 = as_h2((w & hi) | magic);
+  const h2 b2 = as_h2((w8 & lo) | magic);
+  const h2 b3 = as_h2((w8 & hi) | magic);
+  const h2 off = {(f16)1032.0f, (f16)1032.0f};
+  const h2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+  const h2 off16 = {(f16)72.0f, (f16)72.0f};
+  p0 = b0 - off;
+  p1 = b1 * sixteenth - off16;
+  p2 = b2 - off;
+  p3 = b3 * sixteenth - off16;
+}
+
+// Reorders 8 consecutive fp16 values (x0..x7 as pairs (x0,x1),(x2,x3),(x4,x5),(x6,x7)) into
+// the pairing unpack8 produces: (x0,x4),(x1,x5),(x2,x6),(x3,x7).
+RIVER_DEV void pair_for_unpack(const uint32_t in[4], h2 out[4]) {
+  // __builtin_amdgcn_perm(a, b, sel): byte k of result = byte sel_k of {a:b} (b = bytes 0-3)
+  out[0] = as_h2(__builtin_amdgcn_perm(in[2], in[0], 0x05040100u));  // x0 | x4<<16
+  out[1] = as_h2(__builtin_amdgcn_perm(in[2], in[0], 0x07060302u));  // x1 | x5<<16
+  out[2] = as_h2(__builtin_amdgcn_perm(in[3], in[1], 0x05040100u));  // x2 | x6<<16
+  out[3] = as_h2(__builtin_amdgcn_perm(in[3], in[1], 0x07060302u));  // x3 | x7<<16
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave / block reductions (fixed order: deterministic for identical inputs)
+// ---------------------------------------------------------------------------------------
+RIVER_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+RIVER_DEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+RIVER_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over the 256 threads of a block; every thread gets the result. `red` is >= 4 slots.
+RIVER_DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+RIVER_DEV double block_sum_d(double v, double* red) {
+  v = wave_sum_d(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Cross-workgroup "last arriver" protocol. Each workgroup publishes its partial results,
+// then one thread increments a counter with an agent-scope acq_rel atomic. The workgroup
+// that sees count-1 owns the final step; it resets the counter for the next launch.
+// The release half makes this workgroup's earlier global writes visible across XCDs before
+// the increment; the acquire half makes every other workgroup's writes visible to the last.
+// ---------------------------------------------------------------------------------------
+RIVER_DEV bool arrive_last(int* counter, int count, int* lds_flag) {
+  // every thread releases its own partial stores at agent scope (write-back of this XCD's
+  // L2) before the workgroup's single increment
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (old == count - 1);
+  }
+  __syncthreads();
+  const bool last = *lds_flag != 0;
+  if (last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every other workgroup's stores
+  }
+  return last;
+}
+RIVER_DEV void reset_counter(int* counter) {
+  __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+RIVER_DEV uint32_t float_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+RIVER_DEV float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __builtin_bit_cast(float, u);
+}

@@ -1,0 +1,113 @@
+// Argument blocks shared by the host driver (api.cpp) and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "common.hpp"
+
+// Per-layer device pointers: borrowed fp16 backbone weights and the river copy built at init.
+// River matrices use the device int4 layout: rows in logical order, row stride
+// w4_row_bytes(K), element 2i in the low nibble of byte i, padding nibbles 8 (q = 0); fp16
+// scales [N][w4_row_scales(K, group)], padding groups 0.
+//   r_qkv: rows [0,H*D) = wq, [H*D, H*D+Hkv*D) = wk, then wv      (K = d)
+//   r_o:   wo                                                    (K = H*D)
+//   r_gu:  rows [0,F) = w_gate, [F,2F) = w_up                     (K = d)
+//   r_d:   w_down                                                (K = F)
+struct LayerDev {
+  const f16* attn_norm;
+  const f16* wq;
+  const f16* wk;
+  const f16* wv;
+  const f16* wo;
+  const f16* mlp_norm;
+  const f16* wg;
+  const f16* wu;
+  const f16* wd;
+  const uint8_t* r_qkv;
+  const uint8_t* r_o;
+  const uint8_t* r_gu;
+  const uint8_t* r_d;
+  const f16* s_qkv;
+  const f16* s_o;
+  const f16* s_gu;
+  const f16* s_d;
+};
+
+struct Dims {
+  int L, d, H, Hkv, D, F, V, group, B, Tmax, entry, tied, max_prefill;
+  float eps, theta;
+  int hd;    // H*D
+  int nqkv;  // H*D + 2*Hkv*D
+};
+
+// Route codes: which copy of block l a row runs.
+enum { ROUTE_BACKBONE = 0, ROUTE_RIVER = 1 };
+
+// Device error word bits.
+enum { ERR_TOKEN = 1, ERR_FORCED = 2, ERR_POS = 4 };
+
+// Everything a decode kernel needs. Passed by value.
+struct DecodeArgs {
+  Dims dm;
+  const LayerDev* layers;  // device array [L]
+  const f16* embed;        // [V][d]
+  const f16* lm_head;      // [V][d] (the embedding when tied)
+  const f16* final_norm;   // [d]
+  f16* kv;                 // [L][2][B][Hkv][Tmax][D]
+  const float2* rope;      // [Tmax][D/2] (cos, sin)
+  // residual stream and activations (scratch)
+  f16* hs;      // [L+1][B][d]
+  f16* hmid;    // [L][B][d]   (index l-1 for layer l)
+  f16* q;       // [B][H*D]
+  f16* o;       // [B][H*D]
+  f16* a2;      // [B][F]
+  float* inv_attn;  // [L+1][B]  1/rms of hs[l]
+  float* inv_mlp;   // [L][B]    1/rms of hmid[l-1]
+  int* route;       // [L+2][B]  route of layer l
+  int* pos;         // [B]
+  int* step;        // [1]
+  int* err;         // [1]
+  double* red;      // [kMaxRed][4] per-workgroup partial sums
+  int* cnt;         // counters, see CNT_*
+  float* pml;       // attention split partials (m, l): [B][H][smax][2]
+  float* pacc;      // attention split partials acc: [B][H][smax][D]
+  unsigned long long* amax;  // [B] LM-head argmax keys
+  int attn_smax;    // split count of the attention grid
+  // per-call I/O (device pointers)
+  const int* tok_in;     // [B]
+  const int* sched;      // [S][B] forced exit layers or null (tau mode)
+  int* tok_out;          // [S][B]
+  int* exit_out;         // [S][B] or null
+  float* sim_out;        // [S][B][L] or null
+  float* logits;         // [B][V] or null (single step only)
+  float tau;
+};
+
+static constexpr int kMaxRed = 8192;
+// counter slots (each one int)
+static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn: [B][Hkv]
+
+// Decode GEMV operations (one launch each).
+enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
+
+// Prefill activations and state (scratch), passed by value to the prefill kernels.
+struct PfArgs {
+  Dims dm;
+  int M, P;            // M = B*P rows
+  const int* tokens;   // [B][P]
+  const f16* embed;
+  f16* hin;    // [M][max(d, H*D)] block input (residual stream)
+  f16* hout;   // [M][max(d, H*D)] attention output, then block output
+  f16* hmid;   // [M][max(d, H*D)]
+  f16* act;    // [M][max(d, H*D)] normed input / rotated q
+  f16* qkv;    // [M][nqkv]
+  f16* gu;     // [M][2F]
+  f16* a2;     // [M][F]
+  double* cosv;    // [M]
+  int* seq_route;  // [B]
+  int* seq_exit;   // [B]
+  float* min_sim;  // [B][L] or null
+  int* err;
+  f16* kv;
+  const float2* rope;
+};

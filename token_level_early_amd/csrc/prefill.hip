@@ -1,0 +1,512 @@
+// Prompt prefill with a sequence-level exit (paperlayer.ai summary of arXiv 2604.18396v3,
+// section 4 "Inference with Seamless Exit": prefill exits per sequence, generation per token;
+// section 3 "Sequence-level Exit": the latest-exiting token sets the sequence's depth).
+//
+// Layer by layer over all B*P prompt rows:
+//   RMSNorm -> QKV GEMM -> RoPE + KV write (positions 0..P-1 of the shared cache) -> causal
+//   attention -> O GEMM + residual -> RMSNorm -> gate|up GEMM -> SwiGLU -> down GEMM + residual
+//   -> per-token cos(h_t(l-1), h_t(l)) -> per-sequence exit decision (min over tokens > tau).
+// A sequence on the river runs the int4 copy of the remaining blocks; both write the same KV.
+//
+// GEMMs use MFMA (v_mfma_f32_16x16x16_f16): 128x128 output tiles, 4 waves of 64x64. The int4
+// copy is unpacked to exact fp16 codes q in LDS and each k-tile's product is scaled by the
+// fp32 group scale of its column, so river rows compute sum_g s_g * sum_{k in g} q_k x_k.
+#include "params.hpp"
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+enum { EPI_STORE = 0, EPI_RESID = 1 };
+
+struct PfGemmArgs {
+  const f16* A;  // [M][K] activations
+  int M, N, K;
+  // fp16 weights: up to three row segments [seg_start[i], seg_start[i+1]) -> seg_ptr[i]
+  const f16* seg_ptr[3];
+  int seg_start[4];
+  // int4 weights (device layout)
+  const uint8_t* w4;
+  const f16* s4;
+  int group;
+  // per-row route filter: row m belongs to sequence m / P; computed only if route matches
+  const int* seq_route;  // [B]
+  int P;
+  int want_route;
+  // epilogue
+  f16* C;  // [M][N]
+  const f16* R;  // residual [M][N] (EPI_RESID)
+  int epi;
+};
+
+static constexpr int GBM = 128, GBN = 128, GBK = 32, GLDK = GBK + 16;  // 96-byte rows: 16-byte aligned
+
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
+  __shared__ f16 As[GBM][GLDK];
+  __shared__ f16 Bs[GBN][GLDK];
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  // skip tiles whose rows all belong to sequences on the other route
+  {
+    const int mlast = min(g.M, m0 + GBM) - 1;
+    bool any = false;
+    for (int sq = m0 / g.P; sq <= mlast / g.P; ++sq) any |= (g.seq_route[sq] == g.want_route);
+    if (!any) return;
+  }
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  const int64_t rb4 = w4_row_bytes(g.K), rs4 = w4_row_scales(g.K, g.group);
+  const int lr = tid / 2, lh = tid % 2;  // loader: row lr, half lh of the k-tile
+
+  for (int k0 = 0; k0 < g.K; k0 += GBK) {
+    // ---- global -> registers
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+    {
+      const int m = m0 + lr, k = k0 + lh * 16;
+      if (m < g.M) {
+        const f16* src = g.A + (size_t)m * g.K;
+        if (k < g.K) a0 = *(const uint4*)(src + k);
+        if (k + 8 < g.K) a1 = *(const uint4*)(src + k + 8);
+      }
+    }
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
+    uint2 bq = make_uint2(0x88888888u, 0x88888888u);
+    {
+      const int n = n0 + lr, k = k0 + lh * 16;
+      if (n < g.N) {
+        if (MODE == 0) {
+          int si = 0;
+          while (si < 2 && n >= g.seg_start[si + 1]) ++si;
+          const f16* src = g.seg_ptr[si] + (size_t)(n - g.seg_start[si]) * g.K;
+          if (k < g.K) b0 = *(const uint4*)(src + k);
+          if (k + 8 < g.K) b1 = *(const uint4*)(src + k + 8);
+        } else {
+          bq = *(const uint2*)(g.w4 + (size_t)n * rb4 + k / 2);
+        }
+      }
+    }
+    __syncthreads();
+    *(uint4*)&As[lr][lh * 16] = a0;
+    *(uint4*)&As[lr][lh * 16 + 8] = a1;
+    if (MODE == 0) {
+      *(uint4*)&Bs[lr][lh * 16] = b0;
+      *(uint4*)&Bs[lr][lh * 16 + 8] = b1;
+    } else {
+      const uint32_t wd[2] = {bq.x, bq.y};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        h2 p0, p1, p2, p3;
+        unpack8(wd[h], p0, p1, p2, p3);  // pairs (q0,q4),(q1,q5),(q2,q6),(q3,q7)
+        f16* dst = &Bs[lr][lh * 16 + h * 8];
+        dst[0] = p0.x; dst[4] = p0.y;
+        dst[1] = p1.x; dst[5] = p1.y;
+        dst[2] = p2.x; dst[6] = p2.y;
+        dst[3] = p3.x; dst[7] = p3.y;
+      }
+    }
+    __syncthreads();
+    // ---- MFMA over the k-tile
+    f4 tmp[4][4];
+    if (MODE == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tmp[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < GBK; kk += 16) {
+      h4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const h4*)&As[wm + i * 16 + lane % 16][kk + 4 * (lane / 16)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *(const h4*)&Bs[wn + j * 16 + lane % 16][kk + 4 * (lane / 16)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (MODE == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          else
+            tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], tmp[i][j], 0, 0, 0);
+        }
+    }
+    if (MODE == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn + j * 16 + lane % 16;
+        const float s = (n < g.N) ? h2f(g.s4[(size_t)n * rs4 + k0 / g.group]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] += s * tmp[i][j];
+      }
+    }
+  }
+  // ---- epilogue: D[i][j] at row 4*(lane/16)+r, column lane%16 of each 16x16 block
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + lane % 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + i * 16 + 4 * (lane / 16) + r;
+        if (m < g.M && n < g.N && g.seq_route[m / g.P] == g.want_route) {
+          const f16 v = f2h(acc[i][j][r]);
+          if (g.epi == EPI_STORE)
+            g.C[(size_t)m * g.N + n] = v;
+          else
+            g.C[(size_t)m * g.N + n] = f2h(h2f(g.R[(size_t)m * g.N + n]) + h2f(v));
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Elementwise prefill kernels (one workgroup per row unless stated)
+// ---------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_pf_embed(PfArgs p) {
+  const int m = blockIdx.x;
+  int tok = p.tokens[m];
+  if (tok < 0 || tok >= p.dm.V) {
+    if (threadIdx.x == 0) atomicOr(p.err, ERR_TOKEN);
+    tok = 0;
+  }
+  const f16* src = p.embed + (size_t)tok * p.dm.d;
+  for (int i = threadIdx.x; i < p.dm.d; i += kBlock) p.hin[(size_t)m * p.dm.d + i] = src[i];
+}
+
+// out[m] = fp16(x[m] / sqrt(mean(x[m]^2) + eps) * w)
+__global__ __launch_bounds__(kBlock) void k_pf_rmsnorm(const f16* x, const f16* w, f16* out, int n,
+                                                       float eps) {
+  __shared__ double red[4];
+  const int m = blockIdx.x;
+  const f16* xr = x + (size_t)m * n;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += kBlock) {
+    const double v = (double)h2f(xr[i]);
+    s += v * v;
+  }
+  s = block_sum_d(s, red);
+  const float inv = (float)(1.0 / sqrt(s / n + (double)eps));
+  for (int i = threadIdx.x; i < n; i += kBlock)
+    out[(size_t)m * n + i] = f2h(h2f(xr[i]) * inv * h2f(w[i]));
+}
+
+// RoPE on q and k rows of qkv; q -> act [M][H*D]; k, v -> shared cache at (layer, b, kvh, t).
+__global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
+  const Dims& dm = p.dm;
+  const int m = blockIdx.x;
+  const int b = m / p.P, t = m % p.P;
+  const f16* row = p.qkv + (size_t)m * dm.nqkv;
+  const int half = dm.D / 2;
+  const int npairs = (dm.H + dm.Hkv) * half;
+  for (int idx = threadIdx.x; idx < npairs; idx += kBlock) {
+    const int head = idx / half, i = idx % half;
+    const float x0 = h2f(row[head * dm.D + i]), x1 = h2f(row[head * dm.D + i + half]);
+    const float2 cs = p.rope[(size_t)t * half + i];
+    const f16 r0 = f2h(x0 * cs.x - x1 * cs.y), r1 = f2h(x1 * cs.x + x0 * cs.y);
+    if (head < dm.H) {
+      f16* qd = p.act + (size_t)m * dm.hd + head * dm.D;
+      qd[i] = r0;
+      qd[i + half] = r1;
+    } else {
+      const int kvh = head - dm.H;
+      f16* kd = p.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) *
+                           (size_t)dm.Tmax * dm.D + (size_t)t * dm.D;
+      kd[i] = r0;
+      kd[i + half] = r1;
+    }
+  }
+  const int nv = dm.Hkv * dm.D;
+  for (int idx = threadIdx.x; idx < nv; idx += kBlock) {
+    const int kvh = idx / dm.D, i = idx % dm.D;
+    f16* vd = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) *
+                         (size_t)dm.Tmax * dm.D + (size_t)t * dm.D;
+    vd[i] = row[(dm.H + dm.Hkv) * dm.D + idx];
+  }
+}
+
+// Causal attention. Workgroup = (query block, kv head, sequence). 16 lanes per (query, head);
+// QB = 16/G queries x G heads per workgroup; K/V tiles of 64 positions staged in LDS.
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void k_pf_attn(PfArgs p, int layer) {
+  constexpr int QB = 16 / G;
+  constexpr int DPT = D / 16;  // dims per lane
+  constexpr int KT = 64;
+  __shared__ f16 Ks[KT][D];
+  __shared__ f16 Vs[KT][D];
+  const Dims& dm = p.dm;
+  const int qb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int slot = tid / 16, sub = tid % 16;  // slot -> (query, head)
+  const int qi = slot / G, g = slot % G;
+  const int t = qb * QB + qi;  // query position
+  const int h = kvh * G + g;
+  const bool valid = t < p.P;
+  const size_t hs = (size_t)dm.Tmax * D;
+  const f16* Kb = p.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * hs;
+  const f16* Vb = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * hs;
+  const float qs = 1.4426950408889634f / sqrtf((float)D);
+  float qf[DPT], acc[DPT];
+  const int m = b * p.P + (valid ? t : 0);
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    qf[i] = h2f(p.act[(size_t)m * dm.hd + h * D + sub * DPT + i]) * qs;
+    acc[i] = 0.f;
+  }
+  float mx = -__builtin_inff(), l = 0.f;
+  const int tmax_blk = min(p.P - 1, qb * QB + QB - 1);  // last position any query needs
+  for (int k0 = 0; k0 <= tmax_blk; k0 += KT) {
+    __syncthreads();
+    for (int idx = tid; idx < KT * D / 8; idx += kBlock) {
+      const int r = idx / (D / 8), c = (idx % (D / 8)) * 8;
+      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      if (k0 + r < p.P) {
+        kv4 = *(const uint4*)(Kb + (size_t)(k0 + r) * D + c);
+        vv4 = *(const uint4*)(Vb + (size_t)(k0 + r) * D + c);
+      }
+      *(uint4*)&Ks[r][c] = kv4;
+      *(uint4*)&Vs[r][c] = vv4;
+    }
+    __syncthreads();
+    const int kend = min(KT, (valid ? t : -1) - k0 + 1);
+    for (int j = 0; j < kend; ++j) {
+      float sc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) sc = fmaf(qf[i], h2f(Ks[j][sub * DPT + i]), sc);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sc += __shfl_xor(sc, o, kWave);
+      const float mn = fmaxf(mx, sc);
+      const float c = exp2f(mx - mn), pj = exp2f(sc - mn);
+      l = l * c + pj;
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(acc[i], c, pj * h2f(Vs[j][sub * DPT + i]));
+      mx = mn;
+    }
+  }
+  if (valid) {
+    f16* o = p.hout + (size_t)m * dm.hd + h * D;  // attention output goes to hout (scratch)
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) o[sub * DPT + i] = f2h(acc[i] / l);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_pf_swiglu(PfArgs p) {
+  const int m = blockIdx.x;
+  const int F = p.dm.F;
+  const f16* row = p.gu + (size_t)m * 2 * F;
+  for (int f = threadIdx.x; f < F; f += kBlock) {
+    const float g = h2f(row[f]), u = h2f(row[F + f]);
+    p.a2[(size_t)m * F + f] = f2h(g / (1.f + __expf(-g)) * u);
+  }
+}
+
+// s_m = cos(hin[m], hout[m]) in fp64
+__global__ __launch_bounds__(kBlock) void k_pf_cos(PfArgs p) {
+  __shared__ double red[4];
+  const int m = blockIdx.x;
+  const int d = p.dm.d;
+  double s0 = 0, s1 = 0, s2 = 0;
+  for (int i = threadIdx.x; i < d; i += kBlock) {
+    const double a = h2f(p.hin[(size_t)m * d + i]), c = h2f(p.hout[(size_t)m * d + i]);
+    s0 += a * c;
+    s1 += a * a;
+    s2 += c * c;
+  }
+  s0 = block_sum_d(s0, red);
+  s1 = block_sum_d(s1, red);
+  s2 = block_sum_d(s2, red);
+  if (threadIdx.x == 0) p.cosv[m] = (s1 > 0 && s2 > 0) ? s0 / sqrt(s1 * s2) : 0.0;
+}
+
+// Sequence-level exit after backbone layer `layer`. One workgroup per sequence.
+__global__ __launch_bounds__(kBlock) void k_pf_decide(PfArgs p, int layer, int forced, float tau) {
+  __shared__ double red[kBlock];
+  const int b = blockIdx.x;
+  const Dims& dm = p.dm;
+  double mn = 1e300;
+  for (int t = threadIdx.x; t < p.P; t += kBlock) mn = fmin(mn, p.cosv[(size_t)b * p.P + t]);
+  red[threadIdx.x] = mn;
+  __syncthreads();
+  for (int s = kBlock / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmin(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && layer < dm.L && p.seq_route[b] == ROUTE_BACKBONE) {
+    bool ex;
+    if (forced > 0) {
+      ex = (layer == forced);
+    } else if (layer >= dm.entry) {
+      const double s = red[0];
+      if (p.min_sim) p.min_sim[(size_t)b * dm.L + layer - 1] = (float)s;
+      ex = s > (double)tau;
+    } else {
+      ex = false;
+    }
+    if (ex) {
+      p.seq_route[b] = ROUTE_RIVER;
+      p.seq_exit[b] = layer;
+    }
+  }
+}
+
+// Hand the last prompt position of each row to the decode LM head: hs[L][b] = hout[b*P+P-1],
+// inv_attn[L][b], pos[b] = P-1 (the LM head's last arriver advances it to P), step = 0.
+__global__ __launch_bounds__(kBlock) void k_pf_finish(PfArgs p, DecodeArgs a) {
+  __shared__ double red[4];
+  const int b = blockIdx.x;
+  const Dims& dm = p.dm;
+  const f16* src = p.hin + ((size_t)b * p.P + p.P - 1) * dm.d;  // after the final swap
+  f16* dst = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < dm.d; i += kBlock) {
+    dst[i] = src[i];
+    const double v = h2f(src[i]);
+    s += v * v;
+  }
+  s = block_sum_d(s, red);
+  if (threadIdx.x == 0) {
+    a.inv_attn[dm.L * dm.B + b] = (float)(1.0 / sqrt(s / dm.d + (double)dm.eps));
+    a.pos[b] = p.P - 1;
+    if (b == 0) *a.step = 0;
+  }
+}
+
+__global__ void k_pf_init_routes(PfArgs p) {
+  const int b = threadIdx.x;
+  if (b < p.dm.B) {
+    p.seq_route[b] = ROUTE_BACKBONE;
+    p.seq_exit[b] = p.dm.L;
+    if (p.min_sim)
+      for (int l = 0; l < p.dm.L; ++l) p.min_sim[(size_t)b * p.dm.L + l] = __builtin_nanf("");
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+static hipError_t gemm(const PfGemmArgs& g0, const LayerDev& lw, int which, hipStream_t st) {
+  // which: 0 qkv, 1 o, 2 gu, 3 down. Launch the fp16 and the int4 variant; each skips the
+  // tiles whose sequences are on the other route.
+  dim3 grid((g0.N + GBN - 1) / GBN, (g0.M + GBM - 1) / GBM);
+  PfGemmArgs g = g0;
+  g.want_route = ROUTE_BACKBONE;
+  hipLaunchKernelGGL(k_pf_gemm<0>, grid, dim3(kBlock), 0, st, g);
+  g.want_route = ROUTE_RIVER;
+  hipLaunchKernelGGL(k_pf_gemm<1>, grid, dim3(kBlock), 0, st, g);
+  (void)lw;
+  (void)which;
+  return hipGetLastError();
+}
+
+hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const LayerDev* host_layers,
+                                int forced, float tau, hipStream_t st) {
+  const Dims& dm = p.dm;
+  const int M = p.M;
+  hipError_t e;
+  hipLaunchKernelGGL(k_pf_init_routes, dim3(1), dim3(64), 0, st, p);
+  hipLaunchKernelGGL(k_pf_embed, dim3(M), dim3(kBlock), 0, st, p);
+  PfArgs q = p;  // hin/hout swap per layer
+  for (int l = 1; l <= dm.L; ++l) {
+    const LayerDev& lw = host_layers[l - 1];
+    // attention half
+    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(M), dim3(kBlock), 0, st, (const f16*)q.hin, lw.attn_norm,
+                       q.act, dm.d, dm.eps);
+    PfGemmArgs g{};
+    g.M = M;
+    g.group = dm.group;
+    g.seq_route = q.seq_route;
+    g.P = q.P;
+    g.A = q.act;
+    g.N = dm.nqkv;
+    g.K = dm.d;
+    g.seg_ptr[0] = lw.wq;
+    g.seg_ptr[1] = lw.wk;
+    g.seg_ptr[2] = lw.wv;
+    g.seg_start[0] = 0;
+    g.seg_start[1] = dm.hd;
+    g.seg_start[2] = dm.hd + dm.Hkv * dm.D;
+    g.seg_start[3] = dm.nqkv;
+    g.w4 = lw.r_qkv;
+    g.s4 = lw.s_qkv;
+    g.C = q.qkv;
+    g.epi = EPI_STORE;
+    if ((e = gemm(g, lw, 0, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_pf_rope_kv, dim3(M), dim3(kBlock), 0, st, q, l);
+    {
+      const int G = dm.H / dm.Hkv;
+      const int QB = 16 / G;
+      dim3 grid((q.P + QB - 1) / QB, dm.Hkv, dm.B);
+      if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_attn<128, 4>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_attn<64, 4>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_attn<64, 2>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_attn<128, 2>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_attn<128, 1>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_attn<64, 1>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_attn<128, 8>), grid, dim3(kBlock), 0, st, q, l);
+      else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_attn<64, 8>), grid, dim3(kBlock), 0, st, q, l);
+      else return hipErrorInvalidValue;
+    }
+    // O projection + residual: attention output sits in hout
+    g.A = q.hout;
+    g.N = dm.d;
+    g.K = dm.hd;
+    g.seg_ptr[0] = lw.wo;
+    g.seg_start[0] = 0;
+    g.seg_start[1] = dm.d;
+    g.seg_start[2] = dm.d;
+    g.seg_start[3] = dm.d;
+    g.w4 = lw.r_o;
+    g.s4 = lw.s_o;
+    g.C = q.hmid;
+    g.R = q.hin;
+    g.epi = EPI_RESID;
+    if ((e = gemm(g, lw, 1, st)) != hipSuccess) return e;
+    // MLP half
+    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(M), dim3(kBlock), 0, st, (const f16*)q.hmid, lw.mlp_norm,
+                       q.act, dm.d, dm.eps);
+    g.A = q.act;
+    g.N = 2 * dm.F;
+    g.K = dm.d;
+    g.seg_ptr[0] = lw.wg;
+    g.seg_ptr[1] = lw.wu;
+    g.seg_start[0] = 0;
+    g.seg_start[1] = dm.F;
+    g.seg_start[2] = 2 * dm.F;
+    g.seg_start[3] = 2 * dm.F;
+    g.w4 = lw.r_gu;
+    g.s4 = lw.s_gu;
+    g.C = q.gu;
+    g.R = nullptr;
+    g.epi = EPI_STORE;
+    if ((e = gemm(g, lw, 2, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_pf_swiglu, dim3(M), dim3(kBlock), 0, st, q);
+    g.A = q.a2;
+    g.N = dm.d;
+    g.K = dm.F;
+    g.seg_ptr[0] = lw.wd;
+    g.seg_start[0] = 0;
+    g.seg_start[1] = dm.d;
+    g.seg_start[2] = dm.d;
+    g.seg_start[3] = dm.d;
+    g.w4 = lw.r_d;
+    g.s4 = lw.s_d;
+    g.C = q.hout;
+    g.R = q.hmid;
+    g.epi = EPI_RESID;
+    if ((e = gemm(g, lw, 3, st)) != hipSuccess) return e;
+    // sequence-level exit decision after this layer
+    if (l < dm.L) {
+      hipLaunchKernelGGL(k_pf_cos, dim3(M), dim3(kBlock), 0, st, q);
+      hipLaunchKernelGGL(k_pf_decide, dim3(dm.B), dim3(kBlock), 0, st, q, l, forced, tau);
+    }
+    f16* t = q.hin;
+    q.hin = q.hout;
+    q.hout = t;
+  }
+  hipLaunchKernelGGL(k_pf_finish, dim3(dm.B), dim3(kBlock), 0, st, q, a);
+  return hipGetLastError();
+}
