@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Decode throughput of River-LLM token-level early exit on one MI355X.
+
+Workload (default): Llama-3.1-8B-shaped decoder with random fp16 weights and its int4
+(group 128) river copy, batch 1, a 2048-token random prompt prefilled at full depth, then
+--steps decode tokens with forced exit layers drawn uniformly from {8..20} (mean 14).
+A step is one decode token through all 32 layers (backbone up to the exit layer, river
+after it) and the LM head; the timed region replays the captured step graph --steps times
+with inputs resident in HBM.
+
+Also measured in the same run:
+  * per-launch HIP-event timing of every decode kernel (one timed pass per kernel) -> the
+    roofline of the dominant kernel (gate|up + SwiGLU GEMV) and a per-kernel breakdown;
+  * the full-depth fp16 decode (backbone only, no exit test) over the same positions;
+  * the CPU oracle on a bounded sample (one backbone layer, one river layer and the LM head,
+    scaled to a token by the realized mean exit layer).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="llama3.1-8b-shape")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-full", action="store_true", help="skip the full-depth fp16 decode")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip per-kernel timing passes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from token_level_early_amd import bytes_model as bm
+    from token_level_early_amd import configs, river, synth
+
+    cfgd = configs.ALL[args.config]
+    c = configs.model_cfg(cfgd)
+    B, P, S, W = cfgd["batch"], cfgd["prompt"], args.steps, args.warmup
+    L = c["L"]
+    if B != 1:
+        raise SystemExit("the VALU decode path runs batch 1; batched configs are parity cases")
+    dev = "cuda"
+    t0 = time.time()
+    w = synth.weights(c, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    Tmax = P + W + S
+    rv = river.River(c, w, max_seq=Tmax, max_prefill=P, batch=B)
+    torch.cuda.synchronize()
+    log(f"river built in {time.time() - t0:.1f}s")
+    toks = synth.prompt(c, B, P, seed=args.seed, device=dev)
+    sched_np = synth.schedule(cfgd, W + S, B, seed=args.seed)
+    sched = torch.from_numpy(sched_np).to(dev)
+
+    def prefill_and_warm(backbone=False):
+        pre = rv.prefill(toks, prefill_exit=L)
+        if backbone:
+            out = rv.decode_backbone_steps(pre["tokens"], W)
+        else:
+            out = rv.decode_steps(pre["tokens"], sched=sched[:W].contiguous())
+        torch.cuda.synchronize()
+        return out[-1].clone()
+
+    tp = time.time()
+    tok = prefill_and_warm()
+    log(f"prefill {P} + warmup {W} in {time.time() - tp:.2f}s")
+
+    # ---- timed region: S early-exit decode steps (graph replay)
+    ex = torch.empty(S, B, dtype=torch.int32, device=dev)
+    tok_out = torch.empty(S, B, dtype=torch.int32, device=dev)
+    st_sched = sched[W:].contiguous()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    rv.decode_steps(tok, sched=st_sched, tok_out=tok_out, exit_layer=ex)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    exits = ex.cpu().numpy()[:, 0]
+    assert np.array_equal(exits, sched_np[W:, 0]), "realized exit layers differ from the schedule"
+    positions = [P + W + s for s in range(S)]
+    bytes_total = sum(bm.token_bytes(c, int(e), p) for e, p in zip(exits, positions))
+    tok_s = S * B / (ms / 1e3)
+    step_gbs = bytes_total / (ms / 1e3) / 1e9
+    log(f"early exit: {S} steps in {ms:.2f} ms -> {tok_s:.1f} tok/s, {step_gbs:.0f} GB/s "
+        f"({100 * step_gbs / HBM_PEAK_GBS:.1f}% of HBM peak), mean exit {exits.mean():.2f}")
+
+    # ---- per-kernel timing passes (direct launches, HIP events around each launch)
+    kernels = {}
+    if not args.no_breakdown:
+        for op in ("gu", "down", "qkv", "o", "attn", "lm"):
+            tok = prefill_and_warm()
+            per_step = 1 if op == "lm" else L
+            rv.timer_arm(op, S * per_step)
+            rv.decode_steps(tok, sched=st_sched, tok_out=tok_out, exit_layer=ex)
+            durs = np.array(rv.timer_read(S * per_step))
+            tot_b = 0
+            for s in range(S):
+                e = int(exits[s])
+                for l in range(1, per_step + 1):
+                    if op == "lm":
+                        tot_b += bm.op_bytes(c, "lm")
+                    elif op == "attn":
+                        tot_b += bm.op_bytes(c, "attn", pos=positions[s])
+                    else:
+                        tot_b += bm.op_bytes(c, op, river=l > e)
+            n = len(durs)
+            avg_us = 1e3 * durs.mean()
+            gbs = (tot_b / n) / (avg_us * 1e-6) / 1e9
+            kernels[op] = {"launches": n, "avg_us": round(avg_us, 3),
+                           "bytes_per_launch": int(tot_b / n), "GB/s": round(gbs, 1),
+                           "frac": round(gbs / HBM_PEAK_GBS, 4),
+                           "share_of_step": round(durs.sum() / ms, 4)}
+            log(f"  {op:5s} avg {avg_us:8.2f} us  {gbs:7.0f} GB/s  share {durs.sum() / ms:.3f}")
+
+    # ---- full-depth fp16 decode over the same positions
+    full = None
+    if not args.no_full:
+        tok = prefill_and_warm(backbone=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        rv.decode_backbone_steps(tok, S, tok_out=tok_out)
+        ev1.record()
+        torch.cuda.synchronize()
+        fms = ev0.elapsed_time(ev1)
+        fbytes = sum(bm.token_bytes(c, L, p) for p in positions)
+        full = {"tokens_per_s": round(S * B / (fms / 1e3), 2), "ms_per_step": round(fms / S, 4),
+                "GB/s": round(fbytes / (fms / 1e3) / 1e9, 1),
+                "frac": round(fbytes / (fms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "speedup_of_early_exit": round(fms / ms, 4)}
+        log(f"full depth: {full}")
+
+    # ---- CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(c, w, rv, exits, positions, log)
+        log(f"cpu oracle: {cpu}")
+    rv.close()
+
+    dom = kernels.get("gu")
+    roof = None
+    if dom:
+        roof = {"kernel": "k_dec_gemv<OP_GU,...> (gate|up GEMV + SwiGLU, early-exit mode)",
+                "bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom["frac"], "traffic": None,
+                "avg_launch_us": dom["avg_us"], "bytes_per_launch": dom["bytes_per_launch"]}
+    out = {
+        "metric": "decode tokens/s at 8B shape (bs=1,ctx 2048) at fixed exit schedule; % HBM roofline",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(ms / S, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 activations, fp16/int4 weights, fp32 accumulate",
+        "data": "synthetic (seeded random weights, prompt and exit schedule)",
+        "config": {"workload": f"{args.config} decode, batch {B}, prompt {P}, "
+                               f"forced exit e~U{{8..20}} (realized mean {exits.mean():.2f})",
+                   "batch": B, "prompt": P, "decode_steps": S, "positions": [P + W, P + W + S - 1]},
+        "hbm_roofline_pct": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "step": {"bytes_per_token": int(bytes_total / S), "achieved_GB/s": round(step_gbs, 1),
+                 "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "kernels": kernels,
+        "full_depth_fp16": full,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(c, w, rv, exits, positions, log):
+    """Times the CPU oracle (fp64 NumPy) on one backbone layer, one river layer and the LM head
+    at the bench's context length, and scales to ms per decode token with the realized mean
+    exit layer: t_tok = e*t_backbone + (L-e)*t_river + t_head."""
+    import torch
+
+    from oracle import river_oracle as O
+    from token_level_early_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    L = c["L"]
+    lay = [0, 1]
+    host = synth.to_numpy({"embed": w["embed"], "lm_head": w["lm_head"], "final_norm": w["final_norm"],
+                           "layers": [w["layers"][i] if i in lay else None for i in range(L)]})
+    orc = O.RiverOracle(c, host, layers=lay)
+    kv = rv.kv_view()
+    pos = positions[0]
+    Kc = [kv[l, 0, 0, :, : pos + 1].cpu().numpy().copy() for l in lay]
+    Vc = [kv[l, 1, 0, :, : pos + 1].cpu().numpy().copy() for l in lay]
+    h = rv.hidden()[0, 0].cpu().numpy()
+
+    def timed(fn, reps):
+        fn()  # first call pays one-time conversions
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t) / reps
+
+    reps = 3
+    t_bb = timed(lambda: O.block_decode(c, orc.bb[0], orc.norms(0), h, pos, Kc[0], Vc[0]), reps)
+    t_rv = timed(lambda: O.block_decode(c, orc.rv[1], orc.norms(1), h, pos, Kc[1], Vc[1]), reps)
+    t_hd = timed(lambda: orc.head_logits(h), reps)
+    e = float(np.mean(exits))
+    ms_tok = 1e3 * (e * t_bb + (L - e) * t_rv + t_hd)
+    return {"value": round(1e3 / ms_tok, 4), "unit": "tokens/s", "ms_per_token": round(ms_tok, 2),
+            "cores": threads, "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle: backbone block (layer 1), river block (layer 2) and LM "
+                      f"head at position {pos}, {reps} reps each after one untimed call; token "
+                      f"time = e*t_bb + (L-e)*t_river + t_head with realized mean e={e:.2f}"}
+
+
+if __name__ == "__main__":
+    main()

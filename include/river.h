@@ -27,9 +27,10 @@
  *   - Every call returns an int status (RIVER_OK or a negative code). river_last_error()
  *     returns a message for the calling thread's last failure. No C++ exception crosses
  *     the ABI.
- *   - The library allocates only its opaque host handle, a small pinned host status word
- *     and HIP graph objects. Every device buffer (KV cache, river weights, scratch) is
- *     allocated by the caller with the sizes these functions report.
+ *   - The library allocates only host-side objects: its opaque handle, a capture stream, HIP
+ *     graphs of the decode step and (when armed) timing events. Every device buffer (KV
+ *     cache, river weights, scratch) is allocated by the caller with the sizes these
+ *     functions report.
  *   - Calls on one context must not overlap (they share its scratch buffer).
  */
 #ifndef RIVER_H
@@ -121,7 +122,7 @@ int river_workspace_bytes(const river_config* cfg, uint64_t* river_bytes /* host
 int river_init(const river_config* cfg, const river_weights* w /* host struct */, void* kv,
                void* river_buf, void* scratch, void* stream, river_ctx** out /* host */);
 
-/* Frees the host handle, its pinned status word and its graphs. Device buffers are the
+/* Frees the host handle, its stream, graphs and events. Device buffers are the
  * caller's. Synchronises the device. NULL is accepted. */
 int river_destroy(river_ctx* ctx);
 
@@ -169,6 +170,21 @@ int river_decode_step(river_ctx* ctx, const int32_t* tok_in, const int32_t* forc
 int river_decode_steps(river_ctx* ctx, const int32_t* tok_in, const int32_t* sched, int32_t S,
                        float tau, int32_t* tok_out, int32_t* exit_layer, float* sim,
                        void* stream);
+
+/* Full-depth fp16 decode of S steps: every layer on the backbone block, no exit test, no river
+ * (the plain decoder the early exit is measured against). Same token I/O as river_decode_steps
+ * with every forced exit = L; writes the same KV slots. Errors as river_decode_steps. */
+int river_decode_backbone_steps(river_ctx* ctx, const int32_t* tok_in, int32_t S, int32_t* tok_out,
+                                void* stream);
+
+/* Benchmark support: per-launch timing of one kernel of the decode step with HIP events on the
+ * call's stream. op: 0 QKV, 1 attention, 2 O projection, 3 gate|up, 4 down, 5 LM head. While
+ * armed, decode calls enqueue their kernels directly (no graph replay) and record an event pair
+ * around each launch of `op`, up to max_launches pairs. river_timer_read waits for the last
+ * event, writes the durations (ms) of up to *n launches in launch order, sets *n to the count
+ * and disarms. */
+int river_timer_arm(river_ctx* ctx, int32_t op, int32_t max_launches);
+int river_timer_read(river_ctx* ctx, float* ms /* host */, int32_t* n /* host, in/out */);
 
 /* Host mirror of the rows' positions (number of filled KV slots per row). */
 int river_positions(const river_ctx* ctx, int32_t* pos /* host [B] */);

@@ -12,9 +12,12 @@
 #include "params.hpp"
 
 // kernels (decode.hip, quant.hip, prefill.hip)
-hipError_t river_decode_layers(const DecodeArgs& a, hipStream_t st);
-hipError_t river_launch_gemv(const DecodeArgs& a, int op, int layer, hipStream_t st);
+hipError_t river_decode_layers(const DecodeArgs& a, int mode, hipStream_t st,
+                               void (*timer)(void*, int, int), void* tctx, int top);
+hipError_t river_launch_gemv(const DecodeArgs& a, int op, int layer, int mode, hipStream_t st);
 hipError_t river_launch_begin(const DecodeArgs& a, hipStream_t st);
+hipError_t river_launch_head(const DecodeArgs& a, hipStream_t st, void (*timer)(void*, int, int),
+                             void* tctx, int top);
 int river_gemv_max_wg(const Dims& dm);
 hipError_t river_launch_quantize(const f16* W, int N, int K, int group, uint8_t* out, f16* scales,
                                  hipStream_t st);
@@ -199,11 +202,19 @@ struct river_ctx {
   const f16* final_norm;
   std::vector<int32_t> pos_host;
   hipStream_t cap_stream;
-  hipGraph_t graph;
-  hipGraphExec_t exec;
-  bool graph_valid;
-  DecodeArgs graph_key;
+  struct Cached {
+    bool valid = false;
+    DecodeArgs key{};
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+  } graphs[2];  // [mode]: 0 early exit, 1 backbone only
   bool use_graph;
+  // per-launch timing of one op (river_timer_arm)
+  int timer_op = -1;
+  int timer_cap = 0;
+  int timer_n = 0;
+  hipStream_t timer_stream = nullptr;
+  std::vector<hipEvent_t> timer_ev;
 };
 
 static DecodeArgs base_args(const river_ctx* c) {
@@ -294,9 +305,6 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   c->lm_head = (const f16*)(cfg->tied_embeddings ? w->embed : w->lm_head);
   c->final_norm = (const f16*)w->final_norm;
   c->pos_host.assign(cfg->max_batch, 0);
-  c->graph_valid = false;
-  c->graph = nullptr;
-  c->exec = nullptr;
   const char* ng = getenv("RIVER_NO_GRAPH");
   c->use_graph = !(ng && ng[0] == '1');
   hipError_t e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
@@ -372,8 +380,11 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
 int river_destroy(river_ctx* c) {
   if (!c) return RIVER_OK;
   (void)hipDeviceSynchronize();
-  if (c->exec) (void)hipGraphExecDestroy(c->exec);
-  if (c->graph) (void)hipGraphDestroy(c->graph);
+  for (auto& g : c->graphs) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+  }
+  for (hipEvent_t ev : c->timer_ev) (void)hipEventDestroy(ev);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   delete c;
   return RIVER_OK;
@@ -437,7 +448,7 @@ int river_prefill(river_ctx* c, const int32_t* tokens, int32_t P, int32_t prefil
   a.logits = logits;
   hipError_t e = river_launch_prefill(p, a, c->layers.data(), prefill_exit, tau, st);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  e = river_launch_gemv(a, OP_LM, d.L + 1, st);
+  e = river_launch_head(a, st, nullptr, nullptr, -1);
   if (e != hipSuccess) return hip_fail(e, "prefill LM head launch");
   if (seq_exit) {
     e = hipMemcpyAsync(seq_exit, p.seq_exit, (size_t)d.B * 4, hipMemcpyDeviceToDevice, st);
@@ -453,33 +464,50 @@ static bool same_key(const DecodeArgs& x, const DecodeArgs& y) {
          std::memcmp(&x.tau, &y.tau, sizeof(float)) == 0;
 }
 
-static int run_steps(river_ctx* c, const DecodeArgs& a, int S, hipStream_t st) {
+static void timer_hook(void* p, int op, int phase) {
+  river_ctx* c = (river_ctx*)p;
+  (void)op;
+  if (c->timer_n >= c->timer_cap) return;
+  (void)hipEventRecord(c->timer_ev[2 * c->timer_n + phase], c->timer_stream);
+  if (phase == 1) ++c->timer_n;
+}
+
+static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
   hipError_t e = river_launch_begin(a, st);
   if (e != hipSuccess) return hip_fail(e, "begin launch");
-  if (!c->use_graph) {
+  if (c->timer_op >= 0) {  // timed: direct launches with events around the chosen op
+    c->timer_stream = st;
     for (int i = 0; i < S; ++i)
-      if ((e = river_decode_layers(a, st)) != hipSuccess) return hip_fail(e, "decode launch");
+      if ((e = river_decode_layers(a, mode, st, timer_hook, c, c->timer_op)) != hipSuccess)
+        return hip_fail(e, "decode launch");
     return RIVER_OK;
   }
-  if (!c->graph_valid || !same_key(a, c->graph_key)) {
-    if (c->exec) (void)hipGraphExecDestroy(c->exec);
-    if (c->graph) (void)hipGraphDestroy(c->graph);
-    c->exec = nullptr;
-    c->graph = nullptr;
-    c->graph_valid = false;
+  if (!c->use_graph) {
+    for (int i = 0; i < S; ++i)
+      if ((e = river_decode_layers(a, mode, st, nullptr, nullptr, -1)) != hipSuccess)
+        return hip_fail(e, "decode launch");
+    return RIVER_OK;
+  }
+  river_ctx::Cached& g = c->graphs[mode];
+  if (!g.valid || !same_key(a, g.key)) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+    g.exec = nullptr;
+    g.graph = nullptr;
+    g.valid = false;
     e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-    hipError_t le = river_decode_layers(a, c->cap_stream);
-    e = hipStreamEndCapture(c->cap_stream, &c->graph);
+    hipError_t le = river_decode_layers(a, mode, c->cap_stream, nullptr, nullptr, -1);
+    e = hipStreamEndCapture(c->cap_stream, &g.graph);
     if (le != hipSuccess) return hip_fail(le, "decode capture");
     if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
-    e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
+    e = hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0);
     if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
-    c->graph_key = a;
-    c->graph_valid = true;
+    g.key = a;
+    g.valid = true;
   }
   for (int i = 0; i < S; ++i)
-    if ((e = hipGraphLaunch(c->exec, st)) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    if ((e = hipGraphLaunch(g.exec, st)) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
   return RIVER_OK;
 }
 
@@ -498,9 +526,58 @@ int river_decode_steps(river_ctx* c, const int32_t* tok_in, const int32_t* sched
   a.sim_out = sim;
   a.logits = nullptr;
   a.tau = sched ? 0.f : tau;
-  int rc = run_steps(c, a, S, (hipStream_t)stream);
+  int rc = run_steps(c, a, S, 0, (hipStream_t)stream);
   if (rc) return rc;
   for (auto& v : c->pos_host) v += S;
+  return RIVER_OK;
+}
+
+int river_decode_backbone_steps(river_ctx* c, const int32_t* tok_in, int32_t S, int32_t* tok_out,
+                                void* stream) {
+  if (!c || !tok_in || !tok_out) return fail(RIVER_EINVAL, "NULL argument");
+  if (S < 1) return fail(RIVER_EINVAL, "S must be >= 1");
+  for (int32_t p : c->pos_host)
+    if ((int64_t)p + S > c->dm.Tmax) return fail(RIVER_ERANGE, "position would pass max_seq");
+  DecodeArgs a = base_args(c);
+  a.tok_in = tok_in;
+  a.tok_out = tok_out;
+  int rc = run_steps(c, a, S, 1, (hipStream_t)stream);
+  if (rc) return rc;
+  for (auto& v : c->pos_host) v += S;
+  return RIVER_OK;
+}
+
+int river_timer_arm(river_ctx* c, int32_t op, int32_t max_launches) {
+  if (!c) return fail(RIVER_EINVAL, "ctx is NULL");
+  if (op < TOP_QKV || op > TOP_LM) return fail(RIVER_EINVAL, "op must be in [0, 5]");
+  if (max_launches < 1) return fail(RIVER_EINVAL, "max_launches must be >= 1");
+  while ((int)c->timer_ev.size() < 2 * max_launches) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    c->timer_ev.push_back(ev);
+  }
+  c->timer_op = op;
+  c->timer_cap = max_launches;
+  c->timer_n = 0;
+  return RIVER_OK;
+}
+
+int river_timer_read(river_ctx* c, float* ms, int32_t* n) {
+  if (!c || !ms || !n) return fail(RIVER_EINVAL, "NULL argument");
+  if (c->timer_op < 0) return fail(RIVER_EINVAL, "timer not armed");
+  const int cnt = c->timer_n < *n ? c->timer_n : *n;
+  if (cnt > 0) {
+    hipError_t e = hipEventSynchronize(c->timer_ev[2 * (c->timer_n - 1) + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  for (int i = 0; i < cnt; ++i) {
+    hipError_t e = hipEventElapsedTime(&ms[i], c->timer_ev[2 * i], c->timer_ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  }
+  *n = cnt;
+  c->timer_op = -1;
+  c->timer_n = 0;
   return RIVER_OK;
 }
 
@@ -518,7 +595,7 @@ int river_decode_step(river_ctx* c, const int32_t* tok_in, const int32_t* forced
   a.sim_out = sim;
   a.logits = logits;
   a.tau = forced_exit ? 0.f : tau;
-  int rc = run_steps(c, a, 1, (hipStream_t)stream);
+  int rc = run_steps(c, a, 1, 0, (hipStream_t)stream);
   if (rc) return rc;
   for (auto& v : c->pos_host) v += 1;
   return RIVER_OK;

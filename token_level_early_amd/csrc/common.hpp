@@ -110,27 +110,28 @@ RIVER_DEV double block_sum_d(double v, double* red) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Cross-workgroup "last arriver" protocol. Each workgroup publishes its partial results,
-// then one thread increments a counter with an agent-scope acq_rel atomic. The workgroup
-// that sees count-1 owns the final step; it resets the counter for the next launch.
-// The release half makes this workgroup's earlier global writes visible across XCDs before
-// the increment; the acquire half makes every other workgroup's writes visible to the last.
+// Cross-workgroup "last arriver" merge without L2 write-backs. Partial results are written
+// with agent-scope atomic stores (write-through to the device-coherent level, `sc1`) and read
+// back with agent-scope atomic loads (which do not hit a stale line in this XCD's L2). Each
+// wave waits for its own stores to complete (s_waitcnt vmcnt(0)), the workgroup meets at a
+// barrier, and one thread bumps the counter; the workgroup that sees count-1 merges and resets
+// the counter for the next launch. Nothing waits on another workgroup.
 // ---------------------------------------------------------------------------------------
-RIVER_DEV bool arrive_last(int* counter, int count, int* lds_flag) {
-  // every thread releases its own partial stores at agent scope (write-back of this XCD's
-  // L2) before the workgroup's single increment
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+RIVER_DEV void wt_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+RIVER_DEV float wt_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+RIVER_DEV bool arrive_counter(int* counter, int count, int* lds_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = (old == count - 1);
   }
   __syncthreads();
-  const bool last = *lds_flag != 0;
-  if (last) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every other workgroup's stores
-  }
-  return last;
+  return *lds_flag != 0;
 }
 RIVER_DEV void reset_counter(int* counter) {
   __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

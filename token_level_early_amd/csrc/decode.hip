@@ -105,84 +105,82 @@ RIVER_DEV void w4_row(int op, int n, const LayerDev& lw, const Dims& dm, const u
   sp = sbase + (size_t)n * rs;
 }
 
-// Input vector of the GEMV: x = fp16(v * inv * gain) (RMSNorm applied on the fly) or x = v.
-struct XSrc {
-  const f16* v;
-  const f16* gain;
-  float inv;
-  int K;
-};
+// ---------------------------------------------------------------------------------------
+// Loads. Pointers reach the kernels through structs in memory, which hides their address
+// space from the compiler; the casts make every weight/activation access a global_load
+// (vmcnt only), never a flat_load (which LDS waits would also drain).
+// ---------------------------------------------------------------------------------------
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) v4u g_v4u;
+typedef const __attribute__((address_space(1))) f16 g_f16;
+RIVER_DEV uint4 ldg16(const void* p) {
+  const v4u v = *(g_v4u*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+RIVER_DEV f16 ldg2(const f16* p) { return *(g_f16*)p; }
 
-RIVER_DEV void scale8(uint4& u, const XSrc& s, int e) {
-  if (!s.gain) return;
-  const uint4 g = *(const uint4*)(s.gain + e);
+RIVER_DEV double sq8(uint4 u) {
+  const f16* h = (const f16*)&u;
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double x = (double)h2f(h[i]);
+    s += x * x;
+  }
+  return s;
+}
+
+// fp16(v * inv * gain) on 8 values (fp32 products), or v unchanged without a gain
+RIVER_DEV uint4 norm8(uint4 u, uint4 g, float inv, bool has_gain) {
+  if (!has_gain) return u;
   uint32_t* pu = (uint32_t*)&u;
   const uint32_t* pg = (const uint32_t*)&g;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    h2 v = as_h2(pu[j]), gg = as_h2(pg[j]);
+    const h2 v = as_h2(pu[j]), gg = as_h2(pg[j]);
     h2 r;
-    r.x = f2h(h2f(v.x) * s.inv * h2f(gg.x));
-    r.y = f2h(h2f(v.y) * s.inv * h2f(gg.y));
+    r.x = f2h(h2f(v.x) * inv * h2f(gg.x));
+    r.y = f2h(h2f(v.y) * inv * h2f(gg.y));
     pu[j] = as_u32(r);
   }
+  return u;
 }
 
-// fp16 stream: the wave's chunks are cid = ws + c*wpr; lane owns elements cid*512 + lane*8 + [0,8)
-template <int NCH>
-RIVER_DEV void load_x16(const XSrc& s, int ws, int wpr, h2 (&x)[NCH][4]) {
+// Exit-test reduction: dot(u, v), |u|^2, |v|^2 of two d-vectors in fp64, lane j taking 16-byte
+// chunks j, j+64, ... and a fixed xor tree, so every wave that runs it gets identical bits.
+RIVER_DEV void wave_cos3(const f16* u, const f16* v, int d, double& dot, double& nu, double& nv) {
   const int lane = threadIdx.x & (kWave - 1);
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+  for (int base = 0; base < d; base += 4 * kChunkF16) {
+    uint4 ua[4], va[4];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int e = (ws + c * wpr) * kChunkF16 + lane * 8;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (e < s.K) {
-      u = *(const uint4*)(s.v + e);
-      scale8(u, s, e);
+    for (int k = 0; k < 4; ++k) {
+      const int e = base + k * kChunkF16 + lane * 8;
+      const int ee = e < d ? e : 0;
+      ua[k] = ldg16(u + ee);
+      va[k] = ldg16(v + ee);
     }
-    x[c][0] = as_h2(u.x);
-    x[c][1] = as_h2(u.y);
-    x[c][2] = as_h2(u.z);
-    x[c][3] = as_h2(u.w);
-  }
-}
-
-// int4 stream: lane owns elements cid*2048 + lane*32 + [0,32), paired as unpack8 yields
-template <int NCH>
-RIVER_DEV void load_x4(const XSrc& s, int ws, int wpr, h2 (&x)[NCH][16]) {
-  const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
+    for (int k = 0; k < 4; ++k) {
+      if (base + k * kChunkF16 + lane * 8 >= d) continue;
+      const f16* hu = (const f16*)&ua[k];
+      const f16* hv = (const f16*)&va[k];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = (ws + c * wpr) * kChunkW4 + lane * 32 + m * 8;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (e < s.K) {
-        u = *(const uint4*)(s.v + e);
-        scale8(u, s, e);
+      for (int i = 0; i < 8; ++i) {
+        const double x = (double)h2f(hu[i]), y = (double)h2f(hv[i]);
+        s0 += x * y;
+        s1 += x * x;
+        s2 += y * y;
       }
-      const uint32_t in[4] = {u.x, u.y, u.z, u.w};
-      h2 o[4];
-      pair_for_unpack(in, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[c][m * 4 + j] = o[j];
     }
   }
+  dot = wave_sum_d(s0);
+  nu = wave_sum_d(s1);
+  nv = wave_sum_d(s2);
 }
 
 template <int NCH, int RB>
-RIVER_DEV void rows_f16(const f16* const (&rowp)[RB], int K, int ws, int wpr,
-                        const h2 (&x)[NCH][4], float (&acc)[RB]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint4 w[RB][NCH];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int e = (ws + c * wpr) * kChunkF16 + lane * 8;
-      w[rb][c] = (rowp[rb] != nullptr && e < K) ? *(const uint4*)(rowp[rb] + e)
-                                                 : make_uint4(0, 0, 0, 0);
-    }
+RIVER_DEV void dot_rows_f16(const uint4 (&w)[RB][NCH], const h2 (&x)[NCH][4], float (&acc)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float s = 0.f;
@@ -197,25 +195,10 @@ RIVER_DEV void rows_f16(const f16* const (&rowp)[RB], int K, int ws, int wpr,
   }
 }
 
+// int4 rows: per chunk sum_k q_k x_k over the lane's 32 elements (one group), times its scale
 template <int NCH, int RB>
-RIVER_DEV void rows_w4(const uint8_t* const (&rowp)[RB], const f16* const (&sclp)[RB], int nch,
-                       int group, int ws, int wpr, const h2 (&x)[NCH][16], float (&acc)[RB]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint4 w[RB][NCH];
-  float sc[RB][NCH];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int cid = ws + c * wpr;
-      if (rowp[rb] != nullptr && cid < nch) {
-        w[rb][c] = *(const uint4*)(rowp[rb] + (size_t)cid * 1024 + lane * 16);
-        sc[rb][c] = h2f(sclp[rb][(cid * kChunkW4 + lane * 32) / group]);
-      } else {
-        w[rb][c] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        sc[rb][c] = 0.f;
-      }
-    }
+RIVER_DEV void dot_rows_w4(const uint4 (&w)[RB][NCH], const f16 (&sc)[RB][NCH],
+                           const h2 (&x)[NCH][16], float (&acc)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float tot = 0.f;
@@ -232,13 +215,13 @@ RIVER_DEV void rows_w4(const uint8_t* const (&rowp)[RB], const f16* const (&sclp
         s = dot2(p2, x[c][m * 4 + 2], s);
         s = dot2(p3, x[c][m * 4 + 3], s);
       }
-      tot = fmaf(sc[rb][c], s, tot);
+      tot = fmaf(h2f(sc[rb][c]), s, tot);
     }
     acc[rb] = tot;
   }
 }
 
-// Sum of squares of a fp16 vector over the whole block, fixed order (fp64).
+// Block-wide fp64 sum of squares in one fixed order (thread t takes elements t, t+256, ...).
 RIVER_DEV double block_sumsq(const f16* v, int n, double* red) {
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += kBlock) {
@@ -248,162 +231,311 @@ RIVER_DEV double block_sumsq(const f16* v, int n, double* red) {
   return block_sum_d(s, red);
 }
 
-// Sum of red[0..n)[j] for j < 3 over the block in a fixed order; results in out[0..3).
-RIVER_DEV void block_sum_red(const double* red, int n, double* out, double* scratch) {
-  double s0 = 0, s1 = 0, s2 = 0;
-  for (int i = threadIdx.x; i < n; i += kBlock) {
-    s0 += red[i * 4 + 0];
-    s1 += red[i * 4 + 1];
-    s2 += red[i * 4 + 2];
-  }
-  out[0] = block_sum_d(s0, scratch);
-  out[1] = block_sum_d(s1, scratch);
-  out[2] = block_sum_d(s2, scratch);
+RIVER_DEV float inv_rms(double ss, int n, float eps) {
+  return (float)(1.0 / sqrt(ss / n + (double)eps));
 }
 
-template <int NCH16, int WPR16, int NCH4, int WPR4>
-__global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int op, int layer,
-                                                     int nwg16, int nwg4) {
+// Sum of per-wave values over the WPR waves of this wave's row group (fixed order). WPR = 1
+// needs no exchange.
+template <int WPR>
+RIVER_DEV double rowgroup_sum(double v, double* red) {
+  if (WPR == 1) return v;
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  const int g0 = (w / WPR) * WPR;
+  double s = 0.0;
+  for (int j = 0; j < WPR; ++j) s += red[g0 + j];
+  return s;
+}
+
+// One wave's share of a tile on the fp16 stream: RB rows x NCH chunks of 512 elements
+// (chunk ids ws, ws+WPR, ...). Loads weights, the raw input and its gains, normalises the
+// input (computing its rms from the loaded values when `want_norm`), returns the RB dots.
+template <int NCH, int RB, int WPR, bool HAS_GAIN>
+RIVER_DEV void wave_gemv_f16(const f16* const (&rowp)[RB], const f16* xv, const f16* gain, int K,
+                             int ws, bool want_norm, float inv, int dnorm, float eps, double* red,
+                             float (&acc)[RB]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint4 wv[RB][NCH];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = (ws + c * WPR) * kChunkF16 + lane * 8;
+      const bool ok = rowp[rb] != nullptr && e < K;
+      // out-of-range chunks read a valid vector instead and meet x = 0; rows past N are
+      // never stored
+      wv[rb][c] = ldg16(ok ? (const void*)(rowp[rb] + e) : (const void*)xv);
+    }
+  uint4 xr[NCH], gr[NCH] = {};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int e = (ws + c * WPR) * kChunkF16 + lane * 8;
+    const int ee = e < K ? e : 0;
+    xr[c] = ldg16(xv + ee);
+    if (HAS_GAIN) gr[c] = ldg16(gain + ee);
+  }
+  if (want_norm) {
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if ((ws + c * WPR) * kChunkF16 + lane * 8 < K) ss += sq8(xr[c]);
+    ss = rowgroup_sum<WPR>(wave_sum_d(ss), red);
+    inv = inv_rms(ss, dnorm, eps);
+  }
+  h2 x[NCH][4];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const bool okx = (ws + c * WPR) * kChunkF16 + lane * 8 < K;
+    const uint4 u = okx ? norm8(xr[c], gr[c], inv, HAS_GAIN) : make_uint4(0, 0, 0, 0);
+    x[c][0] = as_h2(u.x);
+    x[c][1] = as_h2(u.y);
+    x[c][2] = as_h2(u.z);
+    x[c][3] = as_h2(u.w);
+  }
+  dot_rows_f16<NCH, RB>(wv, x, acc);
+}
+
+// One wave's share of a tile on the int4 stream: RB rows x NCH chunks of 2048 elements.
+template <int NCH, int RB, int WPR, bool HAS_GAIN>
+RIVER_DEV void wave_gemv_w4(const uint8_t* const (&rowp)[RB], const f16* const (&sclp)[RB],
+                            const f16* xv, const f16* gain, int K, int group, int ws,
+                            bool want_norm, float inv, int dnorm, float eps, double* red,
+                            float (&acc)[RB]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nch = (K + kChunkW4 - 1) / kChunkW4;
+  uint4 wv[RB][NCH];
+  f16 sc[RB][NCH];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int cid = ws + c * WPR;
+      const bool ok = rowp[rb] != nullptr && cid < nch;
+      wv[rb][c] = ldg16(ok ? (const void*)(rowp[rb] + (size_t)cid * 1024 + lane * 16) : (const void*)xv);
+      sc[rb][c] = ldg2(ok ? sclp[rb] + (cid * kChunkW4 + lane * 32) / group : xv);
+    }
+  uint4 xr[NCH][4], gr[NCH][4] = {};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = (ws + c * WPR) * kChunkW4 + lane * 32 + m * 8;
+      const int ee = e < K ? e : 0;
+      xr[c][m] = ldg16(xv + ee);
+      if (HAS_GAIN) gr[c][m] = ldg16(gain + ee);
+    }
+  if (want_norm) {
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if ((ws + c * WPR) * kChunkW4 + lane * 32 + m * 8 < K) ss += sq8(xr[c][m]);
+    ss = rowgroup_sum<WPR>(wave_sum_d(ss), red);
+    inv = inv_rms(ss, dnorm, eps);
+  }
+  h2 x[NCH][16];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bool okx = (ws + c * WPR) * kChunkW4 + lane * 32 + m * 8 < K;
+      const uint4 u = okx ? norm8(xr[c][m], gr[c][m], inv, HAS_GAIN) : make_uint4(0, 0, 0, 0);
+      const uint32_t in[4] = {u.x, u.y, u.z, u.w};
+      h2 o[4];
+      pair_for_unpack(in, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[c][m * 4 + j] = o[j];
+    }
+  dot_rows_w4<NCH, RB>(wv, sc, x, acc);
+}
+
+// MODE 0: early-exit decode (both weight streams in the grid; the route of the layer is decided
+//         by every QKV workgroup identically and read from device state by the later kernels).
+// MODE 1: backbone-only decode (the full-depth fp16 model: no river tiles, no exit test).
+template <int OP, int MODE, int NCH16, int WPR16, int NCH4, int WPR4>
+__global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, int nwg16, int nwg4) {
   using T16 = TileF16<WPR16>;
   using T4 = TileW4<WPR4>;
   constexpr int TRMAX = (T16::TR > T4::TR ? T16::TR : T4::TR);
+  constexpr bool kHasGain = (OP == OP_QKV || OP == OP_GU || OP == OP_LM);
   __shared__ float ypart[TRMAX][4];
   __shared__ float y[TRMAX];
   __shared__ double dred[4];
-  __shared__ double dsum[4];
-  __shared__ int lflag;
+  __shared__ double cos3[3];
 
   const Dims& dm = a.dm;
-  const int b = 0;  // batch row (VALU path decodes one row)
-  const int route = (op == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + b];
+  const int b = 0;  // batch row (the VALU path decodes one row)
   const bool is4 = blockIdx.x >= (unsigned)nwg16;
-  if (is4 != (route == ROUTE_RIVER)) return;
-  const int tile = is4 ? (int)blockIdx.x - nwg16 : (int)blockIdx.x;
-  const int TR = is4 ? T4::TR : T16::TR;
-  const int nwg = is4 ? nwg4 : nwg16;
-  const LayerDev* lwp = (op == OP_LM) ? nullptr : &a.layers[layer - 1];
-  const int N = op_rows(op, dm);
-  const int K = op_k(op, dm);
   const int step = *a.step;
+  const LayerDev* lwp = (OP == OP_LM) ? nullptr : &a.layers[layer - 1];
+  const int t = threadIdx.x;
 
-  // ---- input vector -------------------------------------------------------------------
-  XSrc xs;
-  xs.K = K;
-  xs.gain = nullptr;
-  xs.inv = 1.f;
-  if (op == OP_QKV) {
-    xs.gain = lwp->attn_norm;
+  // ---- route of this layer ------------------------------------------------------------
+  int route = ROUTE_BACKBONE;
+  bool have_inv = false;
+  float inv = 1.f;
+  const f16* vin = nullptr;
+  if (OP == OP_QKV) {
     if (layer == 1) {
       int tok = (step == 0) ? a.tok_in[b] : a.tok_out[(step - 1) * dm.B + b];
       if (tok < 0 || tok >= dm.V) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.err, ERR_TOKEN);
+        if (blockIdx.x == 0 && t == 0) atomicOr(a.err, ERR_TOKEN);
         tok = 0;
       }
-      xs.v = a.embed + (size_t)tok * dm.d;
-      const double ss = block_sumsq(xs.v, dm.d, dred);
-      xs.inv = (float)(1.0 / sqrt(ss / dm.d + (double)dm.eps));
-      if (blockIdx.x == (unsigned)(is4 ? nwg16 : 0)) {  // first active workgroup
+      vin = a.embed + (size_t)tok * dm.d;
+      if (blockIdx.x == 0) {
         f16* h0 = a.hs + (size_t)b * dm.d;
-        for (int i = threadIdx.x; i < dm.d; i += kBlock) h0[i] = xs.v[i];
-        if (threadIdx.x == 0) {
-          if (a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
-          a.inv_attn[b] = xs.inv;
-        }
+        for (int i = t; i < dm.d; i += kBlock) h0[i] = vin[i];
+        if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
         if (a.sim_out)
-          for (int i = threadIdx.x; i < dm.L; i += kBlock)
+          for (int i = t; i < dm.L; i += kBlock)
             a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
       }
     } else {
-      xs.v = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
-      xs.inv = a.inv_attn[(layer - 1) * dm.B + b];
+      vin = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+      if (MODE == 0) {
+        // exit test after backbone layer lp = layer-1: cos(h(lp-1), h(lp)) > tau (or forced)
+        const int lp = layer - 1;
+        const int prev = a.route[lp * dm.B + b];
+        if (prev == ROUTE_RIVER) {
+          route = ROUTE_RIVER;
+        } else if (lp >= dm.entry) {
+          if (a.sched) {
+            int e = a.sched[step * dm.B + b];
+            if (e < dm.entry || e > dm.L) {
+              if (blockIdx.x == 0 && t == 0) atomicOr(a.err, ERR_FORCED);
+              e = dm.L;
+            }
+            if (lp == e) route = ROUTE_RIVER;
+          } else {
+            if (t < kWave) {
+              double dot, n1, n2;
+              wave_cos3(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, vin, dm.d, dot, n1, n2);
+              if (t == 0) {
+                cos3[0] = dot;
+                cos3[1] = n1;
+                cos3[2] = n2;
+              }
+            }
+            __syncthreads();
+            const double dot = cos3[0], n1 = cos3[1], n2 = cos3[2];
+            const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
+            if (blockIdx.x == 0 && t == 0 && a.sim_out)
+              a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
+            if (sim > (double)a.tau) route = ROUTE_RIVER;
+            inv = inv_rms(n2, dm.d, dm.eps);
+            have_inv = true;
+          }
+        }
+        if (blockIdx.x == 0 && t == 0) {
+          a.route[layer * dm.B + b] = route;
+          if (route == ROUTE_RIVER && prev == ROUTE_BACKBONE && a.exit_out)
+            a.exit_out[step * dm.B + b] = lp;
+        }
+      }
     }
-  } else if (op == OP_O) {
-    xs.v = a.o + (size_t)b * dm.hd;
-  } else if (op == OP_GU) {
-    xs.v = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
-    xs.gain = lwp->mlp_norm;
-    xs.inv = a.inv_mlp[(layer - 1) * dm.B + b];
-  } else if (op == OP_DOWN) {
-    xs.v = a.a2 + (size_t)b * dm.F;
+  } else if (OP != OP_LM && MODE == 0) {
+    route = a.route[layer * dm.B + b];
+  }
+  if (is4 != (route == ROUTE_RIVER)) return;
+
+  const int tile = is4 ? (int)blockIdx.x - nwg16 : (int)blockIdx.x;
+  const int TR = is4 ? T4::TR : T16::TR;
+  const int N = op_rows(OP, dm);
+  const int K = op_k(OP, dm);
+  const int w = t / kWave, lane = t % kWave;
+
+  // input vector: x = fp16(v * inv * gain), or v itself
+  const f16* xv;
+  const f16* gain = nullptr;
+  bool want_norm = false;
+  if (OP == OP_QKV) {
+    xv = vin;
+    gain = lwp->attn_norm;
+    want_norm = !have_inv;
+  } else if (OP == OP_O) {
+    xv = a.o + (size_t)b * dm.hd;
+  } else if (OP == OP_GU) {
+    xv = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+    gain = lwp->mlp_norm;
+    want_norm = true;
+  } else if (OP == OP_DOWN) {
+    xv = a.a2 + (size_t)b * dm.F;
   } else {
-    xs.v = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
-    xs.gain = a.final_norm;
-    xs.inv = a.inv_attn[dm.L * dm.B + b];
+    xv = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
+    gain = a.final_norm;
+    inv = a.inv_attn[dm.L * dm.B + b];
   }
 
   // ---- GEMV ---------------------------------------------------------------------------
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (!is4) {
     constexpr int RB = kRB16;
     const int rg = w / WPR16, ws = w % WPR16;
-    h2 x[NCH16][4];
-    load_x16<NCH16>(xs, ws, WPR16, x);
     const f16* rowp[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int r = rg * RB + rb;
-      const int n = logical_row(op, tile, r, T16::TR, dm);
-      rowp[rb] = (n < N) ? (op == OP_LM ? a.lm_head + (size_t)n * dm.d : f16_row(op, n, *lwp, a))
+      const int n = logical_row(OP, tile, rg * RB + rb, T16::TR, dm);
+      rowp[rb] = (n < N) ? (OP == OP_LM ? a.lm_head + (size_t)n * dm.d : f16_row(OP, n, *lwp, a))
                          : nullptr;
     }
     float acc[RB];
-    rows_f16<NCH16, RB>(rowp, K, ws, WPR16, x, acc);
+    wave_gemv_f16<NCH16, RB, WPR16, kHasGain>(rowp, xv, gain, K, ws, want_norm, inv, dm.d, dm.eps, dred, acc);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float v = wave_sum(acc[rb]);
       if (lane == 0) ypart[rg * RB + rb][ws] = v;
     }
     __syncthreads();
-    if (threadIdx.x < T16::TR) {
+    if (t < T16::TR) {
       float s = 0.f;
-      for (int j = 0; j < WPR16; ++j) s += ypart[threadIdx.x][j];
-      y[threadIdx.x] = s;
+      for (int j = 0; j < WPR16; ++j) s += ypart[t][j];
+      y[t] = s;
     }
   } else {
     constexpr int RB = kRB4;
     const int rg = w / WPR4, ws = w % WPR4;
-    h2 x[NCH4][16];
-    load_x4<NCH4>(xs, ws, WPR4, x);
     const uint8_t* rowp[RB];
     const f16* sclp[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int r = rg * RB + rb;
-      const int n = logical_row(op, tile, r, T4::TR, dm);
+      const int n = logical_row(OP, tile, rg * RB + rb, T4::TR, dm);
       if (n < N) {
-        w4_row(op, n, *lwp, dm, rowp[rb], sclp[rb]);
+        w4_row(OP, n, *lwp, dm, rowp[rb], sclp[rb]);
       } else {
         rowp[rb] = nullptr;
         sclp[rb] = nullptr;
       }
     }
-    const int nch = (K + kChunkW4 - 1) / kChunkW4;
     float acc[RB];
-    rows_w4<NCH4, RB>(rowp, sclp, nch, dm.group, ws, WPR4, x, acc);
+    wave_gemv_w4<NCH4, RB, WPR4, kHasGain>(rowp, sclp, xv, gain, K, dm.group, ws, want_norm, inv, dm.d,
+                                 dm.eps, dred, acc);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float v = wave_sum(acc[rb]);
       if (lane == 0) ypart[rg * RB + rb][ws] = v;
     }
     __syncthreads();
-    if (threadIdx.x < T4::TR) {
+    if (t < T4::TR) {
       float s = 0.f;
-      for (int j = 0; j < WPR4; ++j) s += ypart[threadIdx.x][j];
-      y[threadIdx.x] = s;
+      for (int j = 0; j < WPR4; ++j) s += ypart[t][j];
+      y[t] = s;
     }
   }
   __syncthreads();
 
   // ---- epilogues ----------------------------------------------------------------------
-  const int t = threadIdx.x;
-  if (op == OP_QKV) {
+  if (OP == OP_QKV) {
     const int pos = a.pos[b];
     const int qk_rows = (dm.H + dm.Hkv) * dm.D;
-    const int n0 = logical_row(op, tile, 0, TR, dm);
+    const int n0 = logical_row(OP, tile, 0, TR, dm);
     if (n0 < qk_rows) {
       const int half = TR / 2;
       if (t < half) {
-        const int n = logical_row(op, tile, t, TR, dm);
+        const int n = logical_row(OP, tile, t, TR, dm);
         const int head = n / dm.D, i = n % dm.D;  // i < D/2
         const float x0 = h2f(f2h(y[t])), x1 = h2f(f2h(y[t + half]));
         const float2 cs = a.rope[(size_t)pos * (dm.D / 2) + i];
@@ -422,7 +554,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int op, int l
         }
       }
     } else if (t < TR) {
-      const int n = logical_row(op, tile, t, TR, dm);
+      const int n = logical_row(OP, tile, t, TR, dm);
       if (n < N) {
         const int vi = n - qk_rows;
         const int kvh = vi / dm.D, i = vi % dm.D;
@@ -431,84 +563,33 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int op, int l
         vd[i] = f2h(y[t]);
       }
     }
-  } else if (op == OP_GU) {
+  } else if (OP == OP_GU) {
     const int half = TR / 2;
     if (t < half) {
-      const int f = logical_row(op, tile, t, TR, dm);
+      const int f = logical_row(OP, tile, t, TR, dm);
       if (f < dm.F) {
         const float g = h2f(f2h(y[t])), u = h2f(f2h(y[t + half]));
         const float sg = g / (1.f + __expf(-g));
         a.a2[(size_t)b * dm.F + f] = f2h(sg * u);
       }
     }
-  } else if (op == OP_O || op == OP_DOWN) {
-    double p0 = 0, p1 = 0, p2 = 0;
+  } else if (OP == OP_O) {
     if (t < TR) {
-      const int n = logical_row(op, tile, t, TR, dm);
+      const int n = tile * TR + t;
       if (n < N) {
-        if (op == OP_O) {
-          const f16 hin = a.hs[((size_t)(layer - 1) * dm.B + b) * dm.d + n];
-          const f16 hm = f2h(h2f(hin) + h2f(f2h(y[t])));
-          a.hmid[((size_t)(layer - 1) * dm.B + b) * dm.d + n] = hm;
-          p2 = (double)h2f(hm) * (double)h2f(hm);
-        } else {
-          const f16 hm = a.hmid[((size_t)(layer - 1) * dm.B + b) * dm.d + n];
-          const f16 ho = f2h(h2f(hm) + h2f(f2h(y[t])));
-          a.hs[((size_t)layer * dm.B + b) * dm.d + n] = ho;
-          const double hp = (double)h2f(a.hs[((size_t)(layer - 1) * dm.B + b) * dm.d + n]);
-          const double hv = (double)h2f(ho);
-          p0 = hp * hv;
-          p1 = hp * hp;
-          p2 = hv * hv;
-        }
+        const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + n;
+        a.hmid[i] = f2h(h2f(a.hs[i]) + h2f(f2h(y[t])));
       }
     }
-    // per-workgroup partials -> red[tile]; the last workgroup finishes the reduction
-    const double s0 = block_sum_d(p0, dred);
-    const double s1 = block_sum_d(p1, dred);
-    const double s2 = block_sum_d(p2, dred);
-    if (t == 0) {
-      a.red[tile * 4 + 0] = s0;
-      a.red[tile * 4 + 1] = s1;
-      a.red[tile * 4 + 2] = s2;
-    }
-    int* counter = a.cnt + (op == OP_O ? CNT_O : CNT_DOWN);
-    if (arrive_last(counter, nwg, &lflag)) {
-      block_sum_red(a.red, nwg, dsum, dred);
-      if (t == 0) {
-        const double dot = dsum[0], n1 = dsum[1], n2 = dsum[2];
-        if (op == OP_O) {
-          a.inv_mlp[(layer - 1) * dm.B + b] = (float)(1.0 / sqrt(n2 / dm.d + (double)dm.eps));
-        } else {
-          a.inv_attn[layer * dm.B + b] = (float)(1.0 / sqrt(n2 / dm.d + (double)dm.eps));
-          if (layer < dm.L) {
-            int nr = route;
-            if (route == ROUTE_BACKBONE) {
-              bool ex = false;
-              if (a.sched) {
-                int e = a.sched[step * dm.B + b];
-                if (e < dm.entry || e > dm.L) {
-                  atomicOr(a.err, ERR_FORCED);
-                  e = dm.L;
-                }
-                ex = (layer == e);
-              } else if (layer >= dm.entry) {
-                const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
-                if (a.sim_out) a.sim_out[((size_t)step * dm.B + b) * dm.L + layer - 1] = (float)sim;
-                ex = sim > (double)a.tau;
-              }
-              if (ex) {
-                nr = ROUTE_RIVER;
-                if (a.exit_out) a.exit_out[step * dm.B + b] = layer;
-              }
-            }
-            a.route[(layer + 1) * dm.B + b] = nr;
-          }
-        }
-        reset_counter(counter);
+  } else if (OP == OP_DOWN) {
+    if (t < TR) {
+      const int n = tile * TR + t;
+      if (n < N) {
+        const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + n;
+        a.hs[(size_t)dm.B * dm.d + i] = f2h(h2f(a.hmid[i]) + h2f(f2h(y[t])));
       }
     }
-  } else {  // OP_LM: logits + argmax (lowest index on ties)
+  } else {  // OP_LM: logits, workgroup argmax (lowest index on ties), one 64-bit atomic max
     if (t == 0) {
       float best = -__builtin_inff();
       int bi = 0x7FFFFFFF;
@@ -522,24 +603,34 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int op, int l
           bi = n;
         }
       }
-      const unsigned long long key =
-          ((unsigned long long)float_key(best) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
+      const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
+                                     (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
       __hip_atomic_fetch_max(a.amax + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    int* counter = a.cnt + CNT_LM;
-    if (arrive_last(counter, nwg, &lflag)) {
-      if (t == 0) {
-        const unsigned long long key =
-            __hip_atomic_load(a.amax + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int tok = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
-        a.tok_out[step * dm.B + b] = tok;
-        a.pos[b] += 1;
-        *a.step = step + 1;
-        __hip_atomic_store(a.amax + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        reset_counter(counter);
-      }
-    }
   }
+}
+
+// 1/rms of the final residual stream (input of the LM head), one workgroup per row.
+__global__ __launch_bounds__(kBlock) void k_final_norm(DecodeArgs a) {
+  __shared__ double red[4];
+  const int b = blockIdx.x;
+  const double ss = block_sumsq(a.hs + ((size_t)a.dm.L * a.dm.B + b) * a.dm.d, a.dm.d, red);
+  if (threadIdx.x == 0) a.inv_attn[a.dm.L * a.dm.B + b] = inv_rms(ss, a.dm.d, a.dm.eps);
+}
+
+// End of a step: greedy token from the argmax key, position and step counters advance.
+__global__ void k_step_end(DecodeArgs a) {
+  const int b = threadIdx.x;
+  const int step = *a.step;
+  if (b < a.dm.B) {
+    const unsigned long long key =
+        __hip_atomic_load(a.amax + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.tok_out[step * a.dm.B + b] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+    __hip_atomic_store(a.amax + b, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.pos[b] += 1;
+  }
+  __syncthreads();
+  if (b == 0) *a.step = step + 1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -582,7 +673,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
     float qf[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 u = *(const uint4*)(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
+      const uint4 u = ldg16(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
       const f16* hp = (const f16*)&u;
 #pragma unroll
       for (int i = 0; i < 8; ++i) qf[g][i] = h2f(hp[i]) * qs;
@@ -600,10 +691,9 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = tb + u * NGRP;
-        if (t < t1) {
-          kk[u] = *(const uint4*)(Kb + (size_t)t * D + d0);
-          vv[u] = *(const uint4*)(Vb + (size_t)t * D + d0);
-        }
+        const size_t tt = (size_t)(t < t1 ? t : t0);
+        kk[u] = ldg16(Kb + tt * D + d0);
+        vv[u] = ldg16(Vb + tt * D + d0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -656,26 +746,29 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
         A += sm_acc[j][g][dd] * sc;
       }
       const size_t pi = pbase + (size_t)g * smax + s;
-      a.pacc[pi * D + dd] = A;
+      wt_store(&a.pacc[pi * D + dd], A);
       if (dd == 0) {
-        a.pml[pi * 2 + 0] = M;
-        a.pml[pi * 2 + 1] = Lsum;
+        wt_store(&a.pml[pi * 2 + 0], M);
+        wt_store(&a.pml[pi * 2 + 1], Lsum);
       }
     }
   }
 
   int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
-  if (arrive_last(counter, smax, &lflag)) {
+  if (arrive_counter(counter, smax, &lflag)) {
     // split weights exp2(m_s - M) / L per query head
     if (threadIdx.x < G) {
       const int g = threadIdx.x;
       float M = -__builtin_inff();
-      for (int j = 0; j < seff; ++j) M = fmaxf(M, a.pml[(pbase + (size_t)g * smax + j) * 2]);
+      for (int j = 0; j < seff; ++j) {
+        sm_w[g][j] = wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2]);
+        M = fmaxf(M, sm_w[g][j]);
+      }
       float Lsum = 0.f;
       for (int j = 0; j < seff; ++j) {
-        const float e = exp2f(a.pml[(pbase + (size_t)g * smax + j) * 2] - M);
+        const float e = exp2f(sm_w[g][j] - M);
         sm_w[g][j] = e;
-        Lsum += a.pml[(pbase + (size_t)g * smax + j) * 2 + 1] * e;
+        Lsum += wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2 + 1]) * e;
       }
       sm_L[g] = Lsum;
     }
@@ -683,7 +776,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
     for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
       const int g = idx / D, dd = idx % D;
       float A = 0.f;
-      for (int j = 0; j < seff; ++j) A += sm_w[g][j] * a.pacc[(pbase + (size_t)g * smax + j) * D + dd];
+      for (int j = 0; j < seff; ++j) A += sm_w[g][j] * wt_load(&a.pacc[(pbase + (size_t)g * smax + j) * D + dd]);
       a.o[(size_t)b * dm.hd + (size_t)(kvh * G + g) * D + dd] = f2h(A / sm_L[g]);
     }
     if (threadIdx.x == 0) reset_counter(counter);
@@ -693,45 +786,57 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
 // ---------------------------------------------------------------------------------------
 // Host-side launchers (called from api.cpp)
 // ---------------------------------------------------------------------------------------
-struct GemvShape {
-  int nwg16, nwg4;
-};
-
-template <int NCH16, int WPR16, int NCH4, int WPR4>
-static hipError_t launch_gemv_t(const DecodeArgs& a, int op, int layer, int N, hipStream_t st,
-                                GemvShape* shape) {
+template <int OP, int MODE, int NCH16, int WPR16, int NCH4, int WPR4>
+static hipError_t launch_gemv_t(const DecodeArgs& a, int layer, int N, hipStream_t st) {
   const int tr16 = TileF16<WPR16>::TR, tr4 = TileW4<WPR4>::TR;
-  int nwg16 = 0, nwg4 = 0;
-  if (op == OP_QKV || op == OP_GU) {
-    nwg16 = (op == OP_GU) ? (N / 2) / (tr16 / 2) : N / tr16;
-    nwg4 = (op == OP_LM) ? 0 : ((op == OP_GU) ? (N / 2) / (tr4 / 2) : N / tr4);
+  int nwg16, nwg4;
+  if (OP == OP_GU) {
+    nwg16 = (N / 2) / (tr16 / 2);
+    nwg4 = (N / 2) / (tr4 / 2);
+  } else if (OP == OP_QKV) {
+    nwg16 = N / tr16;
+    nwg4 = N / tr4;
   } else {
     nwg16 = (N + tr16 - 1) / tr16;
-    nwg4 = (op == OP_LM) ? 0 : (N + tr4 - 1) / tr4;
+    nwg4 = (N + tr4 - 1) / tr4;
   }
-  if (shape) {
-    shape->nwg16 = nwg16;
-    shape->nwg4 = nwg4;
-  }
-  hipLaunchKernelGGL((k_dec_gemv<NCH16, WPR16, NCH4, WPR4>), dim3(nwg16 + nwg4), dim3(kBlock), 0,
-                     st, a, op, layer, nwg16, nwg4);
+  if (OP == OP_LM || MODE == 1) nwg4 = 0;
+  hipLaunchKernelGGL((k_dec_gemv<OP, MODE, NCH16, WPR16, NCH4, WPR4>), dim3(nwg16 + nwg4),
+                     dim3(kBlock), 0, st, a, layer, nwg16, nwg4);
   return hipGetLastError();
 }
 
-// Picks the stream geometry from K: chunks per row nch, waves per row wpr, chunks per wave NCH.
-hipError_t river_launch_gemv(const DecodeArgs& a, int op, int layer, hipStream_t st) {
+// Picks the stream geometry from K: chunks per row (fp16: 512 elements, int4: 2048), waves per
+// row WPR and chunks per wave NCH (fp16 <= 8, int4 <= 4).
+template <int OP, int MODE>
+static hipError_t launch_op(const DecodeArgs& a, int layer, hipStream_t st) {
   const Dims& dm = a.dm;
-  const int N = (op == OP_QKV) ? dm.nqkv : (op == OP_GU) ? 2 * dm.F : (op == OP_LM) ? dm.V : dm.d;
-  const int K = (op == OP_O) ? dm.hd : (op == OP_DOWN) ? dm.F : dm.d;
+  const int N = (OP == OP_QKV) ? dm.nqkv : (OP == OP_GU) ? 2 * dm.F : (OP == OP_LM) ? dm.V : dm.d;
+  const int K = (OP == OP_O) ? dm.hd : (OP == OP_DOWN) ? dm.F : dm.d;
   const int n16 = (K + kChunkF16 - 1) / kChunkF16;
   const int n4 = (K + kChunkW4 - 1) / kChunkW4;
-  // fp16: up to 8 chunks per wave; int4: up to 4
-  if (n16 <= 1 && n4 <= 1) return launch_gemv_t<1, 1, 1, 1>(a, op, layer, N, st, nullptr);
-  if (n16 <= 2 && n4 <= 1) return launch_gemv_t<2, 1, 1, 1>(a, op, layer, N, st, nullptr);
-  if (n16 <= 4 && n4 <= 1) return launch_gemv_t<4, 1, 1, 1>(a, op, layer, N, st, nullptr);
-  if (n16 <= 8 && n4 <= 2) return launch_gemv_t<8, 1, 2, 1>(a, op, layer, N, st, nullptr);
-  if (n16 <= 16 && n4 <= 4) return launch_gemv_t<4, 4, 4, 1>(a, op, layer, N, st, nullptr);
-  if (n16 <= 32 && n4 <= 8) return launch_gemv_t<8, 4, 4, 2>(a, op, layer, N, st, nullptr);
+  if (n16 <= 1 && n4 <= 1) return launch_gemv_t<OP, MODE, 1, 1, 1, 1>(a, layer, N, st);
+  if (n16 <= 2 && n4 <= 1) return launch_gemv_t<OP, MODE, 2, 1, 1, 1>(a, layer, N, st);
+  if (n16 <= 4 && n4 <= 1) return launch_gemv_t<OP, MODE, 4, 1, 1, 1>(a, layer, N, st);
+  if (n16 <= 8 && n4 <= 2) return launch_gemv_t<OP, MODE, 8, 1, 2, 1>(a, layer, N, st);
+  if (n16 <= 16 && n4 <= 4) return launch_gemv_t<OP, MODE, 4, 4, 4, 1>(a, layer, N, st);
+  if (n16 <= 32 && n4 <= 8) return launch_gemv_t<OP, MODE, 8, 4, 4, 2>(a, layer, N, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t river_launch_gemv(const DecodeArgs& a, int op, int layer, int mode, hipStream_t st) {
+  switch (op * 2 + (mode ? 1 : 0)) {
+    case OP_QKV * 2: return launch_op<OP_QKV, 0>(a, layer, st);
+    case OP_QKV * 2 + 1: return launch_op<OP_QKV, 1>(a, layer, st);
+    case OP_O * 2: return launch_op<OP_O, 0>(a, layer, st);
+    case OP_O * 2 + 1: return launch_op<OP_O, 1>(a, layer, st);
+    case OP_GU * 2: return launch_op<OP_GU, 0>(a, layer, st);
+    case OP_GU * 2 + 1: return launch_op<OP_GU, 1>(a, layer, st);
+    case OP_DOWN * 2: return launch_op<OP_DOWN, 0>(a, layer, st);
+    case OP_DOWN * 2 + 1: return launch_op<OP_DOWN, 1>(a, layer, st);
+    case OP_LM * 2:
+    case OP_LM * 2 + 1: return launch_op<OP_LM, 0>(a, layer, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -759,16 +864,44 @@ hipError_t river_launch_attn(const DecodeArgs& a, int layer, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t river_decode_layers(const DecodeArgs& a, hipStream_t st) {
+// Final norm, LM head + argmax, step bookkeeping (also ends a prefill).
+hipError_t river_launch_head(const DecodeArgs& a, hipStream_t st, void (*timer)(void*, int, int),
+                             void* tctx, int top) {
+  hipLaunchKernelGGL(k_final_norm, dim3(a.dm.B), dim3(kBlock), 0, st, a);
+  if (timer && top == TOP_LM) timer(tctx, TOP_LM, 0);
+  hipError_t e = river_launch_gemv(a, OP_LM, a.dm.L + 1, 0, st);
+  if (timer && top == TOP_LM) timer(tctx, TOP_LM, 1);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_step_end, dim3(1), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// Enqueues one decode step. `timer` (optional) is called before and after every launch of the
+// timed op (TOP_* codes) so the host can bracket it with events.
+hipError_t river_decode_layers(const DecodeArgs& a, int mode, hipStream_t st,
+                               void (*timer)(void*, int, int), void* tctx, int top) {
   hipError_t e;
+  auto T = [&](int o, int phase) {
+    if (timer && o == top) timer(tctx, o, phase);
+  };
   for (int l = 1; l <= a.dm.L; ++l) {
-    if ((e = river_launch_gemv(a, OP_QKV, l, st)) != hipSuccess) return e;
+    T(TOP_QKV, 0);
+    if ((e = river_launch_gemv(a, OP_QKV, l, mode, st)) != hipSuccess) return e;
+    T(TOP_QKV, 1);
+    T(TOP_ATTN, 0);
     if ((e = river_launch_attn(a, l, st)) != hipSuccess) return e;
-    if ((e = river_launch_gemv(a, OP_O, l, st)) != hipSuccess) return e;
-    if ((e = river_launch_gemv(a, OP_GU, l, st)) != hipSuccess) return e;
-    if ((e = river_launch_gemv(a, OP_DOWN, l, st)) != hipSuccess) return e;
+    T(TOP_ATTN, 1);
+    T(TOP_O, 0);
+    if ((e = river_launch_gemv(a, OP_O, l, mode, st)) != hipSuccess) return e;
+    T(TOP_O, 1);
+    T(TOP_GU, 0);
+    if ((e = river_launch_gemv(a, OP_GU, l, mode, st)) != hipSuccess) return e;
+    T(TOP_GU, 1);
+    T(TOP_DOWN, 0);
+    if ((e = river_launch_gemv(a, OP_DOWN, l, mode, st)) != hipSuccess) return e;
+    T(TOP_DOWN, 1);
   }
-  return river_launch_gemv(a, OP_LM, a.dm.L + 1, st);
+  return river_launch_head(a, st, timer, tctx, top);
 }
 
 __global__ void k_begin_steps(int* step) {

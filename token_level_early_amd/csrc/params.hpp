@@ -89,6 +89,8 @@ static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn
 
 // Decode GEMV operations (one launch each).
 enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
+// Timer op codes (public, see river_timer_arm): the launches of one decode step in order.
+enum { TOP_QKV = 0, TOP_ATTN = 1, TOP_O = 2, TOP_GU = 3, TOP_DOWN = 4, TOP_LM = 5 };
 
 // Prefill activations and state (scratch), passed by value to the prefill kernels.
 struct PfArgs {

@@ -356,22 +356,14 @@ __global__ __launch_bounds__(kBlock) void k_pf_decide(PfArgs p, int layer, int f
 }
 
 // Hand the last prompt position of each row to the decode LM head: hs[L][b] = hout[b*P+P-1],
-// inv_attn[L][b], pos[b] = P-1 (the LM head's last arriver advances it to P), step = 0.
+// pos[b] = P-1 and step = 0 (the step bookkeeping after the LM head advances them to P and 1).
 __global__ __launch_bounds__(kBlock) void k_pf_finish(PfArgs p, DecodeArgs a) {
-  __shared__ double red[4];
   const int b = blockIdx.x;
   const Dims& dm = p.dm;
   const f16* src = p.hin + ((size_t)b * p.P + p.P - 1) * dm.d;  // after the final swap
   f16* dst = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
-  double s = 0.0;
-  for (int i = threadIdx.x; i < dm.d; i += kBlock) {
-    dst[i] = src[i];
-    const double v = h2f(src[i]);
-    s += v * v;
-  }
-  s = block_sum_d(s, red);
+  for (int i = threadIdx.x; i < dm.d; i += kBlock) dst[i] = src[i];
   if (threadIdx.x == 0) {
-    a.inv_attn[dm.L * dm.B + b] = (float)(1.0 / sqrt(s / dm.d + (double)dm.eps));
     a.pos[b] = p.P - 1;
     if (b == 0) *a.step = 0;
   }

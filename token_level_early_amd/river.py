@@ -73,6 +73,9 @@ def load():
         "river_device_status": [VP, VP],
         "river_export_river": [VP, I32, I32, VP, VP, VP],
         "river_debug_hidden": [VP, VP, VP],
+        "river_decode_backbone_steps": [VP, VP, I32, VP, VP],
+        "river_timer_arm": [VP, I32, I32],
+        "river_timer_read": [VP, P(F32), P(I32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -211,6 +214,26 @@ class River:
         _check(self.lib.river_decode_steps(self.ctx, _ptr(tok_in), _ptr(sched), int(S), float(tau),
                                            _ptr(tok_out), _ptr(exit_layer), _ptr(sim), _stream()))
         return tok_out
+
+    def decode_backbone_steps(self, tok_in, S, tok_out=None):
+        """S full-depth fp16 steps (backbone only, no exit test)."""
+        if tok_out is None:
+            tok_out = torch.empty(S, self.B, dtype=torch.int32, device=tok_in.device)
+        _check(self.lib.river_decode_backbone_steps(self.ctx, _ptr(tok_in), int(S), _ptr(tok_out),
+                                                    _stream()))
+        return tok_out
+
+    TIMER_OPS = {"qkv": 0, "attn": 1, "o": 2, "gu": 3, "down": 4, "lm": 5}
+
+    def timer_arm(self, op, max_launches):
+        _check(self.lib.river_timer_arm(self.ctx, self.TIMER_OPS[op], int(max_launches)))
+
+    def timer_read(self, max_launches):
+        """Per-launch durations (ms) of the armed op, in launch order."""
+        buf = (ctypes.c_float * max_launches)()
+        n = ctypes.c_int32(max_launches)
+        _check(self.lib.river_timer_read(self.ctx, buf, ctypes.byref(n)))
+        return list(buf[: n.value])
 
     def export_river(self, layer, which):
         """Canonical packed nibbles [N][ceil(K/2)] uint8 and scales [N][ceil(K/g)] fp16."""
