@@ -178,9 +178,10 @@ int river_decode_backbone_steps(river_ctx* ctx, const int32_t* tok_in, int32_t S
                                 void* stream);
 
 /* Benchmark support: per-launch timing of one kernel of the decode step with HIP events on the
- * call's stream. op: 0 QKV, 1 attention, 2 O projection, 3 gate|up, 4 down, 5 LM head. While
+ * call's stream. op: 0 QKV, 1 attention, 2 O projection, 3 gate|up, 4 down, 5 LM head, 6 persistent step kernel. While
  * armed, decode calls enqueue their kernels directly (no graph replay) and record an event pair
- * around each launch of `op`, up to max_launches pairs. river_timer_read waits for the last
+ * around each launch of `op`, up to max_launches pairs. op 6 times the launches of the
+ * persistent decode kernel (several decode steps per launch) instead. river_timer_read waits for the last
  * event, writes the durations (ms) of up to *n launches in launch order, sets *n to the count
  * and disarms. */
 int river_timer_arm(river_ctx* ctx, int32_t op, int32_t max_launches);

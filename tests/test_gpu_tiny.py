@@ -165,3 +165,49 @@ def test_multi_step_matches_single_steps(tiny):
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1]) and list(outs[0][1]) == [1, 2, 3, 4, 2, 1]
     assert torch.equal(outs[0][2], outs[1][2])  # deterministic, bit-identical cache
+
+
+def _run_path(w, persist, tau=None, sched=None, P=16, S=6):
+    import os
+    old = os.environ.get("RIVER_PERSIST")
+    os.environ["RIVER_PERSIST"] = "1" if persist else "0"
+    try:
+        rv = river.River(TINY, w, max_seq=P + S + 2, max_prefill=P)
+    finally:
+        if old is None:
+            del os.environ["RIVER_PERSIST"]
+        else:
+            os.environ["RIVER_PERSIST"] = old
+    toks = synth.prompt(TINY, 1, P, seed=4, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=TINY["L"])
+    ex = torch.empty(S, 1, dtype=torch.int32, device="cuda")
+    sim = torch.empty(S, 1, TINY["L"], dtype=torch.float32, device="cuda")
+    if sched is not None:
+        t = rv.decode_steps(pre["tokens"], sched=sched, exit_layer=ex)
+    else:
+        t = rv.decode_steps(pre["tokens"], S=S, tau=tau, exit_layer=ex, sim=sim)
+    out = (t.cpu().numpy().ravel(), ex.cpu().numpy().ravel(), sim.cpu().numpy(),
+           rv.hidden().float().cpu().numpy(), rv.kv_view().float().cpu().numpy(), rv.positions())
+    assert rv.device_status() == river.RIVER_OK
+    rv.close()
+    return out
+
+
+@pytest.mark.parametrize("mode", ["forced", "tau"])
+def test_persistent_kernel_matches_per_op_kernels(tiny, mode):
+    w, wn, orc = tiny
+    S = 6
+    sched = torch.tensor([[1], [3], [2], [4], [2], [1]], dtype=torch.int32, device="cuda")
+    kw = {"sched": sched} if mode == "forced" else {"tau": f32(0.2)}
+    a = _run_path(w, True, S=S, **kw)
+    b = _run_path(w, False, S=S, **kw)
+    assert a[5] == b[5]
+    assert np.array_equal(a[1], b[1])  # exit layers
+    assert rel_err(a[3], b[3]) <= TOL  # last step's residual stream
+    assert rel_err(a[4], b[4]) <= TOL  # whole shared cache
+    agree = (a[0] == b[0]).mean()
+    assert agree >= 5 / 6, (a[0], b[0])
+    if mode == "tau":
+        fin = ~np.isnan(b[2])
+        assert np.array_equal(np.isnan(a[2]), np.isnan(b[2]))
+        assert np.allclose(a[2][fin], b[2][fin], atol=2e-3)

@@ -25,6 +25,10 @@ hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K,
                                uint8_t* packed, uint16_t* scales, hipStream_t st);
 hipError_t river_launch_rope_table(float2* tab, int Tmax, int D, double theta, hipStream_t st);
 hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st);
+const void* river_persist_fn(const Dims& dm, int mode);
+int river_persist_grid(const void* fn);
+hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
+                                unsigned* bar, int* abort, hipStream_t st);
 
 hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const LayerDev* host_layers,
                                 int forced, float tau, hipStream_t st);
@@ -132,7 +136,7 @@ RiverLayout river_layout(const Dims& d) {
 // ---- scratch layout
 struct ScratchLayout {
   uint64_t hs, hmid, q, o, a2, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
-      layers, rope;
+      layers, rope, bar;
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t total;
@@ -166,7 +170,8 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.cnt = take((uint64_t)s.ncnt * 4);
   s.pml = take(B * d.H * s.smax * 2 * 4);
   s.pacc = take(B * d.H * s.smax * d.D * 4);
-  s.amax = take(B * 8);
+  s.amax = take(2 * B * 8);
+  s.bar = take(8);  // grid-barrier counter and abort flag of the persistent kernel
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
   const uint64_t M = B * d.max_prefill;
@@ -215,6 +220,10 @@ struct river_ctx {
   int timer_n = 0;
   hipStream_t timer_stream = nullptr;
   std::vector<hipEvent_t> timer_ev;
+  // persistent decode kernel ([mode]: 0 early exit, 1 backbone only); null = per-op kernels
+  const void* persist_fn[2] = {nullptr, nullptr};
+  int persist_nwg[2] = {0, 0};
+  int persist_chunk = 8;
 };
 
 static DecodeArgs base_args(const river_ctx* c) {
@@ -361,7 +370,7 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   if ((e = river_launch_fill(c->scratch + c->sl.route, (uint64_t)(d.L + 2) * d.B * 4, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.pos, 256 * 3, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.cnt, align256((uint64_t)c->sl.ncnt * 4), 0, st)) ||
-      (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)d.B * 8), 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)2 * d.B * 8), 0, st)) ||
       (e = river_launch_rope_table((float2*)a.rope, d.Tmax, d.D, (double)d.theta, st))) {
     river_destroy(c);
     return hip_fail(e, "init kernels");
@@ -373,6 +382,23 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
     river_destroy(c);
     return hip_fail(e, "layer table upload");
   }
+  const char* pe = getenv("RIVER_PERSIST");
+  if (pe && pe[0] == '1') {
+    for (int m = 0; m < 2; ++m) {
+      const void* fn = river_persist_fn(d, m);
+      const int nwg = fn ? river_persist_grid(fn) : 0;
+      // the attention phase needs one work item per (KV head, split); keep splits <= 64
+      if (fn && nwg >= d.Hkv && nwg / d.Hkv <= c->sl.smax) {
+        c->persist_fn[m] = fn;
+        c->persist_nwg[m] = nwg;
+      } else if (fn && nwg >= d.Hkv) {
+        c->persist_fn[m] = fn;
+        c->persist_nwg[m] = c->sl.smax * d.Hkv;
+      }
+    }
+  }
+  const char* pc = getenv("RIVER_PERSIST_CHUNK");
+  if (pc && atoi(pc) > 0) c->persist_chunk = atoi(pc);
   *out = c;
   return RIVER_OK;
 }
@@ -464,6 +490,7 @@ static bool same_key(const DecodeArgs& x, const DecodeArgs& y) {
          std::memcmp(&x.tau, &y.tau, sizeof(float)) == 0;
 }
 
+
 static void timer_hook(void* p, int op, int phase) {
   river_ctx* c = (river_ctx*)p;
   (void)op;
@@ -472,7 +499,36 @@ static void timer_hook(void* p, int op, int phase) {
   if (phase == 1) ++c->timer_n;
 }
 
+static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
+  const int B = c->dm.B, L = c->dm.L;
+  const int nwg = c->persist_nwg[mode];
+  const int splits = nwg / c->dm.Hkv;
+  unsigned* bar = (unsigned*)(c->scratch + c->sl.bar);
+  int* abort = (int*)(bar + 1);
+  const bool timed = (c->timer_op == TOP_PERSIST);
+  if (timed) c->timer_stream = st;
+  for (int s0 = 0; s0 < S; s0 += c->persist_chunk) {
+    const int n = (S - s0 < c->persist_chunk) ? S - s0 : c->persist_chunk;
+    DecodeArgs b = a;
+    b.tok_in = s0 ? a.tok_out + (size_t)(s0 - 1) * B : a.tok_in;
+    b.sched = a.sched ? a.sched + (size_t)s0 * B : nullptr;
+    b.tok_out = a.tok_out + (size_t)s0 * B;
+    b.exit_out = a.exit_out ? a.exit_out + (size_t)s0 * B : nullptr;
+    b.sim_out = a.sim_out ? a.sim_out + (size_t)s0 * B * L : nullptr;
+    hipError_t e = river_launch_fill(bar, 8, 0, st);
+    if (e == hipSuccess) e = river_launch_fill(c->scratch + c->sl.amax, (int64_t)2 * B * 8, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "barrier/argmax reset");
+    if (timed) timer_hook(c, TOP_PERSIST, 0);
+    e = river_launch_persist(c->persist_fn[mode], b, n, nwg, splits, bar, abort, st);
+    if (timed) timer_hook(c, TOP_PERSIST, 1);
+    if (e != hipSuccess) return hip_fail(e, "persistent decode launch");
+  }
+  return RIVER_OK;
+}
+
 static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
+  if (c->persist_fn[mode] && (c->timer_op < 0 || c->timer_op == TOP_PERSIST))
+    return run_persist(c, a, S, mode, st);
   hipError_t e = river_launch_begin(a, st);
   if (e != hipSuccess) return hip_fail(e, "begin launch");
   if (c->timer_op >= 0) {  // timed: direct launches with events around the chosen op
@@ -549,7 +605,7 @@ int river_decode_backbone_steps(river_ctx* c, const int32_t* tok_in, int32_t S, 
 
 int river_timer_arm(river_ctx* c, int32_t op, int32_t max_launches) {
   if (!c) return fail(RIVER_EINVAL, "ctx is NULL");
-  if (op < TOP_QKV || op > TOP_LM) return fail(RIVER_EINVAL, "op must be in [0, 5]");
+  if (op < TOP_QKV || op > TOP_PERSIST) return fail(RIVER_EINVAL, "op must be in [0, 6]");
   if (max_launches < 1) return fail(RIVER_EINVAL, "max_launches must be >= 1");
   while ((int)c->timer_ev.size() < 2 * max_launches) {
     hipEvent_t ev;

@@ -24,334 +24,9 @@
 // and the launch sequence of a step never changes (graph-capturable).
 #include "params.hpp"
 
-static constexpr int kRB16 = 2;  // rows per wave batch, fp16 stream
-static constexpr int kRB4 = 4;   // rows per wave batch, int4 stream
+#include <type_traits>
 
-template <int WPR>
-struct TileF16 {
-  static constexpr int NRG = 4 / WPR;
-  static constexpr int TR = NRG * kRB16;
-};
-template <int WPR>
-struct TileW4 {
-  static constexpr int NRG = 4 / WPR;
-  static constexpr int TR = NRG * kRB4;
-};
-
-// Logical output row of tile row r. QKV tiles of q/k heads pair row i with row i + D/2 of the
-// same head (rotate-half RoPE needs both); gate|up tiles pair gate row f with up row f.
-RIVER_DEV int logical_row(int op, int tile, int r, int TR, const Dims& dm) {
-  if (op == OP_QKV) {
-    const int qk_tiles = (dm.H + dm.Hkv) * dm.D / TR;
-    if (tile < qk_tiles) {
-      const int tph = dm.D / TR;
-      const int head = tile / tph;
-      const int half = TR / 2;
-      const int i0 = (tile % tph) * half;
-      return head * dm.D + (r < half ? i0 + r : dm.D / 2 + i0 + (r - half));
-    }
-    return tile * TR + r;
-  }
-  if (op == OP_GU) {
-    const int half = TR / 2;
-    return r < half ? tile * half + r : dm.F + tile * half + (r - half);
-  }
-  return tile * TR + r;
-}
-
-RIVER_DEV int op_rows(int op, const Dims& dm) {
-  switch (op) {
-    case OP_QKV: return dm.nqkv;
-    case OP_GU: return 2 * dm.F;
-    case OP_LM: return dm.V;
-    default: return dm.d;
-  }
-}
-RIVER_DEV int op_k(int op, const Dims& dm) {
-  switch (op) {
-    case OP_O: return dm.hd;
-    case OP_DOWN: return dm.F;
-    default: return dm.d;
-  }
-}
-
-RIVER_DEV const f16* f16_row(int op, int n, const LayerDev& lw, const DecodeArgs& a) {
-  const Dims& dm = a.dm;
-  switch (op) {
-    case OP_QKV:
-      if (n < dm.hd) return lw.wq + (size_t)n * dm.d;
-      if (n < dm.hd + dm.Hkv * dm.D) return lw.wk + (size_t)(n - dm.hd) * dm.d;
-      return lw.wv + (size_t)(n - dm.hd - dm.Hkv * dm.D) * dm.d;
-    case OP_O: return lw.wo + (size_t)n * dm.hd;
-    case OP_GU: return n < dm.F ? lw.wg + (size_t)n * dm.d : lw.wu + (size_t)(n - dm.F) * dm.d;
-    case OP_DOWN: return lw.wd + (size_t)n * dm.F;
-    default: return a.lm_head + (size_t)n * dm.d;
-  }
-}
-
-RIVER_DEV void w4_row(int op, int n, const LayerDev& lw, const Dims& dm, const uint8_t*& rp,
-                      const f16*& sp) {
-  const int K = op_k(op, dm);
-  const int64_t rb = w4_row_bytes(K), rs = w4_row_scales(K, dm.group);
-  const uint8_t* base;
-  const f16* sbase;
-  switch (op) {
-    case OP_QKV: base = lw.r_qkv; sbase = lw.s_qkv; break;
-    case OP_O: base = lw.r_o; sbase = lw.s_o; break;
-    case OP_GU: base = lw.r_gu; sbase = lw.s_gu; break;
-    default: base = lw.r_d; sbase = lw.s_d; break;
-  }
-  rp = base + (size_t)n * rb;
-  sp = sbase + (size_t)n * rs;
-}
-
-// ---------------------------------------------------------------------------------------
-// Loads. Pointers reach the kernels through structs in memory, which hides their address
-// space from the compiler; the casts make every weight/activation access a global_load
-// (vmcnt only), never a flat_load (which LDS waits would also drain).
-// ---------------------------------------------------------------------------------------
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) v4u g_v4u;
-typedef const __attribute__((address_space(1))) f16 g_f16;
-RIVER_DEV uint4 ldg16(const void* p) {
-  const v4u v = *(g_v4u*)p;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-RIVER_DEV f16 ldg2(const f16* p) { return *(g_f16*)p; }
-
-RIVER_DEV double sq8(uint4 u) {
-  const f16* h = (const f16*)&u;
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const double x = (double)h2f(h[i]);
-    s += x * x;
-  }
-  return s;
-}
-
-// fp16(v * inv * gain) on 8 values (fp32 products), or v unchanged without a gain
-RIVER_DEV uint4 norm8(uint4 u, uint4 g, float inv, bool has_gain) {
-  if (!has_gain) return u;
-  uint32_t* pu = (uint32_t*)&u;
-  const uint32_t* pg = (const uint32_t*)&g;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const h2 v = as_h2(pu[j]), gg = as_h2(pg[j]);
-    h2 r;
-    r.x = f2h(h2f(v.x) * inv * h2f(gg.x));
-    r.y = f2h(h2f(v.y) * inv * h2f(gg.y));
-    pu[j] = as_u32(r);
-  }
-  return u;
-}
-
-// Exit-test reduction: dot(u, v), |u|^2, |v|^2 of two d-vectors in fp64, lane j taking 16-byte
-// chunks j, j+64, ... and a fixed xor tree, so every wave that runs it gets identical bits.
-RIVER_DEV void wave_cos3(const f16* u, const f16* v, int d, double& dot, double& nu, double& nv) {
-  const int lane = threadIdx.x & (kWave - 1);
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0;
-  for (int base = 0; base < d; base += 4 * kChunkF16) {
-    uint4 ua[4], va[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = base + k * kChunkF16 + lane * 8;
-      const int ee = e < d ? e : 0;
-      ua[k] = ldg16(u + ee);
-      va[k] = ldg16(v + ee);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (base + k * kChunkF16 + lane * 8 >= d) continue;
-      const f16* hu = (const f16*)&ua[k];
-      const f16* hv = (const f16*)&va[k];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double x = (double)h2f(hu[i]), y = (double)h2f(hv[i]);
-        s0 += x * y;
-        s1 += x * x;
-        s2 += y * y;
-      }
-    }
-  }
-  dot = wave_sum_d(s0);
-  nu = wave_sum_d(s1);
-  nv = wave_sum_d(s2);
-}
-
-template <int NCH, int RB>
-RIVER_DEV void dot_rows_f16(const uint4 (&w)[RB][NCH], const h2 (&x)[NCH][4], float (&acc)[RB]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      s = dot2(x[c][0], as_h2(w[rb][c].x), s);
-      s = dot2(x[c][1], as_h2(w[rb][c].y), s);
-      s = dot2(x[c][2], as_h2(w[rb][c].z), s);
-      s = dot2(x[c][3], as_h2(w[rb][c].w), s);
-    }
-    acc[rb] = s;
-  }
-}
-
-// int4 rows: per chunk sum_k q_k x_k over the lane's 32 elements (one group), times its scale
-template <int NCH, int RB>
-RIVER_DEV void dot_rows_w4(const uint4 (&w)[RB][NCH], const f16 (&sc)[RB][NCH],
-                           const h2 (&x)[NCH][16], float (&acc)[RB]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float tot = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const uint32_t ww[4] = {w[rb][c].x, w[rb][c].y, w[rb][c].z, w[rb][c].w};
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        h2 p0, p1, p2, p3;
-        unpack8(ww[m], p0, p1, p2, p3);
-        s = dot2(p0, x[c][m * 4 + 0], s);
-        s = dot2(p1, x[c][m * 4 + 1], s);
-        s = dot2(p2, x[c][m * 4 + 2], s);
-        s = dot2(p3, x[c][m * 4 + 3], s);
-      }
-      tot = fmaf(h2f(sc[rb][c]), s, tot);
-    }
-    acc[rb] = tot;
-  }
-}
-
-// Block-wide fp64 sum of squares in one fixed order (thread t takes elements t, t+256, ...).
-RIVER_DEV double block_sumsq(const f16* v, int n, double* red) {
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += kBlock) {
-    const double x = (double)h2f(v[i]);
-    s += x * x;
-  }
-  return block_sum_d(s, red);
-}
-
-RIVER_DEV float inv_rms(double ss, int n, float eps) {
-  return (float)(1.0 / sqrt(ss / n + (double)eps));
-}
-
-// Sum of per-wave values over the WPR waves of this wave's row group (fixed order). WPR = 1
-// needs no exchange.
-template <int WPR>
-RIVER_DEV double rowgroup_sum(double v, double* red) {
-  if (WPR == 1) return v;
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
-  __syncthreads();
-  const int g0 = (w / WPR) * WPR;
-  double s = 0.0;
-  for (int j = 0; j < WPR; ++j) s += red[g0 + j];
-  return s;
-}
-
-// One wave's share of a tile on the fp16 stream: RB rows x NCH chunks of 512 elements
-// (chunk ids ws, ws+WPR, ...). Loads weights, the raw input and its gains, normalises the
-// input (computing its rms from the loaded values when `want_norm`), returns the RB dots.
-template <int NCH, int RB, int WPR, bool HAS_GAIN>
-RIVER_DEV void wave_gemv_f16(const f16* const (&rowp)[RB], const f16* xv, const f16* gain, int K,
-                             int ws, bool want_norm, float inv, int dnorm, float eps, double* red,
-                             float (&acc)[RB]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint4 wv[RB][NCH];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int e = (ws + c * WPR) * kChunkF16 + lane * 8;
-      const bool ok = rowp[rb] != nullptr && e < K;
-      // out-of-range chunks read a valid vector instead and meet x = 0; rows past N are
-      // never stored
-      wv[rb][c] = ldg16(ok ? (const void*)(rowp[rb] + e) : (const void*)xv);
-    }
-  uint4 xr[NCH], gr[NCH] = {};
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int e = (ws + c * WPR) * kChunkF16 + lane * 8;
-    const int ee = e < K ? e : 0;
-    xr[c] = ldg16(xv + ee);
-    if (HAS_GAIN) gr[c] = ldg16(gain + ee);
-  }
-  if (want_norm) {
-    double ss = 0.0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      if ((ws + c * WPR) * kChunkF16 + lane * 8 < K) ss += sq8(xr[c]);
-    ss = rowgroup_sum<WPR>(wave_sum_d(ss), red);
-    inv = inv_rms(ss, dnorm, eps);
-  }
-  h2 x[NCH][4];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const bool okx = (ws + c * WPR) * kChunkF16 + lane * 8 < K;
-    const uint4 u = okx ? norm8(xr[c], gr[c], inv, HAS_GAIN) : make_uint4(0, 0, 0, 0);
-    x[c][0] = as_h2(u.x);
-    x[c][1] = as_h2(u.y);
-    x[c][2] = as_h2(u.z);
-    x[c][3] = as_h2(u.w);
-  }
-  dot_rows_f16<NCH, RB>(wv, x, acc);
-}
-
-// One wave's share of a tile on the int4 stream: RB rows x NCH chunks of 2048 elements.
-template <int NCH, int RB, int WPR, bool HAS_GAIN>
-RIVER_DEV void wave_gemv_w4(const uint8_t* const (&rowp)[RB], const f16* const (&sclp)[RB],
-                            const f16* xv, const f16* gain, int K, int group, int ws,
-                            bool want_norm, float inv, int dnorm, float eps, double* red,
-                            float (&acc)[RB]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int nch = (K + kChunkW4 - 1) / kChunkW4;
-  uint4 wv[RB][NCH];
-  f16 sc[RB][NCH];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int cid = ws + c * WPR;
-      const bool ok = rowp[rb] != nullptr && cid < nch;
-      wv[rb][c] = ldg16(ok ? (const void*)(rowp[rb] + (size_t)cid * 1024 + lane * 16) : (const void*)xv);
-      sc[rb][c] = ldg2(ok ? sclp[rb] + (cid * kChunkW4 + lane * 32) / group : xv);
-    }
-  uint4 xr[NCH][4], gr[NCH][4] = {};
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = (ws + c * WPR) * kChunkW4 + lane * 32 + m * 8;
-      const int ee = e < K ? e : 0;
-      xr[c][m] = ldg16(xv + ee);
-      if (HAS_GAIN) gr[c][m] = ldg16(gain + ee);
-    }
-  if (want_norm) {
-    double ss = 0.0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if ((ws + c * WPR) * kChunkW4 + lane * 32 + m * 8 < K) ss += sq8(xr[c][m]);
-    ss = rowgroup_sum<WPR>(wave_sum_d(ss), red);
-    inv = inv_rms(ss, dnorm, eps);
-  }
-  h2 x[NCH][16];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const bool okx = (ws + c * WPR) * kChunkW4 + lane * 32 + m * 8 < K;
-      const uint4 u = okx ? norm8(xr[c][m], gr[c][m], inv, HAS_GAIN) : make_uint4(0, 0, 0, 0);
-      const uint32_t in[4] = {u.x, u.y, u.z, u.w};
-      h2 o[4];
-      pair_for_unpack(in, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[c][m * 4 + j] = o[j];
-    }
-  dot_rows_w4<NCH, RB>(wv, sc, x, acc);
-}
+#include "gemv.hpp"
 
 // MODE 0: early-exit decode (both weight streams in the grid; the route of the layer is decided
 //         by every QKV workgroup identically and read from device state by the later kernels).
@@ -360,11 +35,7 @@ template <int OP, int MODE, int NCH16, int WPR16, int NCH4, int WPR4>
 __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, int nwg16, int nwg4) {
   using T16 = TileF16<WPR16>;
   using T4 = TileW4<WPR4>;
-  constexpr int TRMAX = (T16::TR > T4::TR ? T16::TR : T4::TR);
-  constexpr bool kHasGain = (OP == OP_QKV || OP == OP_GU || OP == OP_LM);
-  __shared__ float ypart[TRMAX][4];
-  __shared__ float y[TRMAX];
-  __shared__ double dred[4];
+  __shared__ GemvSmem gsm;
   __shared__ double cos3[3];
 
   const Dims& dm = a.dm;
@@ -414,7 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, in
           } else {
             if (t < kWave) {
               double dot, n1, n2;
-              wave_cos3(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, vin, dm.d, dot, n1, n2);
+              wave_cos3<false>(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, vin, dm.d, dot, n1, n2);
               if (t == 0) {
                 cos3[0] = dot;
                 cos3[1] = n1;
@@ -443,171 +114,35 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, in
   }
   if (is4 != (route == ROUTE_RIVER)) return;
 
+  TileIn in;
+  in.layer = layer;
+  in.step = step;
+  in.pos = (OP == OP_QKV) ? a.pos[b] : 0;
+  in.b = b;
+  in.want_norm = false;
+  in.inv = 1.f;
+  in.gain = nullptr;
+  if (OP == OP_QKV) {
+    in.xv = vin;
+    in.gain = lwp->attn_norm;
+    in.want_norm = !have_inv;
+    in.inv = inv;
+  } else if (OP == OP_O) {
+    in.xv = a.o + (size_t)b * dm.hd;
+  } else if (OP == OP_GU) {
+    in.xv = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+    in.gain = lwp->mlp_norm;
+    in.want_norm = true;
+  } else if (OP == OP_DOWN) {
+    in.xv = a.a2 + (size_t)b * dm.F;
+  } else {
+    in.xv = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
+    in.gain = a.final_norm;
+    in.inv = a.inv_attn[dm.L * dm.B + b];
+  }
+  in.key = a.amax + b;
   const int tile = is4 ? (int)blockIdx.x - nwg16 : (int)blockIdx.x;
-  const int TR = is4 ? T4::TR : T16::TR;
-  const int N = op_rows(OP, dm);
-  const int K = op_k(OP, dm);
-  const int w = t / kWave, lane = t % kWave;
-
-  // input vector: x = fp16(v * inv * gain), or v itself
-  const f16* xv;
-  const f16* gain = nullptr;
-  bool want_norm = false;
-  if (OP == OP_QKV) {
-    xv = vin;
-    gain = lwp->attn_norm;
-    want_norm = !have_inv;
-  } else if (OP == OP_O) {
-    xv = a.o + (size_t)b * dm.hd;
-  } else if (OP == OP_GU) {
-    xv = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
-    gain = lwp->mlp_norm;
-    want_norm = true;
-  } else if (OP == OP_DOWN) {
-    xv = a.a2 + (size_t)b * dm.F;
-  } else {
-    xv = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
-    gain = a.final_norm;
-    inv = a.inv_attn[dm.L * dm.B + b];
-  }
-
-  // ---- GEMV ---------------------------------------------------------------------------
-  if (!is4) {
-    constexpr int RB = kRB16;
-    const int rg = w / WPR16, ws = w % WPR16;
-    const f16* rowp[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int n = logical_row(OP, tile, rg * RB + rb, T16::TR, dm);
-      rowp[rb] = (n < N) ? (OP == OP_LM ? a.lm_head + (size_t)n * dm.d : f16_row(OP, n, *lwp, a))
-                         : nullptr;
-    }
-    float acc[RB];
-    wave_gemv_f16<NCH16, RB, WPR16, kHasGain>(rowp, xv, gain, K, ws, want_norm, inv, dm.d, dm.eps, dred, acc);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float v = wave_sum(acc[rb]);
-      if (lane == 0) ypart[rg * RB + rb][ws] = v;
-    }
-    __syncthreads();
-    if (t < T16::TR) {
-      float s = 0.f;
-      for (int j = 0; j < WPR16; ++j) s += ypart[t][j];
-      y[t] = s;
-    }
-  } else {
-    constexpr int RB = kRB4;
-    const int rg = w / WPR4, ws = w % WPR4;
-    const uint8_t* rowp[RB];
-    const f16* sclp[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int n = logical_row(OP, tile, rg * RB + rb, T4::TR, dm);
-      if (n < N) {
-        w4_row(OP, n, *lwp, dm, rowp[rb], sclp[rb]);
-      } else {
-        rowp[rb] = nullptr;
-        sclp[rb] = nullptr;
-      }
-    }
-    float acc[RB];
-    wave_gemv_w4<NCH4, RB, WPR4, kHasGain>(rowp, sclp, xv, gain, K, dm.group, ws, want_norm, inv, dm.d,
-                                 dm.eps, dred, acc);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float v = wave_sum(acc[rb]);
-      if (lane == 0) ypart[rg * RB + rb][ws] = v;
-    }
-    __syncthreads();
-    if (t < T4::TR) {
-      float s = 0.f;
-      for (int j = 0; j < WPR4; ++j) s += ypart[t][j];
-      y[t] = s;
-    }
-  }
-  __syncthreads();
-
-  // ---- epilogues ----------------------------------------------------------------------
-  if (OP == OP_QKV) {
-    const int pos = a.pos[b];
-    const int qk_rows = (dm.H + dm.Hkv) * dm.D;
-    const int n0 = logical_row(OP, tile, 0, TR, dm);
-    if (n0 < qk_rows) {
-      const int half = TR / 2;
-      if (t < half) {
-        const int n = logical_row(OP, tile, t, TR, dm);
-        const int head = n / dm.D, i = n % dm.D;  // i < D/2
-        const float x0 = h2f(f2h(y[t])), x1 = h2f(f2h(y[t + half]));
-        const float2 cs = a.rope[(size_t)pos * (dm.D / 2) + i];
-        const f16 r0 = f2h(x0 * cs.x - x1 * cs.y);
-        const f16 r1 = f2h(x1 * cs.x + x0 * cs.y);
-        if (head < dm.H) {
-          f16* qd = a.q + (size_t)b * dm.hd + head * dm.D;
-          qd[i] = r0;
-          qd[i + dm.D / 2] = r1;
-        } else {
-          const int kvh = head - dm.H;
-          f16* kd = a.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) *
-                               (size_t)dm.Tmax * dm.D + (size_t)pos * dm.D;
-          kd[i] = r0;
-          kd[i + dm.D / 2] = r1;
-        }
-      }
-    } else if (t < TR) {
-      const int n = logical_row(OP, tile, t, TR, dm);
-      if (n < N) {
-        const int vi = n - qk_rows;
-        const int kvh = vi / dm.D, i = vi % dm.D;
-        f16* vd = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) *
-                             (size_t)dm.Tmax * dm.D + (size_t)pos * dm.D;
-        vd[i] = f2h(y[t]);
-      }
-    }
-  } else if (OP == OP_GU) {
-    const int half = TR / 2;
-    if (t < half) {
-      const int f = logical_row(OP, tile, t, TR, dm);
-      if (f < dm.F) {
-        const float g = h2f(f2h(y[t])), u = h2f(f2h(y[t + half]));
-        const float sg = g / (1.f + __expf(-g));
-        a.a2[(size_t)b * dm.F + f] = f2h(sg * u);
-      }
-    }
-  } else if (OP == OP_O) {
-    if (t < TR) {
-      const int n = tile * TR + t;
-      if (n < N) {
-        const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + n;
-        a.hmid[i] = f2h(h2f(a.hs[i]) + h2f(f2h(y[t])));
-      }
-    }
-  } else if (OP == OP_DOWN) {
-    if (t < TR) {
-      const int n = tile * TR + t;
-      if (n < N) {
-        const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + n;
-        a.hs[(size_t)dm.B * dm.d + i] = f2h(h2f(a.hmid[i]) + h2f(f2h(y[t])));
-      }
-    }
-  } else {  // OP_LM: logits, workgroup argmax (lowest index on ties), one 64-bit atomic max
-    if (t == 0) {
-      float best = -__builtin_inff();
-      int bi = 0x7FFFFFFF;
-      for (int r = 0; r < TR; ++r) {
-        const int n = tile * TR + r;
-        if (n >= N) break;
-        const float v = y[r];
-        if (a.logits) a.logits[(size_t)b * dm.V + n] = v;
-        if (v > best) {
-          best = v;
-          bi = n;
-        }
-      }
-      const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
-                                     (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
-      __hip_atomic_fetch_max(a.amax + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  gemv_tile<OP, false, NCH16, WPR16, NCH4, WPR4>(a, lwp, in, tile, is4, gsm);
 }
 
 // 1/rms of the final residual stream (input of the LM head), one workgroup per row.
@@ -642,22 +177,34 @@ __global__ void k_step_end(DecodeArgs a) {
 static constexpr int kMinChunk = 64;
 
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
-  constexpr int LPT = D / 8;       // lanes per position
-  constexpr int TPW = kWave / LPT;  // positions per wave pass
-  constexpr int NGRP = 4 * TPW;     // position groups per workgroup
-  constexpr int U = 2;              // positions per group per iteration (loads in flight)
-  __shared__ float sm_m[NGRP][G];
-  __shared__ float sm_l[NGRP][G];
-  __shared__ float sm_acc[NGRP][G][D];
-  __shared__ float sm_w[G][64];
-  __shared__ float sm_L[G];
-  __shared__ int lflag;
+struct AttnSmem {
+  static constexpr int LPT = D / 8;         // lanes per position
+  static constexpr int TPW = kWave / LPT;   // positions per wave pass
+  static constexpr int NGRP = 4 * TPW;      // position groups per workgroup
+  float m[NGRP][G];
+  float l[NGRP][G];
+  float acc[NGRP][G][D];
+  float w[G][64];
+  float L[G];
+  int flag;
+};
 
+// One split of one KV head: positions [s*chunk, min(T, (s+1)*chunk)) for the G query heads of
+// KV head kvh of row b, then the last-arriving split merges all splits into a.o. T = pos + 1.
+template <int D, int G, bool COH>
+RIVER_DEV void attn_item(const DecodeArgs& a, int layer, int s, int kvh, int b, int T, int smax,
+                         AttnSmem<D, G>& sm) {
+  constexpr int LPT = AttnSmem<D, G>::LPT;
+  constexpr int TPW = AttnSmem<D, G>::TPW;
+  constexpr int NGRP = AttnSmem<D, G>::NGRP;
+  constexpr int U = 2;  // positions per group per iteration (loads in flight)
+  auto& sm_m = sm.m;
+  auto& sm_l = sm.l;
+  auto& sm_acc = sm.acc;
+  auto& sm_w = sm.w;
+  auto& sm_L = sm.L;
+  int& lflag = sm.flag;
   const Dims& dm = a.dm;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int smax = a.attn_smax;
-  const int T = a.pos[b] + 1;
   const int chunk = max(kMinChunk, (T + smax - 1) / smax);
   const int seff = (T + chunk - 1) / chunk;
   const size_t head_stride = (size_t)dm.Tmax * D;
@@ -673,7 +220,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
     float qf[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 u = ldg16(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
+      const uint4 u = ldx16<COH>(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
       const f16* hp = (const f16*)&u;
 #pragma unroll
       for (int i = 0; i < 8; ++i) qf[g][i] = h2f(hp[i]) * qs;
@@ -777,9 +324,202 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
       const int g = idx / D, dd = idx % D;
       float A = 0.f;
       for (int j = 0; j < seff; ++j) A += sm_w[g][j] * wt_load(&a.pacc[(pbase + (size_t)g * smax + j) * D + dd]);
-      a.o[(size_t)b * dm.hd + (size_t)(kvh * G + g) * D + dd] = f2h(A / sm_L[g]);
+      sth<COH>(a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + dd, f2h(A / sm_L[g]));
     }
     if (threadIdx.x == 0) reset_counter(counter);
+  }
+  __syncthreads();  // LDS reuse by the next item
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
+  __shared__ AttnSmem<D, G> sm;
+  const int b = blockIdx.z;
+  attn_item<D, G, false>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b] + 1, a.attn_smax, sm);
+}
+
+// ---------------------------------------------------------------------------------------
+// Persistent decode: one cooperative launch runs S decode steps of one row. Every workgroup
+// walks the same phase sequence -- per layer QKV, attention, O, gate|up, down, then the LM
+// head -- taking tiles grid-stride, and all workgroups meet at a grid barrier between phases.
+// Routes, the position and the token live in registers (every workgroup derives the same
+// values); activations produced by one workgroup and read by others go through write-through
+// stores and coherent loads (COH = true). The barrier spins with a bound: a workgroup that
+// waits too long raises a shared abort flag and every later barrier returns at once, so every
+// wave always reaches the end of the kernel.
+// ---------------------------------------------------------------------------------------
+static constexpr unsigned kSpinLimit = 1u << 22;
+
+RIVER_DEV void grid_sync(unsigned* bar, unsigned& target, unsigned nwg, int* abort) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have landed
+  __syncthreads();
+  target += nwg;
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++spins & 255u) == 0) {
+        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        if (spins > kSpinLimit) {
+          __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int NCH16_, int WPR16_, int NCH4_, int WPR4_>
+struct Geo {
+  static constexpr int NCH16 = NCH16_, WPR16 = WPR16_, NCH4 = NCH4_, WPR4 = WPR4_;
+  static constexpr int TR16 = TileF16<WPR16_>::TR, TR4 = TileW4<WPR4_>::TR;
+};
+
+template <class GQ, class GO, class GDN, int OP, int MODE>
+RIVER_DEV void phase_tiles(const DecodeArgs& a, const LayerDev* lwp, const TileIn& in, bool r4,
+                           int ntiles, GemvSmem& gsm) {
+  (void)MODE;
+  using Gm = typename std::conditional<OP == OP_O, GO, typename std::conditional<OP == OP_DOWN, GDN, GQ>::type>::type;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
+    gemv_tile<OP, true, Gm::NCH16, Gm::WPR16, Gm::NCH4, Gm::WPR4>(a, lwp, in, tile, r4, gsm);
+}
+
+template <class GQ, class GO, class GDN, int D, int G, int MODE>
+__global__ __launch_bounds__(kBlock) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar,
+                                                    int* abort) {
+  __shared__ GemvSmem gsm;
+  __shared__ AttnSmem<D, G> asm_;
+  __shared__ double cos3[3];
+  const Dims& dm = a.dm;
+  const int b = 0;
+  const unsigned nwg = gridDim.x;
+  const int wg = blockIdx.x, t = threadIdx.x;
+  unsigned target = 0;
+  int pos = a.pos[b];
+  int tok = a.tok_in[b];
+
+  for (int step = 0; step < S; ++step, ++pos) {
+    if (tok < 0 || tok >= dm.V) {
+      if (wg == 0 && t == 0) atomicOr(a.err, ERR_TOKEN);
+      tok = 0;
+    }
+    int e_forced = dm.L;
+    if (MODE == 0 && a.sched) {
+      e_forced = a.sched[step * dm.B + b];
+      if (e_forced < dm.entry || e_forced > dm.L) {
+        if (wg == 0 && t == 0) atomicOr(a.err, ERR_FORCED);
+        e_forced = dm.L;
+      }
+    }
+    int route = ROUTE_BACKBONE;
+    for (int l = 1; l <= dm.L; ++l) {
+      const LayerDev* lwp = &a.layers[l - 1];
+      // ---------------- QKV (+ exit test after layer l-1)
+      TileIn in;
+      in.layer = l;
+      in.step = step;
+      in.pos = pos;
+      in.b = b;
+      in.gain = lwp->attn_norm;
+      in.want_norm = true;
+      in.inv = 1.f;
+      in.key = nullptr;
+      if (l == 1) {
+        in.xv = a.embed + (size_t)tok * dm.d;
+        if (wg == 0) {
+          f16* h0 = a.hs + (size_t)b * dm.d;
+          for (int i = t; i < dm.d; i += kBlock) sth<true>(h0 + i, in.xv[i]);
+          if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
+          if (a.sim_out)
+            for (int i = t; i < dm.L; i += kBlock)
+              a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
+        }
+      } else {
+        in.xv = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
+        const int lp = l - 1;
+        if (MODE == 0 && route == ROUTE_BACKBONE && lp >= dm.entry) {
+          if (a.sched) {
+            if (lp == e_forced) route = ROUTE_RIVER;
+          } else {
+            if (t < kWave) {
+              double dot, n1, n2;
+              wave_cos3<true>(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, in.xv, dm.d, dot, n1, n2);
+              if (t == 0) {
+                cos3[0] = dot;
+                cos3[1] = n1;
+                cos3[2] = n2;
+              }
+            }
+            __syncthreads();
+            const double dot = cos3[0], n1 = cos3[1], n2 = cos3[2];
+            __syncthreads();
+            const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
+            if (wg == 0 && t == 0 && a.sim_out)
+              a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
+            if (sim > (double)a.tau) route = ROUTE_RIVER;
+            in.inv = inv_rms(n2, dm.d, dm.eps);
+            in.want_norm = false;
+          }
+          if (route == ROUTE_RIVER && wg == 0 && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = lp;
+        }
+      }
+      const bool r4 = route == ROUTE_RIVER;
+      phase_tiles<GQ, GO, GDN, OP_QKV, MODE>(a, lwp, in, r4, r4 ? dm.nqkv / GQ::TR4 : dm.nqkv / GQ::TR16, gsm);
+      grid_sync(bar, target, nwg, abort);
+      if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
+        __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      // ---------------- attention
+      for (int it = wg; it < dm.Hkv * splits; it += nwg)
+        attn_item<D, G, true>(a, l, it % splits, it / splits, b, pos + 1, splits, asm_);
+      grid_sync(bar, target, nwg, abort);
+      // ---------------- O + residual
+      in.xv = a.o + (size_t)b * dm.hd;
+      in.gain = nullptr;
+      in.want_norm = false;
+      in.inv = 1.f;
+      phase_tiles<GQ, GO, GDN, OP_O, MODE>(a, lwp, in, r4,
+                                           r4 ? (dm.d + GO::TR4 - 1) / GO::TR4 : (dm.d + GO::TR16 - 1) / GO::TR16, gsm);
+      grid_sync(bar, target, nwg, abort);
+      // ---------------- gate|up + SwiGLU
+      in.xv = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
+      in.gain = lwp->mlp_norm;
+      in.want_norm = true;
+      phase_tiles<GQ, GO, GDN, OP_GU, MODE>(a, lwp, in, r4, r4 ? dm.F / (GQ::TR4 / 2) : dm.F / (GQ::TR16 / 2), gsm);
+      grid_sync(bar, target, nwg, abort);
+      // ---------------- down + residual
+      in.xv = a.a2 + (size_t)b * dm.F;
+      in.gain = nullptr;
+      in.want_norm = false;
+      phase_tiles<GQ, GO, GDN, OP_DOWN, MODE>(a, lwp, in, r4,
+                                              r4 ? (dm.d + GDN::TR4 - 1) / GDN::TR4 : (dm.d + GDN::TR16 - 1) / GDN::TR16, gsm);
+      grid_sync(bar, target, nwg, abort);
+    }
+    // ---------------- LM head (final RMSNorm on the fly) + argmax
+    {
+      TileIn in;
+      in.layer = dm.L + 1;
+      in.step = step;
+      in.pos = pos;
+      in.b = b;
+      in.xv = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
+      in.gain = a.final_norm;
+      in.want_norm = true;
+      in.inv = 1.f;
+      in.key = a.amax + (step & 1) * dm.B + b;
+      phase_tiles<GQ, GO, GDN, OP_LM, MODE>(a, nullptr, in, false, (dm.V + GQ::TR16 - 1) / GQ::TR16, gsm);
+      grid_sync(bar, target, nwg, abort);
+      const unsigned long long k = __hip_atomic_load(in.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+      if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
+    }
+  }
+  if (wg == 0 && t == 0) {
+    a.pos[b] = pos;
+    *a.step = S;
+    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
   }
 }
 
@@ -904,11 +644,74 @@ hipError_t river_decode_layers(const DecodeArgs& a, int mode, hipStream_t st,
   return river_launch_head(a, st, timer, tctx, top);
 }
 
-__global__ void k_begin_steps(int* step) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) *step = 0;
+// Start of a decode call on the per-op path: step counter and both argmax keys cleared.
+__global__ void k_begin_steps(DecodeArgs a) {
+  if (threadIdx.x == 0) *a.step = 0;
+  if ((int)threadIdx.x < 2 * a.dm.B)
+    __hip_atomic_store(a.amax + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t river_launch_begin(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_begin_steps, dim3(1), dim3(64), 0, st, a.step);
+  hipLaunchKernelGGL(k_begin_steps, dim3(1), dim3(64), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Persistent-kernel launchers. Instantiated for the three decoder families of the configs
+// (d/H*D/F of 256/256/688, 2048/2048/8192 and 4096/4096/14336); other shapes use the per-op
+// kernels.
+// ---------------------------------------------------------------------------------------
+static int geo_index(int K) {
+  const int n16 = (K + kChunkF16 - 1) / kChunkF16, n4 = (K + kChunkW4 - 1) / kChunkW4;
+  if (n16 <= 1 && n4 <= 1) return 1;
+  if (n16 <= 2 && n4 <= 1) return 2;
+  if (n16 <= 4 && n4 <= 1) return 3;
+  if (n16 <= 8 && n4 <= 2) return 4;
+  if (n16 <= 16 && n4 <= 4) return 5;
+  if (n16 <= 32 && n4 <= 8) return 6;
+  return 0;
+}
+
+typedef Geo<1, 1, 1, 1> Geo1;
+typedef Geo<2, 1, 1, 1> Geo2;
+typedef Geo<4, 1, 1, 1> Geo3;
+typedef Geo<8, 1, 2, 1> Geo4;
+typedef Geo<4, 4, 4, 1> Geo5;
+typedef Geo<8, 4, 4, 2> Geo6;
+
+// The kernel function for this model and mode, or null when not instantiated.
+const void* river_persist_fn(const Dims& dm, int mode) {
+  if (dm.B != 1) return nullptr;
+  const int gq = geo_index(dm.d), go = geo_index(dm.hd), gd = geo_index(dm.F);
+  const int G = dm.H / dm.Hkv;
+  if (gq == 1 && go == 1 && gd == 2 && dm.D == 64 && G == 2) {
+    return mode ? (const void*)k_persist<Geo1, Geo1, Geo2, 64, 2, 1> : (const void*)k_persist<Geo1, Geo1, Geo2, 64, 2, 0>;
+  }
+  if (gq == 3 && go == 3 && gd == 5 && dm.D == 64 && G == 4) {
+    return mode ? (const void*)k_persist<Geo3, Geo3, Geo5, 64, 4, 1> : (const void*)k_persist<Geo3, Geo3, Geo5, 64, 4, 0>;
+  }
+  if (gq == 4 && go == 4 && gd == 6 && dm.D == 128 && G == 4) {
+    return mode ? (const void*)k_persist<Geo4, Geo4, Geo6, 128, 4, 1> : (const void*)k_persist<Geo4, Geo4, Geo6, 128, 4, 0>;
+  }
+  return nullptr;
+}
+
+// Workgroups of the persistent grid: all co-resident (cooperative launch), at most 2 per CU.
+int river_persist_grid(const void* fn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess) return 0;
+  if (per_cu > 2) per_cu = 2;
+  return cus * per_cu;
+}
+
+hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
+                                unsigned* bar, int* abort, hipStream_t st) {
+  DecodeArgs aa = a;
+  int SS = S, sp = splits;
+  unsigned* br = bar;
+  int* ab = abort;
+  void* args[] = {&aa, &SS, &sp, &br, &ab};
+  return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kBlock), args, 0, st);
 }

@@ -44,7 +44,7 @@ struct Dims {
 enum { ROUTE_BACKBONE = 0, ROUTE_RIVER = 1 };
 
 // Device error word bits.
-enum { ERR_TOKEN = 1, ERR_FORCED = 2, ERR_POS = 4 };
+enum { ERR_TOKEN = 1, ERR_FORCED = 2, ERR_POS = 4, ERR_SYNC = 8 };
 
 // Everything a decode kernel needs. Passed by value.
 struct DecodeArgs {
@@ -71,7 +71,7 @@ struct DecodeArgs {
   int* cnt;         // counters, see CNT_*
   float* pml;       // attention split partials (m, l): [B][H][smax][2]
   float* pacc;      // attention split partials acc: [B][H][smax][D]
-  unsigned long long* amax;  // [B] LM-head argmax keys
+  unsigned long long* amax;  // [2][B] LM-head argmax keys (by step parity in the persistent kernel)
   int attn_smax;    // split count of the attention grid
   // per-call I/O (device pointers)
   const int* tok_in;     // [B]
@@ -90,7 +90,7 @@ static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn
 // Decode GEMV operations (one launch each).
 enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
 // Timer op codes (public, see river_timer_arm): the launches of one decode step in order.
-enum { TOP_QKV = 0, TOP_ATTN = 1, TOP_O = 2, TOP_GU = 3, TOP_DOWN = 4, TOP_LM = 5 };
+enum { TOP_QKV = 0, TOP_ATTN = 1, TOP_O = 2, TOP_GU = 3, TOP_DOWN = 4, TOP_LM = 5, TOP_PERSIST = 6 };
 
 // Prefill activations and state (scratch), passed by value to the prefill kernels.
 struct PfArgs {

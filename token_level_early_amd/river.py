@@ -223,7 +223,7 @@ class River:
                                                     _stream()))
         return tok_out
 
-    TIMER_OPS = {"qkv": 0, "attn": 1, "o": 2, "gu": 3, "down": 4, "lm": 5}
+    TIMER_OPS = {"qkv": 0, "attn": 1, "o": 2, "gu": 3, "down": 4, "lm": 5, "persist": 6}
 
     def timer_arm(self, op, max_launches):
         _check(self.lib.river_timer_arm(self.ctx, self.TIMER_OPS[op], int(max_launches)))
