@@ -135,7 +135,7 @@ RiverLayout river_layout(const Dims& d) {
 
 // ---- scratch layout
 struct ScratchLayout {
-  uint64_t hs, hmid, q, o, a2, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
+  uint64_t hs, hmid, q, o, a2, qkvr, gu, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
       layers, rope, bar;
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
@@ -160,6 +160,8 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.q = take(B * d.hd * 2);
   s.o = take(B * d.hd * 2);
   s.a2 = take(B * d.F * 2);
+  s.qkvr = take(B * d.nqkv * 2);
+  s.gu = take(B * 2 * d.F * 2);
   s.inv_attn = take((d.L + 1) * B * 4);
   s.inv_mlp = take(d.L * B * 4);
   s.route = take((d.L + 2) * B * 4);
@@ -242,6 +244,8 @@ static DecodeArgs base_args(const river_ctx* c) {
   a.q = (f16*)(sc + s.q);
   a.o = (f16*)(sc + s.o);
   a.a2 = (f16*)(sc + s.a2);
+  a.qkvr = (f16*)(sc + s.qkvr);
+  a.gu = (f16*)(sc + s.gu);
   a.inv_attn = (float*)(sc + s.inv_attn);
   a.inv_mlp = (float*)(sc + s.inv_mlp);
   a.route = (int*)(sc + s.route);

@@ -339,191 +339,6 @@ __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Persistent decode: one cooperative launch runs S decode steps of one row. Every workgroup
-// walks the same phase sequence -- per layer QKV, attention, O, gate|up, down, then the LM
-// head -- taking tiles grid-stride, and all workgroups meet at a grid barrier between phases.
-// Routes, the position and the token live in registers (every workgroup derives the same
-// values); activations produced by one workgroup and read by others go through write-through
-// stores and coherent loads (COH = true). The barrier spins with a bound: a workgroup that
-// waits too long raises a shared abort flag and every later barrier returns at once, so every
-// wave always reaches the end of the kernel.
-// ---------------------------------------------------------------------------------------
-static constexpr unsigned kSpinLimit = 1u << 22;
-
-RIVER_DEV void grid_sync(unsigned* bar, unsigned& target, unsigned nwg, int* abort) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have landed
-  __syncthreads();
-  target += nwg;
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned spins = 0;
-    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if ((++spins & 255u) == 0) {
-        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-        if (spins > kSpinLimit) {
-          __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
-}
-
-template <int NCH16_, int WPR16_, int NCH4_, int WPR4_>
-struct Geo {
-  static constexpr int NCH16 = NCH16_, WPR16 = WPR16_, NCH4 = NCH4_, WPR4 = WPR4_;
-  static constexpr int TR16 = TileF16<WPR16_>::TR, TR4 = TileW4<WPR4_>::TR;
-};
-
-template <class GQ, class GO, class GDN, int OP, int MODE>
-RIVER_DEV void phase_tiles(const DecodeArgs& a, const LayerDev* lwp, const TileIn& in, bool r4,
-                           int ntiles, GemvSmem& gsm) {
-  (void)MODE;
-  using Gm = typename std::conditional<OP == OP_O, GO, typename std::conditional<OP == OP_DOWN, GDN, GQ>::type>::type;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
-    gemv_tile<OP, true, Gm::NCH16, Gm::WPR16, Gm::NCH4, Gm::WPR4>(a, lwp, in, tile, r4, gsm);
-}
-
-template <class GQ, class GO, class GDN, int D, int G, int MODE>
-__global__ __launch_bounds__(kBlock) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar,
-                                                    int* abort) {
-  __shared__ GemvSmem gsm;
-  __shared__ AttnSmem<D, G> asm_;
-  __shared__ double cos3[3];
-  const Dims& dm = a.dm;
-  const int b = 0;
-  const unsigned nwg = gridDim.x;
-  const int wg = blockIdx.x, t = threadIdx.x;
-  unsigned target = 0;
-  int pos = a.pos[b];
-  int tok = a.tok_in[b];
-
-  for (int step = 0; step < S; ++step, ++pos) {
-    if (tok < 0 || tok >= dm.V) {
-      if (wg == 0 && t == 0) atomicOr(a.err, ERR_TOKEN);
-      tok = 0;
-    }
-    int e_forced = dm.L;
-    if (MODE == 0 && a.sched) {
-      e_forced = a.sched[step * dm.B + b];
-      if (e_forced < dm.entry || e_forced > dm.L) {
-        if (wg == 0 && t == 0) atomicOr(a.err, ERR_FORCED);
-        e_forced = dm.L;
-      }
-    }
-    int route = ROUTE_BACKBONE;
-    for (int l = 1; l <= dm.L; ++l) {
-      const LayerDev* lwp = &a.layers[l - 1];
-      // ---------------- QKV (+ exit test after layer l-1)
-      TileIn in;
-      in.layer = l;
-      in.step = step;
-      in.pos = pos;
-      in.b = b;
-      in.gain = lwp->attn_norm;
-      in.want_norm = true;
-      in.inv = 1.f;
-      in.key = nullptr;
-      if (l == 1) {
-        in.xv = a.embed + (size_t)tok * dm.d;
-        if (wg == 0) {
-          f16* h0 = a.hs + (size_t)b * dm.d;
-          for (int i = t; i < dm.d; i += kBlock) sth<true>(h0 + i, in.xv[i]);
-          if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
-          if (a.sim_out)
-            for (int i = t; i < dm.L; i += kBlock)
-              a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
-        }
-      } else {
-        in.xv = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
-        const int lp = l - 1;
-        if (MODE == 0 && route == ROUTE_BACKBONE && lp >= dm.entry) {
-          if (a.sched) {
-            if (lp == e_forced) route = ROUTE_RIVER;
-          } else {
-            if (t < kWave) {
-              double dot, n1, n2;
-              wave_cos3<true>(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, in.xv, dm.d, dot, n1, n2);
-              if (t == 0) {
-                cos3[0] = dot;
-                cos3[1] = n1;
-                cos3[2] = n2;
-              }
-            }
-            __syncthreads();
-            const double dot = cos3[0], n1 = cos3[1], n2 = cos3[2];
-            __syncthreads();
-            const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
-            if (wg == 0 && t == 0 && a.sim_out)
-              a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
-            if (sim > (double)a.tau) route = ROUTE_RIVER;
-            in.inv = inv_rms(n2, dm.d, dm.eps);
-            in.want_norm = false;
-          }
-          if (route == ROUTE_RIVER && wg == 0 && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = lp;
-        }
-      }
-      const bool r4 = route == ROUTE_RIVER;
-      phase_tiles<GQ, GO, GDN, OP_QKV, MODE>(a, lwp, in, r4, r4 ? dm.nqkv / GQ::TR4 : dm.nqkv / GQ::TR16, gsm);
-      grid_sync(bar, target, nwg, abort);
-      if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
-        __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      // ---------------- attention
-      for (int it = wg; it < dm.Hkv * splits; it += nwg)
-        attn_item<D, G, true>(a, l, it % splits, it / splits, b, pos + 1, splits, asm_);
-      grid_sync(bar, target, nwg, abort);
-      // ---------------- O + residual
-      in.xv = a.o + (size_t)b * dm.hd;
-      in.gain = nullptr;
-      in.want_norm = false;
-      in.inv = 1.f;
-      phase_tiles<GQ, GO, GDN, OP_O, MODE>(a, lwp, in, r4,
-                                           r4 ? (dm.d + GO::TR4 - 1) / GO::TR4 : (dm.d + GO::TR16 - 1) / GO::TR16, gsm);
-      grid_sync(bar, target, nwg, abort);
-      // ---------------- gate|up + SwiGLU
-      in.xv = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      in.gain = lwp->mlp_norm;
-      in.want_norm = true;
-      phase_tiles<GQ, GO, GDN, OP_GU, MODE>(a, lwp, in, r4, r4 ? dm.F / (GQ::TR4 / 2) : dm.F / (GQ::TR16 / 2), gsm);
-      grid_sync(bar, target, nwg, abort);
-      // ---------------- down + residual
-      in.xv = a.a2 + (size_t)b * dm.F;
-      in.gain = nullptr;
-      in.want_norm = false;
-      phase_tiles<GQ, GO, GDN, OP_DOWN, MODE>(a, lwp, in, r4,
-                                              r4 ? (dm.d + GDN::TR4 - 1) / GDN::TR4 : (dm.d + GDN::TR16 - 1) / GDN::TR16, gsm);
-      grid_sync(bar, target, nwg, abort);
-    }
-    // ---------------- LM head (final RMSNorm on the fly) + argmax
-    {
-      TileIn in;
-      in.layer = dm.L + 1;
-      in.step = step;
-      in.pos = pos;
-      in.b = b;
-      in.xv = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
-      in.gain = a.final_norm;
-      in.want_norm = true;
-      in.inv = 1.f;
-      in.key = a.amax + (step & 1) * dm.B + b;
-      phase_tiles<GQ, GO, GDN, OP_LM, MODE>(a, nullptr, in, false, (dm.V + GQ::TR16 - 1) / GQ::TR16, gsm);
-      grid_sync(bar, target, nwg, abort);
-      const unsigned long long k = __hip_atomic_load(in.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-      if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
-    }
-  }
-  if (wg == 0 && t == 0) {
-    a.pos[b] = pos;
-    *a.step = S;
-    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // Host-side launchers (called from api.cpp)
 // ---------------------------------------------------------------------------------------
 template <int OP, int MODE, int NCH16, int WPR16, int NCH4, int WPR4>
@@ -656,62 +471,3 @@ hipError_t river_launch_begin(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------------
-// Persistent-kernel launchers. Instantiated for the three decoder families of the configs
-// (d/H*D/F of 256/256/688, 2048/2048/8192 and 4096/4096/14336); other shapes use the per-op
-// kernels.
-// ---------------------------------------------------------------------------------------
-static int geo_index(int K) {
-  const int n16 = (K + kChunkF16 - 1) / kChunkF16, n4 = (K + kChunkW4 - 1) / kChunkW4;
-  if (n16 <= 1 && n4 <= 1) return 1;
-  if (n16 <= 2 && n4 <= 1) return 2;
-  if (n16 <= 4 && n4 <= 1) return 3;
-  if (n16 <= 8 && n4 <= 2) return 4;
-  if (n16 <= 16 && n4 <= 4) return 5;
-  if (n16 <= 32 && n4 <= 8) return 6;
-  return 0;
-}
-
-typedef Geo<1, 1, 1, 1> Geo1;
-typedef Geo<2, 1, 1, 1> Geo2;
-typedef Geo<4, 1, 1, 1> Geo3;
-typedef Geo<8, 1, 2, 1> Geo4;
-typedef Geo<4, 4, 4, 1> Geo5;
-typedef Geo<8, 4, 4, 2> Geo6;
-
-// The kernel function for this model and mode, or null when not instantiated.
-const void* river_persist_fn(const Dims& dm, int mode) {
-  if (dm.B != 1) return nullptr;
-  const int gq = geo_index(dm.d), go = geo_index(dm.hd), gd = geo_index(dm.F);
-  const int G = dm.H / dm.Hkv;
-  if (gq == 1 && go == 1 && gd == 2 && dm.D == 64 && G == 2) {
-    return mode ? (const void*)k_persist<Geo1, Geo1, Geo2, 64, 2, 1> : (const void*)k_persist<Geo1, Geo1, Geo2, 64, 2, 0>;
-  }
-  if (gq == 3 && go == 3 && gd == 5 && dm.D == 64 && G == 4) {
-    return mode ? (const void*)k_persist<Geo3, Geo3, Geo5, 64, 4, 1> : (const void*)k_persist<Geo3, Geo3, Geo5, 64, 4, 0>;
-  }
-  if (gq == 4 && go == 4 && gd == 6 && dm.D == 128 && G == 4) {
-    return mode ? (const void*)k_persist<Geo4, Geo4, Geo6, 128, 4, 1> : (const void*)k_persist<Geo4, Geo4, Geo6, 128, 4, 0>;
-  }
-  return nullptr;
-}
-
-// Workgroups of the persistent grid: all co-resident (cooperative launch), at most 2 per CU.
-int river_persist_grid(const void* fn) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlock, 0) != hipSuccess) return 0;
-  if (per_cu > 2) per_cu = 2;
-  return cus * per_cu;
-}
-
-hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
-                                unsigned* bar, int* abort, hipStream_t st) {
-  DecodeArgs aa = a;
-  int SS = S, sp = splits;
-  unsigned* br = bar;
-  int* ab = abort;
-  void* args[] = {&aa, &SS, &sp, &br, &ab};
-  return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kBlock), args, 0, st);
-}

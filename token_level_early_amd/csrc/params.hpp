@@ -61,6 +61,8 @@ struct DecodeArgs {
   f16* q;       // [B][H*D]
   f16* o;       // [B][H*D]
   f16* a2;      // [B][F]
+  f16* qkvr;    // [B][nqkv] un-rotated q|k|v (persistent kernel)
+  f16* gu;      // [B][2F]   gate|up outputs before SwiGLU (persistent kernel)
   float* inv_attn;  // [L+1][B]  1/rms of hs[l]
   float* inv_mlp;   // [L][B]    1/rms of hmid[l-1]
   int* route;       // [L+2][B]  route of layer l
