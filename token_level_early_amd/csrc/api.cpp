@@ -28,7 +28,7 @@ hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st)
 const void* river_persist_fn(const Dims& dm, int mode);
 int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
-                                unsigned* bar, int* abort, hipStream_t st);
+                                unsigned* bar, hipStream_t st);
 
 hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const LayerDev* host_layers,
                                 int forced, float tau, hipStream_t st);
@@ -173,7 +173,7 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.pml = take(B * d.H * s.smax * 2 * 4);
   s.pacc = take(B * d.H * s.smax * d.D * 4);
   s.amax = take(2 * B * 8);
-  s.bar = take(8);  // grid-barrier counter and abort flag of the persistent kernel
+  s.bar = take((uint64_t)kBarWords * 4);  // grid barrier of the persistent kernel
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
   const uint64_t M = B * d.max_prefill;
@@ -508,7 +508,6 @@ static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipSt
   const int nwg = c->persist_nwg[mode];
   const int splits = nwg / c->dm.Hkv;
   unsigned* bar = (unsigned*)(c->scratch + c->sl.bar);
-  int* abort = (int*)(bar + 1);
   const bool timed = (c->timer_op == TOP_PERSIST);
   if (timed) c->timer_stream = st;
   for (int s0 = 0; s0 < S; s0 += c->persist_chunk) {
@@ -519,11 +518,11 @@ static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipSt
     b.tok_out = a.tok_out + (size_t)s0 * B;
     b.exit_out = a.exit_out ? a.exit_out + (size_t)s0 * B : nullptr;
     b.sim_out = a.sim_out ? a.sim_out + (size_t)s0 * B * L : nullptr;
-    hipError_t e = river_launch_fill(bar, 8, 0, st);
+    hipError_t e = river_launch_fill(bar, (int64_t)kBarWords * 4, 0, st);
     if (e == hipSuccess) e = river_launch_fill(c->scratch + c->sl.amax, (int64_t)2 * B * 8, 0, st);
     if (e != hipSuccess) return hip_fail(e, "barrier/argmax reset");
     if (timed) timer_hook(c, TOP_PERSIST, 0);
-    e = river_launch_persist(c->persist_fn[mode], b, n, nwg, splits, bar, abort, st);
+    e = river_launch_persist(c->persist_fn[mode], b, n, nwg, splits, bar, st);
     if (timed) timer_hook(c, TOP_PERSIST, 1);
     if (e != hipSuccess) return hip_fail(e, "persistent decode launch");
   }

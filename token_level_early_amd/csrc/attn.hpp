@@ -1,0 +1,349 @@
+// Split-K GQA decode attention over the shared KV cache (one query position per row).
+//
+// Both River-LLM routes of a layer (the fp16 backbone block and its W4A16 exit-river copy)
+// read and write the same cache, so attention is route-independent: softmax(q K^T / sqrt(D)) V
+// over positions 0..pos of the query's KV head (River-LLM paper, Method: KV sharing between
+// backbone and exit river).
+//
+// Work split: workgroup `s` of KV head `kvh` owns positions [s*chunk, min(T, (s+1)*chunk)).
+// Lane layout: a "slot" of LPP = (G/GL)*D/8 lanes owns one position at a time; inside it,
+// D/8 lanes (8 dims each, one 16-byte K and V load per lane) serve GL query heads of the KV
+// group. Every thread takes U positions per block; the first block's K/V loads, the q loads
+// and (persistent path) the new position's k/v are all issued before any of them is used, and
+// each later block is loaded while the previous one is reduced. Scores are summed across the
+// D/8 lanes with DPP row permutations; softmax is exact per block and merged online (exp2
+// domain). Slots merge inside the wave, waves merge in LDS, and the last-arriving split of a
+// head merges all splits of it (one wave per query head for the weights, one batch of partial
+// loads per thread for the output).
+#pragma once
+
+#include "common.hpp"
+#include "gemv.hpp"
+#include "params.hpp"
+
+static constexpr int kMaxSplit = 64;  // partial-result slots per (row, query head)
+static constexpr int kAttnMinChunk = 64;
+
+template <int D, int G, int NT>
+struct AttnLds {
+  static constexpr int NW = NT / kWave;
+  float acc[NW][G][D];
+  float m[NW][G];
+  float l[NW][G];
+  float w[G][kMaxSplit];
+  int flag;
+};
+
+// Sum / max over the lanes of a wave that differ by multiples of LPT (8 or 16); every lane
+// gets the result.
+template <int LPT>
+RIVER_DEV float xslot_sum(float x) {
+#pragma unroll
+  for (int o = LPT; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+template <int LPT>
+RIVER_DEV float xslot_max(float x) {
+#pragma unroll
+  for (int o = LPT; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+RIVER_DEV float4 ld4_coh(const float* p) {
+  const uint4 u = ldx16<true>(p);
+  return make_float4(__builtin_bit_cast(float, u.x), __builtin_bit_cast(float, u.y),
+                     __builtin_bit_cast(float, u.z), __builtin_bit_cast(float, u.w));
+}
+
+// One split of one KV head for row b at position pos (T = pos + 1 positions).
+//   ROPE = false: rotated q is in a.q and K/V[pos] is already in the cache (per-op path).
+//   ROPE = true : un-rotated q/k/v are in a.qkvr (persistent path): q is rotated here; the
+//                 split that owns position pos rotates k, uses k/v of pos from registers and
+//                 appends them to the cache; activations move through agent-coherent accesses.
+template <int D, int G, int NT, bool ROPE, int UP = 4, int GLP = G>
+RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b, int pos, int nsplit,
+                          AttnLds<D, G, NT>& sm) {
+  constexpr bool COH = ROPE;
+  constexpr int LPT = D / 8;                       // lanes per head (8 dims each)
+  constexpr int GL = GLP;                          // query heads per lane
+  constexpr int HG = G / GL;                       // head groups per slot
+  constexpr int LPP = HG * LPT;                    // lanes per slot
+  constexpr int SPW = kWave / LPP;                 // slots per wave
+  constexpr int NW = NT / kWave;
+  constexpr int NS = NW * SPW;                     // slots per workgroup
+  constexpr int U = UP;                            // positions per thread per block
+  constexpr int BLK = NS * U;
+  constexpr int NCOL = G * D / 4;                  // float4 columns of the merged output
+  constexpr int TPC = NT / NCOL;                   // threads per column in the split merge
+  constexpr int MB = (kMaxSplit / TPC < 16) ? kMaxSplit / TPC : 16;  // partial loads per batch
+  static_assert(LPP <= kWave && HG * GL == G && (LPP == LPT || LPP == kWave), "lane layout");
+  static_assert(NCOL <= NT && (TPC & (TPC - 1)) == 0 && TPC <= kWave, "merge layout");
+  const Dims& dm = a.dm;
+  const int T = pos + 1;
+  const int chunk = max(kAttnMinChunk, (T + nsplit - 1) / nsplit);
+  const int seff = (T + chunk - 1) / chunk;
+  const size_t hstride = (size_t)dm.Tmax * D;
+  f16* Kb = a.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * hstride;
+  f16* Vb = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * hstride;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int slot = w * SPW + lane / LPP;
+  const int hg = (lane % LPP) / LPT;
+  const int sub = lane % LPT, d0 = sub * 8;
+  const size_t pbase = ((size_t)b * dm.H + (size_t)kvh * G) * nsplit;  // + g*nsplit + split
+
+  if (s < seff) {
+    const int t0 = s * chunk, t1 = min(T, t0 + chunk);
+    const bool owner = ROPE && t1 == T;  // this split holds the new position
+
+    auto load_block = [&](int tb, uint4 (&kk)[U], uint4 (&vv)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = tb + slot + u * NS;
+        // past the split (masked later) or the new position of the persistent path (taken
+        // from registers below): read a harmless in-range row instead
+        const size_t tt = (size_t)((t < t1 && !(ROPE && t == pos)) ? t : t0);
+        kk[u] = ldg16(Kb + tt * D + d0);
+        vv[u] = ldg16(Vb + tt * D + d0);
+      }
+    };
+    uint4 kc[U], vc[U];
+    load_block(t0, kc, vc);
+
+    // q of this lane's GL heads, dims [d0, d0+8)
+    const f16* qkv = a.qkvr + (size_t)b * dm.nqkv;
+    uint4 qraw[GL];
+#pragma unroll
+    for (int gl = 0; gl < GL; ++gl) {
+      const int g = hg * GL + gl;
+      qraw[gl] = ROPE ? ldx16<true>(qkv + (size_t)(kvh * G + g) * D + d0)
+                      : ldg16(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
+    }
+    uint4 kraw = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
+    if (owner) {
+      kraw = ldx16<true>(qkv + dm.hd + (size_t)kvh * D + d0);
+      vpos = ldx16<true>(qkv + dm.hd + (size_t)(dm.Hkv + kvh) * D + d0);
+    }
+    float2 cs[8];
+    if (ROPE) {
+      const float2* rope = a.rope + (size_t)pos * (D / 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cs[i] = rope[(d0 + i) % (D / 2)];
+    }
+    // rotate-half RoPE of dims [d0, d0+8), rounded to fp16; the partner dims (d +- D/2) are
+    // held by lane ^ LPT/2 of the same head
+    auto rope8 = [&](uint4 raw) {
+      const uint4 pr = make_uint4(__shfl_xor(raw.x, LPT / 2, kWave), __shfl_xor(raw.y, LPT / 2, kWave),
+                                  __shfl_xor(raw.z, LPT / 2, kWave), __shfl_xor(raw.w, LPT / 2, kWave));
+      const f16* x = (const f16*)&raw;
+      const f16* y = (const f16*)&pr;
+      uint4 out;
+      f16* o = (f16*)&out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xv = h2f(x[i]), yv = h2f(y[i]);
+        o[i] = (d0 < D / 2) ? f2h(xv * cs[i].x - yv * cs[i].y) : f2h(xv * cs[i].x + yv * cs[i].y);
+      }
+      return out;
+    };
+    h2 qh[GL][4];
+#pragma unroll
+    for (int gl = 0; gl < GL; ++gl) {
+      const uint4 u = ROPE ? rope8(qraw[gl]) : qraw[gl];
+      qh[gl][0] = as_h2(u.x);
+      qh[gl][1] = as_h2(u.y);
+      qh[gl][2] = as_h2(u.z);
+      qh[gl][3] = as_h2(u.w);
+    }
+    uint4 kpos = make_uint4(0, 0, 0, 0);
+    if (owner) {
+      kpos = rope8(kraw);
+      if (w == 0 && lane < LPT) {  // append K/V[pos] to the shared cache
+        const unsigned long long k2[2] = {kpos.x | ((unsigned long long)kpos.y << 32), kpos.z | ((unsigned long long)kpos.w << 32)};
+        const unsigned long long v2[2] = {vpos.x | ((unsigned long long)vpos.y << 32), vpos.z | ((unsigned long long)vpos.w << 32)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          __hip_atomic_store((g_u64*)(Kb + (size_t)pos * D + d0) + j, k2[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store((g_u64*)(Vb + (size_t)pos * D + d0) + j, v2[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    // scores are scaled by log2(e)/sqrt(D) after the fp32 dot (exact fp16 products)
+    const float qs = 1.4426950408889634f / sqrtf((float)D);
+
+    float m[GL], l[GL], acc[GL][8];
+#pragma unroll
+    for (int gl = 0; gl < GL; ++gl) {
+      m[gl] = -__builtin_inff();
+      l[gl] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[gl][i] = 0.f;
+    }
+    for (int tb = t0; tb < t1; tb += BLK) {
+      const bool more = tb + BLK < t1;
+      uint4 kn[U], vn[U];
+      if (more) load_block(tb + BLK, kn, vn);
+      if (owner) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (tb + slot + u * NS == pos) {
+            kc[u] = kpos;
+            vc[u] = vpos;
+          }
+      }
+      if (tb + slot < t1) {  // the slot has a position in this block (uniform per slot)
+        float sc[U][GL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const h2 k0 = as_h2(kc[u].x), k1 = as_h2(kc[u].y), k2 = as_h2(kc[u].z), k3 = as_h2(kc[u].w);
+#pragma unroll
+          for (int gl = 0; gl < GL; ++gl)
+            sc[u][gl] = dot2(qh[gl][3], k3, dot2(qh[gl][2], k2, dot2(qh[gl][1], k1, dot2(qh[gl][0], k0, 0.f))));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int gl = 0; gl < GL; ++gl) {
+            const float v = row_sum<LPT>(sc[u][gl]) * qs;
+            sc[u][gl] = (tb + slot + u * NS < t1) ? v : -__builtin_inff();
+          }
+#pragma unroll
+        for (int gl = 0; gl < GL; ++gl) {
+          float mb = m[gl];
+#pragma unroll
+          for (int u = 0; u < U; ++u) mb = fmaxf(mb, sc[u][gl]);
+          const float c = exp2f(m[gl] - mb);  // 0 while m is still -inf (mb is finite here)
+          float p[U], ps = 0.f;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            p[u] = exp2f(sc[u][gl] - mb);
+            ps += p[u];
+          }
+          l[gl] = l[gl] * c + ps;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float x = acc[gl][i] * c;
+#pragma unroll
+            for (int u = 0; u < U; ++u) x = fmaf(p[u], h2f(((const f16*)&vc[u])[i]), x);
+            acc[gl][i] = x;
+          }
+          m[gl] = mb;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kc[u] = kn[u];
+          vc[u] = vn[u];
+        }
+      }
+    }
+    // merge the SPW slots of this wave (lanes that differ by multiples of LPP)
+#pragma unroll
+    for (int gl = 0; gl < GL; ++gl) {
+      const int g = hg * GL + gl;
+      float M = m[gl], lg, xs[8];
+      if (LPP == kWave) {  // one slot per wave
+        lg = l[gl];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[i] = acc[gl][i];
+      } else {
+        M = xslot_max<LPT>(M);
+        const float sc = (m[gl] > -__builtin_inff()) ? exp2f(m[gl] - M) : 0.f;
+        lg = xslot_sum<LPT>(l[gl] * sc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[i] = xslot_sum<LPT>(acc[gl][i] * sc);
+      }
+      if (lane < LPP) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.acc[w][g][d0 + i] = xs[i];
+        if (sub == 0) {
+          sm.m[w][g] = M;
+          sm.l[w][g] = lg;
+        }
+      }
+    }
+    __syncthreads();
+    // merge the NW waves; write this split's partial (scaled to its own max) and (max, sum)
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int g = idx / D, dd = idx % D;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < NW; ++j)
+        if (sm.l[j][g] > 0.f) M = fmaxf(M, sm.m[j][g]);
+      float Ls = 0.f, A = 0.f;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const float sc = (sm.l[j][g] > 0.f) ? exp2f(sm.m[j][g] - M) : 0.f;
+        Ls += sm.l[j][g] * sc;
+        A += sm.acc[j][g][dd] * sc;
+      }
+      const size_t pi = pbase + (size_t)g * nsplit + s;
+      wt_store(&a.pacc[pi * D + dd], A);
+      if (dd == 0) {
+        wt_store(&a.pml[pi * 2 + 0], M);
+        wt_store(&a.pml[pi * 2 + 1], Ls);
+      }
+    }
+  }
+
+  int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
+  if (arrive_counter(counter, nsplit, &sm.flag)) {
+    // last arriver. Split weights exp2(m_j - M) / sum_j l_j exp2(m_j - M): one wave per
+    // query head, lane j holds split j.
+    for (int g = w; g < G; g += NW) {
+      const int j = lane;
+      float mj = -__builtin_inff(), lj = 0.f;
+      if (j < seff) {
+        const size_t pi = pbase + (size_t)g * nsplit + j;
+        mj = wt_load(&a.pml[pi * 2 + 0]);
+        lj = wt_load(&a.pml[pi * 2 + 1]);
+      }
+      const float M = wave_max(mj);
+      const float e = (j < seff) ? exp2f(mj - M) : 0.f;
+      const float Ls = wave_sum(lj * e);
+      sm.w[g][j] = e / Ls;
+    }
+    __syncthreads();
+    {
+      const int col = tid / TPC, r = tid % TPC;
+      const int g = col / (D / 4), d4 = (col % (D / 4)) * 4;
+      float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j0 = r; j0 < seff; j0 += MB * TPC) {
+        float4 v[MB];
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+          const int j = min(j0 + k * TPC, seff - 1);
+          v[k] = ld4_coh(&a.pacc[(pbase + (size_t)g * nsplit + j) * D + d4]);
+        }
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+          const int j = j0 + k * TPC;
+          const float wt = (j < seff) ? sm.w[g][j] : 0.f;
+          A.x = fmaf(wt, v[k].x, A.x);
+          A.y = fmaf(wt, v[k].y, A.y);
+          A.z = fmaf(wt, v[k].z, A.z);
+          A.w = fmaf(wt, v[k].w, A.w);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < TPC; o <<= 1) {
+        A.x += __shfl_xor(A.x, o, kWave);
+        A.y += __shfl_xor(A.y, o, kWave);
+        A.z += __shfl_xor(A.z, o, kWave);
+        A.w += __shfl_xor(A.w, o, kWave);
+      }
+      if (r == 0) {
+        f16 hv[4] = {f2h(A.x), f2h(A.y), f2h(A.z), f2h(A.w)};
+        f16* dst = a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d4;
+        if (COH) {
+          __hip_atomic_store((g_u64*)dst, __builtin_bit_cast(unsigned long long, hv), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          *(uint2*)dst = __builtin_bit_cast(uint2, hv);
+        }
+      }
+    }
+    if (tid == 0) reset_counter(counter);
+  }
+  __syncthreads();  // LDS reuse by the next item
+}

@@ -80,6 +80,37 @@ RIVER_DEV float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
+// DPP lane permutation of a float (full row and bank masks: every lane is written).
+template <int CTRL>
+RIVER_DEV float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N (8 or 16) lanes; every lane of the group gets the sum.
+// quad_perm [1,0,3,2] and [2,3,0,1] make quad sums; the half-row mirror (lane i <-> 7-i) adds
+// the other quad of the 8; the row mirror (i <-> 15-i) adds the other half of the 16.
+template <int N>
+RIVER_DEV float row_sum(float x) {
+  static_assert(N == 8 || N == 16, "row group width");
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  if (N == 16) x += dpp_f<0x140>(x);
+  return x;
+}
+
+// Sum over the wave without LDS traffic: row sums by DPP, then the four row results read as
+// scalars. Every lane gets the result.
+RIVER_DEV float wave_sum_fast(float v) {
+  v = row_sum<16>(v);
+  const int u = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 RIVER_DEV double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

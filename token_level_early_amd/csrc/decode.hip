@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "gemv.hpp"
+#include "attn.hpp"
 
 // MODE 0: early-exit decode (both weight streams in the grid; the route of the layer is decided
 //         by every QKV workgroup identically and read from device state by the later kernels).
@@ -168,174 +169,12 @@ __global__ void k_step_end(DecodeArgs a) {
   if (b == 0) *a.step = step + 1;
 }
 
-// ---------------------------------------------------------------------------------------
-// GQA flash-decode attention over the shared cache. Grid (smax, Hkv, B). Workgroup s covers
-// positions [s*chunk, min(T, (s+1)*chunk)) of one KV head for its G = H/Hkv query heads.
-// Each group of D/8 lanes owns one position at a time (16-byte K and V loads per lane) and
-// keeps an online-softmax state; groups merge in LDS, splits merge in the last arriver.
-// ---------------------------------------------------------------------------------------
-static constexpr int kMinChunk = 64;
-
-template <int D, int G>
-struct AttnSmem {
-  static constexpr int LPT = D / 8;         // lanes per position
-  static constexpr int TPW = kWave / LPT;   // positions per wave pass
-  static constexpr int NGRP = 4 * TPW;      // position groups per workgroup
-  float m[NGRP][G];
-  float l[NGRP][G];
-  float acc[NGRP][G][D];
-  float w[G][64];
-  float L[G];
-  int flag;
-};
-
-// One split of one KV head: positions [s*chunk, min(T, (s+1)*chunk)) for the G query heads of
-// KV head kvh of row b, then the last-arriving split merges all splits into a.o. T = pos + 1.
-template <int D, int G, bool COH>
-RIVER_DEV void attn_item(const DecodeArgs& a, int layer, int s, int kvh, int b, int T, int smax,
-                         AttnSmem<D, G>& sm) {
-  constexpr int LPT = AttnSmem<D, G>::LPT;
-  constexpr int TPW = AttnSmem<D, G>::TPW;
-  constexpr int NGRP = AttnSmem<D, G>::NGRP;
-  constexpr int U = 2;  // positions per group per iteration (loads in flight)
-  auto& sm_m = sm.m;
-  auto& sm_l = sm.l;
-  auto& sm_acc = sm.acc;
-  auto& sm_w = sm.w;
-  auto& sm_L = sm.L;
-  int& lflag = sm.flag;
-  const Dims& dm = a.dm;
-  const int chunk = max(kMinChunk, (T + smax - 1) / smax);
-  const int seff = (T + chunk - 1) / chunk;
-  const size_t head_stride = (size_t)dm.Tmax * D;
-  const f16* Kb = a.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * head_stride;
-  const f16* Vb = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * head_stride;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int grp = w * TPW + lane / LPT, sub = lane % LPT, d0 = sub * 8;
-  const size_t pbase = ((size_t)b * dm.H + (size_t)kvh * G) * smax;  // + g*smax + s
-
-  if (s < seff) {
-    const int t0 = s * chunk, t1 = min(T, t0 + chunk);
-    const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
-    float qf[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 u = ldx16<COH>(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
-      const f16* hp = (const f16*)&u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[g][i] = h2f(hp[i]) * qs;
-    }
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -__builtin_inff();
-      l[g] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
-    }
-    for (int tb = t0 + grp; tb < t1; tb += NGRP * U) {
-      uint4 kk[U], vv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * NGRP;
-        const size_t tt = (size_t)(t < t1 ? t : t0);
-        kk[u] = ldg16(Kb + tt * D + d0);
-        vv[u] = ldg16(Vb + tt * D + d0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * NGRP;
-        if (t >= t1) break;  // uniform within the lane group
-        const f16* kh = (const f16*)&kk[u];
-        const f16* vh = (const f16*)&vv[u];
-        float kf[8], vf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          kf[i] = h2f(kh[i]);
-          vf[i] = h2f(vh[i]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float sc = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sc = fmaf(qf[g][i], kf[i], sc);
-#pragma unroll
-          for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, kWave);
-          const float mn = fmaxf(m[g], sc);
-          const float c = exp2f(m[g] - mn);
-          const float p = exp2f(sc - mn);
-          l[g] = l[g] * c + p;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(acc[g][i], c, p * vf[i]);
-          m[g] = mn;
-        }
-      }
-    }
-    // merge the NGRP groups of this workgroup
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (sub == 0) {
-        sm_m[grp][g] = m[g];
-        sm_l[grp][g] = l[g];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm_acc[grp][g][d0 + i] = acc[g][i];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-      const int g = idx / D, dd = idx % D;
-      float M = -__builtin_inff();
-      for (int j = 0; j < NGRP; ++j) M = fmaxf(M, sm_m[j][g]);
-      float Lsum = 0.f, A = 0.f;
-      for (int j = 0; j < NGRP; ++j) {
-        const float sc = (sm_l[j][g] > 0.f) ? exp2f(sm_m[j][g] - M) : 0.f;
-        Lsum += sm_l[j][g] * sc;
-        A += sm_acc[j][g][dd] * sc;
-      }
-      const size_t pi = pbase + (size_t)g * smax + s;
-      wt_store(&a.pacc[pi * D + dd], A);
-      if (dd == 0) {
-        wt_store(&a.pml[pi * 2 + 0], M);
-        wt_store(&a.pml[pi * 2 + 1], Lsum);
-      }
-    }
-  }
-
-  int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
-  if (arrive_counter(counter, smax, &lflag)) {
-    // split weights exp2(m_s - M) / L per query head
-    if (threadIdx.x < G) {
-      const int g = threadIdx.x;
-      float M = -__builtin_inff();
-      for (int j = 0; j < seff; ++j) {
-        sm_w[g][j] = wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2]);
-        M = fmaxf(M, sm_w[g][j]);
-      }
-      float Lsum = 0.f;
-      for (int j = 0; j < seff; ++j) {
-        const float e = exp2f(sm_w[g][j] - M);
-        sm_w[g][j] = e;
-        Lsum += wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2 + 1]) * e;
-      }
-      sm_L[g] = Lsum;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-      const int g = idx / D, dd = idx % D;
-      float A = 0.f;
-      for (int j = 0; j < seff; ++j) A += sm_w[g][j] * wt_load(&a.pacc[(pbase + (size_t)g * smax + j) * D + dd]);
-      sth<COH>(a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + dd, f2h(A / sm_L[g]));
-    }
-    if (threadIdx.x == 0) reset_counter(counter);
-  }
-  __syncthreads();  // LDS reuse by the next item
-}
-
+// GQA split-K decode attention over the shared cache (attn.hpp). Grid (smax, Hkv, B).
 template <int D, int G>
 __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
-  __shared__ AttnSmem<D, G> sm;
+  __shared__ AttnLds<D, G, kBlock> sm;
   const int b = blockIdx.z;
-  attn_item<D, G, false>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b] + 1, a.attn_smax, sm);
+  attn_split<D, G, kBlock, false>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b], a.attn_smax, sm);
 }
 
 // ---------------------------------------------------------------------------------------

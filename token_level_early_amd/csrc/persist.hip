@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "gemv.hpp"
+#include "attn.hpp"
 
 static constexpr unsigned kSpinLimit = 1u << 22;
 static constexpr int kMaxK = 16384;  // longest GEMV input the LDS staging buffer holds
@@ -42,12 +43,25 @@ RIVER_DEV double pblock_sum_d(double v, double* red) {
   return s;
 }
 
-RIVER_DEV void grid_sync(unsigned* bar, unsigned& target, unsigned nwg, int* abort) {
+// Two-level grid barrier. Workgroups arrive on the counter of their group of kBarGroup; the
+// last arrival of a group bumps the completed-group counter, which every workgroup polls.
+// Counters only grow during a launch (epoch e is complete when the group counter reaches
+// e * group size and the top counter e * groups), so no reset is needed between barriers.
+// This keeps same-address atomics at kBarGroup + groups per barrier instead of one per
+// workgroup.
+RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have landed
   __syncthreads();
-  target += nwg;
+  ++epoch;
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned ng = (nwg + kBarGroup - 1) / kBarGroup;
+    const unsigned g = blockIdx.x / kBarGroup;
+    const unsigned gs = min((unsigned)kBarGroup, nwg - g * kBarGroup);
+    int* abort = (int*)(bar + kBarAbort);
+    const unsigned old = __hip_atomic_fetch_add(bar + (1 + g) * kBarStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == epoch * gs - 1) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned target = epoch * ng;
     unsigned spins = 0;
     while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
@@ -66,26 +80,11 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& target, unsigned nwg, int* abo
 // ---------------------------------------------------------------------------------------
 // LDS
 // ---------------------------------------------------------------------------------------
-// Attention lane mapping: a position is handled by G*LPT lanes, LPT = D/8 lanes per query head
-// (8 dims each); TPW positions per wave pass, NGRP position groups per workgroup.
-template <int D, int G>
-struct AttnBufs {
-  static constexpr int LPT = D / 8;
-  static constexpr int LPP = G * LPT;      // lanes per position
-  static constexpr int TPW = kWave / LPP;  // positions per wave pass
-  static constexpr int NGRP = kPW * TPW;
-  float m[NGRP][G];
-  float l[NGRP][G];
-  float acc[NGRP][G][D];
-  float w[G][64];
-  float L[G];
-};
-
 template <int D, int G>
 struct PSmem {
   union {
     h2 x[kMaxK / 2];  // staged GEMV input
-    AttnBufs<D, G> at;
+    AttnLds<D, G, kPB> at;
   };
   double red[kPW];
   double c3[3];
@@ -223,71 +222,111 @@ RIVER_DEV const f16* row16(const DecodeArgs& a, const LayerDev* lw, int n) {
   return a.lm_head + (size_t)n * dm.d;
 }
 
-// One streamed item: SEG chunks of one row (fp16: 512 elements per chunk, int4: 2048).
+// This wave's rows [r0, r1) of an N-row phase (rows split evenly over all waves of the grid).
+RIVER_DEV void wave_rows(int N, int& r0, int& r1) {
+  const int gw = blockIdx.x * kPW + threadIdx.x / kWave, GW = gridDim.x * kPW;
+  // wave-uniform: keep the row walk (and the row pointers) in scalar registers
+  r0 = __builtin_amdgcn_readfirstlane((int)((long long)gw * N / GW));
+  r1 = __builtin_amdgcn_readfirstlane((int)((long long)(gw + 1) * N / GW));
+}
+
+// Streamed items. fp16 stream: an item is SEG chunks (512 elements each) of one row, a row
+// being nseg items. int4 stream: the padded river layout makes the rows of one matrix a
+// single run of 1 KiB chunks (2048 elements each; the group scales likewise), so a wave's rows
+// [r0, r1) are the flat chunk range [r0*nch, r1*nch) and an item is the next SEG chunks of
+// that range, crossing row ends: every item keeps SEG loads per lane in flight whatever K is.
 template <bool IS4, int SEG>
 struct Seg {
   uint4 w[SEG];
-  f16 s[SEG];
+  h2 s[(SEG + 1) / 2];  // int4 group scales, two chunks per register
 };
 
-template <int OP, bool IS4, int SEG>
-RIVER_DEV void load_seg(const DecodeArgs& a, const LayerDev* lw, int K, int nch, int row, int seg,
-                        Seg<IS4, SEG>& sg) {
+// fp16: chunks [seg*SEG, seg*SEG+SEG) of `row`.
+template <int OP, int SEG>
+RIVER_DEV void load_seg16(const DecodeArgs& a, const LayerDev* lw, int K, int nch, int row, int seg,
+                          Seg<false, SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
-  if (!IS4) {
-    const f16* rp = row16<OP>(a, lw, row);
+  const f16* rp = row16<OP>(a, lw, row);
 #pragma unroll
-    for (int c = 0; c < SEG; ++c) {
-      const int ch = seg * SEG + c;
-      if (ch >= nch) break;  // uniform; dot_seg stops at the same chunk
-      const int e = ch * kChunkF16 + lane * 8;
-      sg.w[c] = ldg16(rp + (e < K ? e : 0));  // past K (ragged row end) meets x = 0
-    }
-  } else {
-    const uint8_t* rp;
-    const f16* sp;
-    w4_row(OP, row, *lw, a.dm, rp, sp);
-#pragma unroll
-    for (int c = 0; c < SEG; ++c) {
-      const int ch = seg * SEG + c;
-      if (ch >= nch) break;
-      sg.w[c] = ldg16(rp + (size_t)ch * 1024 + lane * 16);
-      sg.s[c] = ldg2(sp + (ch * kChunkW4 + lane * 32) / a.dm.group);
-    }
+  for (int c = 0; c < SEG; ++c) {
+    const int ch = seg * SEG + c;
+    if (ch >= nch) break;  // uniform; dot_seg16 stops at the same chunk
+    const int e = ch * kChunkF16 + lane * 8;
+    sg.w[c] = ldg16(rp + (e < K ? e : 0));  // past K (ragged row end) meets x = 0
   }
 }
 
-template <bool IS4, int SEG>
-RIVER_DEV float dot_seg(const Seg<IS4, SEG>& sg, const h2* xl, int nch, int seg) {
+template <int SEG>
+RIVER_DEV float dot_seg16(const Seg<false, SEG>& sg, const h2* xl, int nch, int seg, float acc) {
   const int lane = threadIdx.x & (kWave - 1);
-  float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < SEG; ++c) {
     const int ch = seg * SEG + c;
     if (ch >= nch) break;
-    if (!IS4) {
-      const h2* x = xl + (ch * kWave + lane) * 4;
-      acc = dot2(x[0], as_h2(sg.w[c].x), acc);
-      acc = dot2(x[1], as_h2(sg.w[c].y), acc);
-      acc = dot2(x[2], as_h2(sg.w[c].z), acc);
-      acc = dot2(x[3], as_h2(sg.w[c].w), acc);
-    } else {
-      const uint32_t ww[4] = {sg.w[c].x, sg.w[c].y, sg.w[c].z, sg.w[c].w};
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const h2* x = xl + ((ch * 4 + m) * kWave + lane) * 4;
-        h2 p0, p1, p2, p3;
-        unpack8(ww[m], p0, p1, p2, p3);
-        s = dot2(p0, x[0], s);
-        s = dot2(p1, x[1], s);
-        s = dot2(p2, x[2], s);
-        s = dot2(p3, x[3], s);
-      }
-      acc = fmaf(h2f(sg.s[c]), s, acc);
-    }
+    const h2* x = xl + (ch * kWave + lane) * 4;
+    acc = dot2(x[0], as_h2(sg.w[c].x), acc);
+    acc = dot2(x[1], as_h2(sg.w[c].y), acc);
+    acc = dot2(x[2], as_h2(sg.w[c].z), acc);
+    acc = dot2(x[3], as_h2(sg.w[c].w), acc);
   }
   return acc;
+}
+
+// int4: flat chunks [q0, min(q0 + SEG, qend)) of the matrix starting at (base, sbase).
+template <int SEG>
+RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, int group, int q0, int qend,
+                         Seg<true, SEG>& sg) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint8_t* wp = base + (size_t)q0 * 1024 + lane * 16;
+  const f16* sp = sbase + (size_t)q0 * (kChunkW4 / group) + (lane * 32) / group;
+#pragma unroll
+  for (int c = 0; c < SEG; ++c) {
+    if (q0 + c >= qend) break;  // uniform
+    sg.w[c] = ldg16(wp + c * 1024);
+    const f16 sv = ldg2(sp + c * (kChunkW4 / group));
+    if (c & 1) sg.s[c / 2].y = sv;
+    else sg.s[c / 2].x = sv;
+  }
+}
+
+// Reduces the int4 item starting at flat chunk q0 (chunk ch of row `row`); calls fin(row, lane
+// partial) at every row end and advances (row, ch).
+template <int SEG, typename Fin>
+RIVER_DEV void dot_seg4(const Seg<true, SEG>& sg, const h2* xl, int nch, int q0, int qend, int& row,
+                        int& ch, float& acc, Fin&& fin) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int c = 0; c < SEG; ++c) {
+    if (q0 + c >= qend) break;
+    const uint32_t ww[4] = {sg.w[c].x, sg.w[c].y, sg.w[c].z, sg.w[c].w};
+    float sd = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const h2* x = xl + ((ch * 4 + m) * kWave + lane) * 4;
+      h2 p0, p1, p2, p3;
+      unpack8(ww[m], p0, p1, p2, p3);
+      sd = dot2(p0, x[0], sd);
+      sd = dot2(p1, x[1], sd);
+      sd = dot2(p2, x[2], sd);
+      sd = dot2(p3, x[3], sd);
+    }
+    acc = fmaf(h2f((c & 1) ? sg.s[c / 2].y : sg.s[c / 2].x), sd, acc);
+    if (++ch == nch) {
+      fin(row, acc);
+      acc = 0.f;
+      ch = 0;
+      ++row;
+    }
+  }
+}
+
+// Base of the packed river matrix of OP and of its scales.
+template <int OP>
+RIVER_DEV void w4_base(const LayerDev* lw, const uint8_t*& base, const f16*& sbase) {
+  if (OP == OP_QKV) { base = lw->r_qkv; sbase = lw->s_qkv; }
+  else if (OP == OP_O) { base = lw->r_o; sbase = lw->s_o; }
+  else if (OP == OP_GU) { base = lw->r_gu; sbase = lw->s_gu; }
+  else { base = lw->r_d; sbase = lw->s_d; }
 }
 
 // Epilogue inputs of a streamed phase.
@@ -298,30 +337,28 @@ struct StreamOut {
   unsigned long long* key;  // LM argmax key
 };
 
-// Streams this wave's rows [r0, r1) of an N-row phase; the input vector is staged in xl.
+template <bool IS4>
+RIVER_DEV int n_chunks(int K) {
+  return IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
+}
+
+// Streams this wave's rows of an N-row phase; the input vector is staged in xl and the first
+// item is already in b0 (prefetch_first).
 template <int OP, bool IS4, int SEG>
 RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K, const h2* xl,
                            const StreamOut& so, Seg<IS4, SEG>& b0) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int gw = blockIdx.x * kPW + threadIdx.x / kWave, GW = gridDim.x * kPW;
-  const int r0 = (int)((long long)gw * N / GW), r1 = (int)((long long)(gw + 1) * N / GW);
-  const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
-  const int nseg = (nch + SEG - 1) / SEG;
-  const int nitems = (r1 - r0) * nseg;
+  int r0, r1;
+  wave_rows(N, r0, r1);
+  if (r0 >= r1) return;
+  const int nch = n_chunks<IS4>(K);
   // residuals of this wave's rows, one per lane (O and DOWN)
   f16 res = (f16)0.0f;
   if ((OP == OP_O || OP == OP_DOWN) && r0 + lane < r1) res = ldh<true>(so.resid + r0 + lane);
   float best = -__builtin_inff();
   int bi = 0x7FFFFFFF;
-  Seg<IS4, SEG> b1;  // b0 holds the first segment, issued by prefetch_first
-  float acc = 0.f;
-  auto finish = [&](int it, float part) {
-    acc += part;
-    const int seg = it % nseg;
-    if (seg != nseg - 1) return;
-    const int row = r0 + it / nseg;
-    const float v = wave_sum(acc);
-    acc = 0.f;
+  auto fin = [&](int row, float part) {
+    const float v = wave_sum_fast(part);
     if (OP == OP_LM) {
       if (v > best) {
         best = v;
@@ -341,14 +378,43 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
       if (OP == OP_LM && so.logits) so.logits[row] = v;
     }
   };
-  int it = 0;
-  for (; it + 1 < nitems; it += 2) {
-    load_seg<OP, IS4, SEG>(a, lw, K, nch, r0 + (it + 1) / nseg, (it + 1) % nseg, b1);
-    finish(it, dot_seg<IS4, SEG>(b0, xl, nch, it % nseg));
-    if (it + 2 < nitems) load_seg<OP, IS4, SEG>(a, lw, K, nch, r0 + (it + 2) / nseg, (it + 2) % nseg, b0);
-    finish(it + 1, dot_seg<IS4, SEG>(b1, xl, nch, (it + 1) % nseg));
+  Seg<IS4, SEG> b1;
+  float acc = 0.f;
+  if constexpr (!IS4) {
+    const int nseg = (nch + SEG - 1) / SEG;
+    const int nitems = (r1 - r0) * nseg;
+    auto step = [&](int it, const Seg<false, SEG>& sg) {
+      const int seg = it % nseg;
+      acc = dot_seg16<SEG>(sg, xl, nch, seg, acc);
+      if (seg == nseg - 1) {
+        fin(r0 + it / nseg, acc);
+        acc = 0.f;
+      }
+    };
+    int it = 0;
+    for (; it + 1 < nitems; it += 2) {
+      load_seg16<OP, SEG>(a, lw, K, nch, r0 + (it + 1) / nseg, (it + 1) % nseg, b1);
+      step(it, b0);
+      if (it + 2 < nitems) load_seg16<OP, SEG>(a, lw, K, nch, r0 + (it + 2) / nseg, (it + 2) % nseg, b0);
+      step(it + 1, b1);
+    }
+    if (it < nitems) step(it, b0);
+  } else {
+    const uint8_t* base;
+    const f16* sbase;
+    w4_base<OP>(lw, base, sbase);
+    const int grp = a.dm.group;
+    const int qbeg = r0 * nch, qend = r1 * nch;
+    int row = r0, ch = 0;
+    int q = qbeg;
+    for (; q + SEG < qend; q += 2 * SEG) {
+      load_seg4<SEG>(base, sbase, grp, q + SEG, qend, b1);
+      dot_seg4<SEG>(b0, xl, nch, q, qend, row, ch, acc, fin);
+      if (q + 2 * SEG < qend) load_seg4<SEG>(base, sbase, grp, q + 2 * SEG, qend, b0);
+      dot_seg4<SEG>(b1, xl, nch, q + SEG, qend, row, ch, acc, fin);
+    }
+    if (q < qend) dot_seg4<SEG>(b0, xl, nch, q, qend, row, ch, acc, fin);
   }
-  if (it < nitems) finish(it, dot_seg<IS4, SEG>(b0, xl, nch, it % nseg));
   if (OP == OP_LM && lane == 0 && bi != 0x7FFFFFFF) {
     const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
                                    (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
@@ -356,17 +422,22 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
   }
 }
 
-// Issues the first segment of this wave's rows (weights only: allowed before the inputs of the
+// Issues the first item of this wave's rows (weights only: allowed before the inputs of the
 // phase exist, e.g. before the grid barrier or while the input vector is staged).
 template <int OP, bool IS4, int SEG>
-RIVER_DEV bool prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K,
-                              Seg<IS4, SEG>& pre) {
-  const int gw = blockIdx.x * kPW + threadIdx.x / kWave, GW = gridDim.x * kPW;
-  const int r0 = (int)((long long)gw * N / GW), r1 = (int)((long long)(gw + 1) * N / GW);
-  if (r0 >= r1) return false;
-  const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
-  load_seg<OP, IS4, SEG>(a, lw, K, nch, r0, 0, pre);
-  return true;
+RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K, Seg<IS4, SEG>& pre) {
+  int r0, r1;
+  wave_rows(N, r0, r1);
+  if (r0 >= r1) return;
+  const int nch = n_chunks<IS4>(K);
+  if constexpr (!IS4) {
+    load_seg16<OP, SEG>(a, lw, K, nch, r0, 0, pre);
+  } else {
+    const uint8_t* base;
+    const f16* sbase;
+    w4_base<OP>(lw, base, sbase);
+    load_seg4<SEG>(base, sbase, a.dm.group, r0 * nch, r1 * nch, pre);
+  }
 }
 
 // One GEMV phase: prefetch the first weight segment, stage the input, stream the rows.
@@ -381,192 +452,16 @@ RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K,
 }
 
 // ---------------------------------------------------------------------------------------
-// Attention (one split of one KV head), reading un-rotated q/k/v of the new position
-// ---------------------------------------------------------------------------------------
-static constexpr int kMinChunkP = 64;
-
-template <int D, int G>
-RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b, int pos,
-                          int smax, AttnBufs<D, G>& sm, int* flag) {
-  constexpr int LPT = AttnBufs<D, G>::LPT;
-  constexpr int LPP = AttnBufs<D, G>::LPP;
-  constexpr int TPW = AttnBufs<D, G>::TPW;
-  constexpr int NGRP = AttnBufs<D, G>::NGRP;
-  constexpr int U = 4;  // positions per group per iteration (loads in flight)
-  static_assert(LPP <= kWave, "one position must fit in a wave");
-  const Dims& dm = a.dm;
-  const int T = pos + 1;
-  const int chunk = max(kMinChunkP, (T + smax - 1) / smax);
-  const int seff = (T + chunk - 1) / chunk;
-  const size_t hstride = (size_t)dm.Tmax * D;
-  f16* Kb = a.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * hstride;
-  f16* Vb = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * hstride;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const int grp = w * TPW + lane / LPP;     // position group
-  const int g = (lane % LPP) / LPT;         // query head within the KV group
-  const int sub = lane % LPT, d0 = sub * 8;  // dims [d0, d0+8)
-  const size_t pbase = ((size_t)b * dm.H + (size_t)kvh * G) * smax;
-  const f16* qkv = a.qkvr + (size_t)b * dm.nqkv;
-  const float2* rope = a.rope + (size_t)pos * (D / 2);
-
-  // rotate-half RoPE of dims [d0, d0+8): the partner dims (d +- D/2) sit in lane ^ LPT/2
-  auto rope8 = [&](uint4 raw, float (&out)[8]) {
-    const uint4 pr = make_uint4(__shfl_xor(raw.x, LPT / 2, kWave), __shfl_xor(raw.y, LPT / 2, kWave),
-                                __shfl_xor(raw.z, LPT / 2, kWave), __shfl_xor(raw.w, LPT / 2, kWave));
-    const f16* x = (const f16*)&raw;
-    const f16* y = (const f16*)&pr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int dim = d0 + i;
-      const float xv = h2f(x[i]), yv = h2f(y[i]);
-      if (dim < D / 2) {
-        const float2 cs = rope[dim];
-        out[i] = h2f(f2h(xv * cs.x - yv * cs.y));
-      } else {
-        const float2 cs = rope[dim - D / 2];
-        out[i] = h2f(f2h(xv * cs.x + yv * cs.y));
-      }
-    }
-  };
-
-  if (s < seff) {
-    const int t0 = s * chunk, t1 = min(T, t0 + chunk);
-    if (t1 == T) {
-      // this split owns the new position: rotate k, append K/V[pos] to the shared cache
-      if (w == 0 && lane < LPT) {
-        const uint4 kr = ldx16<true>(qkv + dm.hd + (size_t)kvh * D + d0);
-        float kf[8];
-        rope8(kr, kf);
-        uint4 ko;
-        f16* kh = (f16*)&ko;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kh[i] = f2h(kf[i]);
-        const uint4 vr = ldx16<true>(qkv + dm.hd + (size_t)(dm.Hkv + kvh) * D + d0);
-        const uint32_t* kw = (const uint32_t*)&ko;
-        const uint32_t* vw = (const uint32_t*)&vr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          __hip_atomic_store((__attribute__((address_space(1))) uint32_t*)(Kb + (size_t)pos * D + d0) + j,
-                             kw[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store((__attribute__((address_space(1))) uint32_t*)(Vb + (size_t)pos * D + d0) + j,
-                             vw[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-    const float qs = 1.4426950408889634f / sqrtf((float)D);
-    float qf[8];
-    {
-      const uint4 qr = ldx16<true>(qkv + (size_t)(kvh * G + g) * D + d0);
-      float r[8];
-      rope8(qr, r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[i] = r[i] * qs;
-    }
-    float m = -__builtin_inff(), l = 0.f, acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int tb = t0 + grp; tb < t1; tb += NGRP * U) {
-      uint4 kk[U], vv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * NGRP;
-        const size_t tt = (size_t)(t < t1 ? t : t0);
-        if (tt == (size_t)pos) {  // written above by this workgroup: read through
-          kk[u] = ldx16<true>(Kb + tt * D + d0);
-          vv[u] = ldx16<true>(Vb + tt * D + d0);
-        } else {
-          kk[u] = ldg16(Kb + tt * D + d0);
-          vv[u] = ldg16(Vb + tt * D + d0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * NGRP;
-        if (t >= t1) break;  // uniform within the position's lanes
-        const f16* kh = (const f16*)&kk[u];
-        const f16* vh = (const f16*)&vv[u];
-        float sc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sc = fmaf(qf[i], h2f(kh[i]), sc);
-#pragma unroll
-        for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, kWave);
-        const float mn = fmaxf(m, sc);
-        const float c = exp2f(m - mn);
-        const float p = exp2f(sc - mn);
-        l = l * c + p;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(acc[i], c, p * h2f(vh[i]));
-        m = mn;
-      }
-    }
-    if (sub == 0) {
-      sm.m[grp][g] = m;
-      sm.l[grp][g] = l;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sm.acc[grp][g][d0 + i] = acc[i];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kPB) {
-      const int gg = idx / D, dd = idx % D;
-      float M = -__builtin_inff();
-      for (int j = 0; j < NGRP; ++j) M = fmaxf(M, sm.m[j][gg]);
-      float Ls = 0.f, A = 0.f;
-      for (int j = 0; j < NGRP; ++j) {
-        const float sc = (sm.l[j][gg] > 0.f) ? exp2f(sm.m[j][gg] - M) : 0.f;
-        Ls += sm.l[j][gg] * sc;
-        A += sm.acc[j][gg][dd] * sc;
-      }
-      const size_t pi = pbase + (size_t)gg * smax + s;
-      wt_store(&a.pacc[pi * D + dd], A);
-      if (dd == 0) {
-        wt_store(&a.pml[pi * 2 + 0], M);
-        wt_store(&a.pml[pi * 2 + 1], Ls);
-      }
-    }
-  }
-  int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
-  if (arrive_counter(counter, smax, flag)) {
-    if (threadIdx.x < G) {
-      const int g = threadIdx.x;
-      float M = -__builtin_inff();
-      for (int j = 0; j < seff; ++j) {
-        sm.w[g][j] = wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2]);
-        M = fmaxf(M, sm.w[g][j]);
-      }
-      float Ls = 0.f;
-      for (int j = 0; j < seff; ++j) {
-        const float e = exp2f(sm.w[g][j] - M);
-        sm.w[g][j] = e;
-        Ls += wt_load(&a.pml[(pbase + (size_t)g * smax + j) * 2 + 1]) * e;
-      }
-      sm.L[g] = Ls;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += kPB) {
-      const int g = idx / D, dd = idx % D;
-      float A = 0.f;
-      for (int j = 0; j < seff; ++j) A += sm.w[g][j] * wt_load(&a.pacc[(pbase + (size_t)g * smax + j) * D + dd]);
-      sth<true>(a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + dd, f2h(A / sm.L[g]));
-    }
-    if (threadIdx.x == 0) reset_counter(counter);
-  }
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
 template <int D, int G, int MODE, int SEG16, int SEG4, int NG>
-__global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar,
-                                                    int* abort) {
+__global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar) {
   __shared__ PSmem<D, G> sm;
   const Dims& dm = a.dm;
   const int b = 0;
   const unsigned nwg = gridDim.x;
   const int wg = blockIdx.x, t = threadIdx.x;
-  unsigned target = 0;
+  unsigned epoch = 0;
   int pos = a.pos[b];
   int tok = a.tok_in[b];
   h2* xl = sm.x;
@@ -625,20 +520,20 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
         if (norm_known) gemv_phase<OP_QKV, false, SEG16, true, false, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
         else gemv_phase<OP_QKV, false, SEG16, true, true, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
       }
-      grid_sync(bar, target, nwg, abort);
+      grid_sync(bar, epoch, nwg);
       if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
         __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       // ---------------- attention (+ RoPE and the KV append of position pos)
       for (int it = wg; it < dm.Hkv * splits; it += nwg)
-        attn_split<D, G>(a, l, it % splits, it / splits, b, pos, splits, sm.at, &sm.flag);
-      grid_sync(bar, target, nwg, abort);
+        attn_split<D, G, kPB, true, 1>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
+      grid_sync(bar, epoch, nwg);
       // ---------------- O + residual
       so.out = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
       so.resid = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
       if (r4) gemv_phase<OP_O, true, SEG4, false, false, false, NG>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.red);
       else gemv_phase<OP_O, false, SEG16, false, false, false, NG>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.red);
-      grid_sync(bar, target, nwg, abort);
+      grid_sync(bar, epoch, nwg);
       // ---------------- gate|up
       so.out = a.gu + (size_t)b * 2 * dm.F;
       so.resid = nullptr;
@@ -647,13 +542,13 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
         if (r4) gemv_phase<OP_GU, true, SEG4, true, true, false, NG>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.red);
         else gemv_phase<OP_GU, false, SEG16, true, true, false, NG>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.red);
       }
-      grid_sync(bar, target, nwg, abort);
+      grid_sync(bar, epoch, nwg);
       // ---------------- down (SwiGLU while staging) + residual
       so.out = a.hs + ((size_t)l * dm.B + b) * dm.d;
       so.resid = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
       if (r4) gemv_phase<OP_DOWN, true, SEG4, false, false, true, NG>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.red);
       else gemv_phase<OP_DOWN, false, SEG16, false, false, true, NG>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.red);
-      grid_sync(bar, target, nwg, abort);
+      grid_sync(bar, epoch, nwg);
     }
     // ---------------- LM head (final RMSNorm while staging) + argmax
     {
@@ -662,7 +557,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.key = a.amax + (step & 1) * dm.B + b;
       gemv_phase<OP_LM, false, SEG16, true, true, false, NG>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
                                                          a.final_norm, 1.f, so, xl, sm.red);
-      grid_sync(bar, target, nwg, abort);
+      grid_sync(bar, epoch, nwg);
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
       if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
@@ -671,7 +566,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
   if (wg == 0 && t == 0) {
     a.pos[b] = pos;
     *a.step = S;
-    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
+    if (__hip_atomic_load((int*)(bar + kBarAbort), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
   }
 }
 
@@ -685,7 +580,7 @@ const void* river_persist_fn(const Dims& dm, int mode) {
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
 #define RIVER_PF(D_, G_, NG_)                                                                    \
   if (dm.D == D_ && G == G_ && ng == NG_)                                                        \
-    return mode ? (const void*)k_persist<D_, G_, 1, 8, 4, NG_> : (const void*)k_persist<D_, G_, 0, 8, 4, NG_>;
+    return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_> : (const void*)k_persist<D_, G_, 0, 8, 8, NG_>;
   RIVER_PF(128, 4, 1)
   RIVER_PF(64, 4, 1)
   RIVER_PF(64, 2, 1)
@@ -699,15 +594,14 @@ int river_persist_grid(const void* fn) {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kPB, 0) != hipSuccess) return 0;
-  return per_cu >= 1 ? cus : 0;
+  return (per_cu >= 1 && cus <= kBarGroup * kBarMaxGroups) ? cus : 0;
 }
 
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
-                                unsigned* bar, int* abort, hipStream_t st) {
+                                unsigned* bar, hipStream_t st) {
   DecodeArgs aa = a;
   int SS = S, sp = splits;
   unsigned* br = bar;
-  int* ab = abort;
-  void* args[] = {&aa, &SS, &sp, &br, &ab};
+  void* args[] = {&aa, &SS, &sp, &br};
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kPB), args, 0, st);
 }
