@@ -34,18 +34,18 @@ struct AttnLds {
   int flag;
 };
 
-// Sum / max over the lanes of a wave that differ by multiples of LPT (8 or 16); every lane
-// gets the result.
-template <int LPT>
+// Sum / max over the lanes of a wave that differ by multiples of W (a power of two, < 64);
+// every lane gets the result.
+template <int W>
 RIVER_DEV float xslot_sum(float x) {
 #pragma unroll
-  for (int o = LPT; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+  for (int o = W; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
   return x;
 }
-template <int LPT>
+template <int W>
 RIVER_DEV float xslot_max(float x) {
 #pragma unroll
-  for (int o = LPT; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  for (int o = W; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
   return x;
 }
 
@@ -76,7 +76,7 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
   constexpr int NCOL = G * D / 4;                  // float4 columns of the merged output
   constexpr int TPC = NT / NCOL;                   // threads per column in the split merge
   constexpr int MB = (kMaxSplit / TPC < 16) ? kMaxSplit / TPC : 16;  // partial loads per batch
-  static_assert(LPP <= kWave && HG * GL == G && (LPP == LPT || LPP == kWave), "lane layout");
+  static_assert(LPP <= kWave && HG * GL == G && (LPP & (LPP - 1)) == 0, "lane layout");
   static_assert(NCOL <= NT && (TPC & (TPC - 1)) == 0 && TPC <= kWave, "merge layout");
   const Dims& dm = a.dm;
   const int T = pos + 1;
@@ -247,11 +247,11 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
 #pragma unroll
         for (int i = 0; i < 8; ++i) xs[i] = acc[gl][i];
       } else {
-        M = xslot_max<LPT>(M);
+        M = xslot_max<LPP>(M);
         const float sc = (m[gl] > -__builtin_inff()) ? exp2f(m[gl] - M) : 0.f;
-        lg = xslot_sum<LPT>(l[gl] * sc);
+        lg = xslot_sum<LPP>(l[gl] * sc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xs[i] = xslot_sum<LPT>(acc[gl][i] * sc);
+        for (int i = 0; i < 8; ++i) xs[i] = xslot_sum<LPP>(acc[gl][i] * sc);
       }
       if (lane < LPP) {
 #pragma unroll
@@ -298,9 +298,9 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
         mj = wt_load(&a.pml[pi * 2 + 0]);
         lj = wt_load(&a.pml[pi * 2 + 1]);
       }
-      const float M = wave_max(mj);
+      const float M = wave_max_fast(mj);
       const float e = (j < seff) ? exp2f(mj - M) : 0.f;
-      const float Ls = wave_sum(lj * e);
+      const float Ls = wave_sum_fast(lj * e);
       sm.w[g][j] = e / Ls;
     }
     __syncthreads();
@@ -325,8 +325,21 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
           A.w = fmaf(wt, v[k].w, A.w);
         }
       }
+      // sum over the TPC lanes of the column (quad steps by DPP, wider ones by shuffle)
+      if (TPC >= 2) {
+        A.x += dpp_f<0xB1>(A.x);
+        A.y += dpp_f<0xB1>(A.y);
+        A.z += dpp_f<0xB1>(A.z);
+        A.w += dpp_f<0xB1>(A.w);
+      }
+      if (TPC >= 4) {
+        A.x += dpp_f<0x4E>(A.x);
+        A.y += dpp_f<0x4E>(A.y);
+        A.z += dpp_f<0x4E>(A.z);
+        A.w += dpp_f<0x4E>(A.w);
+      }
 #pragma unroll
-      for (int o = 1; o < TPC; o <<= 1) {
+      for (int o = 4; o < TPC; o <<= 1) {
         A.x += __shfl_xor(A.x, o, kWave);
         A.y += __shfl_xor(A.y, o, kWave);
         A.z += __shfl_xor(A.z, o, kWave);

@@ -49,11 +49,18 @@ RIVER_DEV double pblock_sum_d(double v, double* red) {
 // e * group size and the top counter e * groups), so no reset is needed between barriers.
 // This keeps same-address atomics at kBarGroup + groups per barrier instead of one per
 // workgroup.
-RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg) {
+// `pre` (weight loads of the next phase, which do not depend on the data the barrier
+// protects) is issued while the barrier is pending: by every wave but the polling one before
+// the wait, by the polling wave after it (its poll loads must not queue behind them).
+static constexpr int kPoller = kPB - kWave;  // first lane of the last wave
+template <typename Pre>
+RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg, Pre&& pre) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have landed
   __syncthreads();
   ++epoch;
-  if (threadIdx.x == 0) {
+  const bool poll_wave = threadIdx.x >= kPoller;
+  if (!poll_wave) pre();
+  if (threadIdx.x == kPoller) {
     const unsigned ng = (nwg + kBarGroup - 1) / kBarGroup;
     const unsigned g = blockIdx.x / kBarGroup;
     const unsigned gs = min((unsigned)kBarGroup, nwg - g * kBarGroup);
@@ -75,6 +82,10 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg) {
     }
   }
   __syncthreads();
+  if (poll_wave) pre();
+}
+RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg) {
+  grid_sync(bar, epoch, nwg, [] {});
 }
 
 // ---------------------------------------------------------------------------------------
@@ -82,10 +93,11 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg) {
 // ---------------------------------------------------------------------------------------
 template <int D, int G>
 struct PSmem {
-  union {
+  union __attribute__((aligned(16))) {
     h2 x[kMaxK / 2];  // staged GEMV input
     AttnLds<D, G, kPB> at;
   };
+  float xc[kMaxK / 32];  // int4 stream: per (chunk, lane) bias correction of the staged input
   double red[kPW];
   double c3[3];
   int flag;
@@ -120,18 +132,28 @@ RIVER_DEV uint4 silu_mul8(uint4 g, uint4 u) {
   return g;
 }
 
-// Writes one group of 8 staged values into LDS in the stream's layout.
+// Writes one group of 8 staged values into LDS in the stream's layout. For the int4 stream the
+// odd elements of each pair set are stored divided by 16 (exact) and the bias correction of
+// the (chunk, lane) the group belongs to is summed over its 4 groups (threads t..t+3 stage
+// them; the quad is always complete) -- see dot_seg4 for how both are used.
 template <bool IS4>
-RIVER_DEV void put_group(h2* xl, int g, uint4 u) {
+RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
   h2* dst = xl + lds_group_index<IS4>(g);
   if (IS4) {
     const uint32_t in[4] = {u.x, u.y, u.z, u.w};
     h2 o[4];
-    pair_for_unpack(in, o);
+    pair_for_unpack(in, o);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+    const float xlo = (h2f(o[0].x) + h2f(o[0].y)) + (h2f(o[2].x) + h2f(o[2].y));
+    const float xhi = (h2f(o[1].x) + h2f(o[1].y)) + (h2f(o[3].x) + h2f(o[3].y));
+    const h2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
     dst[0] = o[0];
-    dst[1] = o[1];
+    dst[1] = o[1] * sixteenth;
     dst[2] = o[2];
-    dst[3] = o[3];
+    dst[3] = o[3] * sixteenth;
+    float c = -1032.f * xlo - 72.f * xhi;
+    c += dpp_f<0xB1>(c);
+    c += dpp_f<0x4E>(c);
+    if ((g & 3) == 0) xc[g >> 2] = c;
   } else {
     dst[0] = as_h2(u.x);
     dst[1] = as_h2(u.y);
@@ -146,7 +168,7 @@ RIVER_DEV void put_group(h2* xl, int g, uint4 u) {
 // Without NORM the groups stream through registers.
 template <bool IS4, bool HAS_GAIN, bool NORM, bool SWIGLU, int NG>
 RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, int F, float inv, float eps,
-                       h2* xl, double* red) {
+                       h2* xl, float* xc, double* red) {
   const int t = threadIdx.x;
   const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
   const int ngp = nch * (IS4 ? kChunkW4 : kChunkF16) / 8;
@@ -167,9 +189,9 @@ RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, int F, float inv,
       if (g >= ngp) continue;
       uint4 u = v[i];
       if (HAS_GAIN && g * 8 < K) u = norm8(u, ldg16(gain + g * 8), inv, true);
-      put_group<IS4>(xl, g, u);
+      put_group<IS4>(xl, xc, g, u);
     }
-    for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4>(xl, g, make_uint4(0, 0, 0, 0));
+    for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4>(xl, xc, g, make_uint4(0, 0, 0, 0));
   } else {
     for (int g = t; g < ngp; g += kPB) {
       uint4 u = make_uint4(0, 0, 0, 0);
@@ -178,7 +200,7 @@ RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, int F, float inv,
         if (SWIGLU) u = silu_mul8(u, ldx16<true>(src + F + g * 8));
         if (HAS_GAIN) u = norm8(u, ldg16(gain + g * 8), inv, true);
       }
-      put_group<IS4>(xl, g, u);
+      put_group<IS4>(xl, xc, g, u);
     }
   }
   __syncthreads();
@@ -222,6 +244,15 @@ RIVER_DEV const f16* row16(const DecodeArgs& a, const LayerDev* lw, int n) {
   return a.lm_head + (size_t)n * dm.d;
 }
 
+static constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
+
+// (w & m) | c in one instruction (v_and_or_b32; the mask rides in a scalar register).
+RIVER_DEV uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
 // This wave's rows [r0, r1) of an N-row phase (rows split evenly over all waves of the grid).
 RIVER_DEV void wave_rows(int N, int& r0, int& r1) {
   const int gw = blockIdx.x * kPW + threadIdx.x / kWave, GW = gridDim.x * kPW;
@@ -235,82 +266,129 @@ RIVER_DEV void wave_rows(int N, int& r0, int& r1) {
 // single run of 1 KiB chunks (2048 elements each; the group scales likewise), so a wave's rows
 // [r0, r1) are the flat chunk range [r0*nch, r1*nch) and an item is the next SEG chunks of
 // that range, crossing row ends: every item keeps SEG loads per lane in flight whatever K is.
-template <bool IS4, int SEG>
+template <int SEG>
 struct Seg {
   uint4 w[SEG];
-  h2 s[(SEG + 1) / 2];  // int4 group scales, two chunks per register
+  uint4 sr;  // int4: this lane's share of the item's group scales (fetched per chunk by shuffle)
 };
 
 // fp16: chunks [seg*SEG, seg*SEG+SEG) of `row`.
 template <int OP, int SEG>
 RIVER_DEV void load_seg16(const DecodeArgs& a, const LayerDev* lw, int K, int nch, int row, int seg,
-                          Seg<false, SEG>& sg) {
+                          Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
   const f16* rp = row16<OP>(a, lw, row);
 #pragma unroll
   for (int c = 0; c < SEG; ++c) {
     const int ch = seg * SEG + c;
-    if (ch >= nch) break;  // uniform; dot_seg16 stops at the same chunk
     const int e = ch * kChunkF16 + lane * 8;
-    sg.w[c] = ldg16(rp + (e < K ? e : 0));  // past K (ragged row end) meets x = 0
+    // chunks past the row are never reduced (dot_seg16 stops at nch); every slot is written so
+    // that a buffer is wholly redefined by each load
+    sg.w[c] = (ch < nch) ? ldg16(rp + (e < K ? e : 0)) : make_uint4(0, 0, 0, 0);  // past K meets x = 0
   }
+  sg.sr = make_uint4(0, 0, 0, 0);
 }
 
 template <int SEG>
-RIVER_DEV float dot_seg16(const Seg<false, SEG>& sg, const h2* xl, int nch, int seg, float acc) {
+RIVER_DEV float dot_seg16(const Seg<SEG>& sg, const h2* xl, int nch, int seg, float acc) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int c = 0; c < SEG; ++c) {
     const int ch = seg * SEG + c;
     if (ch >= nch) break;
-    const h2* x = xl + (ch * kWave + lane) * 4;
-    acc = dot2(x[0], as_h2(sg.w[c].x), acc);
-    acc = dot2(x[1], as_h2(sg.w[c].y), acc);
-    acc = dot2(x[2], as_h2(sg.w[c].z), acc);
-    acc = dot2(x[3], as_h2(sg.w[c].w), acc);
+    const uint4 x = ((const uint4*)xl)[ch * kWave + lane];  // one ds_read_b128
+    acc = dot2(as_h2(x.x), as_h2(sg.w[c].x), acc);
+    acc = dot2(as_h2(x.y), as_h2(sg.w[c].y), acc);
+    acc = dot2(as_h2(x.z), as_h2(sg.w[c].z), acc);
+    acc = dot2(as_h2(x.w), as_h2(sg.w[c].w), acc);
   }
   return acc;
 }
 
-// int4: flat chunks [q0, min(q0 + SEG, qend)) of the matrix starting at (base, sbase).
-template <int SEG>
-RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, int group, int q0, int qend,
-                         Seg<true, SEG>& sg) {
+// int4: flat chunks [q0, min(q0 + SEG, qend)) of the matrix starting at (base, sbase). The
+// item's group scales are contiguous too (spc = 2048/group per chunk); one load per lane
+// brings npl = SEG*spc/64 of them (lane L: scales [L*npl, L*npl + npl) of the item) instead of
+// one small load per chunk.
+template <int SEG, int GRP>
+RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, int q0, int qend, Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint8_t* wp = base + (size_t)q0 * 1024 + lane * 16;
-  const f16* sp = sbase + (size_t)q0 * (kChunkW4 / group) + (lane * 32) / group;
 #pragma unroll
-  for (int c = 0; c < SEG; ++c) {
-    if (q0 + c >= qend) break;  // uniform
-    sg.w[c] = ldg16(wp + c * 1024);
-    const f16 sv = ldg2(sp + c * (kChunkW4 / group));
-    if (c & 1) sg.s[c / 2].y = sv;
-    else sg.s[c / 2].x = sv;
+  for (int c = 0; c < SEG; ++c)
+    sg.w[c] = (q0 + c < qend) ? ldg16(wp + c * 1024) : make_uint4(0, 0, 0, 0);
+  constexpr int spc = kChunkW4 / GRP;
+  constexpr int npl = SEG * spc / kWave;
+  static_assert(npl == 1 || npl == 2 || npl == 4 || npl == 8, "scales per lane");
+  const size_t s0 = (size_t)q0 * spc + (size_t)lane * npl;
+  sg.sr = make_uint4(0, 0, 0, 0);
+  if (s0 < (size_t)qend * spc) {  // npl divides both: the lane's scales are all in range
+    const f16* sp = sbase + s0;
+    if (npl == 1) {
+      sg.sr.x = __builtin_bit_cast(unsigned short, ldg2(sp));
+    } else if (npl == 2) {
+      sg.sr.x = *(const __attribute__((address_space(1))) uint32_t*)sp;
+    } else if (npl == 4) {
+      const unsigned long long v = *(const __attribute__((address_space(1))) unsigned long long*)sp;
+      sg.sr.x = (uint32_t)v;
+      sg.sr.y = (uint32_t)(v >> 32);
+    } else {
+      sg.sr = ldg16(sp);
+    }
   }
+}
+
+// Scale of chunk c of an item for this lane's 32 elements: scale index c*spc + lane*spc/64 of
+// the item, held by lane index/npl.
+template <int SEG, int spc, int npl>
+RIVER_DEV float item_scale(const Seg<SEG>& sg, int c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = c * spc + (lane * spc) / kWave;
+  const int src = i / npl, e = i % npl;
+  uint32_t wv;
+  if (npl <= 2) {
+    wv = (uint32_t)__shfl((int)sg.sr.x, src, kWave);
+  } else if (npl == 4) {
+    const uint32_t w0 = (uint32_t)__shfl((int)sg.sr.x, src, kWave);
+    const uint32_t w1 = (uint32_t)__shfl((int)sg.sr.y, src, kWave);
+    wv = (e >> 1) ? w1 : w0;
+  } else {
+    const uint32_t w0 = (uint32_t)__shfl((int)sg.sr.x, src, kWave);
+    const uint32_t w1 = (uint32_t)__shfl((int)sg.sr.y, src, kWave);
+    const uint32_t w2 = (uint32_t)__shfl((int)sg.sr.z, src, kWave);
+    const uint32_t w3 = (uint32_t)__shfl((int)sg.sr.w, src, kWave);
+    const int k = e >> 1;
+    wv = k == 0 ? w0 : k == 1 ? w1 : k == 2 ? w2 : w3;
+  }
+  const unsigned short hv = (unsigned short)((e & 1) ? (wv >> 16) : wv);
+  return h2f(__builtin_bit_cast(f16, hv));
 }
 
 // Reduces the int4 item starting at flat chunk q0 (chunk ch of row `row`); calls fin(row, lane
 // partial) at every row end and advances (row, ch).
-template <int SEG, typename Fin>
-RIVER_DEV void dot_seg4(const Seg<true, SEG>& sg, const h2* xl, int nch, int q0, int qend, int& row,
-                        int& ch, float& acc, Fin&& fin) {
+template <int SEG, int GRP, typename Fin>
+RIVER_DEV void dot_seg4(const Seg<SEG>& sg, const h2* xl, const float* xc, int nch, int q0,
+                        int qend, int& row, int& ch, float& acc, Fin&& fin) {
   const int lane = threadIdx.x & (kWave - 1);
+  constexpr int spc = kChunkW4 / GRP, npl = SEG * spc / kWave;
 #pragma unroll
   for (int c = 0; c < SEG; ++c) {
     if (q0 + c >= qend) break;
-    const uint32_t ww[4] = {sg.w[c].x, sg.w[c].y, sg.w[c].z, sg.w[c].w};
-    float sd = 0.f;
+    // nibbles OR-ed into fp16 1024.0 give 1024 + u (low nibble of each half) or 1024 + 16u
+    // (high nibble); against x (resp. x/16) the dot is sum (u - 8) x + 1032 X_lo + 72 X_hi,
+    // and the staged correction -1032 X_lo - 72 X_hi starts the sum
+    float sd = xc[ch * kWave + lane];
+    uint4 xv[4];  // all four 16-byte reads of this chunk's inputs first
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xv[m] = ((const uint4*)xl)[(ch * 4 + m) * kWave + lane];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const h2* x = xl + ((ch * 4 + m) * kWave + lane) * 4;
-      h2 p0, p1, p2, p3;
-      unpack8(ww[m], p0, p1, p2, p3);
-      sd = dot2(p0, x[0], sd);
-      sd = dot2(p1, x[1], sd);
-      sd = dot2(p2, x[2], sd);
-      sd = dot2(p3, x[3], sd);
+      const uint32_t wm = (&sg.w[c].x)[m], w8 = wm >> 8;
+      sd = dot2(as_h2(and_or(wm, 0x000F000Fu, kMagic)), as_h2(xv[m].x), sd);
+      sd = dot2(as_h2(and_or(wm, 0x00F000F0u, kMagic)), as_h2(xv[m].y), sd);
+      sd = dot2(as_h2(and_or(w8, 0x000F000Fu, kMagic)), as_h2(xv[m].z), sd);
+      sd = dot2(as_h2(and_or(w8, 0x00F000F0u, kMagic)), as_h2(xv[m].w), sd);
     }
-    acc = fmaf(h2f((c & 1) ? sg.s[c / 2].y : sg.s[c / 2].x), sd, acc);
+    acc = fmaf(item_scale<SEG, spc, npl>(sg, c), sd, acc);
     if (++ch == nch) {
       fin(row, acc);
       acc = 0.f;
@@ -344,9 +422,9 @@ RIVER_DEV int n_chunks(int K) {
 
 // Streams this wave's rows of an N-row phase; the input vector is staged in xl and the first
 // item is already in b0 (prefetch_first).
-template <int OP, bool IS4, int SEG>
+template <int OP, bool IS4, int SEG, int GRP>
 RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K, const h2* xl,
-                           const StreamOut& so, Seg<IS4, SEG>& b0) {
+                           const float* xc, const StreamOut& so, Seg<SEG>& b0) {
   const int lane = threadIdx.x & (kWave - 1);
   int r0, r1;
   wave_rows(N, r0, r1);
@@ -378,12 +456,12 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
       if (OP == OP_LM && so.logits) so.logits[row] = v;
     }
   };
-  Seg<IS4, SEG> b1;
+  Seg<SEG> b1;
   float acc = 0.f;
   if constexpr (!IS4) {
     const int nseg = (nch + SEG - 1) / SEG;
     const int nitems = (r1 - r0) * nseg;
-    auto step = [&](int it, const Seg<false, SEG>& sg) {
+    auto step = [&](int it, const Seg<SEG>& sg) {
       const int seg = it % nseg;
       acc = dot_seg16<SEG>(sg, xl, nch, seg, acc);
       if (seg == nseg - 1) {
@@ -403,17 +481,16 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
     const uint8_t* base;
     const f16* sbase;
     w4_base<OP>(lw, base, sbase);
-    const int grp = a.dm.group;
     const int qbeg = r0 * nch, qend = r1 * nch;
     int row = r0, ch = 0;
     int q = qbeg;
     for (; q + SEG < qend; q += 2 * SEG) {
-      load_seg4<SEG>(base, sbase, grp, q + SEG, qend, b1);
-      dot_seg4<SEG>(b0, xl, nch, q, qend, row, ch, acc, fin);
-      if (q + 2 * SEG < qend) load_seg4<SEG>(base, sbase, grp, q + 2 * SEG, qend, b0);
-      dot_seg4<SEG>(b1, xl, nch, q + SEG, qend, row, ch, acc, fin);
+      load_seg4<SEG, GRP>(base, sbase, q + SEG, qend, b1);
+      dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
+      if (q + 2 * SEG < qend) load_seg4<SEG, GRP>(base, sbase, q + 2 * SEG, qend, b0);
+      dot_seg4<SEG, GRP>(b1, xl, xc, nch, q + SEG, qend, row, ch, acc, fin);
     }
-    if (q < qend) dot_seg4<SEG>(b0, xl, nch, q, qend, row, ch, acc, fin);
+    if (q < qend) dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
   }
   if (OP == OP_LM && lane == 0 && bi != 0x7FFFFFFF) {
     const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
@@ -424,11 +501,16 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
 
 // Issues the first item of this wave's rows (weights only: allowed before the inputs of the
 // phase exist, e.g. before the grid barrier or while the input vector is staged).
-template <int OP, bool IS4, int SEG>
-RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K, Seg<IS4, SEG>& pre) {
+template <int OP, bool IS4, int SEG, int GRP>
+RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K, Seg<SEG>& pre) {
   int r0, r1;
   wave_rows(N, r0, r1);
-  if (r0 >= r1) return;
+  if (r0 >= r1) {  // no rows: still define the whole buffer
+#pragma unroll
+    for (int c = 0; c < SEG; ++c) pre.w[c] = make_uint4(0, 0, 0, 0);
+    pre.sr = make_uint4(0, 0, 0, 0);
+    return;
+  }
   const int nch = n_chunks<IS4>(K);
   if constexpr (!IS4) {
     load_seg16<OP, SEG>(a, lw, K, nch, r0, 0, pre);
@@ -436,26 +518,41 @@ RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, in
     const uint8_t* base;
     const f16* sbase;
     w4_base<OP>(lw, base, sbase);
-    load_seg4<SEG>(base, sbase, a.dm.group, r0 * nch, r1 * nch, pre);
+    load_seg4<SEG, GRP>(base, sbase, r0 * nch, r1 * nch, pre);
   }
 }
 
-// One GEMV phase: prefetch the first weight segment, stage the input, stream the rows.
-template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool SWIGLU, int NG>
+// One GEMV phase: stage the input, stream the rows. b0 holds the phase's first item when
+// `have` (issued before the barrier that precedes the phase), else it is issued here first.
+template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool SWIGLU, int NG, int GRP>
 RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K, const f16* src,
-                          const f16* gain, float inv, const StreamOut& so, h2* xl, double* red) {
-  Seg<IS4, SEG> b0;
-  prefetch_first<OP, IS4, SEG>(a, lw, N, K, b0);
-  stage_x<IS4, HAS_GAIN, NORM, SWIGLU, NG>(src, gain, K, a.dm.F, inv, a.dm.eps, xl, red);
-  stream_rows<OP, IS4, SEG>(a, lw, N, K, xl, so, b0);
+                          const f16* gain, float inv, const StreamOut& so, h2* xl, float* xc,
+                          double* red, Seg<SEG>& b0, bool have) {
+  if (!have) prefetch_first<OP, IS4, SEG, GRP>(a, lw, N, K, b0);
+  stage_x<IS4, HAS_GAIN, NORM, SWIGLU, NG>(src, gain, K, a.dm.F, inv, a.dm.eps, xl, xc, red);
+  stream_rows<OP, IS4, SEG, GRP>(a, lw, N, K, xl, xc, so, b0);
   __syncthreads();  // LDS reuse by the next phase
+}
+
+// First item of the next phase on the route's weight stream; returns what `pre` now holds
+// (1: fp16 item, 2: int4 item).
+template <int OP, int SEG, int GRP>
+RIVER_DEV int prefetch_route(const DecodeArgs& a, const LayerDev* lw, int N, int K, bool r4, Seg<SEG>& pre) {
+  if (r4) {
+    prefetch_first<OP, true, SEG, GRP>(a, lw, N, K, pre);
+    return 2;
+  }
+  prefetch_first<OP, false, SEG, GRP>(a, lw, N, K, pre);
+  return 1;
 }
 
 // ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
-template <int D, int G, int MODE, int SEG16, int SEG4, int NG>
+template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP>
 __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar) {
+  static_assert(SEG16 == SEG4, "one prefetch buffer serves both weight streams");
+  constexpr int SEG = SEG16;
   __shared__ PSmem<D, G> sm;
   const Dims& dm = a.dm;
   const int b = 0;
@@ -465,6 +562,8 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
   int pos = a.pos[b];
   int tok = a.tok_in[b];
   h2* xl = sm.x;
+  Seg<SEG> pre;  // first weight item of the next GEMV phase, issued during the barrier before it
+  int pf = 0;    // what `pre` holds: 0 nothing, 1 fp16 item, 2 int4 item
 
   for (int step = 0; step < S; ++step, ++pos) {
     if (tok < 0 || tok >= dm.V) {
@@ -514,11 +613,11 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       StreamOut so{};
       so.out = a.qkvr + (size_t)b * dm.nqkv;
       if (r4) {
-        if (norm_known) gemv_phase<OP_QKV, true, SEG4, true, false, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
-        else gemv_phase<OP_QKV, true, SEG4, true, true, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
+        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
       } else {
-        if (norm_known) gemv_phase<OP_QKV, false, SEG16, true, false, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
-        else gemv_phase<OP_QKV, false, SEG16, true, true, false, NG>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.red);
+        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
       }
       grid_sync(bar, epoch, nwg);
       if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
@@ -526,38 +625,49 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
                            __HIP_MEMORY_SCOPE_AGENT);
       // ---------------- attention (+ RoPE and the KV append of position pos)
       for (int it = wg; it < dm.Hkv * splits; it += nwg)
-        attn_split<D, G, kPB, true, 1>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
-      grid_sync(bar, epoch, nwg);
+        attn_split<D, G, kPB, true, 2, 1>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
+      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre); });
       // ---------------- O + residual
       so.out = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
       so.resid = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_O, true, SEG4, false, false, false, NG>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.red);
-      else gemv_phase<OP_O, false, SEG16, false, false, false, NG>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.red);
-      grid_sync(bar, epoch, nwg);
+      if (r4) gemv_phase<OP_O, true, SEG, false, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_O, false, SEG, false, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_GU, SEG, GRP>(a, lw, 2 * dm.F, dm.d, r4, pre); });
       // ---------------- gate|up
       so.out = a.gu + (size_t)b * 2 * dm.F;
       so.resid = nullptr;
       {
         const f16* src = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-        if (r4) gemv_phase<OP_GU, true, SEG4, true, true, false, NG>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.red);
-        else gemv_phase<OP_GU, false, SEG16, true, true, false, NG>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.red);
+        if (r4) gemv_phase<OP_GU, true, SEG, true, true, false, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_GU, false, SEG, true, true, false, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       }
-      grid_sync(bar, epoch, nwg);
+      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_DOWN, SEG, GRP>(a, lw, dm.d, dm.F, r4, pre); });
       // ---------------- down (SwiGLU while staging) + residual
       so.out = a.hs + ((size_t)l * dm.B + b) * dm.d;
       so.resid = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_DOWN, true, SEG4, false, false, true, NG>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.red);
-      else gemv_phase<OP_DOWN, false, SEG16, false, false, true, NG>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.red);
-      grid_sync(bar, epoch, nwg);
+      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      // next phase: QKV of layer l+1 on its route (the exit test may still switch a backbone
+      // guess to the river, which then loads its own first item) or the LM head
+      const bool next_r4 = r4 || (MODE == 0 && a.sched && l == e_forced && l >= dm.entry);
+      if (l < dm.L) {
+        const LayerDev* ln = &a.layers[l];
+        grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, ln, dm.nqkv, dm.d, next_r4, pre); });
+      } else {
+        grid_sync(bar, epoch, nwg, [&] {
+          prefetch_first<OP_LM, false, SEG, GRP>(a, nullptr, dm.V, dm.d, pre);
+          pf = 1;
+        });
+      }
     }
     // ---------------- LM head (final RMSNorm while staging) + argmax
     {
       StreamOut so{};
       so.logits = a.logits ? a.logits + (size_t)b * dm.V : nullptr;
       so.key = a.amax + (step & 1) * dm.B + b;
-      gemv_phase<OP_LM, false, SEG16, true, true, false, NG>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
-                                                         a.final_norm, 1.f, so, xl, sm.red);
-      grid_sync(bar, epoch, nwg);
+      gemv_phase<OP_LM, false, SEG, true, true, false, NG, GRP>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
+                                                               a.final_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
       if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
@@ -578,12 +688,13 @@ const void* river_persist_fn(const Dims& dm, int mode) {
   if (dm.B != 1 || dm.d > kMaxK || dm.hd > kMaxK || dm.F > kMaxK) return nullptr;
   const int G = dm.H / dm.Hkv;
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
-#define RIVER_PF(D_, G_, NG_)                                                                    \
-  if (dm.D == D_ && G == G_ && ng == NG_)                                                        \
-    return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_> : (const void*)k_persist<D_, G_, 0, 8, 8, NG_>;
-  RIVER_PF(128, 4, 1)
-  RIVER_PF(64, 4, 1)
-  RIVER_PF(64, 2, 1)
+#define RIVER_PF(D_, G_, NG_, GRP_)                                                              \
+  if (dm.D == D_ && G == G_ && ng == NG_ && dm.group == GRP_)                                    \
+    return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_>                            \
+                : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_>;
+  RIVER_PF(128, 4, 1, 128)
+  RIVER_PF(64, 4, 1, 128)
+  RIVER_PF(64, 2, 1, 64)
 #undef RIVER_PF
   return nullptr;
 }
