@@ -5,11 +5,11 @@ Workload (default): Llama-3.1-8B-shaped decoder with random fp16 weights and its
 (group 128) river copy, batch 1, a 2048-token random prompt prefilled at full depth, then
 --steps decode tokens with forced exit layers drawn uniformly from {8..20} (mean 14).
 A step is one decode token through all 32 layers (backbone up to the exit layer, river
-after it) and the LM head; the timed region replays the captured step graph --steps times
-with inputs resident in HBM.
+after it) and the LM head; the timed region runs --steps steps with inputs resident in HBM.
 
-The decode step runs as one persistent cooperative kernel (8 steps per launch). Also
-measured in the same run:
+The decode runs as one persistent cooperative kernel (8 steps per launch; with
+RIVER_PERSIST=0 the per-op kernels replayed from a captured graph). Also measured in the
+same run:
   * per-launch HIP-event timing of that kernel over the same S steps -> the roofline object;
   * per-launch timing of every per-op decode kernel (the graph path, one pass per kernel) ->
     a per-kernel breakdown of that path;
@@ -45,6 +45,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-full", action="store_true", help="skip the full-depth fp16 decode")
     ap.add_argument("--no-breakdown", action="store_true", help="skip per-kernel timing passes")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -52,6 +54,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calib_copy:
+        calib_copy(torch)
+        return
 
     from token_level_early_amd import bytes_model as bm
     from token_level_early_amd import configs, river, synth
@@ -186,6 +192,17 @@ def main():
                 "bound": "hbm", "achieved": roof_pass["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": roof_pass["frac"], "traffic": None,
                 "avg_launch_us": roof_pass["avg_us"], "bytes_per_launch": roof_pass["bytes_per_launch"]}
+    elif "gu" in kernels:  # per-op path: its largest kernel
+        g = kernels["gu"]
+        roof = {"kernel": "k_dec_gemv gate|up (per-op path)", "bound": "hbm", "achieved": g["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g["frac"], "traffic": None,
+                "avg_launch_us": g["avg_us"], "bytes_per_launch": g["bytes_per_launch"]}
+    if roof is not None:
+        tr = pmc_traffic(roof)
+        if tr is not None:
+            roof["traffic"] = tr["bytes_per_launch"]
+            roof["traffic_detail"] = tr
+
     out = {
         "metric": "decode tokens/s at 8B shape (bs=1,ctx 2048) at fixed exit schedule; % HBM roofline",
         "value": round(tok_s, 2),
@@ -211,6 +228,52 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+PMC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "k_persist_llama8b_decode_pmc.json")
+KERNEL_SOURCES = ("persist.hip", "attn.hpp", "gemv.hpp", "common.hpp", "params.hpp", "api.cpp")
+
+
+def kernel_source_hash():
+    """Hash of the sources that define the persistent decode kernel and its launch."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_level_early_amd", "csrc")
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(roof):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by the plain-copy calibration), or None when those
+    counters were taken on other kernel sources or another kernel."""
+    try:
+        with open(PMC_FILE) as f:
+            pm = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pm.get("source_hash") != kernel_source_hash() or not roof["kernel"].startswith(pm.get("kernel", "?")):
+        return None
+    return {"bytes_per_launch": pm["hbm_bytes_per_launch"], "fetch_bytes": pm["fetch_bytes_per_launch"],
+            "write_bytes": pm["write_bytes_per_launch"],
+            "ratio_to_algorithmic": round(pm["hbm_bytes_per_launch"] / pm["algorithmic_bytes_per_launch_same_launches"], 4),
+            "launches": pm["workload"],
+            "calibration": pm["calibration"], "source": os.path.relpath(PMC_FILE, os.path.dirname(PMC_FILE) + "/..")}
+
+
+def calib_copy(torch):
+    """A plain device copy of known size, three times, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: each copy reads and writes exactly 512 MiB."""
+    n = 256 << 20  # fp16 elements = 512 MiB
+    x = torch.ones(n, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": 2 * n, "copies": 3}), flush=True)
 
 
 def cpu_baseline(c, w, rv, exits, positions, log):

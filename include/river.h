@@ -166,7 +166,12 @@ int river_decode_step(river_ctx* ctx, const int32_t* tok_in, const int32_t* forc
  *   tok_in     [B] first input tokens
  *   sched      [S][B] forced exit layers, or NULL for tau mode
  *   tok_out    [S][B]; exit_layer [S][B] or NULL; sim [S][B][L] or NULL
- * Same semantics and errors as S calls of river_decode_step. */
+ * Same semantics and errors as S calls of river_decode_step.
+ * Execution: a batch-1 context whose shapes the persistent decode kernel covers runs up to 8
+ * steps per cooperative launch (one workgroup per compute unit, grid barriers between the
+ * phases of a step); otherwise -- or when the environment variable RIVER_PERSIST is "0" at
+ * river_init -- the per-op kernels run, replayed from a captured graph. Both give the same
+ * results up to floating-point summation order. */
 int river_decode_steps(river_ctx* ctx, const int32_t* tok_in, const int32_t* sched, int32_t S,
                        float tau, int32_t* tok_out, int32_t* exit_layer, float* sim,
                        void* stream);
@@ -186,6 +191,10 @@ int river_decode_backbone_steps(river_ctx* ctx, const int32_t* tok_in, int32_t S
  * and disarms. */
 int river_timer_arm(river_ctx* ctx, int32_t op, int32_t max_launches);
 int river_timer_read(river_ctx* ctx, float* ms /* host */, int32_t* n /* host, in/out */);
+
+/* Which kernels serve the decode calls of this context: 1 the persistent decode kernel, 0 the
+ * per-op kernels (see river_decode_steps). Host-only. Returns RIVER_EINVAL for NULL. */
+int river_decode_path(const river_ctx* ctx, int32_t* persistent /* host */);
 
 /* Host mirror of the rows' positions (number of filled KV slots per row). */
 int river_positions(const river_ctx* ctx, int32_t* pos /* host [B] */);

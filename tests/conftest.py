@@ -17,3 +17,16 @@ def pytest_configure(config):
 def has_gpu():
     import torch
     return torch.cuda.is_available()
+
+
+@pytest.fixture(params=["persistent", "per_op"])
+def decode_path(request):
+    """Runs the test once per decode path: the persistent kernel (default) and the per-op
+    kernels (RIVER_PERSIST=0 at context creation)."""
+    old = os.environ.get("RIVER_PERSIST")
+    os.environ["RIVER_PERSIST"] = "1" if request.param == "persistent" else "0"
+    yield request.param
+    if old is None:
+        del os.environ["RIVER_PERSIST"]
+    else:
+        os.environ["RIVER_PERSIST"] = old

@@ -76,5 +76,6 @@ def test_init_rejects_null_arguments_before_any_device_work():
                         ctypes.c_void_p(1), None, ctypes.byref(ctx))
     assert rc == river.RIVER_EINVAL
     assert lib.river_destroy(None) == river.RIVER_OK
+    assert lib.river_decode_path(None, None) == river.RIVER_EINVAL
     assert lib.river_decode_step(None, None, None, 0.5, None, None, None, None, None) == river.RIVER_EINVAL
     assert lib.river_prefill(None, None, 1, 0, 0.5, None, None, None, None, None) == river.RIVER_EINVAL

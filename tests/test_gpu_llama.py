@@ -27,7 +27,7 @@ def _exit_frac_by(rv, c, tok, tau, steps, by):
     return float((ex.cpu().numpy() <= by).mean())
 
 
-def test_llama1b_prefill_and_decode_match_oracle():
+def test_llama1b_prefill_and_decode_match_oracle(decode_path):
     cfg = configs.LLAMA_1B
     c = configs.model_cfg(cfg)
     P, S = cfg["prompt"], 6
@@ -51,6 +51,7 @@ def test_llama1b_prefill_and_decode_match_oracle():
     orc = O.RiverOracle(c, synth.to_numpy(w))
     Tmax = P + S + 4
     rv = river.River(c, w, max_seq=Tmax, max_prefill=P)
+    assert rv.decode_path() == decode_path
     kvo = orc.new_kv(1, Tmax)
     pre = rv.prefill(toks, prefill_exit=0, tau=tau, logits=True, min_sim=True)
     ge = pre["seq_exit"].cpu().numpy()
@@ -134,11 +135,12 @@ def test_llama8b_prefill_kv_layer1_matches_oracle(llama8b):
     rv.close()
 
 
-def test_llama8b_decode_slices_match_oracle(llama8b):
+def test_llama8b_decode_slices_match_oracle(llama8b, decode_path):
     cfg, c, w = llama8b
     P, W, S = cfg["prompt"], 4, 3
     L = c["L"]
     rv = river.River(c, w, max_seq=P + W + S + 4, max_prefill=P)
+    assert rv.decode_path() == decode_path
     toks = synth.prompt(c, 1, P, seed=0, device="cuda")
     sched = torch.from_numpy(synth.schedule(cfg, W + S, 1, seed=0)).to("cuda")
     pre = rv.prefill(toks, prefill_exit=L)
@@ -175,7 +177,7 @@ def test_llama8b_decode_slices_match_oracle(llama8b):
     rv.close()
 
 
-def test_llama8b_backbone_only_decode_equals_forced_full_depth(llama8b):
+def test_llama8b_backbone_only_decode_equals_forced_full_depth(llama8b, decode_path):
     cfg, c, w = llama8b
     P, S = 256, 4
     L = c["L"]

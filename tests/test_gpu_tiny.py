@@ -55,12 +55,13 @@ def _kv_compare(rv, kvo, upto):
 
 
 @pytest.mark.parametrize("mode", ["forced2", "tau"])
-def test_tiny_prefill_and_decode_match_oracle(tiny, mode):
+def test_tiny_prefill_and_decode_match_oracle(tiny, mode, decode_path):
     w, wn, orc = tiny
     cfg = configs.TINY
     P, S = cfg["prompt"], cfg["steps"]
     Tmax = P + S + 8
     rv = river.River(TINY, w, max_seq=Tmax, max_prefill=P)
+    assert rv.decode_path() == decode_path
     toks = synth.prompt(TINY, 1, P, seed=0, device="cuda")
     kvo = orc.new_kv(1, Tmax)
     tau = f32(cfg["tau"])
@@ -103,7 +104,7 @@ def test_tiny_prefill_and_decode_match_oracle(tiny, mode):
     rv.close()
 
 
-def test_tau_extremes(tiny):
+def test_tau_extremes(tiny, decode_path):
     w, wn, orc = tiny
     rv = river.River(TINY, w, max_seq=64)
     toks = synth.prompt(TINY, 1, 8, seed=1, device="cuda")
@@ -140,7 +141,7 @@ def test_position_overflow_is_rejected_on_host(tiny):
     rv.close()
 
 
-def test_multi_step_matches_single_steps(tiny):
+def test_multi_step_matches_single_steps(tiny, decode_path):
     w, wn, orc = tiny
     S = 6
     sched = torch.tensor([[1], [2], [3], [4], [2], [1]], dtype=torch.int32, device="cuda")

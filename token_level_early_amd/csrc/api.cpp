@@ -386,8 +386,10 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
     river_destroy(c);
     return hip_fail(e, "layer table upload");
   }
+  // the persistent decode kernel is the default path; RIVER_PERSIST=0 selects the per-op
+  // kernels (graph-captured), which also serve shapes the persistent kernel does not cover
   const char* pe = getenv("RIVER_PERSIST");
-  if (pe && pe[0] == '1') {
+  if (!(pe && pe[0] == '0')) {
     for (int m = 0; m < 2; ++m) {
       const void* fn = river_persist_fn(d, m);
       const int nwg = fn ? river_persist_grid(fn) : 0;
@@ -417,6 +419,12 @@ int river_destroy(river_ctx* c) {
   for (hipEvent_t ev : c->timer_ev) (void)hipEventDestroy(ev);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   delete c;
+  return RIVER_OK;
+}
+
+int river_decode_path(const river_ctx* c, int32_t* persistent) {
+  if (!c || !persistent) return fail(RIVER_EINVAL, "null argument");
+  *persistent = (c->persist_fn[0] != nullptr) ? 1 : 0;
   return RIVER_OK;
 }
 

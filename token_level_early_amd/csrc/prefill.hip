@@ -233,37 +233,56 @@ __global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
 
 // Causal attention. Workgroup = (query block, kv head, sequence). 16 lanes per (query, head);
 // QB = 16/G queries x G heads per workgroup; K/V tiles of 64 positions staged in LDS.
+// Causal GQA prompt attention on MFMA (flash-attention style). Workgroup = one KV head and
+// 32 query positions; wave g handles query head kvh*G + g, so a staged K/V tile serves all G
+// heads of the group. Per 64-key tile: S^T = K Q^T (v_mfma_f32_16x16x16_f16, fp32), causal mask,
+// online softmax in the exp2 domain, then O^T += V^T P^T with P rounded to fp16. Computing the
+// transposes puts each lane on one query column, so the softmax state and the rescale of the
+// output accumulators are per-lane scalars and the probabilities come out of the score
+// accumulators already in the operand layout of the second product. The exact result is
+// softmax(q K^T / sqrt(D)) V over positions 0..t (the prompt attention every block runs).
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void k_pf_attn(PfArgs p, int layer) {
-  constexpr int QB = 16 / G;
-  constexpr int DPT = D / 16;  // dims per lane
-  constexpr int KT = 64;
-  __shared__ f16 Ks[KT][D];
-  __shared__ f16 Vs[KT][D];
+__global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
+  constexpr int KT = 64, QW = 32;
+  constexpr int NK = D / 16;  // 16-wide steps over the head dimension
+  __shared__ f16 Ks[KT][D + 8];   // [key][dim]
+  __shared__ f16 Vt[D][KT + 8];   // [dim][key]
   const Dims& dm = p.dm;
-  const int qb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int slot = tid / 16, sub = tid % 16;  // slot -> (query, head)
-  const int qi = slot / G, g = slot % G;
-  const int t = qb * QB + qi;  // query position
-  const int h = kvh * G + g;
-  const bool valid = t < p.P;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int q0 = blockIdx.x * QW;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int lr = lane % 16, lq = lane / 16;
+  const int h = kvh * G + w;
   const size_t hs = (size_t)dm.Tmax * D;
   const f16* Kb = p.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * hs;
   const f16* Vb = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * hs;
-  const float qs = 1.4426950408889634f / sqrtf((float)D);
-  float qf[DPT], acc[DPT];
-  const int m = b * p.P + (valid ? t : 0);
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
+
+  // Q^T operand: lane supplies Q[q = q0 + qb*16 + lr][dims ks*16 + 4*lq .. +3]
+  h4 qf[2][NK];
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) {
-    qf[i] = h2f(p.act[(size_t)m * dm.hd + h * D + sub * DPT + i]) * qs;
-    acc[i] = 0.f;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int t = q0 + qb * 16 + lr;
+    const f16* qrow = p.act + ((size_t)b * p.P + (t < p.P ? t : 0)) * dm.hd + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      h4 v = *(const h4*)(qrow + ks * 16 + 4 * lq);
+      if (t >= p.P) v = (h4){0, 0, 0, 0};
+      qf[qb][ks] = v;
+    }
   }
-  float mx = -__builtin_inff(), l = 0.f;
-  const int tmax_blk = min(p.P - 1, qb * QB + QB - 1);  // last position any query needs
-  for (int k0 = 0; k0 <= tmax_blk; k0 += KT) {
+  f4 o[NK][2];  // O^T: lane holds dims db*16 + 4*lq + r of query qb*16 + lr
+#pragma unroll
+  for (int db = 0; db < NK; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = (f4){0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-__builtin_inff(), -__builtin_inff()};
+  float lsum[2] = {0.f, 0.f};  // this lane's share of the softmax denominator
+
+  const int kend = min(p.P, q0 + QW);  // keys [0, kend) can be visible to this block
+  for (int k0 = 0; k0 < kend; k0 += KT) {
     __syncthreads();
-    for (int idx = tid; idx < KT * D / 8; idx += kBlock) {
+    for (int idx = tid; idx < KT * D / 8; idx += G * kWave) {
       const int r = idx / (D / 8), c = (idx % (D / 8)) * 8;
       uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
       if (k0 + r < p.P) {
@@ -271,28 +290,93 @@ __global__ __launch_bounds__(kBlock) void k_pf_attn(PfArgs p, int layer) {
         vv4 = *(const uint4*)(Vb + (size_t)(k0 + r) * D + c);
       }
       *(uint4*)&Ks[r][c] = kv4;
-      *(uint4*)&Vs[r][c] = vv4;
+      const f16* vh = (const f16*)&vv4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Vt[c + i][r] = vh[i];
     }
     __syncthreads();
-    const int kend = min(KT, (valid ? t : -1) - k0 + 1);
-    for (int j = 0; j < kend; ++j) {
-      float sc = 0.f;
+    // S^T[key][q] for 4 key blocks x 2 query blocks
+    f4 sc[4][2];
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) sc = fmaf(qf[i], h2f(Ks[j][sub * DPT + i]), sc);
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sc += __shfl_xor(sc, o, kWave);
-      const float mn = fmaxf(mx, sc);
-      const float c = exp2f(mx - mn), pj = exp2f(sc - mn);
-      l = l * c + pj;
+      for (int qb = 0; qb < 2; ++qb) sc[kb][qb] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(acc[i], c, pj * h2f(Vs[j][sub * DPT + i]));
-      mx = mn;
+    for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const h4 kf = *(const h4*)&Ks[kb * 16 + lr][ks * 16 + 4 * lq];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x16f16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
+      }
+    }
+    // mask, tile max per query column, online rescale
+    h4 pf[4][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int t = q0 + qb * 16 + lr;
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kb * 16 + 4 * lq + r;
+          const float v = (key <= t && key < p.P) ? sc[kb][qb][r] * qs : -__builtin_inff();
+          sc[kb][qb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const float mn = fmaxf(mrow[qb], mt);
+      const bool live = mn > -__builtin_inff();  // some visible key so far
+      const float c = live ? exp2f(mrow[qb] - mn) : 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        h4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = live ? exp2f(sc[kb][qb][r] - mn) : 0.f;
+          pv[r] = (f16)e;
+          ps += e;
+        }
+        pf[kb][qb] = pv;
+      }
+      lsum[qb] = lsum[qb] * c + ps;
+      mrow[qb] = mn;
+#pragma unroll
+      for (int db = 0; db < NK; ++db) o[db][qb] *= c;
+    }
+    // O^T[dim][q] += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int db = 0; db < NK; ++db) {
+        const h4 vf = *(const h4*)&Vt[db * 16 + lr][kb * 16 + 4 * lq];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf[kb][qb], o[db][qb], 0, 0, 0);
+      }
     }
   }
-  if (valid) {
-    f16* o = p.hout + (size_t)m * dm.hd + h * D;  // attention output goes to hout (scratch)
+  // denominators (the four lanes of a query column hold disjoint keys), normalise, store
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) o[sub * DPT + i] = f2h(acc[i] / l);
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int t = q0 + qb * 16 + lr;
+    if (t < p.P) {
+      f16* orow = p.hout + ((size_t)b * p.P + t) * dm.hd + (size_t)h * D;  // attention output -> hout
+#pragma unroll
+      for (int db = 0; db < NK; ++db) {
+        h4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (f16)(o[db][qb][r] / l);
+        *(h4*)(orow + db * 16 + 4 * lq) = v;
+      }
+    }
   }
 }
 
@@ -430,16 +514,15 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
     hipLaunchKernelGGL(k_pf_rope_kv, dim3(M), dim3(kBlock), 0, st, q, l);
     {
       const int G = dm.H / dm.Hkv;
-      const int QB = 16 / G;
-      dim3 grid((q.P + QB - 1) / QB, dm.Hkv, dm.B);
-      if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_attn<128, 4>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_attn<64, 4>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_attn<64, 2>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_attn<128, 2>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_attn<128, 1>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_attn<64, 1>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_attn<128, 8>), grid, dim3(kBlock), 0, st, q, l);
-      else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_attn<64, 8>), grid, dim3(kBlock), 0, st, q, l);
+      dim3 grid((q.P + 31) / 32, dm.Hkv, dm.B);
+      if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_fattn<128, 4>), grid, dim3(4 * kWave), 0, st, q, l);
+      else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_fattn<64, 4>), grid, dim3(4 * kWave), 0, st, q, l);
+      else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_fattn<64, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+      else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_fattn<128, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+      else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_fattn<128, 1>), grid, dim3(kWave), 0, st, q, l);
+      else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_fattn<64, 1>), grid, dim3(kWave), 0, st, q, l);
+      else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_fattn<128, 8>), grid, dim3(8 * kWave), 0, st, q, l);
+      else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_fattn<64, 8>), grid, dim3(8 * kWave), 0, st, q, l);
       else return hipErrorInvalidValue;
     }
     // O projection + residual: attention output sits in hout

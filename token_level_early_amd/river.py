@@ -70,6 +70,7 @@ def load():
         "river_decode_step": [VP, VP, VP, F32, VP, VP, VP, VP, VP],
         "river_decode_steps": [VP, VP, VP, I32, F32, VP, VP, VP, VP],
         "river_positions": [VP, P(I32)],
+        "river_decode_path": [VP, P(I32)],
         "river_device_status": [VP, VP],
         "river_export_river": [VP, I32, I32, VP, VP, VP],
         "river_debug_hidden": [VP, VP, VP],
@@ -174,6 +175,12 @@ class River:
         arr = (ctypes.c_int32 * self.B)()
         _check(self.lib.river_positions(self.ctx, arr))
         return list(arr)
+
+    def decode_path(self):
+        """"persistent" or "per_op": the kernels that serve this context's decode calls."""
+        v = ctypes.c_int32()
+        _check(self.lib.river_decode_path(self.ctx, ctypes.byref(v)))
+        return "persistent" if v.value else "per_op"
 
     def device_status(self):
         return self.lib.river_device_status(self.ctx, _stream())
