@@ -195,3 +195,69 @@ def test_llama8b_backbone_only_decode_equals_forced_full_depth(llama8b, decode_p
         rv.close()
     assert np.array_equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_llama8b_64k_context_prefill_and_decode_slices(llama8b, decode_path):
+    """The 65536-token configuration at full size, checked on sampled outputs with the GPU's
+    own shared cache as the oracle's context (teacher forcing): layer-1 K/V at sampled prompt
+    positions (embedding -> norm -> projection -> RoPE), layer-2 K/V at sampled positions far
+    into the prompt (one prompt-attention block over up to 65536 positions, then layer 2's
+    projection), and whole decode blocks at sampled layers for two decode tokens."""
+    _, c, w = llama8b
+    cfg = configs.LLAMA_8B_64K
+    P, S = cfg["prompt"], 2
+    L, Hkv, D = c["L"], c["Hkv"], c["D"]
+    rv = river.River(c, w, max_seq=P + S + 2, max_prefill=P)
+    assert rv.decode_path() == decode_path
+    toks = synth.prompt(c, 1, P, seed=5, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=L)
+    torch.cuda.synchronize()
+    kv = rv.kv_view()
+    tk = toks[0].cpu().numpy()
+    used = [0, 1, 7, 8, L - 1]  # 0-based layers the checks below run
+    orc = O.RiverOracle(c, synth.to_numpy({"embed": w["embed"], "lm_head": w["lm_head"],
+                                            "final_norm": w["final_norm"],
+                                            "layers": [w["layers"][i] if i in used else None
+                                                       for i in range(L)]}),
+                        layers=used)
+    # layer-1 K/V and layer-2 K/V at sampled prompt positions
+    for t in (0, 1, 4097, 40000, P - 1):
+        h0 = w["embed"][int(tk[t])].cpu().numpy()
+        K1 = kv[0, 0, 0, :, : t + 1].cpu().numpy().copy()
+        V1 = kv[0, 1, 0, :, : t + 1].cpu().numpy().copy()
+        k1_gpu, v1_gpu = K1[:, t].copy(), V1[:, t].copy()
+        h1 = O.block_decode(c, orc.weights_for(0, False), orc.norms(0), h0, t, K1, V1)
+        assert rel_err(k1_gpu, K1[:, t]) <= TOL, t
+        assert rel_err(v1_gpu, V1[:, t]) <= TOL, t
+        lw = orc.weights_for(1, False)
+        a = O.rmsnorm(h1, orc.norms(1)["attn_norm"], c["eps"]).astype(np.float64)
+        k2 = O.to_f16(lw["wk"] @ a).reshape(Hkv, D)
+        v2 = O.to_f16(lw["wv"] @ a).reshape(Hkv, D)
+        cs, sn = O.rope_cos_sin(t, D, c["theta"])
+        k2 = O.apply_rope(k2, cs, sn)
+        assert rel_err(kv[1, 0, 0, :, t].float().cpu().numpy(), k2) <= TOL, t
+        assert rel_err(kv[1, 1, 0, :, t].float().cpu().numpy(), v2) <= TOL, t
+    # decode blocks at sampled layers
+    es = [8, L]  # one early exit and one full-depth token (the config mixes both)
+    cur = pre["tokens"]
+    for s, e in enumerate(es):
+        pos = P + s
+        fe = torch.tensor([e], dtype=torch.int32, device="cuda")
+        r = rv.decode_step(cur, forced_exit=fe, logits=True)
+        assert int(r["exit_layer"][0]) == e
+        hs = rv.hidden()[:, 0].cpu().numpy()
+        kv = rv.kv_view()
+        for l in sorted({1, e, min(e + 1, L), L}):
+            Kl = kv[l - 1, 0, 0, :, : pos + 1].cpu().numpy().copy()
+            Vl = kv[l - 1, 1, 0, :, : pos + 1].cpu().numpy().copy()
+            k_gpu, v_gpu = Kl[:, pos].copy(), Vl[:, pos].copy()
+            out = O.block_decode(c, orc.weights_for(l - 1, l > e), orc.norms(l - 1), hs[l - 1], pos, Kl, Vl)
+            assert rel_err(hs[l], out) <= TOL, (s, l)
+            assert rel_err(k_gpu, Kl[:, pos]) <= TOL, (s, l)
+            assert rel_err(v_gpu, Vl[:, pos]) <= TOL, (s, l)
+        lg = orc.head_logits(hs[L])
+        assert rel_err(r["logits"][0].cpu().numpy(), lg) <= TOL
+        assert top1_checked(int(r["tokens"][0]), lg) is not False
+        cur = r["tokens"]
+    assert rv.positions() == [P + S]
+    rv.close()
