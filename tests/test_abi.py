@@ -52,7 +52,8 @@ def test_river_buffer_covers_int4_copy():
     ("entry_layer", 0, "entry_layer"),
     ("entry_layer", 33, "entry_layer"),
     ("d_model", 4100, "d_model"),
-    ("max_batch", 3, "max_batch"),
+    ("max_batch", 17, "max_batch"),
+    ("max_batch", 0, "max_batch"),
     ("rms_eps", 0.0, "rms_eps"),
 ])
 def test_bad_config_rejected(field, value, msg):

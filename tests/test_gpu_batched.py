@@ -1,0 +1,155 @@
+"""GPU parity of batched decode (several rows per step, each with its own exit layer) against
+the CPU oracle: the tiny decoder with 4 rows end to end, and the Llama-3.1-8B shape with 16
+rows and 4096-token prompts (the batch-16 configuration) on sampled rows and layers."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import river_oracle as O
+from token_level_early_amd import configs, river, synth
+from tests._util import TOL, f32, rel_err, top1_checked
+
+pytestmark = pytest.mark.gpu
+
+TINY = configs.model_cfg(configs.TINY)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.weights(TINY, seed=0, device="cuda")
+    return w, O.RiverOracle(TINY, synth.to_numpy(w))
+
+
+@pytest.mark.parametrize("mode", ["forced", "tau"])
+def test_tiny_batch4_matches_oracle(tiny, mode):
+    w, orc = tiny
+    B, P, S = 4, 24, 8
+    L = TINY["L"]
+    Tmax = P + S + 4
+    rv = river.River(TINY, w, max_seq=Tmax, max_prefill=P, batch=B)
+    assert rv.decode_path() == "per_op"
+    toks = synth.prompt(TINY, B, P, seed=7, device="cuda")
+    kvo = orc.new_kv(B, Tmax)
+    tau = f32(0.95)
+    if mode == "forced":
+        pre = rv.prefill(toks, prefill_exit=L, logits=True)
+        opre = orc.prefill(kvo, toks.cpu().numpy(), prefill_exit=L)
+    else:
+        pre = rv.prefill(toks, prefill_exit=0, tau=tau, logits=True)
+        ge = pre["seq_exit"].cpu().numpy()
+        opre = orc.prefill(kvo, toks.cpu().numpy(), tau=tau, gpu_seq_exit=ge)
+        assert np.array_equal(ge, opre["seq_exit"])
+    for b in range(B):
+        assert rel_err(pre["logits"][b].cpu().numpy(), opre["logits"][b]) <= TOL, b
+        assert top1_checked(int(pre["tokens"][b]), opre["logits"][b]) is not False, b
+    rng = np.random.default_rng(3)
+    cur = pre["tokens"]
+    exits = []
+    for s in range(S):
+        if mode == "forced":
+            fe = rng.integers(1, L + 1, size=B).astype(np.int32)  # rows disagree on most layers
+            r = rv.decode_step(cur, forced_exit=torch.from_numpy(fe).cuda(), logits=True)
+            o = orc.decode_step(kvo, cur.cpu().numpy(), forced_exit=list(fe))
+        else:
+            r = rv.decode_step(cur, tau=tau, logits=True, sim=True)
+            ge = r["exit_layer"].cpu().numpy()
+            o = orc.decode_step(kvo, cur.cpu().numpy(), tau=tau, gpu_exit=ge)
+            sim = r["sim"].cpu().numpy()
+            fin = ~np.isnan(o["sim"])
+            assert np.array_equal(np.isnan(sim), np.isnan(o["sim"])), s
+            assert np.allclose(sim[fin], o["sim"][fin], atol=2e-3), s
+        hs = rv.hidden().float().cpu().numpy()
+        assert np.array_equal(r["exit_layer"].cpu().numpy(), o["exit_layer"]), s
+        for b in range(B):
+            assert rel_err(hs[:, b], o["hs"][:, b]) <= TOL, (s, b)
+            assert rel_err(r["logits"][b].cpu().numpy(), o["logits"][b]) <= TOL, (s, b)
+            assert top1_checked(int(r["tokens"][b]), o["logits"][b]) is not False, (s, b)
+        exits.append(r["exit_layer"].cpu().numpy())
+        cur = r["tokens"]
+    kv = rv.kv_view().float().cpu().numpy()
+    upto = P + S
+    for l in range(L):
+        for j, ref in ((0, kvo.K), (1, kvo.V)):
+            assert rel_err(kv[l, j, :, :, :upto], ref[l, :, :, :upto]) <= TOL, (l, j)
+    assert float(np.abs(kv[:, :, :, :, upto:]).max()) == 0.0
+    assert rv.positions() == [upto] * B
+    assert rv.device_status() == river.RIVER_OK
+    if mode == "forced":
+        assert len(set(np.concatenate(exits).tolist())) > 1
+    rv.close()
+
+
+def test_tiny_batch4_multi_step_equals_single_steps(tiny):
+    w, _ = tiny
+    B, P, S = 4, 16, 5
+    L = TINY["L"]
+    sched = torch.tensor(np.random.default_rng(5).integers(1, L + 1, size=(S, B)), dtype=torch.int32,
+                         device="cuda")
+    outs = []
+    for multi in (False, True):
+        rv = river.River(TINY, w, max_seq=P + S + 2, max_prefill=P, batch=B)
+        toks = synth.prompt(TINY, B, P, seed=8, device="cuda")
+        pre = rv.prefill(toks, prefill_exit=L)
+        if multi:
+            ex = torch.empty(S, B, dtype=torch.int32, device="cuda")
+            t = rv.decode_steps(pre["tokens"], sched=sched, exit_layer=ex)
+            outs.append((t.cpu().numpy(), ex.cpu().numpy(), rv.kv_view().cpu()))
+        else:
+            cur, tt, ee = pre["tokens"], [], []
+            for s in range(S):
+                r = rv.decode_step(cur, forced_exit=sched[s])
+                tt.append(r["tokens"].cpu().numpy())
+                ee.append(r["exit_layer"].cpu().numpy())
+                cur = r["tokens"]
+            outs.append((np.stack(tt), np.stack(ee), rv.kv_view().cpu()))
+        rv.close()
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+    assert np.array_equal(outs[0][1], sched.cpu().numpy())
+    assert torch.equal(outs[0][2], outs[1][2])
+
+
+def test_llama8b_batch16_decode_slices_match_oracle():
+    cfg = configs.LLAMA_8B_BS16
+    c = configs.model_cfg(cfg)
+    B, P, S = cfg["batch"], cfg["prompt"], 2
+    L = c["L"]
+    w = synth.weights(c, seed=0, device="cuda")
+    rv = river.River(c, w, max_seq=P + S + 2, max_prefill=P, batch=B)
+    toks = synth.prompt(c, B, P, seed=0, device="cuda")
+    sched = torch.from_numpy(synth.schedule(cfg, S, B, seed=0)).to("cuda")  # U{8..32} per row
+    pre = rv.prefill(toks, prefill_exit=L)
+    rows = [0, 7, 15]
+    es_rows = {b: [int(sched[s, b]) for s in range(S)] for b in rows}
+    layers = sorted({1, L} | {e for v in es_rows.values() for e in v} |
+                    {min(e + 1, L) for v in es_rows.values() for e in v})
+    orc = O.RiverOracle(c, synth.to_numpy({"embed": w["embed"], "lm_head": w["lm_head"],
+                                            "final_norm": w["final_norm"],
+                                            "layers": [w["layers"][i] if i + 1 in layers else None
+                                                       for i in range(L)]}),
+                        layers=[l - 1 for l in layers])
+    cur = pre["tokens"]
+    for s in range(S):
+        pos = P + s
+        r = rv.decode_step(cur, forced_exit=sched[s], logits=True)
+        assert np.array_equal(r["exit_layer"].cpu().numpy(), sched[s].cpu().numpy())
+        hs_all = rv.hidden().cpu().numpy()  # [L+1][B][d]
+        kv = rv.kv_view()
+        for b in rows:
+            e = es_rows[b][s]
+            hs = hs_all[:, b]
+            for l in sorted({1, e, min(e + 1, L), L}):
+                Kl = kv[l - 1, 0, b, :, : pos + 1].cpu().numpy().copy()
+                Vl = kv[l - 1, 1, b, :, : pos + 1].cpu().numpy().copy()
+                k_gpu, v_gpu = Kl[:, pos].copy(), Vl[:, pos].copy()
+                out = O.block_decode(c, orc.weights_for(l - 1, l > e), orc.norms(l - 1), hs[l - 1], pos, Kl, Vl)
+                assert rel_err(hs[l], out) <= TOL, (s, b, l)
+                assert rel_err(k_gpu, Kl[:, pos]) <= TOL, (s, b, l)
+                assert rel_err(v_gpu, Vl[:, pos]) <= TOL, (s, b, l)
+            lg = orc.head_logits(hs[L])
+            assert rel_err(r["logits"][b].cpu().numpy(), lg) <= TOL, (s, b)
+            assert top1_checked(int(r["tokens"][b]), lg) is not False, (s, b)
+        cur = r["tokens"]
+    assert rv.positions() == [P + S] * B
+    rv.close()

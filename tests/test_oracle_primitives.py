@@ -259,3 +259,4 @@ def test_silu_values():
 def test_argmax_lowest_index_on_ties():
     assert O.argmax_lowest([1.0, 3.0, 2.0, 3.0]) == 1
     assert O.argmax_lowest([5.0, 5.0]) == 0
+

@@ -26,7 +26,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
-SOURCES = ["api.cpp", "quant.hip", "decode.hip", "prefill.hip", "persist.hip"]
+SOURCES = ["api.cpp", "quant.hip", "decode.hip", "prefill.hip", "persist.hip", "batched.hip"]
 
 
 def _compile(src):

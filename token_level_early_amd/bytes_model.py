@@ -59,3 +59,43 @@ def token_bytes(c, e, pos):
         total += op_bytes(c, "attn", pos=pos)
     total += op_bytes(c, "lm")
     return total
+
+
+def batch_step_bytes(c, exits, positions):
+    """Algorithmic bytes of one batched decode step: row b exits after e_b backbone layers and
+    runs at position p_b. At layer l the backbone matrices (and norm gains) are read once if any
+    row runs l on the backbone, the river copy once if any row has exited; every row reads its
+    own K/V of positions 0..p_b and appends one slot; each row reads its embedding row; the
+    final norm and the LM head are read once for all rows."""
+    L, d = c["L"], c["d"]
+    kv = 2 * c["Hkv"] * c["D"] * 2
+    total = 0
+    for l in range(1, L + 1):
+        for river, used in ((False, any(e >= l for e in exits)), (True, any(e < l for e in exits))):
+            if used:
+                total += sum(matrix_bytes(N, K, river, c["group"]) for N, K in op_params(c).values())
+                total += 4 * d  # attention and MLP norm gains
+    for p in positions:
+        total += L * kv * (p + 1) + L * kv + 2 * d
+    total += 2 * d + 2 * c["V"] * d
+    return total
+
+
+def batch_op_bytes(c, op, exits, layer, positions):
+    """Algorithmic bytes of one batched launch of `op` at `layer` (see batch_step_bytes): the
+    matrices of each weight stream some row uses at that layer (with that stream's norm gains
+    for qkv and gu), plus each row's K/V append (qkv) or K/V read (attn); lm: head + final norm."""
+    d = c["d"]
+    kv = 2 * c["Hkv"] * c["D"] * 2
+    if op == "attn":
+        return sum(kv * (p + 1) for p in positions)
+    if op == "lm":
+        return 2 * c["V"] * d + 2 * d
+    N, K = op_params(c)[op]
+    total = 0
+    for river, used in ((False, any(e >= layer for e in exits)), (True, any(e < layer for e in exits))):
+        if used:
+            total += matrix_bytes(N, K, river, c["group"]) + (2 * d if op in ("qkv", "gu") else 0)
+    if op == "qkv":
+        total += kv * len(exits)
+    return total

@@ -29,6 +29,10 @@ const void* river_persist_fn(const Dims& dm, int mode);
 int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
                                 unsigned* bar, hipStream_t st);
+hipError_t river_decode_layers_batched(const DecodeArgs& a, f16* xn, int mode, hipStream_t st,
+                                       void (*timer)(void*, int, int), void* tctx, int top);
+hipError_t river_launch_head_batched(const DecodeArgs& a, f16* xn, hipStream_t st,
+                                     void (*timer)(void*, int, int), void* tctx, int top);
 
 hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const LayerDev* host_layers,
                                 int forced, float tau, hipStream_t st);
@@ -66,8 +70,7 @@ int check_cfg(const river_config* c) {
   const int hd = c->n_heads * c->head_dim;
   if (c->d_model > 16384 || hd > 16384 || c->d_ffn > 16384)
     return fail(RIVER_EINVAL, "d_model, n_heads*head_dim and d_ffn must be <= 16384");
-  if (c->max_batch != 1)
-    return fail(RIVER_EINVAL, "max_batch must be 1 (batched decode is not built yet)");
+  if (c->max_batch < 1 || c->max_batch > 16) return fail(RIVER_EINVAL, "max_batch must be in [1, 16]");
   if (c->max_seq < 1) return fail(RIVER_EINVAL, "max_seq must be >= 1");
   if (c->max_prefill < 1 || c->max_prefill > c->max_seq)
     return fail(RIVER_EINVAL, "max_prefill must be in [1, max_seq]");
@@ -136,7 +139,7 @@ RiverLayout river_layout(const Dims& d) {
 // ---- scratch layout
 struct ScratchLayout {
   uint64_t hs, hmid, q, o, a2, qkvr, gu, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
-      layers, rope, bar;
+      layers, rope, bar, xn;
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t total;
@@ -174,6 +177,7 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.pacc = take(B * d.H * s.smax * d.D * 4);
   s.amax = take(2 * B * 8);
   s.bar = take((uint64_t)kBarWords * 4);  // grid barrier of the persistent kernel
+  s.xn = take(B * d.d * 2);                // batched decode: normalised block inputs
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
   const uint64_t M = B * d.max_prefill;
@@ -486,7 +490,8 @@ int river_prefill(river_ctx* c, const int32_t* tokens, int32_t P, int32_t prefil
   a.logits = logits;
   hipError_t e = river_launch_prefill(p, a, c->layers.data(), prefill_exit, tau, st);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  e = river_launch_head(a, st, nullptr, nullptr, -1);
+  e = (d.B > 1) ? river_launch_head_batched(a, (f16*)(sc + s.xn), st, nullptr, nullptr, -1)
+               : river_launch_head(a, st, nullptr, nullptr, -1);
   if (e != hipSuccess) return hip_fail(e, "prefill LM head launch");
   if (seq_exit) {
     e = hipMemcpyAsync(seq_exit, p.seq_exit, (size_t)d.B * 4, hipMemcpyDeviceToDevice, st);
@@ -537,6 +542,13 @@ static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipSt
   return RIVER_OK;
 }
 
+// One decode step on the per-op kernels: batch 1 or the batched (MFMA) kernels.
+static hipError_t step_layers(river_ctx* c, const DecodeArgs& a, int mode, hipStream_t st,
+                              void (*timer)(void*, int, int), void* tctx, int top) {
+  if (c->dm.B > 1) return river_decode_layers_batched(a, (f16*)(c->scratch + c->sl.xn), mode, st, timer, tctx, top);
+  return river_decode_layers(a, mode, st, timer, tctx, top);
+}
+
 static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
   if (c->persist_fn[mode] && (c->timer_op < 0 || c->timer_op == TOP_PERSIST))
     return run_persist(c, a, S, mode, st);
@@ -545,13 +557,13 @@ static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStre
   if (c->timer_op >= 0) {  // timed: direct launches with events around the chosen op
     c->timer_stream = st;
     for (int i = 0; i < S; ++i)
-      if ((e = river_decode_layers(a, mode, st, timer_hook, c, c->timer_op)) != hipSuccess)
+      if ((e = step_layers(c, a, mode, st, timer_hook, c, c->timer_op)) != hipSuccess)
         return hip_fail(e, "decode launch");
     return RIVER_OK;
   }
   if (!c->use_graph) {
     for (int i = 0; i < S; ++i)
-      if ((e = river_decode_layers(a, mode, st, nullptr, nullptr, -1)) != hipSuccess)
+      if ((e = step_layers(c, a, mode, st, nullptr, nullptr, -1)) != hipSuccess)
         return hip_fail(e, "decode launch");
     return RIVER_OK;
   }
@@ -564,7 +576,7 @@ static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStre
     g.valid = false;
     e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-    hipError_t le = river_decode_layers(a, mode, c->cap_stream, nullptr, nullptr, -1);
+    hipError_t le = step_layers(c, a, mode, c->cap_stream, nullptr, nullptr, -1);
     e = hipStreamEndCapture(c->cap_stream, &g.graph);
     if (le != hipSuccess) return hip_fail(le, "decode capture");
     if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");

@@ -1,0 +1,359 @@
+// Batched early-exit decode (2..16 rows) with matrix cores.
+//
+// Each row keeps its own route: at layer l, rows that are still on the backbone use block l's
+// fp16 weights and rows that have exited use its W4A16 river copy (River-LLM paper, Method:
+// token-level exit with one shared KV cache). A projection launch therefore has two weight
+// streams; each workgroup serves one 16-column tile of one stream for all rows at once and
+// skips its stream entirely when no row needs it, so a layer reads both copies only when its
+// rows disagree.
+//
+// GEMM core: Y[16 rows][16 cols] = X[16][K] W[cols][K]^T on v_mfma_f32_16x16x16_f16 with fp32
+// accumulation; the batch is padded to 16 rows. Every lane loads 8 consecutive K elements of
+// one input row (A operand) and of one weight row (B operand) per 32-wide K window and feeds
+// them to two MFMAs; a dot product does not depend on which lane slot carries which K index as
+// long as both operands agree, so the two 4-element halves need no particular order. The int4
+// stream turns 8 nibbles into exact fp16 integers (the 0x6400 exponent trick, pairs (0,4),
+// (1,5), (2,6), (3,7)), permutes the input the same way, sums one quantisation group on the
+// MFMA and applies the fp32 group scale per output column. The four waves of a workgroup split
+// K and meet in LDS.
+//
+// Per layer: k_b_prep (exit test per row, then the attention RMSNorm) -> QKV (RoPE, q and the
+// KV append at each row's position) -> attention (the split-K kernel shared with batch 1, one
+// grid slice per row) -> O + residual -> k_b_prep (MLP RMSNorm) -> gate|up + SwiGLU -> down +
+// residual. Head: final RMSNorm, fp16 LM head with a per-row 64-bit atomic-max argmax, step end.
+#include "gemv.hpp"
+
+static constexpr int kBR = 16;  // rows of an MFMA tile (the batch, padded)
+
+typedef _Float16 bh4 __attribute__((ext_vector_type(4)));
+typedef float bf4 __attribute__((ext_vector_type(4)));
+
+RIVER_DEV bh4 lo4(uint4 u) { return __builtin_bit_cast(bh4, make_uint2(u.x, u.y)); }
+RIVER_DEV bh4 hi4(uint4 u) { return __builtin_bit_cast(bh4, make_uint2(u.z, u.w)); }
+
+// ---------------------------------------------------------------------------------------
+// Per-row preparation: KIND 0 = exit test + attention RMSNorm of layer `layer`'s input,
+// KIND 1 = MLP RMSNorm of h_mid, KIND 2 = final RMSNorm of h(L). Writes xn[b][d].
+// ---------------------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int mode, f16* xn) {
+  __shared__ double red[4];
+  const Dims& dm = a.dm;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int step = *a.step;
+  const f16* hin;
+  const f16* gain;
+  if (KIND == 0) {
+    const LayerDev& lw = a.layers[layer - 1];
+    gain = lw.attn_norm;
+    int route = ROUTE_BACKBONE;
+    if (layer == 1) {
+      int tok = (step == 0) ? a.tok_in[b] : a.tok_out[(step - 1) * dm.B + b];
+      if (tok < 0 || tok >= dm.V) {
+        if (t == 0) atomicOr(a.err, ERR_TOKEN);
+        tok = 0;
+      }
+      hin = a.embed + (size_t)tok * dm.d;
+      f16* h0 = a.hs + (size_t)b * dm.d;
+      for (int i = t; i < dm.d; i += kBlock) h0[i] = hin[i];
+      if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
+      if (a.sim_out)
+        for (int i = t; i < dm.L; i += kBlock) a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
+    } else {
+      hin = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+      if (mode == 0) {
+        const int lp = layer - 1;
+        const int prev = a.route[lp * dm.B + b];
+        if (prev == ROUTE_RIVER) {
+          route = ROUTE_RIVER;
+        } else if (lp >= dm.entry) {
+          if (a.sched) {
+            int e = a.sched[step * dm.B + b];
+            if (e < dm.entry || e > dm.L) {
+              if (t == 0) atomicOr(a.err, ERR_FORCED);
+              e = dm.L;
+            }
+            if (lp == e) route = ROUTE_RIVER;
+          } else {
+            const f16* hprev = a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d;
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+            for (int i = t; i < dm.d; i += kBlock) {
+              const double x = (double)h2f(hprev[i]), y = (double)h2f(hin[i]);
+              s0 += x * y;
+              s1 += x * x;
+              s2 += y * y;
+            }
+            const double dot = block_sum_d(s0, red), n1 = block_sum_d(s1, red), n2 = block_sum_d(s2, red);
+            const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
+            if (t == 0 && a.sim_out) a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
+            if (sim > (double)a.tau) route = ROUTE_RIVER;
+          }
+          if (route == ROUTE_RIVER && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = lp;
+        }
+      }
+    }
+    if (t == 0) a.route[layer * dm.B + b] = route;
+  } else if (KIND == 1) {
+    hin = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+    gain = a.layers[layer - 1].mlp_norm;
+  } else {
+    hin = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
+    gain = a.final_norm;
+  }
+  // RMSNorm (fp64 sum of squares), rounded to fp16 like every other path's staging
+  double ss = 0.0;
+  for (int i = t; i < dm.d; i += kBlock) {
+    const double x = (double)h2f(hin[i]);
+    ss += x * x;
+  }
+  const float inv = inv_rms(block_sum_d(ss, red), dm.d, dm.eps);
+  f16* out = xn + (size_t)b * dm.d;
+  for (int g = t; g * 8 < dm.d; g += kBlock)
+    *(uint4*)(out + g * 8) = norm8(*(const uint4*)(hin + g * 8), *(const uint4*)(gain + g * 8), inv, true);
+}
+
+// ---------------------------------------------------------------------------------------
+// Batched projection: grid (tiles of 16 logical columns, stream), 4 waves splitting K.
+// ---------------------------------------------------------------------------------------
+struct BSmem {
+  float part[4][kBR][kBR];
+  float y[kBR][kBR];
+  int need;
+};
+
+template <int OP>
+__global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, const f16* xin) {
+  __shared__ BSmem sm;
+  const Dims& dm = a.dm;
+  const int tile = blockIdx.x, stream = blockIdx.y;  // stream 0 backbone fp16, 1 river int4
+  const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
+  const int N = op_rows(OP, dm), K = op_k(OP, dm);
+  const LayerDev* lw = (OP == OP_LM) ? nullptr : &a.layers[layer - 1];
+  // does any row run this stream at this layer?
+  if (t == 0) sm.need = 0;
+  __syncthreads();
+  if (t < dm.B) {
+    const int r = (OP == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + t];
+    if (r == stream) atomicOr(&sm.need, 1);
+  }
+  __syncthreads();
+  if (!sm.need) return;
+
+  // this lane's weight column (logical row of the weight matrix)
+  const int col = lane % 16, kq = lane / 16;
+  const int n = logical_row(OP, tile, col, kBR, dm);
+  const bool nok = n < N;
+  const int xrow = lane % 16;  // batch row fed by this lane (A operand)
+  const bool xok = xrow < dm.B;
+  const f16* xp = xin + (size_t)(xok ? xrow : 0) * K;
+
+  bf4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (stream == 0) {
+    const f16* wrow = (OP == OP_LM) ? a.lm_head + (size_t)(nok ? n : 0) * dm.d : f16_row(OP, nok ? n : 0, *lw, a);
+    const int nwin = (K + 31) / 32;
+    const int w0 = w * nwin / 4, w1 = (w + 1) * nwin / 4;
+    int win = w0;
+    for (; win + 4 <= w1; win += 4) {  // four windows' loads in flight
+      uint4 xa[4], wb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = (win + u) * 32 + kq * 8;
+        const bool ok = k < K;
+        xa[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
+        wb[u] = (ok && nok) ? ldg16(wrow + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa[u]), lo4(wb[u]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa[u]), hi4(wb[u]), acc, 0, 0, 0);
+      }
+    }
+    for (; win < w1; ++win) {
+      const int k = win * 32 + kq * 8;
+      const bool ok = k < K;
+      const uint4 xa = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
+      const uint4 wb = (ok && nok) ? ldg16(wrow + k) : make_uint4(0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa), lo4(wb), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa), hi4(wb), acc, 0, 0, 0);
+    }
+  } else {
+    const uint8_t* rp;
+    const f16* sp;
+    w4_row(OP, nok ? n : 0, *lw, dm, rp, sp);
+    const int g = dm.group, wpg = g / 32;  // 32-wide windows per group
+    const int ng = (K + g - 1) / g;
+    const int g0 = w * ng / 4, g1 = (w + 1) * ng / 4;
+    for (int grp = g0; grp < g1; ++grp) {
+      bf4 tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < wpg; ++u) {
+        const int k = grp * g + u * 32 + kq * 8;
+        const bool ok = k < K;
+        const uint4 xr = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
+        // 8 nibbles of this lane's weight row: bytes k/2 .. k/2+3 (padding nibbles are q = 0)
+        const uint32_t wq = nok ? *(const __attribute__((address_space(1))) uint32_t*)(rp + k / 2) : 0x88888888u;
+        h2 p0, p1, p2, p3;
+        unpack8(wq, p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+        const uint32_t in[4] = {xr.x, xr.y, xr.z, xr.w};
+        h2 xo[4];
+        pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+        const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
+        const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
+        const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
+        const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
+        tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp, 0, 0, 0);
+        tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp, 0, 0, 0);
+      }
+      const float s = nok ? h2f(sp[grp]) : 0.f;  // scale of (column n, group grp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, tmp[r], acc[r]);
+    }
+  }
+  // lane holds Y[row 4*kq + r][col]; sum the four waves' K slices
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sm.part[w][4 * kq + r][col] = acc[r];
+  __syncthreads();
+  {
+    const int row = t / kBR, c = t % kBR;
+    sm.y[row][c] = (sm.part[0][row][c] + sm.part[1][row][c]) + (sm.part[2][row][c] + sm.part[3][row][c]);
+  }
+  __syncthreads();
+
+  // epilogue: thread -> (row b, tile column c), rows on this stream only
+  const int b = t / kBR, c = t % kBR;
+  if (b >= dm.B) return;
+  if (OP != OP_LM && a.route[layer * dm.B + b] != stream) return;
+  const float yv = sm.y[b][c];
+  if (OP == OP_QKV) {
+    const int pos = a.pos[b];
+    const int qk_rows = (dm.H + dm.Hkv) * dm.D;
+    const int n0 = logical_row(OP, tile, 0, kBR, dm);
+    if (n0 < qk_rows) {
+      if (c < kBR / 2) {
+        const int nn = logical_row(OP, tile, c, kBR, dm);
+        const int head = nn / dm.D, i = nn % dm.D;  // i < D/2
+        const float x0 = h2f(f2h(yv)), x1 = h2f(f2h(sm.y[b][c + kBR / 2]));
+        const float2 cs = a.rope[(size_t)pos * (dm.D / 2) + i];
+        const f16 r0 = f2h(x0 * cs.x - x1 * cs.y);
+        const f16 r1 = f2h(x1 * cs.x + x0 * cs.y);
+        f16* dst;
+        if (head < dm.H) {
+          dst = a.q + (size_t)b * dm.hd + head * dm.D;
+        } else {
+          const int kvh = head - dm.H;
+          dst = a.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * (size_t)dm.Tmax * dm.D +
+                (size_t)pos * dm.D;
+        }
+        dst[i] = r0;
+        dst[i + dm.D / 2] = r1;
+      }
+    } else {
+      const int nn = logical_row(OP, tile, c, kBR, dm);
+      if (nn < N) {
+        const int vi = nn - qk_rows;
+        const int kvh = vi / dm.D, i = vi % dm.D;
+        a.kv[((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * (size_t)dm.Tmax * dm.D +
+             (size_t)pos * dm.D + i] = f2h(yv);
+      }
+    }
+  } else if (OP == OP_GU) {
+    if (c < kBR / 2) {
+      const int f = logical_row(OP, tile, c, kBR, dm);
+      if (f < dm.F) {
+        const float gg = h2f(f2h(yv)), uu = h2f(f2h(sm.y[b][c + kBR / 2]));
+        const float sg = gg / (1.f + __expf(-gg));
+        a.a2[(size_t)b * dm.F + f] = f2h(sg * uu);
+      }
+    }
+  } else if (OP == OP_O) {
+    const int nn = tile * kBR + c;
+    if (nn < N) {
+      const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + nn;
+      a.hmid[i] = f2h(h2f(a.hs[i]) + h2f(f2h(yv)));
+    }
+  } else if (OP == OP_DOWN) {
+    const int nn = tile * kBR + c;
+    if (nn < N) {
+      const size_t i = ((size_t)(layer - 1) * dm.B + b) * dm.d + nn;
+      a.hs[(size_t)dm.B * dm.d + i] = f2h(h2f(a.hmid[i]) + h2f(f2h(yv)));
+    }
+  } else {  // OP_LM: the row's best column of this tile (lowest index on ties)
+    const int nn = tile * kBR + c;
+    float v = (nn < N) ? yv : -__builtin_inff();
+    if (a.logits && nn < N) a.logits[(size_t)b * dm.V + nn] = yv;
+    if (c == 0) {
+      float best = -__builtin_inff();
+      int bi = 0x7FFFFFFF;
+      for (int j = 0; j < kBR; ++j) {
+        const int nj = tile * kBR + j;
+        if (nj >= N) break;
+        const float vj = sm.y[b][j];
+        if (vj > best) {
+          best = vj;
+          bi = nj;
+        }
+      }
+      if (bi != 0x7FFFFFFF) {
+        const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
+                                       (unsigned long long)(0xFFFFFFFFu - (uint32_t)bi);
+        __hip_atomic_fetch_max(a.amax + b, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    (void)v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------------------
+hipError_t river_launch_attn(const DecodeArgs& a, int layer, hipStream_t st);
+hipError_t river_launch_step_end(const DecodeArgs& a, hipStream_t st);
+
+template <int OP>
+static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const f16* xin, hipStream_t st) {
+  const Dims& dm = a.dm;
+  const int N = (OP == OP_QKV) ? dm.nqkv : (OP == OP_GU) ? 2 * dm.F : (OP == OP_LM) ? dm.V : dm.d;
+  const int tiles = (N + kBR - 1) / kBR;
+  const int streams = (OP == OP_LM || mode == 1) ? 1 : 2;
+  hipLaunchKernelGGL((k_b_gemm<OP>), dim3(tiles, streams), dim3(kBlock), 0, st, a, layer, xin);
+  return hipGetLastError();
+}
+
+hipError_t river_launch_head_batched(const DecodeArgs& a, f16* xn, hipStream_t st,
+                                     void (*timer)(void*, int, int), void* tctx, int top) {
+  hipLaunchKernelGGL((k_b_prep<2>), dim3(a.dm.B), dim3(kBlock), 0, st, a, a.dm.L, 0, xn);
+  if (timer && top == TOP_LM) timer(tctx, TOP_LM, 0);
+  hipError_t e = launch_b_gemm<OP_LM>(a, a.dm.L + 1, 0, xn, st);
+  if (timer && top == TOP_LM) timer(tctx, TOP_LM, 1);
+  if (e != hipSuccess) return e;
+  return river_launch_step_end(a, st);
+}
+
+// One batched decode step (mode 0 early exit, 1 backbone only). `xn` is scratch [B][d].
+hipError_t river_decode_layers_batched(const DecodeArgs& a, f16* xn, int mode, hipStream_t st,
+                                       void (*timer)(void*, int, int), void* tctx, int top) {
+  hipError_t e;
+  auto T = [&](int o, int phase) {
+    if (timer && o == top) timer(tctx, o, phase);
+  };
+  const Dims& dm = a.dm;
+  for (int l = 1; l <= dm.L; ++l) {
+    hipLaunchKernelGGL((k_b_prep<0>), dim3(dm.B), dim3(kBlock), 0, st, a, l, mode, xn);
+    T(TOP_QKV, 0);
+    if ((e = launch_b_gemm<OP_QKV>(a, l, mode, xn, st)) != hipSuccess) return e;
+    T(TOP_QKV, 1);
+    T(TOP_ATTN, 0);
+    if ((e = river_launch_attn(a, l, st)) != hipSuccess) return e;
+    T(TOP_ATTN, 1);
+    T(TOP_O, 0);
+    if ((e = launch_b_gemm<OP_O>(a, l, mode, a.o, st)) != hipSuccess) return e;
+    T(TOP_O, 1);
+    hipLaunchKernelGGL((k_b_prep<1>), dim3(dm.B), dim3(kBlock), 0, st, a, l, mode, xn);
+    T(TOP_GU, 0);
+    if ((e = launch_b_gemm<OP_GU>(a, l, mode, xn, st)) != hipSuccess) return e;
+    T(TOP_GU, 1);
+    T(TOP_DOWN, 0);
+    if ((e = launch_b_gemm<OP_DOWN>(a, l, mode, a.a2, st)) != hipSuccess) return e;
+    T(TOP_DOWN, 1);
+  }
+  return river_launch_head_batched(a, xn, st, timer, tctx, top);
+}

@@ -270,6 +270,11 @@ hipError_t river_launch_head(const DecodeArgs& a, hipStream_t st, void (*timer)(
   return hipGetLastError();
 }
 
+hipError_t river_launch_step_end(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_step_end, dim3(1), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 // Enqueues one decode step. `timer` (optional) is called before and after every launch of the
 // timed op (TOP_* codes) so the host can bracket it with events.
 hipError_t river_decode_layers(const DecodeArgs& a, int mode, hipStream_t st,
