@@ -87,10 +87,11 @@ struct DecodeArgs {
 
 static constexpr int kMaxRed = 8192;
 // Grid barrier of the persistent kernel, in u32 words: the completed-group counter at 0, the
-// abort flag at kBarAbort, the arrival counter of workgroup group g at (g + 1) * kBarStride
-// (groups of kBarGroup workgroups; every counter on its own 256-byte line).
+// abort flag at kBarAbort, the arrival counter of workgroup group g at (g + 1) * kBarStride and
+// its release flag at (kBarMaxGroups + 1 + g) * kBarStride (groups of kBarGroup workgroups;
+// every word on its own 256-byte line).
 static constexpr int kBarGroup = 16, kBarStride = 64, kBarMaxGroups = 64, kBarAbort = 32;
-static constexpr int kBarWords = (kBarMaxGroups + 1) * kBarStride;
+static constexpr int kBarWords = (2 * kBarMaxGroups + 1) * kBarStride;
 // counter slots (each one int)
 static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn: [B][Hkv]
 

@@ -44,11 +44,12 @@ RIVER_DEV double pblock_sum_d(double v, double* red) {
 }
 
 // Two-level grid barrier. Workgroups arrive on the counter of their group of kBarGroup; the
-// last arrival of a group bumps the completed-group counter, which every workgroup polls.
-// Counters only grow during a launch (epoch e is complete when the group counter reaches
-// e * group size and the top counter e * groups), so no reset is needed between barriers.
-// This keeps same-address atomics at kBarGroup + groups per barrier instead of one per
-// workgroup.
+// last arrival of a group bumps the completed-group counter; the arrival that completes the
+// last group writes the epoch into every group's release flag, and each workgroup polls its own
+// group's flag. Counters and flags only grow during a launch (epoch e is complete when the
+// group counter reaches e * group size and the top counter e * groups), so no reset is needed
+// between barriers. Same-address atomics per barrier: kBarGroup + groups instead of one per
+// workgroup; pollers per line: kBarGroup instead of the whole grid.
 // `pre` (weight loads of the next phase, which do not depend on the data the barrier
 // protects) is issued while the barrier is pending: by every wave but the polling one before
 // the wait, by the polling wave after it (its poll loads must not queue behind them).
@@ -65,12 +66,17 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg, Pre&& pre
     const unsigned g = blockIdx.x / kBarGroup;
     const unsigned gs = min((unsigned)kBarGroup, nwg - g * kBarGroup);
     int* abort = (int*)(bar + kBarAbort);
+    unsigned* flags = bar + (kBarMaxGroups + 1) * kBarStride;
     const unsigned old = __hip_atomic_fetch_add(bar + (1 + g) * kBarStride, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (old == epoch * gs - 1) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned target = epoch * ng;
+    if (old == epoch * gs - 1) {
+      const unsigned top = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top == epoch * ng - 1)
+        for (unsigned j = 0; j < ng; ++j)
+          __hip_atomic_store(flags + j * kBarStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     unsigned spins = 0;
-    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(flags + g * kBarStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
       __builtin_amdgcn_s_sleep(1);
       if ((++spins & 255u) == 0) {
         if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
