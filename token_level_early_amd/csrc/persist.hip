@@ -59,14 +59,11 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg, Pre&& pre
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have landed
   __syncthreads();
   ++epoch;
-  const bool poll_wave = threadIdx.x >= kPoller;
-  if (!poll_wave) pre();
-  if (threadIdx.x == kPoller) {
-    const unsigned ng = (nwg + kBarGroup - 1) / kBarGroup;
-    const unsigned g = blockIdx.x / kBarGroup;
+  const unsigned ng = (nwg + kBarGroup - 1) / kBarGroup;
+  const unsigned g = blockIdx.x / kBarGroup;
+  unsigned* flags = bar + (kBarMaxGroups + 1) * kBarStride;
+  if (threadIdx.x == kPoller) {  // arrive first, so the prefetch below does not queue ahead of it
     const unsigned gs = min((unsigned)kBarGroup, nwg - g * kBarGroup);
-    int* abort = (int*)(bar + kBarAbort);
-    unsigned* flags = bar + (kBarMaxGroups + 1) * kBarStride;
     const unsigned old = __hip_atomic_fetch_add(bar + (1 + g) * kBarStride, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
     if (old == epoch * gs - 1) {
@@ -75,6 +72,12 @@ RIVER_DEV void grid_sync(unsigned* bar, unsigned& epoch, unsigned nwg, Pre&& pre
         for (unsigned j = 0; j < ng; ++j)
           __hip_atomic_store(flags + j * kBarStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  __syncthreads();
+  const bool poll_wave = threadIdx.x >= kPoller;
+  if (!poll_wave) pre();
+  if (threadIdx.x == kPoller) {
+    int* abort = (int*)(bar + kBarAbort);
     unsigned spins = 0;
     while (__hip_atomic_load(flags + g * kBarStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
       __builtin_amdgcn_s_sleep(1);
