@@ -12,9 +12,9 @@
 // and (persistent path) the new position's k/v are all issued before any of them is used, and
 // each later block is loaded while the previous one is reduced. Scores are summed across the
 // D/8 lanes with DPP row permutations; softmax is exact per block and merged online (exp2
-// domain). Slots merge inside the wave, waves merge in LDS, and the last-arriving split of a
-// head merges all splits of it (one wave per query head for the weights, one batch of partial
-// loads per thread for the output).
+// domain). The slots merge in LDS, and the last-arriving split of a head merges all splits of
+// it (one wave per query head for the weights, one batch of partial loads per thread for the
+// output).
 #pragma once
 
 #include "common.hpp"
@@ -24,30 +24,17 @@
 static constexpr int kMaxSplit = 64;  // partial-result slots per (row, query head)
 static constexpr int kAttnMinChunk = 64;
 
-template <int D, int G, int NT>
+// LDS of one attention split: per-slot softmax state (slots = position lanes of the workgroup;
+// GL query heads per lane, see attn_split), the split weights of the final merge, a flag.
+template <int D, int G, int NT, int GL = G>
 struct AttnLds {
-  static constexpr int NW = NT / kWave;
-  float acc[NW][G][D];
-  float m[NW][G];
-  float l[NW][G];
+  static constexpr int NS = (NT / kWave) * (kWave / ((G / GL) * (D / 8)));
+  float acc[NS][G][D];
+  float m[NS][G];
+  float l[NS][G];
   float w[G][kMaxSplit];
   int flag;
 };
-
-// Sum / max over the lanes of a wave that differ by multiples of W (a power of two, < 64);
-// every lane gets the result.
-template <int W>
-RIVER_DEV float xslot_sum(float x) {
-#pragma unroll
-  for (int o = W; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
-  return x;
-}
-template <int W>
-RIVER_DEV float xslot_max(float x) {
-#pragma unroll
-  for (int o = W; o < kWave; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
-}
 
 RIVER_DEV float4 ld4_coh(const float* p) {
   const uint4 u = ldx16<true>(p);
@@ -62,7 +49,7 @@ RIVER_DEV float4 ld4_coh(const float* p) {
 //                 appends them to the cache; activations move through agent-coherent accesses.
 template <int D, int G, int NT, bool ROPE, int UP = 4, int GLP = G>
 RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b, int pos, int nsplit,
-                          AttnLds<D, G, NT>& sm) {
+                          AttnLds<D, G, NT, GLP>& sm) {
   constexpr bool COH = ROPE;
   constexpr int LPT = D / 8;                       // lanes per head (8 dims each)
   constexpr int GL = GLP;                          // query heads per lane
@@ -237,42 +224,26 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
         }
       }
     }
-    // merge the SPW slots of this wave (lanes that differ by multiples of LPP)
+    // every slot's softmax state to LDS, then merge the NS slots per (query head, dim)
 #pragma unroll
     for (int gl = 0; gl < GL; ++gl) {
       const int g = hg * GL + gl;
-      float M = m[gl], lg, xs[8];
-      if (LPP == kWave) {  // one slot per wave
-        lg = l[gl];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xs[i] = acc[gl][i];
-      } else {
-        M = xslot_max<LPP>(M);
-        const float sc = (m[gl] > -__builtin_inff()) ? exp2f(m[gl] - M) : 0.f;
-        lg = xslot_sum<LPP>(l[gl] * sc);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xs[i] = xslot_sum<LPP>(acc[gl][i] * sc);
-      }
-      if (lane < LPP) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sm.acc[w][g][d0 + i] = xs[i];
-        if (sub == 0) {
-          sm.m[w][g] = M;
-          sm.l[w][g] = lg;
-        }
+      for (int i = 0; i < 8; ++i) sm.acc[slot][g][d0 + i] = acc[gl][i];
+      if (sub == 0) {
+        sm.m[slot][g] = m[gl];
+        sm.l[slot][g] = l[gl];
       }
     }
     __syncthreads();
-    // merge the NW waves; write this split's partial (scaled to its own max) and (max, sum)
+    // write this split's partial (scaled to its own max) and (max, sum)
     for (int idx = tid; idx < G * D; idx += NT) {
       const int g = idx / D, dd = idx % D;
       float M = -__builtin_inff();
-#pragma unroll
-      for (int j = 0; j < NW; ++j)
+      for (int j = 0; j < NS; ++j)
         if (sm.l[j][g] > 0.f) M = fmaxf(M, sm.m[j][g]);
       float Ls = 0.f, A = 0.f;
-#pragma unroll
-      for (int j = 0; j < NW; ++j) {
+      for (int j = 0; j < NS; ++j) {
         const float sc = (sm.l[j][g] > 0.f) ? exp2f(sm.m[j][g] - M) : 0.f;
         Ls += sm.l[j][g] * sc;
         A += sm.acc[j][g][dd] * sc;

@@ -104,7 +104,7 @@ template <int D, int G>
 struct PSmem {
   union __attribute__((aligned(16))) {
     h2 x[kMaxK / 2];  // staged GEMV input
-    AttnLds<D, G, kPB> at;
+    AttnLds<D, G, kPB, 1> at;
   };
   float xc[kMaxK / 32];  // int4 stream: per (chunk, lane) bias correction of the staged input
   double red[kPW];
