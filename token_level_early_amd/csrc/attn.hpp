@@ -62,7 +62,7 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
   constexpr int BLK = NS * U;
   constexpr int NCOL = G * D / 4;                  // float4 columns of the merged output
   constexpr int TPC = NT / NCOL;                   // threads per column in the split merge
-  constexpr int MB = (kMaxSplit / TPC < 16) ? kMaxSplit / TPC : 16;  // partial loads per batch
+  constexpr int MB = (kMaxSplit / TPC < 8) ? kMaxSplit / TPC : 8;  // partial loads per batch
   static_assert(LPP <= kWave && HG * GL == G && (LPP & (LPP - 1)) == 0, "lane layout");
   static_assert(NCOL <= NT && (TPC & (TPC - 1)) == 0 && TPC <= kWave, "merge layout");
   const Dims& dm = a.dm;
@@ -260,32 +260,48 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
   int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
   if (arrive_counter(counter, nsplit, &sm.flag)) {
     // last arriver. Split weights exp2(m_j - M) / sum_j l_j exp2(m_j - M): one wave per
-    // query head, lane j holds split j.
-    for (int g = w; g < G; g += NW) {
-      const int j = lane;
-      float mj = -__builtin_inff(), lj = 0.f;
-      if (j < seff) {
-        const size_t pi = pbase + (size_t)g * nsplit + j;
-        mj = wt_load(&a.pml[pi * 2 + 0]);
-        lj = wt_load(&a.pml[pi * 2 + 1]);
+    // query head, lane j holds split j. The (m, l) loads and the first batch of partial-sum
+    // loads are issued together, so the merge waits on memory once.
+    constexpr int GW = (G + NW - 1) / NW;  // query heads per wave
+    float mj[GW], lj[GW];
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int g = w + i * NW;
+      mj[i] = -__builtin_inff();
+      lj[i] = 0.f;
+      if (g < G && lane < seff) {
+        const size_t pi = pbase + (size_t)g * nsplit + lane;
+        mj[i] = wt_load(&a.pml[pi * 2 + 0]);
+        lj[i] = wt_load(&a.pml[pi * 2 + 1]);
       }
-      const float M = wave_max_fast(mj);
-      const float e = (j < seff) ? exp2f(mj - M) : 0.f;
-      const float Ls = wave_sum_fast(lj * e);
-      sm.w[g][j] = e / Ls;
+    }
+    const int col = tid / TPC, r = tid % TPC;
+    const int g = col / (D / 4), d4 = (col % (D / 4)) * 4;
+    float4 v[MB];
+    auto load_batch = [&](int j0) {
+#pragma unroll
+      for (int k = 0; k < MB; ++k) {
+        const int j = j0 + k * TPC;
+        v[k] = (j < seff) ? ld4_coh(&a.pacc[(pbase + (size_t)g * nsplit + j) * D + d4])
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    load_batch(r);
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int gw = w + i * NW;
+      if (gw < G) {
+        const float M = wave_max_fast(mj[i]);
+        const float e = (lane < seff) ? exp2f(mj[i] - M) : 0.f;
+        const float Ls = wave_sum_fast(lj[i] * e);
+        sm.w[gw][lane] = e / Ls;
+      }
     }
     __syncthreads();
     {
-      const int col = tid / TPC, r = tid % TPC;
-      const int g = col / (D / 4), d4 = (col % (D / 4)) * 4;
       float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int j0 = r; j0 < seff; j0 += MB * TPC) {
-        float4 v[MB];
-#pragma unroll
-        for (int k = 0; k < MB; ++k) {
-          const int j = min(j0 + k * TPC, seff - 1);
-          v[k] = ld4_coh(&a.pacc[(pbase + (size_t)g * nsplit + j) * D + d4]);
-        }
+        if (j0 != r) load_batch(j0);
 #pragma unroll
         for (int k = 0; k < MB; ++k) {
           const int j = j0 + k * TPC;
