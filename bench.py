@@ -47,7 +47,15 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true", help="skip per-kernel timing passes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
+                                                        "CALIB_WRITE_CSV", "BENCH_LOG"),
+                    help="host only: write the HBM-traffic summary of k_persist from rocprofv3 "
+                         "counter CSVs (FETCH_SIZE / WRITE_SIZE runs of this script, then the same "
+                         "two counters on --calib-copy) and the bench output of the FETCH_SIZE run")
     args = ap.parse_args()
+    if args.pmc_summary:
+        write_pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -188,7 +196,8 @@ def main():
         roof = {"kernel": f"k_persist (early-exit decode, {rv_chunk} steps per launch)",
                 "bound": "hbm", "achieved": roof_pass["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": roof_pass["frac"], "traffic": None,
-                "avg_launch_us": roof_pass["avg_us"], "bytes_per_launch": roof_pass["bytes_per_launch"]}
+                "avg_launch_us": roof_pass["avg_us"], "bytes_per_launch": roof_pass["bytes_per_launch"],
+                "launches": roof_pass["launches"], "steps_per_launch": rv_chunk}
     elif "gu" in kernels:  # per-op path: its largest kernel
         g = kernels["gu"]
         roof = {"kernel": "gate|up projection (per-op path)" if B == 1 else "k_b_gemm gate|up (batched MFMA)",
@@ -263,6 +272,57 @@ def pmc_traffic(roof):
             "ratio_to_algorithmic": round(pm["hbm_bytes_per_launch"] / pm["algorithmic_bytes_per_launch_same_launches"], 4),
             "launches": pm["workload"],
             "calibration": pm["calibration"], "source": os.path.relpath(PMC_FILE, os.path.dirname(PMC_FILE) + "/..")}
+
+
+def _pmc_rows(path, name_prefix, counter):
+    """Per-dispatch values (KiB) of `counter` for kernels whose name starts with name_prefix,
+    in dispatch order, from a rocprofv3 counter-collection CSV."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and r["Kernel_Name"].lstrip("void ").startswith(name_prefix):
+                rows.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return [v for _, v in sorted(rows)]
+
+
+def write_pmc_summary(f_csv, w_csv, cf_csv, cw_csv, bench_log):
+    """profiles/k_persist_llama8b_decode_pmc.json from the four counter runs: FETCH_SIZE and
+    WRITE_SIZE of the last `roofline.launches` k_persist dispatches (the roofline pass), each
+    scaled by what the same counter reads per byte of a plain 512 MiB device copy."""
+    line = [l for l in open(bench_log) if l.startswith("{") and '"metric"' in l][-1]
+    out = json.loads(line)
+    roof = out["roofline"]
+    n = int(roof["launches"])
+    fetch = _pmc_rows(f_csv, "k_persist", "FETCH_SIZE")[-n:]
+    write = _pmc_rows(w_csv, "k_persist", "WRITE_SIZE")[-n:]
+    cf = _pmc_rows(cf_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    cw = _pmc_rows(cw_csv, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    if len(fetch) != n or len(write) != n or not cf or not cw:
+        raise SystemExit(f"pmc summary: expected {n} k_persist dispatches and copy dispatches in the CSVs")
+    copy_bytes = 512 << 20
+    kf, kw = sum(cf) / len(cf), sum(cw) / len(cw)
+    fs, ws = copy_bytes / (kf * 1024), copy_bytes / (kw * 1024)
+    fb = sum(fetch) / n * 1024 * fs
+    wb = sum(write) / n * 1024 * ws
+    summary = {
+        "kernel": "k_persist",
+        "workload": (f"{out['config']['workload']}, {roof['steps_per_launch']} steps per launch "
+                     f"(roofline-pass launches of bench.py --no-cpu --no-full --no-breakdown --steps {out['steps']})"),
+        "source_hash": kernel_source_hash(),
+        "fetch_bytes_per_launch": int(fb),
+        "write_bytes_per_launch": int(wb),
+        "hbm_bytes_per_launch": int(fb + wb),
+        "algorithmic_bytes_per_launch_same_launches": int(roof["bytes_per_launch"]),
+        "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib_per_copy": kf, "write_size_kib_per_copy": kw,
+                        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+                        "copy_kernel": "__amd_rocclr_copyBuffer (torch copy_ of 512 MiB)"},
+        "raw_kib_per_dispatch": {"FETCH_SIZE": fetch, "WRITE_SIZE": write},
+    }
+    with open(PMC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: summary[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch_same_launches")}))
 
 
 def calib_copy(torch):
