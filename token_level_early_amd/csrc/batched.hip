@@ -152,60 +152,87 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
     const f16* wrow = (OP == OP_LM) ? a.lm_head + (size_t)(nok ? n : 0) * dm.d : f16_row(OP, nok ? n : 0, *lw, a);
     const int nwin = (K + 31) / 32;
     const int w0 = w * nwin / 4, w1 = (w + 1) * nwin / 4;
-    int win = w0;
-    for (; win + 4 <= w1; win += 4) {  // four windows' loads in flight
-      uint4 xa[4], wb[4];
+    // batches of four 32-wide windows, double-buffered: the next batch's loads are in flight
+    // while the current one runs on the MFMA
+    auto load4 = [&](int win, uint4 (&xa)[4], uint4 (&wb)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k = (win + u) * 32 + kq * 8;
-        const bool ok = k < K;
+        const bool ok = win + u < w1 && k < K;
         xa[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
         wb[u] = (ok && nok) ? ldg16(wrow + k) : make_uint4(0, 0, 0, 0);
       }
+    };
+    auto mma4 = [&](const uint4 (&xa)[4], const uint4 (&wb)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         acc = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa[u]), lo4(wb[u]), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa[u]), hi4(wb[u]), acc, 0, 0, 0);
       }
-    }
-    for (; win < w1; ++win) {
-      const int k = win * 32 + kq * 8;
-      const bool ok = k < K;
-      const uint4 xa = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
-      const uint4 wb = (ok && nok) ? ldg16(wrow + k) : make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa), lo4(wb), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa), hi4(wb), acc, 0, 0, 0);
+    };
+    uint4 xa0[4], wb0[4], xa1[4], wb1[4];
+    int win = w0;
+    if (win < w1) load4(win, xa0, wb0);
+    for (; win < w1; win += 8) {
+      if (win + 4 < w1) load4(win + 4, xa1, wb1);
+      mma4(xa0, wb0);  // windows past w1 are zero: they add nothing
+      if (win + 8 < w1) load4(win + 8, xa0, wb0);
+      if (win + 4 < w1) mma4(xa1, wb1);
     }
   } else {
     const uint8_t* rp;
     const f16* sp;
     w4_row(OP, nok ? n : 0, *lw, dm, rp, sp);
-    const int g = dm.group, wpg = g / 32;  // 32-wide windows per group
+    const int g = dm.group, wpg = g / 32;  // 32-wide windows per group (1, 2 or 4)
     const int ng = (K + g - 1) / g;
     const int g0 = w * ng / 4, g1 = (w + 1) * ng / 4;
-    for (int grp = g0; grp < g1; ++grp) {
-      bf4 tmp = {0.f, 0.f, 0.f, 0.f};
-      for (int u = 0; u < wpg; ++u) {
-        const int k = grp * g + u * 32 + kq * 8;
-        const bool ok = k < K;
-        const uint4 xr = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
-        // 8 nibbles of this lane's weight row: bytes k/2 .. k/2+3 (padding nibbles are q = 0)
-        const uint32_t wq = nok ? *(const __attribute__((address_space(1))) uint32_t*)(rp + k / 2) : 0x88888888u;
-        h2 p0, p1, p2, p3;
-        unpack8(wq, p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-        const uint32_t in[4] = {xr.x, xr.y, xr.z, xr.w};
-        h2 xo[4];
-        pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-        const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
-        const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
-        const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
-        const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
-        tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp, 0, 0, 0);
-        tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp, 0, 0, 0);
-      }
-      const float s = nok ? h2f(sp[grp]) : 0.f;  // scale of (column n, group grp)
+    // one group's windows and its scale per batch, double-buffered across groups
+    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4], float& sc) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = fmaf(s, tmp[r], acc[r]);
+      for (int u = 0; u < 4; ++u) {
+        xr[u] = make_uint4(0, 0, 0, 0);
+        wq[u] = 0x88888888u;
+        if (u < wpg) {
+          const int k = grp * g + u * 32 + kq * 8;
+          const bool ok = k < K;
+          xr[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
+          // 8 nibbles of this lane's weight row: bytes k/2 .. k/2+3 (padding nibbles are q = 0)
+          if (nok) wq[u] = *(const __attribute__((address_space(1))) uint32_t*)(rp + k / 2);
+        }
+      }
+      sc = nok ? h2f(sp[grp]) : 0.f;  // scale of (column n, group grp)
+    };
+    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4], float sc) {
+      bf4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < wpg) {
+          h2 p0, p1, p2, p3;
+          unpack8(wq[u], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+          const uint32_t in[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+          h2 xo[4];
+          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+          const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
+          const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
+          const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
+          const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
+          tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp, 0, 0, 0);
+          tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, tmp[r], acc[r]);
+    };
+    uint4 xr0[4], xr1[4];
+    uint32_t wq0[4], wq1[4];
+    float sc0 = 0.f, sc1 = 0.f;
+    int grp = g0;
+    if (grp < g1) loadg(grp, xr0, wq0, sc0);
+    for (; grp < g1; grp += 2) {
+      if (grp + 1 < g1) loadg(grp + 1, xr1, wq1, sc1);
+      mmag(xr0, wq0, sc0);
+      if (grp + 2 < g1) loadg(grp + 2, xr0, wq0, sc0);
+      if (grp + 1 < g1) mmag(xr1, wq1, sc1);
     }
   }
   // lane holds Y[row 4*kq + r][col]; sum the four waves' K slices
