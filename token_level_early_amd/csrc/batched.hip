@@ -115,9 +115,14 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
 // ---------------------------------------------------------------------------------------
 // Batched projection: grid (tiles of 16 logical columns, stream), 4 waves splitting K.
 // ---------------------------------------------------------------------------------------
+// 16-column tiles per workgroup: four for gate|up (two weight streams, the int4 one reading
+// four times its own bytes of input per tile); one elsewhere, where fewer workgroups measured
+// slower
+static constexpr int kTW = 4;
+__host__ __device__ constexpr int b_tw(int op) { return op == OP_GU ? 4 : 1; }
 struct BSmem {
-  float part[4][kBR][kBR];
-  float y[kBR][kBR];
+  float part[4][kTW][kBR][kBR];  // per wave (K slice)
+  float y[kTW][kBR][kBR];
   int need;
 };
 
@@ -125,7 +130,7 @@ template <int OP>
 __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, const f16* xin) {
   __shared__ BSmem sm;
   const Dims& dm = a.dm;
-  const int tile = blockIdx.x, stream = blockIdx.y;  // stream 0 backbone fp16, 1 river int4
+  const int stream = blockIdx.y;  // stream 0 backbone fp16, 1 river int4
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
   const int N = op_rows(OP, dm), K = op_k(OP, dm);
   const LayerDev* lw = (OP == OP_LM) ? nullptr : &a.layers[layer - 1];
@@ -139,93 +144,122 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
   __syncthreads();
   if (!sm.need) return;
 
-  // this lane's weight column (logical row of the weight matrix)
+  // TW 16-column tiles per workgroup: every wave reads each input window once for all of
+  // them (the inputs come from L2 for every tile, as many bytes as the fp16 weights)
+  constexpr int TW = b_tw(OP);
+  const int tile0 = blockIdx.x * TW;
   const int col = lane % 16, kq = lane / 16;
-  const int n = logical_row(OP, tile, col, kBR, dm);
-  const bool nok = n < N;
+  int n[TW];
+  bool nok[TW];
+#pragma unroll
+  for (int s = 0; s < TW; ++s) {  // this lane's weight column in tile s
+    n[s] = logical_row(OP, tile0 + s, col, kBR, dm);
+    nok[s] = n[s] < N;
+  }
   const int xrow = lane % 16;  // batch row fed by this lane (A operand)
   const bool xok = xrow < dm.B;
   const f16* xp = xin + (size_t)(xok ? xrow : 0) * K;
 
-  bf4 acc = {0.f, 0.f, 0.f, 0.f};
+  bf4 acc[TW];
+#pragma unroll
+  for (int s = 0; s < TW; ++s) acc[s] = bf4{0.f, 0.f, 0.f, 0.f};
   if (stream == 0) {
-    const f16* wrow = (OP == OP_LM) ? a.lm_head + (size_t)(nok ? n : 0) * dm.d : f16_row(OP, nok ? n : 0, *lw, a);
+    const f16* wrow[TW];
+#pragma unroll
+    for (int s = 0; s < TW; ++s)
+      wrow[s] = (OP == OP_LM) ? a.lm_head + (size_t)(nok[s] ? n[s] : 0) * dm.d : f16_row(OP, nok[s] ? n[s] : 0, *lw, a);
     const int nwin = (K + 31) / 32;
     const int w0 = w * nwin / 4, w1 = (w + 1) * nwin / 4;
-    // batches of four 32-wide windows, double-buffered: the next batch's loads are in flight
+    // batches of two 32-wide windows, double-buffered: the next batch's loads are in flight
     // while the current one runs on the MFMA
-    auto load4 = [&](int win, uint4 (&xa)[4], uint4 (&wb)[4]) {
+    constexpr int WB = 2;
+    auto loadb = [&](int win, uint4 (&xa)[WB], uint4 (&wb)[WB][TW]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < WB; ++u) {
         const int k = (win + u) * 32 + kq * 8;
         const bool ok = win + u < w1 && k < K;
         xa[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
-        wb[u] = (ok && nok) ? ldg16(wrow + k) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto mma4 = [&](const uint4 (&xa)[4], const uint4 (&wb)[4]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa[u]), lo4(wb[u]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa[u]), hi4(wb[u]), acc, 0, 0, 0);
+        for (int s = 0; s < TW; ++s) wb[u][s] = (ok && nok[s]) ? ldg16(wrow[s] + k) : make_uint4(0, 0, 0, 0);
       }
     };
-    uint4 xa0[4], wb0[4], xa1[4], wb1[4];
+    auto mmab = [&](const uint4 (&xa)[WB], const uint4 (&wb)[WB][TW]) {
+#pragma unroll
+      for (int u = 0; u < WB; ++u)
+#pragma unroll
+        for (int s = 0; s < TW; ++s) {
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa[u]), lo4(wb[u][s]), acc[s], 0, 0, 0);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa[u]), hi4(wb[u][s]), acc[s], 0, 0, 0);
+        }
+    };
+    uint4 xa0[WB], wb0[WB][TW], xa1[WB], wb1[WB][TW];
     int win = w0;
-    if (win < w1) load4(win, xa0, wb0);
-    for (; win < w1; win += 8) {
-      if (win + 4 < w1) load4(win + 4, xa1, wb1);
-      mma4(xa0, wb0);  // windows past w1 are zero: they add nothing
-      if (win + 8 < w1) load4(win + 8, xa0, wb0);
-      if (win + 4 < w1) mma4(xa1, wb1);
+    if (win < w1) loadb(win, xa0, wb0);
+    for (; win < w1; win += 2 * WB) {
+      if (win + WB < w1) loadb(win + WB, xa1, wb1);
+      mmab(xa0, wb0);  // windows past w1 are zero: they add nothing
+      if (win + 2 * WB < w1) loadb(win + 2 * WB, xa0, wb0);
+      if (win + WB < w1) mmab(xa1, wb1);
     }
   } else {
-    const uint8_t* rp;
-    const f16* sp;
-    w4_row(OP, nok ? n : 0, *lw, dm, rp, sp);
+    const uint8_t* rp[TW];
+    const f16* sp[TW];
+#pragma unroll
+    for (int s = 0; s < TW; ++s) w4_row(OP, nok[s] ? n[s] : 0, *lw, dm, rp[s], sp[s]);
     const int g = dm.group, wpg = g / 32;  // 32-wide windows per group (1, 2 or 4)
     const int ng = (K + g - 1) / g;
     const int g0 = w * ng / 4, g1 = (w + 1) * ng / 4;
-    // one group's windows and its scale per batch, double-buffered across groups
-    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4], float& sc) {
+    // one group's windows and scales per batch, double-buffered across groups
+    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4][TW], float (&sc)[TW]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         xr[u] = make_uint4(0, 0, 0, 0);
-        wq[u] = 0x88888888u;
+#pragma unroll
+        for (int s = 0; s < TW; ++s) wq[u][s] = 0x88888888u;
         if (u < wpg) {
           const int k = grp * g + u * 32 + kq * 8;
           const bool ok = k < K;
           xr[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
           // 8 nibbles of this lane's weight row: bytes k/2 .. k/2+3 (padding nibbles are q = 0)
-          if (nok) wq[u] = *(const __attribute__((address_space(1))) uint32_t*)(rp + k / 2);
+#pragma unroll
+          for (int s = 0; s < TW; ++s)
+            if (nok[s]) wq[u][s] = *(const __attribute__((address_space(1))) uint32_t*)(rp[s] + k / 2);
         }
       }
-      sc = nok ? h2f(sp[grp]) : 0.f;  // scale of (column n, group grp)
+#pragma unroll
+      for (int s = 0; s < TW; ++s) sc[s] = nok[s] ? h2f(sp[s][grp]) : 0.f;  // scale of (column, group)
     };
-    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4], float sc) {
-      bf4 tmp = {0.f, 0.f, 0.f, 0.f};
+    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4][TW], const float (&sc)[TW]) {
+      bf4 tmp[TW];
+#pragma unroll
+      for (int s = 0; s < TW; ++s) tmp[s] = bf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u < wpg) {
-          h2 p0, p1, p2, p3;
-          unpack8(wq[u], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
           const uint32_t in[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
           h2 xo[4];
           pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
           const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
           const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
-          const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
-          const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
-          tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp, 0, 0, 0);
-          tmp = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp, 0, 0, 0);
+#pragma unroll
+          for (int s = 0; s < TW; ++s) {
+            h2 p0, p1, p2, p3;
+            unpack8(wq[u][s], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+            const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
+            const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
+            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp[s], 0, 0, 0);
+            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp[s], 0, 0, 0);
+          }
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, tmp[r], acc[r]);
+      for (int s = 0; s < TW; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s], tmp[s][r], acc[s][r]);
     };
     uint4 xr0[4], xr1[4];
-    uint32_t wq0[4], wq1[4];
-    float sc0 = 0.f, sc1 = 0.f;
+    uint32_t wq0[4][TW], wq1[4][TW];
+    float sc0[TW], sc1[TW];
     int grp = g0;
     if (grp < g1) loadg(grp, xr0, wq0, sc0);
     for (; grp < g1; grp += 2) {
@@ -235,21 +269,24 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
       if (grp + 1 < g1) mmag(xr1, wq1, sc1);
     }
   }
-  // lane holds Y[row 4*kq + r][col]; sum the four waves' K slices
+  // lane holds Y[row 4*kq + r][col] of each tile; sum the four waves' K slices
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sm.part[w][4 * kq + r][col] = acc[r];
+  for (int s = 0; s < TW; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.part[w][s][4 * kq + r][col] = acc[s][r];
   __syncthreads();
-  {
-    const int row = t / kBR, c = t % kBR;
-    sm.y[row][c] = (sm.part[0][row][c] + sm.part[1][row][c]) + (sm.part[2][row][c] + sm.part[3][row][c]);
+  for (int i = t; i < TW * kBR * kBR; i += kBlock) {
+    const int s = i / (kBR * kBR), row = (i / kBR) % kBR, c = i % kBR;
+    sm.y[s][row][c] = (sm.part[0][s][row][c] + sm.part[1][s][row][c]) + (sm.part[2][s][row][c] + sm.part[3][s][row][c]);
   }
   __syncthreads();
 
-  // epilogue: thread -> (row b, tile column c), rows on this stream only
+  // epilogue per 16-column tile: thread -> (row b, tile column c), rows on this stream only
+  auto epilogue = [&](int tile, const float (&y)[kBR][kBR]) {
   const int b = t / kBR, c = t % kBR;
   if (b >= dm.B) return;
   if (OP != OP_LM && a.route[layer * dm.B + b] != stream) return;
-  const float yv = sm.y[b][c];
+  const float yv = y[b][c];
   if (OP == OP_QKV) {
     const int pos = a.pos[b];
     const int qk_rows = (dm.H + dm.Hkv) * dm.D;
@@ -258,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
       if (c < kBR / 2) {
         const int nn = logical_row(OP, tile, c, kBR, dm);
         const int head = nn / dm.D, i = nn % dm.D;  // i < D/2
-        const float x0 = h2f(f2h(yv)), x1 = h2f(f2h(sm.y[b][c + kBR / 2]));
+        const float x0 = h2f(f2h(yv)), x1 = h2f(f2h(y[b][c + kBR / 2]));
         const float2 cs = a.rope[(size_t)pos * (dm.D / 2) + i];
         const f16 r0 = f2h(x0 * cs.x - x1 * cs.y);
         const f16 r1 = f2h(x1 * cs.x + x0 * cs.y);
@@ -286,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
     if (c < kBR / 2) {
       const int f = logical_row(OP, tile, c, kBR, dm);
       if (f < dm.F) {
-        const float gg = h2f(f2h(yv)), uu = h2f(f2h(sm.y[b][c + kBR / 2]));
+        const float gg = h2f(f2h(yv)), uu = h2f(f2h(y[b][c + kBR / 2]));
         const float sg = gg / (1.f + __expf(-gg));
         a.a2[(size_t)b * dm.F + f] = f2h(sg * uu);
       }
@@ -313,7 +350,7 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
       for (int j = 0; j < kBR; ++j) {
         const int nj = tile * kBR + j;
         if (nj >= N) break;
-        const float vj = sm.y[b][j];
+        const float vj = y[b][j];
         if (vj > best) {
           best = vj;
           bi = nj;
@@ -327,6 +364,9 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
     }
     (void)v;
   }
+  };
+#pragma unroll
+  for (int s = 0; s < TW; ++s) epilogue(tile0 + s, sm.y[s]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -339,7 +379,7 @@ template <int OP>
 static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const f16* xin, hipStream_t st) {
   const Dims& dm = a.dm;
   const int N = (OP == OP_QKV) ? dm.nqkv : (OP == OP_GU) ? 2 * dm.F : (OP == OP_LM) ? dm.V : dm.d;
-  const int tiles = (N + kBR - 1) / kBR;
+  const int tiles = ((N + kBR - 1) / kBR + b_tw(OP) - 1) / b_tw(OP);  // workgroups of 16-column tiles
   const int streams = (OP == OP_LM || mode == 1) ? 1 : 2;
   hipLaunchKernelGGL((k_b_gemm<OP>), dim3(tiles, streams), dim3(kBlock), 0, st, a, layer, xin);
   return hipGetLastError();
