@@ -22,9 +22,10 @@ def test_batch_byte_model_reduces_to_the_single_row_model():
     assert both == 24 * w4
 
 
-def test_byte_model_matches_the_published_per_layer_figures():
-    """8B per-layer weight bytes as derived in the survey of the pages: 436.22 MB fp16 and
-    112.48 MB int4 + scales (group 128), LM head 1.051 GB."""
+def test_byte_model_matches_hand_derived_per_layer_figures():
+    """8B per-layer weight bytes worked out by hand from the Llama-3.1-8B shape
+    (P_l = 218,103,808 parameters per block): 2*P_l + 4d = 436.22 MB fp16, P_l/2 + 2*P_l/128
+    + 4d = 112.48 MB int4 + scales (group 128); LM head 2*V*d = 1.051 GB."""
     c = configs.model_cfg(configs.LLAMA_8B)
     d = c["d"]
     w16 = sum(bm.matrix_bytes(N, K, False, 128) for N, K in bm.op_params(c).values()) + 4 * d
