@@ -36,6 +36,23 @@ def test_kv_layout_is_one_backbone_sized_cache(name):
     assert d.total_bytes == c["L"] * 2 * c["Hkv"] * Tmax * c["D"] * 2
 
 
+def test_long_context_adds_no_second_kv_set():
+    """The caller's cache is the only KV storage: raising max_seq from 1000 to 65600 positions
+    (the 64K-prompt workload) grows the library's scratch only by the RoPE table (cos, sin per
+    position and frequency, fp32), never by anything proportional to L * positions."""
+    c = configs.model_cfg(configs.LLAMA_8B)
+    t1, t2 = 1000, 65600
+    _, s1 = river.workspace_bytes(river.make_config(c, t1, 512))
+    _, s2 = river.workspace_bytes(river.make_config(c, t2, 512))
+    rope = (t2 - t1) * (c["D"] // 2) * 8
+    kv_growth = c["L"] * 2 * c["Hkv"] * (t2 - t1) * c["D"] * 2
+    assert s2 - s1 <= rope + 4096, (s1, s2, rope)
+    assert s2 - s1 < kv_growth / 256  # the RoPE table: 256 B per position against 128 KiB of KV
+    k1 = river.kv_layout(river.make_config(c, t1, 512)).total_bytes
+    k2 = river.kv_layout(river.make_config(c, t2, 512)).total_bytes
+    assert k2 - k1 == kv_growth
+
+
 def test_river_buffer_covers_int4_copy():
     c = configs.model_cfg(configs.LLAMA_8B)
     rb, sb = river.workspace_bytes(river.make_config(c, 2400, 2048))
