@@ -47,7 +47,7 @@ def test_long_context_adds_no_second_kv_set():
     rope = (t2 - t1) * (c["D"] // 2) * 8
     kv_growth = c["L"] * 2 * c["Hkv"] * (t2 - t1) * c["D"] * 2
     assert s2 - s1 <= rope + 4096, (s1, s2, rope)
-    assert s2 - s1 < kv_growth / 256  # the RoPE table: 256 B per position against 128 KiB of KV
+    assert s2 - s1 <= kv_growth / 256  # the RoPE table: 512 B per position against 128 KiB of KV
     k1 = river.kv_layout(river.make_config(c, t1, 512)).total_bytes
     k2 = river.kv_layout(river.make_config(c, t2, 512)).total_bytes
     assert k2 - k1 == kv_growth
