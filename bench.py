@@ -139,9 +139,12 @@ def main():
             launch_bytes.append(sum(step_bytes[lo:hi]))
         avg_us = 1e3 * float(np.mean(durs))
         gbs = float(np.mean(launch_bytes)) / (avg_us * 1e-6) / 1e9
+        # spread over the launches: tokens/s of each launch (its steps x rows / its duration)
+        lt = [(min(S, (i + 1) * rv_chunk) - i * rv_chunk) * B / (durs[i] / 1e3) for i in range(n_launch)]
         roof_pass = {"launches": n_launch, "steps_per_launch": rv_chunk, "avg_us": round(avg_us, 2),
                      "bytes_per_launch": int(np.mean(launch_bytes)), "GB/s": round(gbs, 1),
-                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "tokens_per_s_p10_p50_p90": [round(float(np.percentile(lt, q)), 1) for q in (10, 50, 90)]}
         log(f"persistent kernel: {roof_pass}")
 
     # ---- per-kernel timing passes of the per-op kernels (direct launches, HIP events)
@@ -197,7 +200,8 @@ def main():
                 "bound": "hbm", "achieved": roof_pass["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": roof_pass["frac"], "traffic": None,
                 "avg_launch_us": roof_pass["avg_us"], "bytes_per_launch": roof_pass["bytes_per_launch"],
-                "launches": roof_pass["launches"], "steps_per_launch": rv_chunk}
+                "launches": roof_pass["launches"], "steps_per_launch": rv_chunk,
+                "tokens_per_s_p10_p50_p90": roof_pass["tokens_per_s_p10_p50_p90"]}
     elif "gu" in kernels:  # per-op path: its largest kernel
         g = kernels["gu"]
         roof = {"kernel": "gate|up projection (per-op path)" if B == 1 else "k_b_gemm gate|up (batched MFMA)",
