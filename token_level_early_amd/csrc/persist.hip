@@ -13,8 +13,9 @@
 // vector, which every workgroup stages once per phase in LDS (normalised on the fly). No
 // workgroup-level synchronisation happens per row; each row's dot product ends in a wave
 // reduction and lane 0 stores the result. RoPE and the KV append move to the attention phase
-// (the split that owns the new position rotates k, writes K/V[pos], then attends), SwiGLU to
-// the staging of the down projection's input.
+// (the split that owns the new position rotates k, writes K/V[pos], then attends); SwiGLU to
+// the gate|up epilogue (each wave owns whole gate/up row pairs, so it is computed once per
+// pair instead of once per workgroup while staging the down projection's input).
 //
 // Routes, the position and the token stay in registers (every workgroup derives identical
 // values); activations cross XCDs through write-through stores and coherent loads. The grid
@@ -29,6 +30,14 @@ static constexpr unsigned kSpinLimit = 1u << 22;
 static constexpr int kMaxK = 16384;  // longest GEMV input the LDS staging buffer holds
 static constexpr int kPB = 512;      // threads per persistent workgroup (one per CU)
 static constexpr int kPW = kPB / kWave;
+// attention lane layout of the persistent kernel: positions per thread per block and query
+// heads per lane (see attn_split)
+#ifndef RIVER_PATTN_U
+#define RIVER_PATTN_U 2
+#endif
+#ifndef RIVER_PATTN_GL
+#define RIVER_PATTN_GL 1
+#endif
 
 // Sum over the kPB threads of the workgroup, fixed order; every thread gets the result.
 RIVER_DEV double pblock_sum_d(double v, double* red) {
@@ -104,7 +113,7 @@ template <int D, int G>
 struct PSmem {
   union __attribute__((aligned(16))) {
     h2 x[kMaxK / 2];  // staged GEMV input
-    AttnLds<D, G, kPB, 1> at;
+    AttnLds<D, G, kPB, (RIVER_PATTN_GL < G ? RIVER_PATTN_GL : G)> at;
   };
   float xc[kMaxK / 32];  // int4 stream: per (chunk, lane) bias correction of the staged input
   double red[kPW];
@@ -124,21 +133,6 @@ RIVER_DEV int lds_group_index(int g) {  // g: group of 8 elements -> h2 index
   const int e = g * 8;
   const int c = e / kChunkW4, j = (e % kChunkW4) / 32, m = (e % 32) / 8;
   return ((c * 4 + m) * kWave + j) * 4;
-}
-
-RIVER_DEV uint4 silu_mul8(uint4 g, uint4 u) {
-  uint32_t* pg = (uint32_t*)&g;
-  const uint32_t* pu = (const uint32_t*)&u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const h2 gv = as_h2(pg[j]), uv = as_h2(pu[j]);
-    h2 r;
-    const float g0 = h2f(gv.x), g1 = h2f(gv.y);
-    r.x = f2h(g0 / (1.f + __expf(-g0)) * h2f(uv.x));
-    r.y = f2h(g1 / (1.f + __expf(-g1)) * h2f(uv.y));
-    pg[j] = as_u32(r);
-  }
-  return g;
 }
 
 // Writes one group of 8 staged values into LDS in the stream's layout. For the int4 stream the
@@ -171,22 +165,23 @@ RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
   }
 }
 
-// x = fp16(src * inv * gain) (HAS_GAIN), silu(g)*u of a gate|up vector (SWIGLU), or src, staged
-// into LDS. NORM: inv = 1/rms(src) computed here in a fixed order (identical in every
+// x = fp16(src * inv * gain) (HAS_GAIN) or src, staged into LDS. NORM: inv = 1/rms(src) computed here in a fixed order (identical in every
 // workgroup); then each thread holds its NG groups of 8 values across the reduction.
 // Without NORM the groups stream through registers.
-template <bool IS4, bool HAS_GAIN, bool NORM, bool SWIGLU, int NG>
-RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, int F, float inv, float eps,
+template <bool IS4, bool HAS_GAIN, bool NORM, int NG>
+RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, float inv, float eps,
                        h2* xl, float* xc, double* red) {
   const int t = threadIdx.x;
   const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
   const int ngp = nch * (IS4 ? kChunkW4 : kChunkF16) / 8;
   if (NORM) {
-    uint4 v[NG];
+    // the input and the gain are loaded together, before the reduction
+    uint4 v[NG], gv[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int g = t + i * kPB;
       v[i] = (g * 8 < K) ? ldx16<true>(src + g * 8) : make_uint4(0, 0, 0, 0);
+      gv[i] = (HAS_GAIN && g * 8 < K) ? ldg16(gain + g * 8) : make_uint4(0, 0, 0, 0);
     }
     double ss = 0.0;
 #pragma unroll
@@ -197,19 +192,27 @@ RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, int F, float inv,
       const int g = t + i * kPB;
       if (g >= ngp) continue;
       uint4 u = v[i];
-      if (HAS_GAIN && g * 8 < K) u = norm8(u, ldg16(gain + g * 8), inv, true);
+      if (HAS_GAIN && g * 8 < K) u = norm8(u, gv[i], inv, true);
       put_group<IS4>(xl, xc, g, u);
     }
     for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4>(xl, xc, g, make_uint4(0, 0, 0, 0));
   } else {
-    for (int g = t; g < ngp; g += kPB) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (g * 8 < K) {
-        u = ldx16<true>(src + g * 8);
-        if (SWIGLU) u = silu_mul8(u, ldx16<true>(src + F + g * 8));
-        if (HAS_GAIN) u = norm8(u, ldg16(gain + g * 8), inv, true);
+    // the thread's groups in pairs, both loads issued before either is used
+    for (int g0 = t; g0 < ngp; g0 += 2 * kPB) {
+      uint4 v[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g = g0 + i * kPB;
+        v[i] = (g * 8 < K) ? ldx16<true>(src + g * 8) : make_uint4(0, 0, 0, 0);
       }
-      put_group<IS4>(xl, xc, g, u);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g = g0 + i * kPB;
+        if (g >= ngp) break;  // ngp is a multiple of 4: whole quads stay together
+        uint4 u = v[i];
+        if (HAS_GAIN && g * 8 < K) u = norm8(u, ldg16(gain + g * 8), inv, true);
+        put_group<IS4>(xl, xc, g, u);
+      }
     }
   }
   __syncthreads();
@@ -270,6 +273,30 @@ RIVER_DEV void wave_rows(int N, int& r0, int& r1) {
   r1 = __builtin_amdgcn_readfirstlane((int)((long long)(gw + 1) * N / GW));
 }
 
+// The rows a wave streams, as a virtual range [0, nv): virtual row v is physical row
+// r0 + v below `split` and r0 + jump + v from there on. Every phase but gate|up takes a
+// contiguous slice; gate|up takes whole (gate j, up j) pairs -- its gate rows [j0, j1), then
+// the matching up rows [F + j0, F + j1) -- so the wave that finishes up row j also holds
+// gate row j and applies SwiGLU itself.
+struct RowRange {
+  int r0, nv, split, jump;
+  RIVER_DEV int row(int v) const { return v < split ? r0 + v : r0 + jump + v; }
+  // physical chunk of virtual chunk q (nch chunks per row)
+  RIVER_DEV int chunk(int q, int nch) const { return q < split * nch ? r0 * nch + q : (r0 + jump) * nch + q; }
+};
+template <int OP>
+RIVER_DEV RowRange wave_range(int N) {
+  int r0, r1;
+  if (OP == OP_GU) {
+    const int F = N / 2;
+    wave_rows(F, r0, r1);
+    const int n = r1 - r0;
+    return RowRange{r0, 2 * n, n, F - n};
+  }
+  wave_rows(N, r0, r1);
+  return RowRange{r0, r1 - r0, r1 - r0, 0};
+}
+
 // Streamed items. fp16 stream: an item is SEG chunks (512 elements each) of one row, a row
 // being nseg items. int4 stream: the padded river layout makes the rows of one matrix a
 // single run of 1 KiB chunks (2048 elements each; the group scales likewise), so a wave's rows
@@ -319,19 +346,20 @@ RIVER_DEV float dot_seg16(const Seg<SEG>& sg, const h2* xl, int nch, int seg, fl
 // brings npl = SEG*spc/64 of them (lane L: scales [L*npl, L*npl + npl) of the item) instead of
 // one small load per chunk.
 template <int SEG, int GRP>
-RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, int q0, int qend, Seg<SEG>& sg) {
+RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const RowRange& rr, int nch, int q0,
+                         int qend, Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint8_t* wp = base + (size_t)q0 * 1024 + lane * 16;
 #pragma unroll
   for (int c = 0; c < SEG; ++c)
-    sg.w[c] = (q0 + c < qend) ? ldg16(wp + c * 1024) : make_uint4(0, 0, 0, 0);
+    sg.w[c] = (q0 + c < qend) ? ldg16(base + (size_t)rr.chunk(q0 + c, nch) * 1024 + lane * 16)
+                              : make_uint4(0, 0, 0, 0);
   constexpr int spc = kChunkW4 / GRP;
   constexpr int npl = SEG * spc / kWave;
   static_assert(npl == 1 || npl == 2 || npl == 4 || npl == 8, "scales per lane");
-  const size_t s0 = (size_t)q0 * spc + (size_t)lane * npl;
+  const int s0 = q0 * spc + lane * npl;  // virtual scale index; npl divides spc
   sg.sr = make_uint4(0, 0, 0, 0);
-  if (s0 < (size_t)qend * spc) {  // npl divides both: the lane's scales are all in range
-    const f16* sp = sbase + s0;
+  if (s0 < qend * spc) {  // npl divides both: the lane's scales are all in range
+    const f16* sp = sbase + (size_t)rr.chunk(s0 / spc, nch) * spc + s0 % spc;
     if (npl == 1) {
       sg.sr.x = __builtin_bit_cast(unsigned short, ldg2(sp));
     } else if (npl == 2) {
@@ -435,32 +463,44 @@ template <int OP, bool IS4, int SEG, int GRP>
 RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K, const h2* xl,
                            const float* xc, const StreamOut& so, Seg<SEG>& b0) {
   const int lane = threadIdx.x & (kWave - 1);
-  int r0, r1;
-  wave_rows(N, r0, r1);
-  if (r0 >= r1) return;
+  const RowRange rr = wave_range<OP>(N);
+  if (rr.nv <= 0) return;
+  const int r0 = rr.r0, r1 = rr.r0 + rr.nv;  // contiguous for every phase but gate|up
   const int nch = n_chunks<IS4>(K);
   // residuals of this wave's rows, one per lane (O and DOWN)
   f16 res = (f16)0.0f;
   if ((OP == OP_O || OP == OP_DOWN) && r0 + lane < r1) res = ldh<true>(so.resid + r0 + lane);
   float best = -__builtin_inff();
   int bi = 0x7FFFFFFF;
-  auto fin = [&](int row, float part) {
+  float gk = 0.f;  // gate|up: gate row r0 + lane of this wave (its value before rounding)
+  auto fin = [&](int vrow, float part) {
     const float v = wave_sum_fast(part);
+    if (OP == OP_GU) {
+      // a2[j] = fp16(silu(fp16(gate_j)) * fp16(up_j)), stored by the wave holding both
+      if (vrow < rr.split) {
+        if (lane == vrow) gk = v;
+      } else {
+        const int j = vrow - rr.split;
+        const float g0 = h2f(f2h(__shfl(gk, j, kWave)));
+        if (lane == 0) sth<true>(so.out + r0 + j, f2h(g0 / (1.f + __expf(-g0)) * h2f(f2h(v))));
+      }
+      return;
+    }
+    const int row = r0 + vrow;
     if (OP == OP_LM) {
       if (v > best) {
         best = v;
         bi = row;
       }
     }
-    const int rr = row - r0;
     f16 rv = (f16)0.0f;
     if (OP == OP_O || OP == OP_DOWN) {
-      const int src = rr < kWave ? rr : 0;
+      const int src = vrow < kWave ? vrow : 0;
       rv = __builtin_bit_cast(f16, (unsigned short)__shfl(__builtin_bit_cast(unsigned short, res), src, kWave));
-      if (rr >= kWave) rv = ldh<true>(so.resid + row);
+      if (vrow >= kWave) rv = ldh<true>(so.resid + row);
     }
     if (lane == 0) {
-      if (OP == OP_QKV || OP == OP_GU) sth<true>(so.out + row, f2h(v));
+      if (OP == OP_QKV) sth<true>(so.out + row, f2h(v));
       if (OP == OP_O || OP == OP_DOWN) sth<true>(so.out + row, f2h(h2f(rv) + h2f(f2h(v))));
       if (OP == OP_LM && so.logits) so.logits[row] = v;
     }
@@ -469,20 +509,20 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
   float acc = 0.f;
   if constexpr (!IS4) {
     const int nseg = (nch + SEG - 1) / SEG;
-    const int nitems = (r1 - r0) * nseg;
+    const int nitems = rr.nv * nseg;
     auto step = [&](int it, const Seg<SEG>& sg) {
       const int seg = it % nseg;
       acc = dot_seg16<SEG>(sg, xl, nch, seg, acc);
       if (seg == nseg - 1) {
-        fin(r0 + it / nseg, acc);
+        fin(it / nseg, acc);
         acc = 0.f;
       }
     };
     int it = 0;
     for (; it + 1 < nitems; it += 2) {
-      load_seg16<OP, SEG>(a, lw, K, nch, r0 + (it + 1) / nseg, (it + 1) % nseg, b1);
+      load_seg16<OP, SEG>(a, lw, K, nch, rr.row((it + 1) / nseg), (it + 1) % nseg, b1);
       step(it, b0);
-      if (it + 2 < nitems) load_seg16<OP, SEG>(a, lw, K, nch, r0 + (it + 2) / nseg, (it + 2) % nseg, b0);
+      if (it + 2 < nitems) load_seg16<OP, SEG>(a, lw, K, nch, rr.row((it + 2) / nseg), (it + 2) % nseg, b0);
       step(it + 1, b1);
     }
     if (it < nitems) step(it, b0);
@@ -490,13 +530,13 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
     const uint8_t* base;
     const f16* sbase;
     w4_base<OP>(lw, base, sbase);
-    const int qbeg = r0 * nch, qend = r1 * nch;
-    int row = r0, ch = 0;
-    int q = qbeg;
+    const int qend = rr.nv * nch;  // virtual chunks
+    int row = 0, ch = 0;
+    int q = 0;
     for (; q + SEG < qend; q += 2 * SEG) {
-      load_seg4<SEG, GRP>(base, sbase, q + SEG, qend, b1);
+      load_seg4<SEG, GRP>(base, sbase, rr, nch, q + SEG, qend, b1);
       dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
-      if (q + 2 * SEG < qend) load_seg4<SEG, GRP>(base, sbase, q + 2 * SEG, qend, b0);
+      if (q + 2 * SEG < qend) load_seg4<SEG, GRP>(base, sbase, rr, nch, q + 2 * SEG, qend, b0);
       dot_seg4<SEG, GRP>(b1, xl, xc, nch, q + SEG, qend, row, ch, acc, fin);
     }
     if (q < qend) dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
@@ -512,9 +552,8 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
 // phase exist, e.g. before the grid barrier or while the input vector is staged).
 template <int OP, bool IS4, int SEG, int GRP>
 RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K, Seg<SEG>& pre) {
-  int r0, r1;
-  wave_rows(N, r0, r1);
-  if (r0 >= r1) {  // no rows: still define the whole buffer
+  const RowRange rr = wave_range<OP>(N);
+  if (rr.nv <= 0) {  // no rows: still define the whole buffer
 #pragma unroll
     for (int c = 0; c < SEG; ++c) pre.w[c] = make_uint4(0, 0, 0, 0);
     pre.sr = make_uint4(0, 0, 0, 0);
@@ -522,23 +561,23 @@ RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, in
   }
   const int nch = n_chunks<IS4>(K);
   if constexpr (!IS4) {
-    load_seg16<OP, SEG>(a, lw, K, nch, r0, 0, pre);
+    load_seg16<OP, SEG>(a, lw, K, nch, rr.row(0), 0, pre);
   } else {
     const uint8_t* base;
     const f16* sbase;
     w4_base<OP>(lw, base, sbase);
-    load_seg4<SEG, GRP>(base, sbase, r0 * nch, r1 * nch, pre);
+    load_seg4<SEG, GRP>(base, sbase, rr, nch, 0, rr.nv * nch, pre);
   }
 }
 
 // One GEMV phase: stage the input, stream the rows. b0 holds the phase's first item when
 // `have` (issued before the barrier that precedes the phase), else it is issued here first.
-template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool SWIGLU, int NG, int GRP>
+template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, int NG, int GRP>
 RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K, const f16* src,
                           const f16* gain, float inv, const StreamOut& so, h2* xl, float* xc,
                           double* red, Seg<SEG>& b0, bool have) {
   if (!have) prefetch_first<OP, IS4, SEG, GRP>(a, lw, N, K, b0);
-  stage_x<IS4, HAS_GAIN, NORM, SWIGLU, NG>(src, gain, K, a.dm.F, inv, a.dm.eps, xl, xc, red);
+  stage_x<IS4, HAS_GAIN, NORM, NG>(src, gain, K, inv, a.dm.eps, xl, xc, red);
   stream_rows<OP, IS4, SEG, GRP>(a, lw, N, K, xl, xc, so, b0);
   __syncthreads();  // LDS reuse by the next phase
 }
@@ -622,11 +661,11 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       StreamOut so{};
       so.out = a.qkvr + (size_t)b * dm.nqkv;
       if (r4) {
-        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, true, SEG, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
       } else {
-        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
-        else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        else gemv_phase<OP_QKV, false, SEG, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
       }
       grid_sync(bar, epoch, nwg);
       if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
@@ -634,28 +673,28 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
                            __HIP_MEMORY_SCOPE_AGENT);
       // ---------------- attention (+ RoPE and the KV append of position pos)
       for (int it = wg; it < dm.Hkv * splits; it += nwg)
-        attn_split<D, G, kPB, true, 2, 1>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
+        attn_split<D, G, kPB, true, RIVER_PATTN_U, (RIVER_PATTN_GL < G ? RIVER_PATTN_GL : G)>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre); });
       // ---------------- O + residual
       so.out = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
       so.resid = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_O, true, SEG, false, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_O, false, SEG, false, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      if (r4) gemv_phase<OP_O, true, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_O, false, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_GU, SEG, GRP>(a, lw, 2 * dm.F, dm.d, r4, pre); });
       // ---------------- gate|up
       so.out = a.gu + (size_t)b * 2 * dm.F;
       so.resid = nullptr;
       {
         const f16* src = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-        if (r4) gemv_phase<OP_GU, true, SEG, true, true, false, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_GU, false, SEG, true, true, false, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (r4) gemv_phase<OP_GU, true, SEG, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_GU, false, SEG, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       }
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_DOWN, SEG, GRP>(a, lw, dm.d, dm.F, r4, pre); });
-      // ---------------- down (SwiGLU while staging) + residual
+      // ---------------- down (input: the SwiGLU vector the gate|up phase wrote) + residual
       so.out = a.hs + ((size_t)l * dm.B + b) * dm.d;
       so.resid = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_DOWN, false, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       // next phase: QKV of layer l+1 on its route (the exit test may still switch a backbone
       // guess to the river, which then loads its own first item) or the LM head
       const bool next_r4 = r4 || (MODE == 0 && a.sched && l == e_forced && l >= dm.entry);
@@ -674,7 +713,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       StreamOut so{};
       so.logits = a.logits ? a.logits + (size_t)b * dm.V : nullptr;
       so.key = a.amax + (step & 1) * dm.B + b;
-      gemv_phase<OP_LM, false, SEG, true, true, false, NG, GRP>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
+      gemv_phase<OP_LM, false, SEG, true, true, NG, GRP>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
                                                                a.final_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
