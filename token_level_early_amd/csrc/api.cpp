@@ -140,6 +140,7 @@ RiverLayout river_layout(const Dims& d) {
 struct ScratchLayout {
   uint64_t hs, hmid, q, o, a2, qkvr, gu, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
       layers, rope, bar, xn;
+  uint64_t t_qkv, t_o, t_a2, t_hmid, t_hs, tagc, t_end;  // tagged activations [t_qkv, t_end)
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t total;
@@ -177,6 +178,13 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.pacc = take(B * d.H * s.smax * d.D * 4);
   s.amax = take(2 * B * 8);
   s.bar = take((uint64_t)kBarWords * 4);  // grid barrier of the persistent kernel
+  s.t_qkv = take((uint64_t)d.nqkv * 4);
+  s.t_o = take((uint64_t)2 * d.hd * 4);
+  s.t_a2 = take((uint64_t)d.F * 4);
+  s.t_hmid = take((uint64_t)d.L * d.d * 4);
+  s.t_hs = take((uint64_t)(d.L + 1) * d.d * 4);
+  s.tagc = take(4);
+  s.t_end = off;
   s.xn = take(B * d.d * 2);                // batched decode: normalised block inputs
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
@@ -261,6 +269,12 @@ static DecodeArgs base_args(const river_ctx* c) {
   a.pml = (float*)(sc + s.pml);
   a.pacc = (float*)(sc + s.pacc);
   a.amax = (unsigned long long*)(sc + s.amax);
+  a.t_qkv = (uint32_t*)(sc + s.t_qkv);
+  a.t_o = (uint32_t*)(sc + s.t_o);
+  a.t_a2 = (uint32_t*)(sc + s.t_a2);
+  a.t_hmid = (uint32_t*)(sc + s.t_hmid);
+  a.t_hs = (uint32_t*)(sc + s.t_hs);
+  a.tagc = (uint32_t*)(sc + s.tagc);
   a.attn_smax = s.smax;
   return a;
 }
@@ -379,6 +393,7 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
       (e = river_launch_fill(c->scratch + c->sl.pos, 256 * 3, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.cnt, align256((uint64_t)c->sl.ncnt * 4), 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)2 * d.B * 8), 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.t_qkv, c->sl.t_end - c->sl.t_qkv, 0, st)) ||
       (e = river_launch_rope_table((float2*)a.rope, d.Tmax, d.D, (double)d.theta, st))) {
     river_destroy(c);
     return hip_fail(e, "init kernels");
@@ -396,7 +411,10 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   if (!(pe && pe[0] == '0')) {
     for (int m = 0; m < 2; ++m) {
       const void* fn = river_persist_fn(d, m);
-      const int nwg = fn ? river_persist_grid(fn) : 0;
+      // every workgroup takes one attention split of one KV head (the splits of all heads
+      // order the reuse of the kernel's activation buffers), so the grid is a multiple of Hkv
+      int nwg = fn ? river_persist_grid(fn) : 0;
+      nwg -= nwg % d.Hkv;
       // the attention phase needs one work item per (KV head, split); keep splits <= 64
       if (fn && nwg >= d.Hkv && nwg / d.Hkv <= c->sl.smax) {
         c->persist_fn[m] = fn;

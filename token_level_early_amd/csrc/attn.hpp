@@ -36,6 +36,19 @@ struct AttnLds {
   int flag;
 };
 
+// Tagged mode of the persistent kernel: q/k/v are read from tagged words (the QKV phase's
+// output, polled, no grid barrier before attention), the merged output is written as tagged
+// words, and the split counter only grows during a launch (the last arriver of use k sees
+// target - 1 with target = splits * (k + 1)), so nothing has to reset it between layers.
+struct AttnTag {
+  const uint32_t* qkv;  // [nqkv] tagged q|k|v of this layer
+  uint32_t* o;          // [H*D] tagged merged output
+  uint32_t tag;         // tag of this layer's use of both
+  int* abort;
+  int* counter;         // this KV head's split counter
+  int target;
+};
+
 RIVER_DEV float4 ld4_coh(const float* p) {
   const uint4 u = ldx16<true>(p);
   return make_float4(__builtin_bit_cast(float, u.x), __builtin_bit_cast(float, u.y),
@@ -47,9 +60,10 @@ RIVER_DEV float4 ld4_coh(const float* p) {
 //   ROPE = true : un-rotated q/k/v are in a.qkvr (persistent path): q is rotated here; the
 //                 split that owns position pos rotates k, uses k/v of pos from registers and
 //                 appends them to the cache; activations move through agent-coherent accesses.
-template <int D, int G, int NT, bool ROPE, int UP = 4, int GLP = G>
+template <int D, int G, int NT, bool ROPE, int UP = 4, int GLP = G, bool TG = false>
 RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b, int pos, int nsplit,
-                          AttnLds<D, G, NT, GLP>& sm) {
+                          AttnLds<D, G, NT, GLP>& sm, const AttnTag& tg = AttnTag{}) {
+  static_assert(!TG || ROPE, "tagged mode is the persistent kernel's");
   constexpr bool COH = ROPE;
   constexpr int LPT = D / 8;                       // lanes per head (8 dims each)
   constexpr int GL = GLP;                          // query heads per lane
@@ -96,25 +110,45 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
     uint4 kc[U], vc[U];
     load_block(t0, kc, vc);
 
-    // q of this lane's GL heads, dims [d0, d0+8)
-    const f16* qkv = a.qkvr + (size_t)b * dm.nqkv;
-    uint4 qraw[GL];
-#pragma unroll
-    for (int gl = 0; gl < GL; ++gl) {
-      const int g = hg * GL + gl;
-      qraw[gl] = ROPE ? ldx16<true>(qkv + (size_t)(kvh * G + g) * D + d0)
-                      : ldg16(a.q + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d0);
-    }
-    uint4 kraw = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
-    if (owner) {
-      kraw = ldx16<true>(qkv + dm.hd + (size_t)kvh * D + d0);
-      vpos = ldx16<true>(qkv + dm.hd + (size_t)(dm.Hkv + kvh) * D + d0);
-    }
     float2 cs[8];
     if (ROPE) {
       const float2* rope = a.rope + (size_t)pos * (D / 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) cs[i] = rope[(d0 + i) % (D / 2)];
+    }
+    // q of this lane's GL heads, dims [d0, d0+8)
+    const f16* qkv = a.qkvr + (size_t)b * dm.nqkv;
+    uint4 qraw[GL];
+    uint4 kraw = make_uint4(0, 0, 0, 0), vpos = make_uint4(0, 0, 0, 0);
+    const size_t ki = dm.hd + (size_t)kvh * D + d0, vi = dm.hd + (size_t)(dm.Hkv + kvh) * D + d0;
+    if constexpr (TG) {  // q of the lane's heads (and k, v of pos for the owner) in one wait
+      const uint32_t* pp[GL + 2];
+      bool use[GL + 2];
+      uint4 got[GL + 2];
+#pragma unroll
+      for (int gl = 0; gl < GL; ++gl) {
+        pp[gl] = tg.qkv + (size_t)(kvh * G + hg * GL + gl) * D + d0;
+        use[gl] = true;
+      }
+      pp[GL] = tg.qkv + ki;
+      pp[GL + 1] = tg.qkv + vi;
+      use[GL] = use[GL + 1] = owner;
+      ld_tag8n<GL + 2>(pp, use, tg.tag, tg.abort, got);
+#pragma unroll
+      for (int gl = 0; gl < GL; ++gl) qraw[gl] = got[gl];
+      kraw = got[GL];
+      vpos = got[GL + 1];
+    } else {
+#pragma unroll
+      for (int gl = 0; gl < GL; ++gl) {
+        const int g = hg * GL + gl;
+        const size_t qi = (size_t)(kvh * G + g) * D + d0;
+        qraw[gl] = ROPE ? ldx16<true>(qkv + qi) : ldg16(a.q + (size_t)b * dm.hd + qi);
+      }
+      if (owner) {
+        kraw = ldx16<true>(qkv + ki);
+        vpos = ldx16<true>(qkv + vi);
+      }
     }
     // rotate-half RoPE of dims [d0, d0+8), rounded to fp16; the partner dims (d +- D/2) are
     // held by lane ^ LPT/2 of the same head
@@ -257,8 +291,8 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
     }
   }
 
-  int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
-  if (arrive_counter(counter, nsplit, &sm.flag)) {
+  int* counter = TG ? tg.counter : a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
+  if (arrive_counter(counter, TG ? tg.target : nsplit, &sm.flag)) {
     // last arriver. Split weights exp2(m_j - M) / sum_j l_j exp2(m_j - M): one wave per
     // query head, lane j holds split j. The (m, l) loads and the first batch of partial-sum
     // loads are issued together, so the merge waits on memory once.
@@ -335,7 +369,9 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
       if (r == 0) {
         f16 hv[4] = {f2h(A.x), f2h(A.y), f2h(A.z), f2h(A.w)};
         f16* dst = a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d4;
-        if (COH) {
+        if (TG) {
+          st_tag4(tg.o + (size_t)(kvh * G + g) * D + d4, __builtin_bit_cast(uint2, hv), tg.tag);
+        } else if (COH) {
           __hip_atomic_store((g_u64*)dst, __builtin_bit_cast(unsigned long long, hv), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         } else {
@@ -343,7 +379,7 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
         }
       }
     }
-    if (tid == 0) reset_counter(counter);
+    if (!TG && tid == 0) reset_counter(counter);
   }
   __syncthreads();  // LDS reuse by the next item
 }

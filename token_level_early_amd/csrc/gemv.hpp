@@ -133,6 +133,116 @@ RIVER_DEV void sth(f16* p, f16 v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------------------
+// Tagged activations (persistent kernel). A value that crosses workgroups inside one launch is
+// stored as a 32-bit word: the fp16 value in the low half and a 16-bit use tag in the high
+// half. A consumer polls the words it reads until each carries the tag of the use it waits
+// for, instead of meeting every other workgroup at a grid barrier. One word is written by
+// one 32-bit store, so a word with the expected tag holds that use's value; every use rewrites
+// every word of its buffer and consecutive uses of a buffer carry different tags, so a stale
+// word never matches. The spin is bounded: a consumer that waits too long raises the abort
+// word, after which every wait returns at once (the host reports a device error).
+// ---------------------------------------------------------------------------------------
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+static constexpr unsigned kTagSpinLimit = 1u << 20;
+
+RIVER_DEV void st_tag(uint32_t* p, f16 v, uint32_t tag) {
+  __hip_atomic_store((g_u32*)p, (tag << 16) | (uint32_t)__builtin_bit_cast(unsigned short, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Four tagged words at p (16-byte aligned) from four fp16 values.
+RIVER_DEV void st_tag4(uint32_t* p, uint2 v, uint32_t tag) {
+  const unsigned long long t = ((unsigned long long)tag << 48) | ((unsigned long long)tag << 16);
+  const unsigned long long w0 = t | (v.x & 0xFFFFull) | ((unsigned long long)(v.x >> 16) << 32);
+  const unsigned long long w1 = t | (v.y & 0xFFFFull) | ((unsigned long long)(v.y >> 16) << 32);
+  __hip_atomic_store((g_u64*)p, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((g_u64*)p + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded spin step: true when the wait must end (abort raised here or elsewhere).
+RIVER_DEV bool tag_spin(unsigned& spins, int* abort) {
+  ++spins;
+  if ((spins & 255u) == 0) {
+    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return true;
+    if (spins > kTagSpinLimit) {
+      __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return true;
+    }
+  }
+  __builtin_amdgcn_s_sleep(1);
+  return false;
+}
+
+// N groups of 8 tagged words at once (use[i] false: group i is not read and reads as 0): every
+// group's loads are issued before any is checked, and only the groups not yet ready are
+// reloaded, so a wait costs one round trip however many groups a thread reads.
+RIVER_DEV bool tag8_ok(uint4 lo, uint4 hi, uint32_t t2) {
+  return (((lo.x >> 16) | (lo.y & 0xFFFF0000u)) == t2) & (((lo.z >> 16) | (lo.w & 0xFFFF0000u)) == t2) &
+         (((hi.x >> 16) | (hi.y & 0xFFFF0000u)) == t2) & (((hi.z >> 16) | (hi.w & 0xFFFF0000u)) == t2);
+}
+template <int N>
+RIVER_DEV void ld_tag8n(const uint32_t* const (&p)[N], const bool (&use)[N], const uint32_t (&tag)[N],
+                        int* abort, uint4 (&out)[N]) {
+  uint4 lo[N], hi[N];
+  bool ok[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    lo[i] = hi[i] = make_uint4(0, 0, 0, 0);
+    if (use[i]) {
+      lo[i] = ldx16<true>(p[i]);
+      hi[i] = ldx16<true>(p[i] + 4);
+    }
+  }
+  unsigned spins = 0;
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      ok[i] = !use[i] || tag8_ok(lo[i], hi[i], tag[i] | (tag[i] << 16));
+      all &= ok[i];
+    }
+    if (all || tag_spin(spins, abort)) break;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!ok[i]) {
+        lo[i] = ldx16<true>(p[i]);
+        hi[i] = ldx16<true>(p[i] + 4);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    out[i] = use[i] ? make_uint4((lo[i].x & 0xFFFFu) | (lo[i].y << 16), (lo[i].z & 0xFFFFu) | (lo[i].w << 16),
+                                 (hi[i].x & 0xFFFFu) | (hi[i].y << 16), (hi[i].z & 0xFFFFu) | (hi[i].w << 16))
+                    : make_uint4(0, 0, 0, 0);
+}
+// The 8 fp16 values of the tagged words p[0..8) (32-byte aligned), once all carry `tag`.
+RIVER_DEV uint4 ld_tag8(const uint32_t* p, uint32_t tag, int* abort) {
+  const uint32_t* pp[1] = {p};
+  const bool use[1] = {true};
+  uint4 out[1];
+  const uint32_t tg[1] = {tag};
+  ld_tag8n<1>(pp, use, tg, abort, out);
+  return out[0];
+}
+// Same, one tag for all groups.
+template <int N>
+RIVER_DEV void ld_tag8n(const uint32_t* const (&p)[N], const bool (&use)[N], uint32_t tag, int* abort,
+                        uint4 (&out)[N]) {
+  uint32_t tg[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) tg[i] = tag;
+  ld_tag8n<N>(p, use, tg, abort, out);
+}
+RIVER_DEV f16 ld_tag1(const uint32_t* p, uint32_t tag, int* abort) {
+  uint32_t w;
+  unsigned spins = 0;
+  while (true) {
+    w = __hip_atomic_load((g_u32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((w >> 16) == tag || tag_spin(spins, abort)) break;
+  }
+  return __builtin_bit_cast(f16, (unsigned short)(w & 0xFFFFu));
+}
+
 RIVER_DEV double sq8(uint4 u) {
   const f16* h = (const f16*)&u;
   double s = 0.0;

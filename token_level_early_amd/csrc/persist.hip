@@ -165,24 +165,41 @@ RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
   }
 }
 
-// x = fp16(src * inv * gain) (HAS_GAIN) or src, staged into LDS. NORM: inv = 1/rms(src) computed here in a fixed order (identical in every
-// workgroup); then each thread holds its NG groups of 8 values across the reduction.
-// Without NORM the groups stream through registers.
-template <bool IS4, bool HAS_GAIN, bool NORM, int NG>
-RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, float inv, float eps,
-                       h2* xl, float* xc, double* red) {
+// x = fp16(src * inv * gain) (HAS_GAIN) or src, staged into LDS. TAG: src is a tagged vector
+// (see ld_tag8n) whose words must carry `tag`; else a plain fp16 vector that does not change
+// during the launch (the embedding row). NORM: inv = 1/rms(src) computed here in a fixed
+// order (identical in every workgroup). Each thread reads its groups of 8 values two at a
+// time (both waits in one round trip), together with their gains.
+template <bool IS4, bool HAS_GAIN, bool NORM, bool TAG, int NG>
+RIVER_DEV void stage_x(const void* src, uint32_t tag, int* abort, const f16* gain, int K, float inv,
+                       float eps, h2* xl, float* xc, double* red) {
   const int t = threadIdx.x;
   const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
   const int ngp = nch * (IS4 ? kChunkW4 : kChunkF16) / 8;
-  if (NORM) {
-    // the input and the gain are loaded together, before the reduction
-    uint4 v[NG], gv[NG];
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int g = t + i * kPB;
-      v[i] = (g * 8 < K) ? ldx16<true>(src + g * 8) : make_uint4(0, 0, 0, 0);
-      gv[i] = (HAS_GAIN && g * 8 < K) ? ldg16(gain + g * 8) : make_uint4(0, 0, 0, 0);
+  // groups g0 and g0 + kPB of the source (zero past K)
+  auto load2 = [&](int g0, uint4 (&v)[2]) {
+    const int g1 = g0 + kPB;
+    if (TAG) {
+      const uint32_t* ts = (const uint32_t*)src;
+      const uint32_t* pp[2] = {ts + (size_t)g0 * 8, ts + (size_t)(g1 * 8 < K ? g1 : g0) * 8};
+      const bool use[2] = {g0 * 8 < K, g1 * 8 < K};
+      ld_tag8n<2>(pp, use, tag, abort, v);
+    } else {
+      const f16* ps = (const f16*)src;
+      v[0] = (g0 * 8 < K) ? ldg16(ps + (size_t)g0 * 8) : make_uint4(0, 0, 0, 0);
+      v[1] = (g1 * 8 < K) ? ldg16(ps + (size_t)g1 * 8) : make_uint4(0, 0, 0, 0);
     }
+  };
+  if (NORM) {
+    static_assert(NG <= 2, "normalised inputs: at most two groups per thread");
+    uint4 v[2], gv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = t + i * kPB;
+      gv[i] = (HAS_GAIN && i < NG && g * 8 < K) ? ldg16(gain + g * 8) : make_uint4(0, 0, 0, 0);
+    }
+    load2(t, v);
+    if (NG < 2) v[1] = make_uint4(0, 0, 0, 0);
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < NG; ++i) ss += sq8(v[i]);
@@ -197,14 +214,9 @@ RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, float inv, float 
     }
     for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4>(xl, xc, g, make_uint4(0, 0, 0, 0));
   } else {
-    // the thread's groups in pairs, both loads issued before either is used
     for (int g0 = t; g0 < ngp; g0 += 2 * kPB) {
       uint4 v[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int g = g0 + i * kPB;
-        v[i] = (g * 8 < K) ? ldx16<true>(src + g * 8) : make_uint4(0, 0, 0, 0);
-      }
+      load2(g0, v);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int g = g0 + i * kPB;
@@ -218,12 +230,19 @@ RIVER_DEV void stage_x(const f16* src, const f16* gain, int K, float inv, float 
   __syncthreads();
 }
 
-// Exit-test reduction of cos(h(l-1), h(l)) over the whole block in a fixed order.
-RIVER_DEV void block_cos(const f16* u, const f16* v, int d, double* red, double& dot, double& nu,
+// Exit-test reduction of cos(h(l-1), h(l)) over the whole block in a fixed order. h(l-1) is the
+// embedding row (up, plain) or a tagged residual-stream vector (ut); h(l) is tagged.
+RIVER_DEV void block_cos(const f16* up, const uint32_t* ut, uint32_t utag, const uint32_t* vt,
+                         uint32_t vtag, int* abort, int d, double* red, double& dot, double& nu,
                          double& nv) {
   double s0 = 0, s1 = 0, s2 = 0;
   for (int g = threadIdx.x; g * 8 < d; g += kPB) {
-    const uint4 a = ldx16<true>(u + g * 8), b = ldx16<true>(v + g * 8);
+    uint4 ab[2];
+    const uint32_t* pp[2] = {ut ? ut + g * 8 : vt + g * 8, vt + g * 8};
+    const bool use[2] = {ut != nullptr, true};
+    const uint32_t tg[2] = {utag, vtag};
+    ld_tag8n<2>(pp, use, tg, abort, ab);
+    const uint4 a = up ? ldg16(up + g * 8) : ab[0], b = ab[1];
     const f16* ha = (const f16*)&a;
     const f16* hb = (const f16*)&b;
 #pragma unroll
@@ -446,8 +465,13 @@ RIVER_DEV void w4_base(const LayerDev* lw, const uint8_t*& base, const f16*& sba
 
 // Epilogue inputs of a streamed phase.
 struct StreamOut {
-  f16* out;           // QKV -> qkvr, GU -> gu, O -> hmid, DOWN -> hs[l]
-  const f16* resid;   // O, DOWN: residual input
+  uint32_t* out;      // tagged output: QKV -> q|k|v, O -> h_mid, GU -> SwiGLU vector, DOWN -> h(l)
+  uint32_t tag;       // its tag
+  f16* copy;          // DOWN: plain copy of h(l) (the residual stream kept for inspection)
+  const f16* pres;    // O, DOWN: residual input, plain (the embedding row) ...
+  const uint32_t* tres;  // ... or tagged
+  uint32_t rtag;
+  int* abort;
   float* logits;      // LM (optional)
   unsigned long long* key;  // LM argmax key
 };
@@ -468,8 +492,11 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
   const int r0 = rr.r0, r1 = rr.r0 + rr.nv;  // contiguous for every phase but gate|up
   const int nch = n_chunks<IS4>(K);
   // residuals of this wave's rows, one per lane (O and DOWN)
+  auto resid = [&](int row) {
+    return so.pres ? ldg2(so.pres + row) : ld_tag1(so.tres + row, so.rtag, so.abort);
+  };
   f16 res = (f16)0.0f;
-  if ((OP == OP_O || OP == OP_DOWN) && r0 + lane < r1) res = ldh<true>(so.resid + r0 + lane);
+  if ((OP == OP_O || OP == OP_DOWN) && r0 + lane < r1) res = resid(r0 + lane);
   float best = -__builtin_inff();
   int bi = 0x7FFFFFFF;
   float gk = 0.f;  // gate|up: gate row r0 + lane of this wave (its value before rounding)
@@ -482,7 +509,7 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
       } else {
         const int j = vrow - rr.split;
         const float g0 = h2f(f2h(__shfl(gk, j, kWave)));
-        if (lane == 0) sth<true>(so.out + r0 + j, f2h(g0 / (1.f + __expf(-g0)) * h2f(f2h(v))));
+        if (lane == 0) st_tag(so.out + r0 + j, f2h(g0 / (1.f + __expf(-g0)) * h2f(f2h(v))), so.tag);
       }
       return;
     }
@@ -497,11 +524,15 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
     if (OP == OP_O || OP == OP_DOWN) {
       const int src = vrow < kWave ? vrow : 0;
       rv = __builtin_bit_cast(f16, (unsigned short)__shfl(__builtin_bit_cast(unsigned short, res), src, kWave));
-      if (vrow >= kWave) rv = ldh<true>(so.resid + row);
+      if (vrow >= kWave) rv = resid(row);
     }
     if (lane == 0) {
-      if (OP == OP_QKV) sth<true>(so.out + row, f2h(v));
-      if (OP == OP_O || OP == OP_DOWN) sth<true>(so.out + row, f2h(h2f(rv) + h2f(f2h(v))));
+      if (OP == OP_QKV) st_tag(so.out + row, f2h(v), so.tag);
+      if (OP == OP_O || OP == OP_DOWN) {
+        const f16 h = f2h(h2f(rv) + h2f(f2h(v)));
+        st_tag(so.out + row, h, so.tag);
+        if (OP == OP_DOWN) so.copy[row] = h;
+      }
       if (OP == OP_LM && so.logits) so.logits[row] = v;
     }
   };
@@ -570,14 +601,15 @@ RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, in
   }
 }
 
-// One GEMV phase: stage the input, stream the rows. b0 holds the phase's first item when
-// `have` (issued before the barrier that precedes the phase), else it is issued here first.
-template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, int NG, int GRP>
-RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K, const f16* src,
-                          const f16* gain, float inv, const StreamOut& so, h2* xl, float* xc,
-                          double* red, Seg<SEG>& b0, bool have) {
+// One GEMV phase: stage the input (waiting for its tagged words), stream the rows. b0 holds the
+// phase's first item when `have` (issued at the end of the previous phase), else it is issued
+// here first.
+template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool TAG, int NG, int GRP>
+RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K, const void* src,
+                          uint32_t stag, const f16* gain, float inv, const StreamOut& so, h2* xl,
+                          float* xc, double* red, Seg<SEG>& b0, bool have) {
   if (!have) prefetch_first<OP, IS4, SEG, GRP>(a, lw, N, K, b0);
-  stage_x<IS4, HAS_GAIN, NORM, NG>(src, gain, K, inv, a.dm.eps, xl, xc, red);
+  stage_x<IS4, HAS_GAIN, NORM, TAG, NG>(src, stag, so.abort, gain, K, inv, a.dm.eps, xl, xc, red);
   stream_rows<OP, IS4, SEG, GRP>(a, lw, N, K, xl, xc, so, b0);
   __syncthreads();  // LDS reuse by the next phase
 }
@@ -601,6 +633,7 @@ template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP>
 __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar) {
   static_assert(SEG16 == SEG4, "one prefetch buffer serves both weight streams");
   constexpr int SEG = SEG16;
+  constexpr int AGL = RIVER_PATTN_GL < G ? RIVER_PATTN_GL : G;
   __shared__ PSmem<D, G> sm;
   const Dims& dm = a.dm;
   const int b = 0;
@@ -610,14 +643,20 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
   int pos = a.pos[b];
   int tok = a.tok_in[b];
   h2* xl = sm.x;
-  Seg<SEG> pre;  // first weight item of the next GEMV phase, issued during the barrier before it
+  Seg<SEG> pre;  // first weight item of the next GEMV phase, issued at the end of the previous one
   int pf = 0;    // what `pre` holds: 0 nothing, 1 fp16 item, 2 int4 item
+  int* abort = (int*)(bar + kBarAbort);
+  // Use tags: (step, layer) of this launch. The counter advances by S*(L+1) per launch (at the
+  // end), so tags continue across launches and graph replays; 0 is never a tag.
+  const uint32_t tbase = __hip_atomic_load(a.tagc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto tag_of = [&](int st, int l) { return 1u + (tbase + (uint32_t)(st * (dm.L + 1) + l)) % 65535u; };
 
   for (int step = 0; step < S; ++step, ++pos) {
     if (tok < 0 || tok >= dm.V) {
       if (wg == 0 && t == 0) atomicOr(a.err, ERR_TOKEN);
       tok = 0;
     }
+    const f16* emb = a.embed + (size_t)tok * dm.d;  // h(0)
     int e_forced = dm.L;
     if (MODE == 0 && a.sched) {
       e_forced = a.sched[step * dm.B + b];
@@ -629,14 +668,17 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
     int route = ROUTE_BACKBONE;
     for (int l = 1; l <= dm.L; ++l) {
       const LayerDev* lw = &a.layers[l - 1];
+      const uint32_t tg = tag_of(step, l), tgp = tag_of(step, l - 1);
+      const uint32_t* hin_t = a.t_hs + (size_t)(l - 1) * dm.d;  // h(l-1), l > 1
+      uint32_t* hmid_t = a.t_hmid + (size_t)(l - 1) * dm.d;
+      uint32_t* o_t = a.t_o + (size_t)(l & 1) * dm.hd;  // two buffers by layer parity
       // ---------------- QKV (exit test after block l-1 first)
-      const f16* hin = (l == 1) ? a.embed + (size_t)tok * dm.d : a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
       bool norm_known = false;
       float inv = 1.f;
       if (l == 1) {
         if (wg == 0) {
           f16* h0 = a.hs + (size_t)b * dm.d;
-          for (int i = t; i < dm.d; i += kPB) sth<true>(h0 + i, hin[i]);
+          for (int i = t; i < dm.d; i += kPB) h0[i] = emb[i];
           if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
           if (a.sim_out)
             for (int i = t; i < dm.L; i += kPB)
@@ -648,7 +690,8 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
           if (lp == e_forced) route = ROUTE_RIVER;
         } else {
           double dot, n1, n2;
-          block_cos(a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d, hin, dm.d, sm.red, dot, n1, n2);
+          block_cos(lp == 1 ? emb : nullptr, lp == 1 ? nullptr : a.t_hs + (size_t)(lp - 1) * dm.d,
+                    tag_of(step, lp - 1), hin_t, tgp, abort, dm.d, sm.red, dot, n1, n2);
           const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
           if (wg == 0 && t == 0 && a.sim_out) a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
           if (sim > (double)a.tau) route = ROUTE_RIVER;
@@ -659,72 +702,97 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       }
       const bool r4 = route == ROUTE_RIVER;
       StreamOut so{};
-      so.out = a.qkvr + (size_t)b * dm.nqkv;
-      if (r4) {
-        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_QKV, true, SEG, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+      so.abort = abort;
+      so.out = a.t_qkv;
+      so.tag = tg;
+      if (l == 1) {
+        gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+      } else if (r4) {
+        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, true, SEG, true, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
       } else {
-        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
-        else gemv_phase<OP_QKV, false, SEG, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        else gemv_phase<OP_QKV, false, SEG, true, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
       }
-      grid_sync(bar, epoch, nwg);
-      if (l == 1 && wg == 0 && t == 0)  // key of the next step: last read before this barrier
+      // ---------------- attention (+ RoPE and the KV append of position pos); waits for q|k|v
+      {
+        const int use = step * dm.L + (l - 1);  // split counters only grow during a launch
+        for (int it = wg; it < dm.Hkv * splits; it += nwg) {
+          const int kvh = it / splits;
+          const AttnTag at{a.t_qkv, o_t, tg, abort, (int*)(bar + kBarAttn + kvh * kBarStride), splits * (use + 1)};
+          attn_split<D, G, kPB, true, RIVER_PATTN_U, AGL, true>(a, l, it % splits, kvh, b, pos, splits, sm.at, at);
+        }
+      }
+      pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre);
+      // ---------------- O + residual
+      so = StreamOut{};
+      so.abort = abort;
+      so.out = hmid_t;
+      so.tag = tg;
+      if (l == 1) {
+        so.pres = emb;
+      } else {
+        so.tres = hin_t;
+        so.rtag = tgp;
+      }
+      if (r4) gemv_phase<OP_O, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_O, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      // The argmax key of the next step is the one every workgroup read after the previous
+      // step's barrier; having staged all of o, this workgroup knows every split (hence every
+      // workgroup) has passed this step's layer-1 attention, so none still reads that key.
+      if (l == 1 && wg == 0 && t == 0)
         __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      // ---------------- attention (+ RoPE and the KV append of position pos)
-      for (int it = wg; it < dm.Hkv * splits; it += nwg)
-        attn_split<D, G, kPB, true, RIVER_PATTN_U, (RIVER_PATTN_GL < G ? RIVER_PATTN_GL : G)>(a, l, it % splits, it / splits, b, pos, splits, sm.at);
-      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre); });
-      // ---------------- O + residual
-      so.out = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      so.resid = a.hs + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_O, true, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_O, false, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.hd, a.o + (size_t)b * dm.hd, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
-      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_GU, SEG, GRP>(a, lw, 2 * dm.F, dm.d, r4, pre); });
-      // ---------------- gate|up
-      so.out = a.gu + (size_t)b * 2 * dm.F;
-      so.resid = nullptr;
-      {
-        const f16* src = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-        if (r4) gemv_phase<OP_GU, true, SEG, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_GU, false, SEG, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, src, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
-      }
-      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_DOWN, SEG, GRP>(a, lw, dm.d, dm.F, r4, pre); });
-      // ---------------- down (input: the SwiGLU vector the gate|up phase wrote) + residual
-      so.out = a.hs + ((size_t)l * dm.B + b) * dm.d;
-      so.resid = a.hmid + ((size_t)(l - 1) * dm.B + b) * dm.d;
-      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_DOWN, false, SEG, false, false, NG, GRP>(a, lw, dm.d, dm.F, a.gu + (size_t)b * 2 * dm.F, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      pf = prefetch_route<OP_GU, SEG, GRP>(a, lw, 2 * dm.F, dm.d, r4, pre);
+      // ---------------- gate|up (+ SwiGLU in the epilogue)
+      so = StreamOut{};
+      so.abort = abort;
+      so.out = a.t_a2;
+      so.tag = tg;
+      if (r4) gemv_phase<OP_GU, true, SEG, true, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_GU, false, SEG, true, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      pf = prefetch_route<OP_DOWN, SEG, GRP>(a, lw, dm.d, dm.F, r4, pre);
+      // ---------------- down (input: the SwiGLU vector) + residual -> h(l)
+      so = StreamOut{};
+      so.abort = abort;
+      so.out = a.t_hs + (size_t)l * dm.d;
+      so.tag = tg;
+      so.copy = a.hs + ((size_t)l * dm.B + b) * dm.d;
+      so.tres = hmid_t;
+      so.rtag = tg;
+      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
+      else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       // next phase: QKV of layer l+1 on its route (the exit test may still switch a backbone
       // guess to the river, which then loads its own first item) or the LM head
       const bool next_r4 = r4 || (MODE == 0 && a.sched && l == e_forced && l >= dm.entry);
       if (l < dm.L) {
-        const LayerDev* ln = &a.layers[l];
-        grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, ln, dm.nqkv, dm.d, next_r4, pre); });
+        pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[l], dm.nqkv, dm.d, next_r4, pre);
       } else {
-        grid_sync(bar, epoch, nwg, [&] {
-          prefetch_first<OP_LM, false, SEG, GRP>(a, nullptr, dm.V, dm.d, pre);
-          pf = 1;
-        });
+        prefetch_first<OP_LM, false, SEG, GRP>(a, nullptr, dm.V, dm.d, pre);
+        pf = 1;
       }
     }
-    // ---------------- LM head (final RMSNorm while staging) + argmax
+    // ---------------- LM head (final RMSNorm while staging) + argmax; the one grid barrier of
+    // a step (every workgroup needs the whole argmax)
     {
       StreamOut so{};
+      so.abort = abort;
       so.logits = a.logits ? a.logits + (size_t)b * dm.V : nullptr;
       so.key = a.amax + (step & 1) * dm.B + b;
-      gemv_phase<OP_LM, false, SEG, true, true, NG, GRP>(a, nullptr, dm.V, dm.d, a.hs + ((size_t)dm.L * dm.B + b) * dm.d,
-                                                               a.final_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      gemv_phase<OP_LM, false, SEG, true, true, true, NG, GRP>(a, nullptr, dm.V, dm.d, a.t_hs + (size_t)dm.L * dm.d,
+                                                               tag_of(step, dm.L), a.final_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
       if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
     }
   }
-  if (wg == 0 && t == 0) {
+  if (wg == 0 && t == 0) {  // every workgroup read the tag counter before the last barrier
     a.pos[b] = pos;
     *a.step = S;
-    if (__hip_atomic_load((int*)(bar + kBarAbort), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
+    __hip_atomic_store(a.tagc, (tbase + (uint32_t)(S * (dm.L + 1))) % 65535u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
   }
 }
 
@@ -734,6 +802,8 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
 // The kernel function for this model and mode (batch 1, GEMV inputs up to 16384), or null.
 const void* river_persist_fn(const Dims& dm, int mode) {
   if (dm.B != 1 || dm.d > kMaxK || dm.hd > kMaxK || dm.F > kMaxK) return nullptr;
+  // tagged vectors are read in groups of 8 words; one split counter line per KV head
+  if (dm.d % 8 || dm.hd % 8 || dm.F % 8 || dm.Hkv > kBarMaxAttn) return nullptr;
   const int G = dm.H / dm.Hkv;
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
 #define RIVER_PF(D_, G_, NG_, GRP_)                                                              \
