@@ -140,7 +140,7 @@ RiverLayout river_layout(const Dims& d) {
 struct ScratchLayout {
   uint64_t hs, hmid, q, o, a2, qkvr, gu, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
       layers, rope, bar, xn;
-  uint64_t t_qkv, t_o, t_a2, t_hmid, t_hs, tagc, t_end;  // tagged activations [t_qkv, t_end)
+  uint64_t t_qkv, t_o, t_a2, t_hmid, t_hs, t_part, tagc, t_end;  // tagged activations [t_qkv, t_end)
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t total;
@@ -183,7 +183,8 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.t_a2 = take((uint64_t)d.F * 4);
   s.t_hmid = take((uint64_t)d.L * d.d * 4);
   s.t_hs = take((uint64_t)(d.L + 1) * d.d * 4);
-  s.tagc = take(4);
+  s.t_part = take((uint64_t)d.H * s.smax * (d.D + 2) * 8);
+  s.tagc = take(8);
   s.t_end = off;
   s.xn = take(B * d.d * 2);                // batched decode: normalised block inputs
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
@@ -274,6 +275,7 @@ static DecodeArgs base_args(const river_ctx* c) {
   a.t_a2 = (uint32_t*)(sc + s.t_a2);
   a.t_hmid = (uint32_t*)(sc + s.t_hmid);
   a.t_hs = (uint32_t*)(sc + s.t_hs);
+  a.t_part = (unsigned long long*)(sc + s.t_part);
   a.tagc = (uint32_t*)(sc + s.tagc);
   a.attn_smax = s.smax;
   return a;
@@ -412,9 +414,12 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
     for (int m = 0; m < 2; ++m) {
       const void* fn = river_persist_fn(d, m);
       // every workgroup takes one attention split of one KV head (the splits of all heads
-      // order the reuse of the kernel's activation buffers), so the grid is a multiple of Hkv
+      // order the reuse of the kernel's activation buffers): the grid is Hkv times a power
+      // of two, at least the query heads per KV head (each split merges a slice of one head)
       int nwg = fn ? river_persist_grid(fn) : 0;
-      nwg -= nwg % d.Hkv;
+      int sp = 1;
+      while (2 * sp * d.Hkv <= nwg) sp *= 2;
+      nwg = (sp >= d.H / d.Hkv) ? sp * d.Hkv : 0;
       // the attention phase needs one work item per (KV head, split); keep splits <= 64
       if (fn && nwg >= d.Hkv && nwg / d.Hkv <= c->sl.smax) {
         c->persist_fn[m] = fn;

@@ -37,17 +37,46 @@ struct AttnLds {
 };
 
 // Tagged mode of the persistent kernel: q/k/v are read from tagged words (the QKV phase's
-// output, polled, no grid barrier before attention), the merged output is written as tagged
-// words, and the split counter only grows during a launch (the last arriver of use k sees
-// target - 1 with target = splits * (k + 1)), so nothing has to reset it between layers.
+// output, polled: no grid barrier before attention). Each split publishes its partial result
+// as 64-bit words (fp32 value | 32-bit use tag << 32) -- a split with no positions publishes an
+// empty one -- and every split workgroup of the KV head then merges its own slice of the head
+// group's G*D outputs from all splits' partials (polled; one cross-lane reduction over the
+// splits, no counter, no last arriver), writing them as tagged words. Every workgroup thus
+// publishes something each layer that the next phase's inputs depend on.
 struct AttnTag {
-  const uint32_t* qkv;  // [nqkv] tagged q|k|v of this layer
-  uint32_t* o;          // [H*D] tagged merged output
-  uint32_t tag;         // tag of this layer's use of both
+  const uint32_t* qkv;       // [nqkv] tagged q|k|v of this layer
+  uint32_t* o;               // [H*D] tagged merged output
+  uint32_t tag;              // 16-bit tag of this layer's use of both
+  unsigned long long* part;  // [H][nsplit][D+2] split partials: acc[D], then max, sum
+  uint32_t tag32;            // tag of this layer's partials
   int* abort;
-  int* counter;         // this KV head's split counter
-  int target;
 };
+
+RIVER_DEV void st_part(unsigned long long* p, float v, uint32_t tag32) {
+  __hip_atomic_store((g_u64*)p, ((unsigned long long)tag32 << 32) | __builtin_bit_cast(uint32_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// (max, sum) and, when `acc` is set, one accumulator of a split's partial, once all three
+// carry tag32 (one round trip; see ld_tag8n for the bounded wait).
+RIVER_DEV void ld_part3(const unsigned long long* pm, const unsigned long long* pa, bool acc,
+                        uint32_t tag32, int* abort, float& m, float& l, float& av) {
+  unsigned long long w0, w1, w2 = (unsigned long long)tag32 << 32;
+  w0 = __hip_atomic_load((g_u64*)pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  w1 = __hip_atomic_load((g_u64*)pm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (acc) w2 = __hip_atomic_load((g_u64*)pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned spins = 0;
+  while (true) {
+    const bool o0 = (uint32_t)(w0 >> 32) == tag32, o1 = (uint32_t)(w1 >> 32) == tag32,
+               o2 = (uint32_t)(w2 >> 32) == tag32;
+    if ((o0 & o1 & o2) || tag_spin(spins, abort)) break;
+    if (!o0) w0 = __hip_atomic_load((g_u64*)pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!o1) w1 = __hip_atomic_load((g_u64*)pm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!o2) w2 = __hip_atomic_load((g_u64*)pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  m = __builtin_bit_cast(float, (uint32_t)w0);
+  l = __builtin_bit_cast(float, (uint32_t)w1);
+  av = acc ? __builtin_bit_cast(float, (uint32_t)w2) : 0.f;
+}
 
 RIVER_DEV float4 ld4_coh(const float* p) {
   const uint4 u = ldx16<true>(p);
@@ -282,17 +311,61 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
         Ls += sm.l[j][g] * sc;
         A += sm.acc[j][g][dd] * sc;
       }
-      const size_t pi = pbase + (size_t)g * nsplit + s;
-      wt_store(&a.pacc[pi * D + dd], A);
-      if (dd == 0) {
-        wt_store(&a.pml[pi * 2 + 0], M);
-        wt_store(&a.pml[pi * 2 + 1], Ls);
+      if constexpr (TG) {
+        unsigned long long* r = tg.part + ((size_t)(kvh * G + g) * nsplit + s) * (D + 2);
+        st_part(r + dd, A, tg.tag32);
+        if (dd == 0) {
+          st_part(r + D, M, tg.tag32);
+          st_part(r + D + 1, Ls, tg.tag32);
+        }
+      } else {
+        const size_t pi = pbase + (size_t)g * nsplit + s;
+        wt_store(&a.pacc[pi * D + dd], A);
+        if (dd == 0) {
+          wt_store(&a.pml[pi * 2 + 0], M);
+          wt_store(&a.pml[pi * 2 + 1], Ls);
+        }
       }
+    }
+  } else if constexpr (TG) {  // no positions in this split: an empty partial (max -inf, sum 0)
+    for (int g = tid; g < G; g += NT) {
+      unsigned long long* r = tg.part + ((size_t)(kvh * G + g) * nsplit + s) * (D + 2);
+      st_part(r + D, -__builtin_inff(), tg.tag32);
+      st_part(r + D + 1, 0.f, tg.tag32);
     }
   }
 
-  int* counter = TG ? tg.counter : a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
-  if (arrive_counter(counter, TG ? tg.target : nsplit, &sm.flag)) {
+  if constexpr (TG) {
+    // this workgroup's slice: VPW consecutive outputs of one query head (nsplit and G*D are
+    // powers of two and nsplit >= G, so VPW divides D). Lanes [k*P, k*P + P) of a wave hold
+    // splits 0..P-1 of one output; max, sum and the weighted sum reduce across them.
+    const int P = nsplit;
+    const int VPW = (G * D >= P) ? G * D / P : 1;
+    const int v0 = s * VPW;
+    if (v0 < G * D) {
+      const int g = v0 / D, dbase = v0 % D;
+      for (int idx = tid; idx < VPW * P; idx += NT) {
+        const int j = idx % P, v = idx / P;
+        const unsigned long long* r = tg.part + ((size_t)(kvh * G + g) * P + j) * (D + 2);
+        float mj, lj, aj;
+        ld_part3(r + D, r + dbase + v, j < seff, tg.tag32, tg.abort, mj, lj, aj);
+        float M = mj;
+        for (int o = 1; o < P; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+        const float e = (j < seff) ? exp2f(mj - M) : 0.f;
+        float Lsum = lj * e, A = aj * e;
+        for (int o = 1; o < P; o <<= 1) {
+          Lsum += __shfl_xor(Lsum, o, kWave);
+          A += __shfl_xor(A, o, kWave);
+        }
+        if (j == 0) st_tag(tg.o + (size_t)(kvh * G + g) * D + dbase + v, f2h(A / Lsum), tg.tag);
+      }
+    }
+    __syncthreads();  // LDS reuse by the next item
+    return;
+  }
+
+  int* counter = a.cnt + CNT_ATTN + b * dm.Hkv + kvh;
+  if (arrive_counter(counter, nsplit, &sm.flag)) {
     // last arriver. Split weights exp2(m_j - M) / sum_j l_j exp2(m_j - M): one wave per
     // query head, lane j holds split j. The (m, l) loads and the first batch of partial-sum
     // loads are issued together, so the merge waits on memory once.
@@ -369,9 +442,7 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
       if (r == 0) {
         f16 hv[4] = {f2h(A.x), f2h(A.y), f2h(A.z), f2h(A.w)};
         f16* dst = a.o + (size_t)b * dm.hd + (size_t)(kvh * G + g) * D + d4;
-        if (TG) {
-          st_tag4(tg.o + (size_t)(kvh * G + g) * D + d4, __builtin_bit_cast(uint2, hv), tg.tag);
-        } else if (COH) {
+        if (COH) {
           __hip_atomic_store((g_u64*)dst, __builtin_bit_cast(unsigned long long, hv), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         } else {
@@ -379,7 +450,7 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
         }
       }
     }
-    if (!TG && tid == 0) reset_counter(counter);
+    if (tid == 0) reset_counter(counter);
   }
   __syncthreads();  // LDS reuse by the next item
 }

@@ -150,15 +150,6 @@ RIVER_DEV void st_tag(uint32_t* p, f16 v, uint32_t tag) {
   __hip_atomic_store((g_u32*)p, (tag << 16) | (uint32_t)__builtin_bit_cast(unsigned short, v),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Four tagged words at p (16-byte aligned) from four fp16 values.
-RIVER_DEV void st_tag4(uint32_t* p, uint2 v, uint32_t tag) {
-  const unsigned long long t = ((unsigned long long)tag << 48) | ((unsigned long long)tag << 16);
-  const unsigned long long w0 = t | (v.x & 0xFFFFull) | ((unsigned long long)(v.x >> 16) << 32);
-  const unsigned long long w1 = t | (v.y & 0xFFFFull) | ((unsigned long long)(v.y >> 16) << 32);
-  __hip_atomic_store((g_u64*)p, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store((g_u64*)p + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Bounded spin step: true when the wait must end (abort raised here or elsewhere).
 RIVER_DEV bool tag_spin(unsigned& spins, int* abort) {
   ++spins;

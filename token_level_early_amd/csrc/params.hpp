@@ -80,7 +80,8 @@ struct DecodeArgs {
   uint32_t* t_a2;    // [F]
   uint32_t* t_hmid;  // [L][d]
   uint32_t* t_hs;    // [L+1][d]  (row 0 unused: h(0) is the embedding row)
-  uint32_t* tagc;    // [1] tag counter, advanced by every launch
+  unsigned long long* t_part;  // [H][splits][D+2] attention split partials (fp32 | tag32 << 32)
+  uint32_t* tagc;    // [2] tag counters (16-bit activations, 32-bit partials), advanced per launch
   int attn_smax;    // split count of the attention grid
   // per-call I/O (device pointers)
   const int* tok_in;     // [B]
@@ -96,11 +97,9 @@ static constexpr int kMaxRed = 8192;
 // Grid barrier of the persistent kernel, in u32 words: the completed-group counter at 0, the
 // abort flag at kBarAbort, the arrival counter of workgroup group g at (g + 1) * kBarStride and
 // its release flag at (kBarMaxGroups + 1 + g) * kBarStride (groups of kBarGroup workgroups;
-// every word on its own 256-byte line), then the attention split counter of KV head h at
-// kBarAttn + h * kBarStride.
+// every word on its own 256-byte line).
 static constexpr int kBarGroup = 16, kBarStride = 64, kBarMaxGroups = 64, kBarAbort = 32;
-static constexpr int kBarAttn = (2 * kBarMaxGroups + 1) * kBarStride, kBarMaxAttn = 64;
-static constexpr int kBarWords = kBarAttn + kBarMaxAttn * kBarStride;
+static constexpr int kBarWords = (2 * kBarMaxGroups + 1) * kBarStride;
 // counter slots (each one int)
 static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn: [B][Hkv]
 

@@ -649,7 +649,10 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
   // Use tags: (step, layer) of this launch. The counter advances by S*(L+1) per launch (at the
   // end), so tags continue across launches and graph replays; 0 is never a tag.
   const uint32_t tbase = __hip_atomic_load(a.tagc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tbase32 = __hip_atomic_load(a.tagc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   auto tag_of = [&](int st, int l) { return 1u + (tbase + (uint32_t)(st * (dm.L + 1) + l)) % 65535u; };
+  // attention partials: a slot may go unwritten for many uses (a split past the context), so
+  // their tag is 32 bits wide
 
   for (int step = 0; step < S; ++step, ++pos) {
     if (tok < 0 || tok >= dm.V) {
@@ -716,12 +719,9 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       }
       // ---------------- attention (+ RoPE and the KV append of position pos); waits for q|k|v
       {
-        const int use = step * dm.L + (l - 1);  // split counters only grow during a launch
-        for (int it = wg; it < dm.Hkv * splits; it += nwg) {
-          const int kvh = it / splits;
-          const AttnTag at{a.t_qkv, o_t, tg, abort, (int*)(bar + kBarAttn + kvh * kBarStride), splits * (use + 1)};
-          attn_split<D, G, kPB, true, RIVER_PATTN_U, AGL, true>(a, l, it % splits, kvh, b, pos, splits, sm.at, at);
-        }
+        const AttnTag at{a.t_qkv, o_t, tg, a.t_part, tbase32 + (uint32_t)(step * (dm.L + 1) + l), abort};
+        for (int it = wg; it < dm.Hkv * splits; it += nwg)
+          attn_split<D, G, kPB, true, RIVER_PATTN_U, AGL, true>(a, l, it % splits, it / splits, b, pos, splits, sm.at, at);
       }
       pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre);
       // ---------------- O + residual
@@ -792,6 +792,8 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
     *a.step = S;
     __hip_atomic_store(a.tagc, (tbase + (uint32_t)(S * (dm.L + 1))) % 65535u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.tagc + 1, tbase32 + (uint32_t)(S * (dm.L + 1)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
     if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicOr(a.err, ERR_SYNC);
   }
 }
@@ -802,9 +804,10 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
 // The kernel function for this model and mode (batch 1, GEMV inputs up to 16384), or null.
 const void* river_persist_fn(const Dims& dm, int mode) {
   if (dm.B != 1 || dm.d > kMaxK || dm.hd > kMaxK || dm.F > kMaxK) return nullptr;
-  // tagged vectors are read in groups of 8 words; one split counter line per KV head
-  if (dm.d % 8 || dm.hd % 8 || dm.F % 8 || dm.Hkv > kBarMaxAttn) return nullptr;
+  // tagged vectors are read in groups of 8 words; the split merge needs G*D a power of two
+  if (dm.d % 8 || dm.hd % 8 || dm.F % 8) return nullptr;
   const int G = dm.H / dm.Hkv;
+  if ((G & (G - 1)) || (dm.D & (dm.D - 1))) return nullptr;
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
 #define RIVER_PF(D_, G_, NG_, GRP_)                                                              \
   if (dm.D == D_ && G == G_ && ng == NG_ && dm.group == GRP_)                                    \
