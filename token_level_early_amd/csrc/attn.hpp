@@ -228,23 +228,22 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[gl][i] = 0.f;
     }
-    for (int tb = t0; tb < t1; tb += BLK) {
-      const bool more = tb + BLK < t1;
-      uint4 kn[U], vn[U];
-      if (more) load_block(tb + BLK, kn, vn);
-      if (owner) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (tb + slot + u * NS == pos) {
-            kc[u] = kpos;
-            vc[u] = vpos;
-          }
-      }
+    // one block of positions [tb, tb + BLK) from the registers kk/vv
+    // (the new position's k/v come from registers: selected where used, the ring itself is
+    // never written outside its loads)
+    auto process = [&](int tb, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
       if (tb + slot < t1) {  // the slot has a position in this block (uniform per slot)
+        uint4 kk[U], vv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool np = owner && tb + slot + u * NS == pos;
+          kk[u] = np ? kpos : kr[u];
+          vv[u] = np ? vpos : vr[u];
+        }
         float sc[U][GL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const h2 k0 = as_h2(kc[u].x), k1 = as_h2(kc[u].y), k2 = as_h2(kc[u].z), k3 = as_h2(kc[u].w);
+          const h2 k0 = as_h2(kk[u].x), k1 = as_h2(kk[u].y), k2 = as_h2(kk[u].z), k3 = as_h2(kk[u].w);
 #pragma unroll
           for (int gl = 0; gl < GL; ++gl)
             sc[u][gl] = dot2(qh[gl][3], k3, dot2(qh[gl][2], k2, dot2(qh[gl][1], k1, dot2(qh[gl][0], k0, 0.f))));
@@ -273,19 +272,28 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
           for (int i = 0; i < 8; ++i) {
             float x = acc[gl][i] * c;
 #pragma unroll
-            for (int u = 0; u < U; ++u) x = fmaf(p[u], h2f(((const f16*)&vc[u])[i]), x);
+            for (int u = 0; u < U; ++u) x = fmaf(p[u], h2f(((const f16*)&vv[u])[i]), x);
             acc[gl][i] = x;
           }
           m[gl] = mb;
         }
       }
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kc[u] = kn[u];
-          vc[u] = vn[u];
-        }
-      }
+    };
+    // Two register buffers in a ring: a block's loads are in flight while the previous one is
+    // reduced. The loads are unconditional (positions past the split read a harmless in-range
+    // row and are masked; a block past the end is a no-op) and the stages are fenced from the
+    // scheduler, which would otherwise pull uses of a just-issued load ahead of the other
+    // block's arithmetic and wait on it at once.
+    uint4 kn[U], vn[U];
+    for (int tb = t0; tb < t1; tb += 2 * BLK) {
+      load_block(tb + BLK, kn, vn);
+      __builtin_amdgcn_sched_barrier(0);
+      process(tb, kc, vc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_block(tb + 2 * BLK, kc, vc);
+      __builtin_amdgcn_sched_barrier(0);
+      process(tb + BLK, kn, vn);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // every slot's softmax state to LDS, then merge the NS slots per (query head, dim)
 #pragma unroll
