@@ -25,7 +25,7 @@ hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K,
                                uint8_t* packed, uint16_t* scales, hipStream_t st);
 hipError_t river_launch_rope_table(float2* tab, int Tmax, int D, double theta, hipStream_t st);
 hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st);
-const void* river_persist_fn(const Dims& dm, int mode);
+const void* river_persist_fn(const Dims& dm, int mode, int long_ctx);
 int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
                                 unsigned* bar, hipStream_t st);
@@ -237,6 +237,7 @@ struct river_ctx {
   std::vector<hipEvent_t> timer_ev;
   // persistent decode kernel ([mode]: 0 early exit, 1 backbone only); null = per-op kernels
   const void* persist_fn[2] = {nullptr, nullptr};
+  const void* persist_fn_long[2] = {nullptr, nullptr};  // launches reaching kPersistLongCtx
   int persist_nwg[2] = {0, 0};
   int persist_chunk = 8;
 };
@@ -412,7 +413,9 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   const char* pe = getenv("RIVER_PERSIST");
   if (!(pe && pe[0] == '0')) {
     for (int m = 0; m < 2; ++m) {
-      const void* fn = river_persist_fn(d, m);
+      const void* fn = river_persist_fn(d, m, 0);
+      const void* fn_long = river_persist_fn(d, m, 1);
+      if (fn_long && river_persist_grid(fn_long) < (fn ? river_persist_grid(fn) : 0)) fn_long = fn;
       // every workgroup takes one attention split of one KV head (the splits of all heads
       // order the reuse of the kernel's activation buffers): the grid is Hkv times a power
       // of two, at least the query heads per KV head (each split merges a slice of one head)
@@ -423,9 +426,11 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
       // the attention phase needs one work item per (KV head, split); keep splits <= 64
       if (fn && nwg >= d.Hkv && nwg / d.Hkv <= c->sl.smax) {
         c->persist_fn[m] = fn;
+        c->persist_fn_long[m] = fn_long;
         c->persist_nwg[m] = nwg;
       } else if (fn && nwg >= d.Hkv) {
         c->persist_fn[m] = fn;
+        c->persist_fn_long[m] = fn_long;
         c->persist_nwg[m] = c->sl.smax * d.Hkv;
       }
     }
@@ -558,7 +563,9 @@ static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipSt
     if (e == hipSuccess) e = river_launch_fill(c->scratch + c->sl.amax, (int64_t)2 * B * 8, 0, st);
     if (e != hipSuccess) return hip_fail(e, "barrier/argmax reset");
     if (timed) timer_hook(c, TOP_PERSIST, 0);
-    e = river_launch_persist(c->persist_fn[mode], b, n, nwg, splits, bar, st);
+    const bool long_ctx = (int64_t)c->pos_host[0] + s0 + n - 1 >= kPersistLongCtx;
+    e = river_launch_persist(long_ctx ? c->persist_fn_long[mode] : c->persist_fn[mode], b, n, nwg,
+                             splits, bar, st);
     if (timed) timer_hook(c, TOP_PERSIST, 1);
     if (e != hipSuccess) return hip_fail(e, "persistent decode launch");
   }

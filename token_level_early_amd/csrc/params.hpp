@@ -100,6 +100,8 @@ static constexpr int kMaxRed = 8192;
 // every word on its own 256-byte line).
 static constexpr int kBarGroup = 16, kBarStride = 64, kBarMaxGroups = 64, kBarAbort = 32;
 static constexpr int kBarWords = (2 * kBarMaxGroups + 1) * kBarStride;
+// Persistent decode: launches that reach this position run the long-context kernel variant.
+static constexpr int kPersistLongCtx = 8192;
 // counter slots (each one int)
 static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn: [B][Hkv]
 

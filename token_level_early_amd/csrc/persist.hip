@@ -30,11 +30,8 @@ static constexpr unsigned kSpinLimit = 1u << 22;
 static constexpr int kMaxK = 16384;  // longest GEMV input the LDS staging buffer holds
 static constexpr int kPB = 512;      // threads per persistent workgroup (one per CU)
 static constexpr int kPW = kPB / kWave;
-// attention lane layout of the persistent kernel: positions per thread per block and query
-// heads per lane (see attn_split)
-#ifndef RIVER_PATTN_U
-#define RIVER_PATTN_U 2
-#endif
+// attention lane layout of the persistent kernel: query heads per lane (see attn_split); the
+// positions per thread per block are the kernel's AU parameter (2, or 4 from kPersistLongCtx)
 #ifndef RIVER_PATTN_GL
 #define RIVER_PATTN_GL 1
 #endif
@@ -629,7 +626,7 @@ RIVER_DEV int prefetch_route(const DecodeArgs& a, const LayerDev* lw, int N, int
 // ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
-template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP>
+template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP, int AU>
 __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar) {
   static_assert(SEG16 == SEG4, "one prefetch buffer serves both weight streams");
   constexpr int SEG = SEG16;
@@ -721,7 +718,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       {
         const AttnTag at{a.t_qkv, o_t, tg, a.t_part, tbase32 + (uint32_t)(step * (dm.L + 1) + l), abort};
         for (int it = wg; it < dm.Hkv * splits; it += nwg)
-          attn_split<D, G, kPB, true, RIVER_PATTN_U, AGL, true>(a, l, it % splits, it / splits, b, pos, splits, sm.at, at);
+          attn_split<D, G, kPB, true, AU, AGL, true>(a, l, it % splits, it / splits, b, pos, splits, sm.at, at);
       }
       pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre);
       // ---------------- O + residual
@@ -802,7 +799,10 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
 // Launchers
 // ---------------------------------------------------------------------------------------
 // The kernel function for this model and mode (batch 1, GEMV inputs up to 16384), or null.
-const void* river_persist_fn(const Dims& dm, int mode) {
+// `long_ctx`: the variant for launches that reach position kPersistLongCtx, whose attention
+// keeps twice the K/V in flight per lane (a separate kernel: carrying both loop shapes in one
+// costs the short-context case registers).
+const void* river_persist_fn(const Dims& dm, int mode, int long_ctx) {
   if (dm.B != 1 || dm.d > kMaxK || dm.hd > kMaxK || dm.F > kMaxK) return nullptr;
   // tagged vectors are read in groups of 8 words; the split merge needs G*D a power of two
   if (dm.d % 8 || dm.hd % 8 || dm.F % 8) return nullptr;
@@ -810,9 +810,13 @@ const void* river_persist_fn(const Dims& dm, int mode) {
   if ((G & (G - 1)) || (dm.D & (dm.D - 1))) return nullptr;
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
 #define RIVER_PF(D_, G_, NG_, GRP_)                                                              \
-  if (dm.D == D_ && G == G_ && ng == NG_ && dm.group == GRP_)                                    \
-    return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_>                            \
-                : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_>;
+  if (dm.D == D_ && G == G_ && ng == NG_ && dm.group == GRP_) {                                  \
+    if (long_ctx)                                                                                \
+      return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_, 4>                       \
+                  : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 4>;                      \
+    return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_, 2>                         \
+                : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 2>;                        \
+  }
   RIVER_PF(128, 4, 1, 128)
   RIVER_PF(64, 4, 1, 128)
   RIVER_PF(64, 2, 1, 64)
