@@ -213,7 +213,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": g["frac"], "traffic": None,
                 "avg_launch_us": g["avg_us"], "bytes_per_launch": g["bytes_per_launch"]}
     if roof is not None:
-        tr = pmc_traffic(roof)
+        tr = pmc_traffic(roof, args.config)
         if tr is not None:
             roof["traffic"] = tr["bytes_per_launch"]
             roof["traffic_detail"] = tr
@@ -266,16 +266,18 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(roof):
+def pmc_traffic(roof, config):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE, scaled by the plain-copy calibration), or None when those
-    counters were taken on other kernel sources or another kernel."""
+    counters were taken on other kernel sources, another kernel or another workload."""
     try:
         with open(PMC_FILE) as f:
             pm = json.load(f)
     except (OSError, ValueError):
         return None
     if pm.get("source_hash") != kernel_source_hash() or not roof["kernel"].startswith(pm.get("kernel", "?")):
+        return None
+    if pm.get("workload", "").split(" ")[0] != config:  # counted on another workload
         return None
     return {"bytes_per_launch": pm["hbm_bytes_per_launch"], "fetch_bytes": pm["fetch_bytes_per_launch"],
             "write_bytes": pm["write_bytes_per_launch"],

@@ -168,10 +168,12 @@ int river_decode_step(river_ctx* ctx, const int32_t* tok_in, const int32_t* forc
  *   tok_out    [S][B]; exit_layer [S][B] or NULL; sim [S][B][L] or NULL
  * Same semantics and errors as S calls of river_decode_step.
  * Execution: a batch-1 context whose shapes the persistent decode kernel covers runs up to 8
- * steps per cooperative launch (one workgroup per compute unit, grid barriers between the
- * phases of a step); otherwise -- or when the environment variable RIVER_PERSIST is "0" at
- * river_init -- the per-op kernels run, replayed from a captured graph. Both give the same
- * results up to floating-point summation order. */
+ * steps per cooperative launch (one workgroup per compute unit; inside a step each phase waits
+ * only for the activations it reads, one grid barrier per step after the LM head); otherwise --
+ * or when the environment variable RIVER_PERSIST is "0" at river_init -- the per-op kernels
+ * run, replayed from a captured graph. Both give the same results up to floating-point
+ * summation order. A wait inside the persistent kernel that exceeds its bound ends the launch
+ * early and is reported as RIVER_EDEVICE. */
 int river_decode_steps(river_ctx* ctx, const int32_t* tok_in, const int32_t* sched, int32_t S,
                        float tau, int32_t* tok_out, int32_t* exit_layer, float* sim,
                        void* stream);
