@@ -212,3 +212,39 @@ def test_persistent_kernel_matches_per_op_kernels(tiny, mode):
         fin = ~np.isnan(b[2])
         assert np.array_equal(np.isnan(a[2]), np.isnan(b[2]))
         assert np.allclose(a[2][fin], b[2][fin], atol=2e-3)
+
+
+def test_persistent_tags_wrap_and_long_context_switch(tiny):
+    """The persistent kernel's 16-bit activation tags wrap after 65535 uses (13107 steps of the
+    4-layer decoder), and launches that reach position 8192 switch to the long-context kernel
+    variant. Decoding 13200 steps across both raises no device error (a stale tag matching, or
+    a wait that never ends, would abort the launch and set the error word) and is deterministic:
+    two contexts decoding the same prompt produce the same tokens and residual stream."""
+    import os
+    w, wn, orc = tiny
+    P, S = 16, 13200
+    old = os.environ.get("RIVER_PERSIST")
+    os.environ["RIVER_PERSIST"] = "1"
+    outs = []
+    try:
+        for _ in range(2):
+            rv = river.River(TINY, w, max_seq=P + S + 2, max_prefill=P)
+            assert rv.decode_path() == "persistent"
+            toks = synth.prompt(TINY, 1, P, seed=5, device="cuda")
+            pre = rv.prefill(toks, prefill_exit=TINY["L"])
+            sched = torch.full((S, 1), 2, dtype=torch.int32, device="cuda")
+            t = rv.decode_steps(pre["tokens"], sched=sched)
+            torch.cuda.synchronize()
+            assert rv.device_status() == river.RIVER_OK
+            assert rv.positions() == [P + S]
+            outs.append((t.cpu().numpy().ravel(), rv.hidden().float().cpu().numpy()))
+            rv.close()
+    finally:
+        if old is None:
+            del os.environ["RIVER_PERSIST"]
+        else:
+            os.environ["RIVER_PERSIST"] = old
+    toks0, hs0 = outs[0]
+    assert ((toks0 >= 0) & (toks0 < TINY["V"])).all()
+    assert np.array_equal(toks0, outs[1][0])
+    assert np.array_equal(hs0, outs[1][1])
