@@ -187,6 +187,25 @@ def main():
                 "speedup_of_early_exit": round(fms / ms, 4)}
         log(f"full depth: {full}")
 
+    # ---- all-river decode (forced exit 0: every block on the int4 copy) over the same positions:
+    # the all-quantised comparator, the speed the early exit approaches as exits move earlier
+    allr = None
+    if not args.no_full:
+        tok = prefill_and_warm()
+        zero = torch.zeros_like(st_sched)
+        torch.cuda.synchronize()
+        ev0.record()
+        rv.decode_steps(tok, sched=zero, tok_out=tok_out)
+        ev1.record()
+        torch.cuda.synchronize()
+        zms = ev0.elapsed_time(ev1)
+        zbytes = sum(bm.batch_step_bytes(c, [0] * B, [p] * B) for p in positions)
+        allr = {"tokens_per_s": round(S * B / (zms / 1e3), 2), "ms_per_step": round(zms / S, 4),
+                "GB/s": round(zbytes / (zms / 1e3) / 1e9, 1),
+                "frac": round(zbytes / (zms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "speedup_over_full_depth": round(fms / zms, 4) if full else None}
+        log(f"all river: {allr}")
+
     # ---- achievable ceiling on this part: a plain device copy and a plain read of 1 GiB
     ceiling = hbm_ceiling(torch)
     log(f"measured HBM ceiling: {ceiling}")
@@ -245,6 +264,7 @@ def main():
         "hbm_measured_ceiling": ceiling,
         "kernels_per_op_path": kernels,
         "full_depth_fp16": full,
+        "all_river_int4": allr,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -19,7 +19,9 @@
  * Conventions
  *   - Layers are 1-based in the text (l = 1..L). The exit layer e of a token is the number of
  *     backbone layers it ran: layers 1..e on the backbone, e+1..L on the river. e = L means
- *     no exit. Exit tests run after backbone layers l in [entry_layer, L-1].
+ *     no exit; a forced e = 0 runs every layer on the river (the all-int4 "Full Quantization"
+ *     comparator of the paperlayer.ai summary, section 5). Exit tests run after backbone
+ *     layers l in [entry_layer, L-1].
  *   - Pointers are DEVICE pointers unless marked "host". fp16 tensors are IEEE binary16,
  *     row-major. `stream` is a hipStream_t passed as void* (NULL = the null stream); all
  *     device work of a call is enqueued on it and the call returns without synchronising,
@@ -148,7 +150,7 @@ int river_prefill(river_ctx* ctx, const int32_t* tokens, int32_t P, int32_t pref
  * exactly one KV slot per layer at pos[b] -- from the backbone block or its river copy,
  * whichever ran -- and then pos[b] += 1.
  *   tok_in       [B] int32 (may alias tok_out)
- *   forced_exit  [B] int32 exit layer in [entry, L], or NULL for tau mode (exit after backbone
+ *   forced_exit  [B] int32 exit layer in {0} or [entry, L], or NULL for tau mode (exit after backbone
  *                layer l in [entry, L-1] iff cos(h(l-1), h(l)) > tau). An out-of-range forced
  *                value is treated as L and flags RIVER_EDEVICE (river_device_status).
  *   tok_out      [B] int32 greedy next token (lowest index on ties)

@@ -392,8 +392,10 @@ class RiverOracle:
                     margin=1e-3, keep_hidden=True):
         """One generated token per row at position kv.pos[b].
 
-        forced_exit [B] (exit after backbone layer e; e = L never exits) or tau (with the
-        GPU's exit_layer [B] used only where |s - tau| <= margin).
+        forced_exit [B] (exit after backbone layer e; e = L never exits; e = 0 runs no backbone
+        block at all: every block on the river, the pages' "Full Quantization" comparator of
+        [paperlayer] §5) or tau (with the GPU's exit_layer [B] used only where |s - tau| <=
+        margin).
         Returns dict: tokens [B], logits [B][V] fp64, exit_layer [B], sim [B][L] (s(l) at
         index l-1, NaN where not computed), hs [L+1][B][d] fp16 (hs[0] = embedding row).
         """
@@ -412,7 +414,9 @@ class RiverOracle:
             h = self.embed16[int(tokens[b])].copy()
             if keep_hidden:
                 hs[0, b] = h
-            exited = False
+            exited = forced_exit is not None and int(forced_exit[b]) == 0
+            if exited:
+                exit_layer[b] = 0
             for l in range(1, L + 1):
                 W = self.weights_for(l - 1, exited)
                 h_new = block_decode(c, W, self.norms(l - 1), h, pos,

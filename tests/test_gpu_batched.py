@@ -48,7 +48,7 @@ def test_tiny_batch4_matches_oracle(tiny, mode):
     exits = []
     for s in range(S):
         if mode == "forced":
-            fe = rng.integers(1, L + 1, size=B).astype(np.int32)  # rows disagree on most layers
+            fe = rng.integers(0, L + 1, size=B).astype(np.int32)  # rows disagree on most layers; 0 = all river
             r = rv.decode_step(cur, forced_exit=torch.from_numpy(fe).cuda(), logits=True)
             o = orc.decode_step(kvo, cur.cpu().numpy(), forced_exit=list(fe))
         else:

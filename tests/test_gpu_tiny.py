@@ -248,3 +248,43 @@ def test_persistent_tags_wrap_and_long_context_switch(tiny):
     assert ((toks0 >= 0) & (toks0 < TINY["V"])).all()
     assert np.array_equal(toks0, outs[1][0])
     assert np.array_equal(hs0, outs[1][1])
+
+
+def test_tiny_forced_zero_all_river_matches_oracle(tiny, decode_path):
+    """Forced exit 0 runs every block on the river (the all-int4 "Full Quantization" comparator,
+    paperlayer summary §5). A schedule mixing 0 with ordinary exits, on both decode paths,
+    against the oracle step by step (teacher-forced with the GPU's tokens); the multi-step call
+    gives the same exits and tokens as the single steps."""
+    w, wn, orc = tiny
+    L, P = TINY["L"], 16
+    sched = [0, 0, 3, 0, 1, L, 0]
+    S = len(sched)
+    rv = river.River(TINY, w, max_seq=P + S + 4, max_prefill=P)
+    assert rv.decode_path() == decode_path
+    toks = synth.prompt(TINY, 1, P, seed=2, device="cuda")
+    kvo = orc.new_kv(1, P + S + 4)
+    pre = rv.prefill(toks, prefill_exit=L)
+    orc.prefill(kvo, toks.cpu().numpy(), prefill_exit=L)
+    cur = pre["tokens"]
+    got = []
+    for s, e in enumerate(sched):
+        fe = torch.tensor([e], dtype=torch.int32, device="cuda")
+        r = rv.decode_step(cur, forced_exit=fe, logits=True)
+        o = orc.decode_step(kvo, cur.cpu().numpy(), forced_exit=[e])
+        assert int(r["exit_layer"][0]) == e == int(o["exit_layer"][0]), s
+        _compare_step(rv, r, o, P, s, "forced0")
+        cur = r["tokens"]
+        got.append(int(cur[0]))
+    _kv_compare(rv, kvo, P + S)
+    assert rv.device_status() == river.RIVER_OK
+    rv.close()
+
+    rv = river.River(TINY, w, max_seq=P + S + 4, max_prefill=P)
+    pre = rv.prefill(toks, prefill_exit=L)
+    ex = torch.empty(S, 1, dtype=torch.int32, device="cuda")
+    sch = torch.tensor(sched, dtype=torch.int32, device="cuda").view(S, 1)
+    t = rv.decode_steps(pre["tokens"], sched=sch, exit_layer=ex)
+    assert ex.cpu().numpy().ravel().tolist() == sched
+    assert t.cpu().numpy().ravel().tolist() == got
+    assert rv.device_status() == river.RIVER_OK
+    rv.close()

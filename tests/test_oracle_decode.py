@@ -259,3 +259,27 @@ def test_prefill_sequence_exit_uses_min_over_tokens(tiny_model):
     # tau between min and max: some tokens would exit, the latest one keeps the sequence
     r = tiny_model.prefill(tiny_model.new_kv(1, P), toks, tau=(lo + hi) / 2)
     assert r["seq_exit"][0] != 1
+
+
+def test_forced_zero_runs_every_block_on_the_river():
+    """Forced exit 0 (the pages' all-int4 "Full Quantization" comparator, paperlayer summary
+    §5): no backbone block. With int4-representable weights the river is the backbone exactly,
+    so the result equals the full-backbone run bit for bit; with ordinary weights block 1
+    already differs from a run that exits after backbone block 1."""
+    L = TINY["L"]
+    w = synth.to_numpy(synth.representable_weights(TINY, seed=1))
+    m = O.RiverOracle(TINY, w)
+    _, a, kva = _run(m, 1, 8, 3, forced=[[0]] * 3)
+    _, b, kvb = _run(m, 1, 8, 3, forced=[[L]] * 3)
+    for ra, rb in zip(a, b):
+        assert ra["exit_layer"][0] == 0
+        assert (ra["hs"] == rb["hs"]).all() and (ra["logits"] == rb["logits"]).all()
+    assert (kva.K == kvb.K).all() and (kva.V == kvb.V).all()
+
+    m2 = O.RiverOracle(TINY, synth.to_numpy(synth.weights(TINY, seed=0)))
+    _, z, kvz = _run(m2, 1, 8, 1, forced=[[0]])
+    _, one, kv1 = _run(m2, 1, 8, 1, forced=[[1]])
+    assert (z[0]["hs"][0] == one[0]["hs"][0]).all()        # same embedding row
+    assert (z[0]["hs"][1] != one[0]["hs"][1]).any()        # block 1: river vs backbone
+    assert (kvz.K[0, 0, :, 8] != kv1.K[0, 0, :, 8]).any()  # its K slot at the decode position
+    assert (kvz.count == kv1.count).all()                  # same slots written once

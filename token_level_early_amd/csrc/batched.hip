@@ -59,6 +59,10 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
       if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
       if (a.sim_out)
         for (int i = t; i < dm.L; i += kBlock) a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
+      if (mode == 0 && a.sched && a.sched[step * dm.B + b] == 0) {  // no backbone block at all
+        route = ROUTE_RIVER;
+        if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = 0;
+      }
     } else {
       hin = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
       if (mode == 0) {
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
         } else if (lp >= dm.entry) {
           if (a.sched) {
             int e = a.sched[step * dm.B + b];
-            if (e < dm.entry || e > dm.L) {
+            if ((e < dm.entry && e != 0) || e > dm.L) {
               if (t == 0) atomicOr(a.err, ERR_FORCED);
               e = dm.L;
             }

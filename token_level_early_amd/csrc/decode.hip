@@ -67,6 +67,13 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, in
           for (int i = t; i < dm.L; i += kBlock)
             a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
       }
+      if (MODE == 0) {  // forced exit 0: no backbone block at all
+        if (a.sched && a.sched[step * dm.B + b] == 0) route = ROUTE_RIVER;
+        if (blockIdx.x == 0 && t == 0) {
+          a.route[dm.B + b] = route;  // layer 1's route, read by its later ops and the next exit test
+          if (route == ROUTE_RIVER && a.exit_out) a.exit_out[step * dm.B + b] = 0;
+        }
+      }
     } else {
       vin = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
       if (MODE == 0) {
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_dec_gemv(DecodeArgs a, int layer, in
         } else if (lp >= dm.entry) {
           if (a.sched) {
             int e = a.sched[step * dm.B + b];
-            if (e < dm.entry || e > dm.L) {
+            if ((e < dm.entry && e != 0) || e > dm.L) {
               if (blockIdx.x == 0 && t == 0) atomicOr(a.err, ERR_FORCED);
               e = dm.L;
             }

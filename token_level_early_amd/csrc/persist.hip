@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
     int e_forced = dm.L;
     if (MODE == 0 && a.sched) {
       e_forced = a.sched[step * dm.B + b];
-      if (e_forced < dm.entry || e_forced > dm.L) {
+      if ((e_forced < dm.entry && e_forced != 0) || e_forced > dm.L) {  // 0: every block on the river
         if (wg == 0 && t == 0) atomicOr(a.err, ERR_FORCED);
         e_forced = dm.L;
       }
@@ -684,6 +684,10 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
             for (int i = t; i < dm.L; i += kPB)
               a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
         }
+        if (MODE == 0 && a.sched && e_forced == 0) {  // no backbone block at all
+          route = ROUTE_RIVER;
+          if (wg == 0 && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = 0;
+        }
       } else if (MODE == 0 && route == ROUTE_BACKBONE && l - 1 >= dm.entry) {
         const int lp = l - 1;
         if (a.sched) {
@@ -706,7 +710,8 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.out = a.t_qkv;
       so.tag = tg;
       if (l == 1) {
-        gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (r4) gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
       } else if (r4) {
         if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
         else gemv_phase<OP_QKV, true, SEG, true, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
