@@ -52,6 +52,10 @@ def main():
                     help="host only: write the HBM-traffic summary of k_persist from rocprofv3 "
                          "counter CSVs (FETCH_SIZE / WRITE_SIZE runs of this script, then the same "
                          "two counters on --calib-copy) and the bench output of the FETCH_SIZE run")
+    ap.add_argument("--tau-sweep", type=int, default=0, metavar="N",
+                    help="instead of the forced-schedule run: decode in tau mode at N values of tau "
+                         "(quantiles of the similarities of a no-exit run) and report tokens/s "
+                         "against the realised exit layers (batch 1)")
     args = ap.parse_args()
     if args.pmc_summary:
         write_pmc_summary(*args.pmc_summary)
@@ -85,6 +89,10 @@ def main():
     torch.cuda.synchronize()
     log(f"river built in {time.time() - t0:.1f}s")
     toks = synth.prompt(c, B, P, seed=args.seed, device=dev)
+    if args.tau_sweep:
+        tau_sweep(args, c, cfgd, rv, toks, S, W, P, L, torch, bm, log)
+        rv.close()
+        return
     sched_np = synth.schedule(cfgd, W + S, B, seed=args.seed)
     sched = torch.from_numpy(sched_np).to(dev)
 
@@ -284,6 +292,52 @@ def kernel_source_hash():
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def tau_sweep(args, c, cfgd, rv, toks, S, W, P, L, torch, bm, log):
+    """Speed against exit rate in tau mode (the pages' trade-off between exit rate and speed,
+    here on synthetic inputs, so without an accuracy axis). A run with tau = 2 (cos <= 1: never
+    exits) records s(l) of every tested layer; the sweep's tau values are quantiles of those;
+    each tau then decodes the same S positions after the same prefill and warm-up."""
+    if rv.B != 1:
+        raise SystemExit("--tau-sweep measures batch 1")
+    dev = "cuda"
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(tau, sim=None):
+        pre = rv.prefill(toks, prefill_exit=L)
+        out = rv.decode_steps(pre["tokens"], S=W, tau=tau)
+        torch.cuda.synchronize()
+        ex = torch.empty(S, 1, dtype=torch.int32, device=dev)
+        ev0.record()
+        rv.decode_steps(out[-1].clone(), S=S, tau=tau, exit_layer=ex, sim=sim)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1), ex.cpu().numpy()[:, 0]
+
+    sim = torch.empty(S, 1, L, dtype=torch.float32, device=dev)
+    run(2.0, sim)
+    sv = sim.cpu().numpy()[:, 0, :]
+    sv = sv[~np.isnan(sv)]
+    qs = np.linspace(0.05, 0.95, args.tau_sweep)
+    taus = [float(np.float32(np.quantile(sv, q))) for q in qs]
+    positions = [P + W + s for s in range(S)]
+    points = []
+    for q, tau in zip(qs, taus):
+        ms, ex = run(tau)
+        nbytes = sum(bm.batch_step_bytes(c, [int(e)], [p]) for e, p in zip(ex, positions))
+        gbs = nbytes / (ms / 1e3) / 1e9
+        pt = {"tau": round(tau, 6), "similarity_quantile": round(float(q), 3),
+              "tokens_per_s": round(S / (ms / 1e3), 2), "mean_exit_layer": round(float(ex.mean()), 3),
+              "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        points.append(pt)
+        log(f"tau sweep: {pt}")
+    print(json.dumps({"metric": f"decode tokens/s against exit rate, tau mode, {args.config}",
+                      "unit": "tokens/s", "n_gpus": 1, "steps": S, "warmup": W,
+                      "higher_is_better": True, "data": "synthetic (seeded random weights and prompt)",
+                      "config": {"workload": f"{cfgd['name']} decode, batch 1, prompt {P}, tau mode",
+                                 "similarities": "s(l) of a no-exit run, layers >= entry"},
+                      "tau_sweep": points}))
 
 
 def pmc_traffic(roof, config):
