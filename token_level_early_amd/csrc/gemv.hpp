@@ -206,15 +206,6 @@ RIVER_DEV void ld_tag8n(const uint32_t* const (&p)[N], const bool (&use)[N], con
                                  (hi[i].x & 0xFFFFu) | (hi[i].y << 16), (hi[i].z & 0xFFFFu) | (hi[i].w << 16))
                     : make_uint4(0, 0, 0, 0);
 }
-// The 8 fp16 values of the tagged words p[0..8) (32-byte aligned), once all carry `tag`.
-RIVER_DEV uint4 ld_tag8(const uint32_t* p, uint32_t tag, int* abort) {
-  const uint32_t* pp[1] = {p};
-  const bool use[1] = {true};
-  uint4 out[1];
-  const uint32_t tg[1] = {tag};
-  ld_tag8n<1>(pp, use, tg, abort, out);
-  return out[0];
-}
 // Same, one tag for all groups.
 template <int N>
 RIVER_DEV void ld_tag8n(const uint32_t* const (&p)[N], const bool (&use)[N], uint32_t tag, int* abort,
