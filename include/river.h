@@ -219,6 +219,20 @@ int river_export_river(river_ctx* ctx, int32_t layer, int32_t which, uint8_t* pa
  * (index 0 = embedding row, index l = output of block l), into the device buffer `dst`. */
 int river_debug_hidden(river_ctx* ctx, void* dst, void* stream);
 
+/* Debug support: KV-slot write counts, the check that the shared cache never has an absent
+ * or doubly written slot whatever the exit schedule (chatpaper.ai abstract: the KV Cache
+ * Absence problem; paperlayer section 4 "KV-Shared Exit Layer": exit layers write the slot the
+ * backbone would have written; appendix A.3: one KV set). Only a library built with
+ * RIVER_DEBUG_KV_COUNT (libriver_kvcount.so) counts: it keeps one 32-bit counter per element of
+ * the cache, incremented by every store of that element (in prefill and in every decode path),
+ * cleared by river_init. river_kv_write_counts writes cnt[l][b][t] (uint8, device buffer of
+ * L*B*max_seq bytes) = how many times slot (layer l, row b, position t) was written: the common
+ * count of its 2*Hkv*D elements, capped at 254, or 255 when its elements were written unequal
+ * numbers of times. Enqueued on `stream`. A release library returns RIVER_EINVAL.
+ * river_kv_counting sets *enabled to 1 in the debug library, 0 otherwise (host-only). */
+int river_kv_write_counts(river_ctx* ctx, uint8_t* cnt, void* stream);
+int river_kv_counting(int32_t* enabled /* host */);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* river_last_error(void);
 

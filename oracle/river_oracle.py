@@ -331,21 +331,26 @@ class RiverOracle:
     mlp_norm, w_gate, w_up, w_down.
     cfg keys: L, d, H, Hkv, D, F, V, eps, theta, group, entry (E_min).
     ``layers`` restricts which layers are materialised (for per-layer slices of a
-    large model); the others must not be run.
+    large model); the others must not be run. ``river_layers`` (default: ``layers``)
+    restricts the river copies separately, so a run whose exit layers are known ahead
+    holds only the backbone blocks it runs and the river blocks it runs.
     """
 
-    def __init__(self, cfg, weights, layers=None):
+    def __init__(self, cfg, weights, layers=None, river_layers=None):
         self.cfg = dict(cfg)
         self.cfg.setdefault("entry", 1)
         self.L = cfg["L"]
         self.w16 = weights
         idx = range(self.L) if layers is None else layers
+        ridx = idx if river_layers is None else river_layers
         self.bb = {}
         self.rv = {}
         self.qcodes = {}
         for i in idx:
             lw = weights["layers"][i]
             self.bb[i] = {m: np.asarray(lw[m]).astype(F64) for m in _MATS}
+        for i in ridx:
+            lw = weights["layers"][i]
             self.rv[i] = {}
             self.qcodes[i] = {}
             for m in _MATS:

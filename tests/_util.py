@@ -3,11 +3,18 @@
 import numpy as np
 
 TOL = 1e-2  # max|gpu - oracle| / rms(oracle) for one block (or the head) on the same inputs
-# End to end through many random-weight blocks, fp16 rounding differences are amplified: with
-# the 16-block 1B decoder, flipping the fp16 rounding of 0.1% of h(1) by one ulp moves the
-# final logits by 0.85% of their rms in the oracle itself. End-to-end comparisons over more
-# than a few blocks therefore use TOL_E2E together with exact top-1 agreement.
+# End to end through many random-weight blocks, fp16 rounding differences compound: the oracle
+# itself, run with every linear map accumulated in fp32 instead of fp64 (the same algorithm and
+# fp16 storage points), moves the 16-block 1B decoder's logits by 1.0-1.2e-2 of their rms
+# (tests/test_oracle_noise_floor.py). End-to-end comparisons over more than a few blocks
+# therefore use TOL_E2E (twice that floor) together with exact top-1 agreement, and every block
+# is also checked at TOL on the GPU's own inputs.
 TOL_E2E = 3e-2
+# Greedy tokens are compared wherever the oracle's top-2 gap exceeds 1e-2 of rms(logits); the
+# near-tied steps are counted, and a test fails if more than this fraction of its compared
+# steps (at least one step always allowed) were near ties.
+MAX_NEAR_TIE_FRAC = 0.1
+TOP1 = {"checked": 0, "near": 0}
 
 
 def rel_err(gpu, ref):
@@ -23,7 +30,9 @@ def top1_checked(gpu_tok, ref_logits, margin_frac=1e-2):
     lg = np.asarray(ref_logits, dtype=np.float64)
     order = np.argsort(-lg, kind="stable")
     gap = lg[order[0]] - lg[order[1]]
+    TOP1["checked"] += 1
     if gap <= margin_frac * np.sqrt(np.mean(lg * lg)):
+        TOP1["near"] += 1
         return None
     return int(gpu_tok) == int(np.flatnonzero(lg == lg.max())[0])
 

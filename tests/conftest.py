@@ -30,3 +30,16 @@ def decode_path(request):
         del os.environ["RIVER_PERSIST"]
     else:
         os.environ["RIVER_PERSIST"] = old
+
+
+@pytest.fixture(autouse=True)
+def near_tie_budget():
+    """Counts the greedy-token comparisons a test makes (tests/_util.top1_checked) and fails the
+    test when more than MAX_NEAR_TIE_FRAC of them were near ties (not compared)."""
+    from tests import _util
+    _util.TOP1["checked"] = _util.TOP1["near"] = 0
+    yield
+    n, near = _util.TOP1["checked"], _util.TOP1["near"]
+    if n:
+        print(f"top-1 comparisons: {n}, near ties (not compared): {near}")
+    assert near <= max(1, int(_util.MAX_NEAR_TIE_FRAC * n)), f"{near} near-tied steps of {n}"

@@ -97,3 +97,15 @@ def test_init_rejects_null_arguments_before_any_device_work():
     assert lib.river_decode_path(None, None) == river.RIVER_EINVAL
     assert lib.river_decode_step(None, None, None, 0.5, None, None, None, None, None) == river.RIVER_EINVAL
     assert lib.river_prefill(None, None, 1, 0, 0.5, None, None, None, None, None) == river.RIVER_EINVAL
+
+
+def test_kv_write_counting_only_in_the_debug_build():
+    """river_kv_counting (host-only) reports 0 in the release library and 1 in the library built
+    with RIVER_DEBUG_KV_COUNT; both export the same symbols."""
+    flag = ctypes.c_int32(-1)
+    assert river.load().river_kv_counting(ctypes.byref(flag)) == 0 and flag.value == 0
+    dbg = river.load(river.LIB_KVCOUNT_PATH)
+    flag = ctypes.c_int32(-1)
+    assert dbg.river_kv_counting(ctypes.byref(flag)) == 0 and flag.value == 1
+    for n in _declared():
+        assert hasattr(dbg, n), n

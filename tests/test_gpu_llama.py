@@ -261,3 +261,134 @@ def test_llama8b_64k_context_prefill_and_decode_slices(llama8b, decode_path):
         cur = r["tokens"]
     assert rv.positions() == [P + S]
     rv.close()
+
+
+def test_llama8b_river_export_bit_exact_group128(llama8b):
+    """The device quantiser's river copy of one 8B-shape block (group 128; K = 4096 and 14336)
+    is bit-exact with the oracle's codes and scales."""
+    _, c, w = llama8b
+    rv = river.River(c, w, max_seq=16, max_prefill=16)
+    layer = 5
+    lw = {m: w["layers"][layer][m].cpu().numpy() for m in river.MATS}
+    for which, m in enumerate(river.MATS):
+        packed, scales = rv.export_river(layer, which)
+        q, s = O.quantize_w4(lw[m], c["group"])
+        assert np.array_equal(packed.cpu().numpy(), O.pack_nibbles(q)), m
+        assert np.array_equal(scales.cpu().numpy().view(np.uint16), s.view(np.uint16)), m
+    rv.close()
+
+
+def _slice_check(c, orc, rv, r, e, pos, layers, tag):
+    """Teacher-forced oracle blocks at `layers` on the GPU's own h(l-1) and cache, and the head."""
+    L = c["L"]
+    hs = rv.hidden()[:, 0].cpu().numpy()
+    kv = rv.kv_view()
+    for l in layers:
+        Kl = kv[l - 1, 0, 0, :, : pos + 1].cpu().numpy().copy()
+        Vl = kv[l - 1, 1, 0, :, : pos + 1].cpu().numpy().copy()
+        k_gpu, v_gpu = Kl[:, pos].copy(), Vl[:, pos].copy()
+        out = O.block_decode(c, orc.weights_for(l - 1, l > e), orc.norms(l - 1), hs[l - 1], pos, Kl, Vl)
+        assert rel_err(hs[l], out) <= TOL, (tag, l)
+        assert rel_err(k_gpu, Kl[:, pos]) <= TOL, (tag, l)
+        assert rel_err(v_gpu, Vl[:, pos]) <= TOL, (tag, l)
+    lg = orc.head_logits(hs[L])
+    assert rel_err(r["logits"][0].cpu().numpy(), lg) <= TOL, tag
+    assert top1_checked(int(r["tokens"][0]), lg) is not False, tag
+    return hs
+
+
+def test_llama8b_chained_launches_match_single_steps_and_oracle(llama8b, decode_path):
+    """The bench's launch pattern: 20 forced-schedule steps in one call (persistent path: launches
+    of 8, 8 and 4 steps chained on the device) give the same tokens, exit layers and shared cache,
+    bit for bit, as 20 single-step calls; steps 9 and 17 of the single-step run are checked
+    against oracle blocks at the layers around their exits and the LM head."""
+    cfg, c, w = llama8b
+    P, S = cfg["prompt"], 20
+    L = c["L"]
+    sched = torch.from_numpy(synth.schedule(cfg, S, 1, seed=7)).to("cuda")
+    es = [int(x) for x in sched[:, 0].cpu()]
+    checks = {8: None, 16: None}
+    layers = {s: sorted({1, es[s], min(es[s] + 1, L), L}) for s in checks}
+    need = sorted({l - 1 for v in layers.values() for l in v})
+    orc = O.RiverOracle(c, synth.to_numpy({"embed": w["embed"], "lm_head": w["lm_head"],
+                                            "final_norm": w["final_norm"],
+                                            "layers": [w["layers"][i] if i in need else None
+                                                       for i in range(L)]}), layers=need)
+    toks = synth.prompt(c, 1, P, seed=7, device="cuda")
+    out = []
+    for multi in (True, False):
+        rv = river.River(c, w, max_seq=P + S + 2, max_prefill=P)
+        assert rv.decode_path() == decode_path
+        pre = rv.prefill(toks, prefill_exit=L)
+        if multi:
+            ex = torch.empty(S, 1, dtype=torch.int32, device="cuda")
+            t = rv.decode_steps(pre["tokens"], sched=sched, exit_layer=ex)
+            tt, ee = t.cpu().numpy().ravel(), ex.cpu().numpy().ravel()
+        else:
+            cur, tl, el = pre["tokens"], [], []
+            for s in range(S):
+                r = rv.decode_step(cur, forced_exit=sched[s], logits=s in checks)
+                assert int(r["exit_layer"][0]) == es[s]
+                if s in checks:
+                    _slice_check(c, orc, rv, r, es[s], P + s, layers[s], ("step", s + 1))
+                tl.append(int(r["tokens"][0]))
+                el.append(int(r["exit_layer"][0]))
+                cur = r["tokens"]
+            tt, ee = np.array(tl), np.array(el)
+        torch.cuda.synchronize()
+        assert rv.device_status() == river.RIVER_OK
+        out.append((tt, ee, rv.kv_view()[:, :, 0, :, : P + S].clone()))
+        rv.close()
+    assert np.array_equal(out[0][1], np.array(es)) and np.array_equal(out[1][1], np.array(es))
+    assert np.array_equal(out[0][0], out[1][0])
+    assert torch.equal(out[0][2], out[1][2])
+
+
+def test_llama8b_tau_mode_slices_match_oracle(llama8b, decode_path):
+    """Tau mode at the 8B shape: a first step with tau = 2 (never exits) records s(l); tau is then
+    set to the median of those similarities so that the next steps exit part-way. Each step's
+    similarities are recomputed by the oracle from the GPU's stored residual stream, the exit
+    layer must follow the rule wherever |s - tau| > 1e-3, and oracle blocks check the layers
+    around the exit."""
+    cfg, c, w = llama8b
+    P, S = 512, 3
+    L = c["L"]
+    rv = river.River(c, w, max_seq=P + S + 2, max_prefill=P)
+    assert rv.decode_path() == decode_path
+    toks = synth.prompt(c, 1, P, seed=9, device="cuda")
+    pre = rv.prefill(toks, prefill_exit=L)
+    r = rv.decode_step(pre["tokens"], tau=2.0, sim=True)
+    assert int(r["exit_layer"][0]) == L
+    sv = r["sim"][0].cpu().numpy()
+    tau = f32(np.median(sv[~np.isnan(sv)]))
+    cur = r["tokens"]
+    exits = []
+    orc = None
+    for s in range(S):
+        pos = P + 1 + s
+        r = rv.decode_step(cur, tau=tau, logits=True, sim=True)
+        e = int(r["exit_layer"][0])
+        hs = rv.hidden()[:, 0].cpu().numpy()
+        sim = r["sim"][0].cpu().numpy()
+        # the GPU's decision against its own stored states: s(l) for l in [entry, e], exit at e
+        for l in range(1, L):
+            if l <= e and l >= c["entry"]:
+                so = O.cosine(hs[l - 1], hs[l])
+                assert abs(sim[l - 1] - so) < 1e-4, (s, l, sim[l - 1], so)
+                if abs(so - tau) > 1e-3:
+                    assert (so > tau) == (l == e), (s, l, so, tau, e)
+            else:
+                assert np.isnan(sim[l - 1]), (s, l)
+        if orc is None:
+            need = sorted({0, e - 1, min(e, L - 1), L - 1})
+            orc = O.RiverOracle(c, synth.to_numpy({"embed": w["embed"], "lm_head": w["lm_head"],
+                                                    "final_norm": w["final_norm"],
+                                                    "layers": [w["layers"][i] if i in need else None
+                                                               for i in range(L)]}), layers=need)
+        lay = sorted(l for l in {1, e, min(e + 1, L), L} if l - 1 in orc.bb)
+        _slice_check(c, orc, rv, r, e, pos, lay, ("tau step", s))
+        exits.append(e)
+        cur = r["tokens"]
+    print("tau", tau, "exit layers", exits)
+    assert any(e < L for e in exits)
+    rv.close()

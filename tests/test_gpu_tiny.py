@@ -288,3 +288,102 @@ def test_tiny_forced_zero_all_river_matches_oracle(tiny, decode_path):
     assert t.cpu().numpy().ravel().tolist() == got
     assert rv.device_status() == river.RIVER_OK
     rv.close()
+
+
+def test_prefill_after_decode_reuses_context(tiny, decode_path):
+    """A context that decoded (an odd number of steps, which leaves the persistent kernel's
+    last argmax key in slot 0) and is then prefilled with another prompt gives exactly what a
+    fresh context gives for that prompt, and the oracle's answer."""
+    w, wn, orc = tiny
+    L, P = TINY["L"], 12
+    t1 = synth.prompt(TINY, 1, P, seed=21, device="cuda")
+    t2 = synth.prompt(TINY, 1, P, seed=22, device="cuda")
+    rv = river.River(TINY, w, max_seq=P + 8, max_prefill=P)
+    assert rv.decode_path() == decode_path
+    pre = rv.prefill(t1, prefill_exit=L)
+    r = rv.decode_step(pre["tokens"], forced_exit=torch.tensor([2], dtype=torch.int32, device="cuda"))
+    rv.decode_steps(r["tokens"], sched=torch.tensor([[1], [3], [L]], dtype=torch.int32, device="cuda"))
+    again = rv.prefill(t2, prefill_exit=L, logits=True)
+    torch.cuda.synchronize()
+    assert rv.positions() == [P]
+    fresh = river.River(TINY, w, max_seq=P + 8, max_prefill=P)
+    ref = fresh.prefill(t2, prefill_exit=L, logits=True)
+    torch.cuda.synchronize()
+    assert int(again["tokens"][0]) == int(ref["tokens"][0])
+    assert torch.equal(again["logits"], ref["logits"])
+    kvo = orc.new_kv(1, P + 8)
+    o = orc.prefill(kvo, t2.cpu().numpy(), prefill_exit=L)
+    assert rel_err(again["logits"][0].cpu().numpy(), o["logits"][0]) <= TOL
+    assert top1_checked(int(again["tokens"][0]), o["logits"][0]) is not False
+    # and decoding continues from position P as on the fresh context
+    a = rv.decode_step(again["tokens"], forced_exit=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    b = fresh.decode_step(ref["tokens"], forced_exit=torch.tensor([1], dtype=torch.int32, device="cuda"))
+    assert int(a["tokens"][0]) == int(b["tokens"][0])
+    assert torch.equal(rv.kv_view()[:, :, 0, :, : P + 1], fresh.kv_view()[:, :, 0, :, : P + 1])
+    rv.close()
+    fresh.close()
+
+
+@pytest.mark.parametrize("mode", ["forced", "tau"])
+def test_chained_launches_equal_single_steps(tiny, mode, decode_path):
+    """S = 20 decode steps in one call -- on the persistent path three chained launches of at
+    most 8 steps, each starting from the previous launch's last token and tag counter -- give
+    bit for bit the tokens, exit layers, similarities and shared cache of 20 single-step calls;
+    the last step's residual stream matches the oracle teacher-forced with the GPU's tokens."""
+    w, wn, orc = tiny
+    L, P, S = TINY["L"], 16, 20
+    rng = np.random.default_rng(17)
+    sched_np = rng.integers(0, L + 1, size=(S, 1)).astype(np.int32)
+    tau = f32(0.3)
+    toks = synth.prompt(TINY, 1, P, seed=23, device="cuda")
+    runs = []
+    for multi in (True, False):
+        rv = river.River(TINY, w, max_seq=P + S + 2, max_prefill=P)
+        assert rv.decode_path() == decode_path
+        pre = rv.prefill(toks, prefill_exit=L)
+        if multi:
+            ex = torch.empty(S, 1, dtype=torch.int32, device="cuda")
+            sim = torch.empty(S, 1, L, dtype=torch.float32, device="cuda")
+            if mode == "forced":
+                t = rv.decode_steps(pre["tokens"], sched=torch.from_numpy(sched_np).cuda(), exit_layer=ex, sim=sim)
+            else:
+                t = rv.decode_steps(pre["tokens"], S=S, tau=tau, exit_layer=ex, sim=sim)
+            tt, ee, ss = t.cpu().numpy().ravel(), ex.cpu().numpy().ravel(), sim.cpu().numpy()[:, 0]
+        else:
+            cur, tl, el, sl = pre["tokens"], [], [], []
+            for s in range(S):
+                if mode == "forced":
+                    r = rv.decode_step(cur, forced_exit=torch.from_numpy(sched_np[s]).cuda())
+                else:
+                    r = rv.decode_step(cur, tau=tau)
+                tl.append(int(r["tokens"][0]))
+                el.append(int(r["exit_layer"][0]))
+                sl.append(r["sim"][0].cpu().numpy())
+                cur = r["tokens"]
+            tt, ee, ss = np.array(tl), np.array(el), np.stack(sl)
+        torch.cuda.synchronize()
+        assert rv.device_status() == river.RIVER_OK
+        runs.append((tt, ee, ss, rv.kv_view().cpu(), rv.hidden().cpu(), rv.positions(),
+                     int(pre["tokens"][0])))
+        rv.close()
+    (ta, ea, sa, ka, ha, pa, first), (tb, eb, sb, kb, hb, pb, _) = runs
+    assert pa == pb == [P + S]
+    assert np.array_equal(ta, tb) and np.array_equal(ea, eb)
+    assert np.array_equal(np.isnan(sa), np.isnan(sb)) and np.array_equal(sa[~np.isnan(sa)], sb[~np.isnan(sb)])
+    assert torch.equal(ka, kb) and torch.equal(ha, hb)
+    if mode == "forced":
+        assert np.array_equal(ea, sched_np.ravel())
+    # oracle over the same 20 steps, teacher-forced with the GPU's tokens (and its decisions
+    # inside the tau margin)
+    kvo = orc.new_kv(1, P + S + 2)
+    orc.prefill(kvo, toks.cpu().numpy(), prefill_exit=L)
+    cur = first
+    for s in range(S):
+        if mode == "forced":
+            o = orc.decode_step(kvo, [cur], forced_exit=[int(sched_np[s, 0])])
+        else:
+            o = orc.decode_step(kvo, [cur], tau=tau, gpu_exit=[int(ea[s])])
+        assert int(o["exit_layer"][0]) == int(ea[s]), s
+        cur = int(ta[s])
+    assert rel_err(ha[:, 0].float().numpy(), o["hs"][:, 0]) <= TOL
+    assert rel_err(ka.float().numpy()[:, :, 0], np.stack([kvo.K[:, 0], kvo.V[:, 0]], axis=1)) <= TOL

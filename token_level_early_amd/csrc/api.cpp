@@ -25,6 +25,8 @@ hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K,
                                uint8_t* packed, uint16_t* scales, hipStream_t st);
 hipError_t river_launch_rope_table(float2* tab, int Tmax, int D, double theta, hipStream_t st);
 hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st);
+hipError_t river_launch_kv_slot_counts(const uint32_t* cnt, int L, int B, int Hkv, int Tmax, int D,
+                                       uint8_t* out, hipStream_t st);
 const void* river_persist_fn(const Dims& dm, int mode, int long_ctx);
 int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
@@ -143,6 +145,7 @@ struct ScratchLayout {
   uint64_t t_qkv, t_o, t_a2, t_hmid, t_hs, t_part, tagc, t_end;  // tagged activations [t_qkv, t_end)
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
+  uint64_t kvcnt;  // debug build: per-element KV write counters (0 bytes otherwise)
   uint64_t total;
   int smax;
   int ncnt;
@@ -202,6 +205,11 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.pf_route = take(B * 4);
   s.pf_exit = take(B * 4);
   s.pf_minsim = take(B * d.L * 4);
+#ifdef RIVER_DEBUG_KV_COUNT
+  s.kvcnt = take((uint64_t)d.L * 2 * B * d.Hkv * d.Tmax * d.D * 4);
+#else
+  s.kvcnt = off;
+#endif
   s.total = off;
   return s;
 }
@@ -279,6 +287,9 @@ static DecodeArgs base_args(const river_ctx* c) {
   a.t_part = (unsigned long long*)(sc + s.t_part);
   a.tagc = (uint32_t*)(sc + s.tagc);
   a.attn_smax = s.smax;
+#ifdef RIVER_DEBUG_KV_COUNT
+  a.kvcnt = (uint32_t*)(sc + s.kvcnt);
+#endif
   return a;
 }
 
@@ -397,6 +408,7 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
       (e = river_launch_fill(c->scratch + c->sl.cnt, align256((uint64_t)c->sl.ncnt * 4), 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)2 * d.B * 8), 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.t_qkv, c->sl.t_end - c->sl.t_qkv, 0, st)) ||
+      (e = river_launch_fill(c->scratch + c->sl.kvcnt, c->sl.total - c->sl.kvcnt, 0, st)) ||
       (e = river_launch_rope_table((float2*)a.rope, d.Tmax, d.D, (double)d.theta, st))) {
     river_destroy(c);
     return hip_fail(e, "init kernels");
@@ -514,9 +526,14 @@ int river_prefill(river_ctx* c, const int32_t* tokens, int32_t P, int32_t prefil
   p.kv = (f16*)c->kv;
   p.rope = (const float2*)(sc + s.rope);
   DecodeArgs a = base_args(c);
+  p.kvcnt = a.kvcnt;
   a.tok_out = next_tok;
   a.logits = logits;
-  hipError_t e = river_launch_prefill(p, a, c->layers.data(), prefill_exit, tau, st);
+  // The LM head below takes an atomic max into argmax slot 0; a persistent decode launch leaves
+  // the key of its last step in slot (S-1)&1, so both slots start from zero here.
+  hipError_t e = river_launch_fill(sc + s.amax, (int64_t)2 * d.B * 8, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "argmax reset");
+  e = river_launch_prefill(p, a, c->layers.data(), prefill_exit, tau, st);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   e = (d.B > 1) ? river_launch_head_batched(a, (f16*)(sc + s.xn), st, nullptr, nullptr, -1)
                : river_launch_head(a, st, nullptr, nullptr, -1);
@@ -544,11 +561,11 @@ static void timer_hook(void* p, int op, int phase) {
   if (phase == 1) ++c->timer_n;
 }
 
-static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
+static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st,
+                       unsigned* bar) {
   const int B = c->dm.B, L = c->dm.L;
   const int nwg = c->persist_nwg[mode];
   const int splits = nwg / c->dm.Hkv;
-  unsigned* bar = (unsigned*)(c->scratch + c->sl.bar);
   const bool timed = (c->timer_op == TOP_PERSIST);
   if (timed) c->timer_stream = st;
   for (int s0 = 0; s0 < S; s0 += c->persist_chunk) {
@@ -560,7 +577,7 @@ static int run_persist(river_ctx* c, const DecodeArgs& a, int S, int mode, hipSt
     b.exit_out = a.exit_out ? a.exit_out + (size_t)s0 * B : nullptr;
     b.sim_out = a.sim_out ? a.sim_out + (size_t)s0 * B * L : nullptr;
     hipError_t e = river_launch_fill(bar, (int64_t)kBarWords * 4, 0, st);
-    if (e == hipSuccess) e = river_launch_fill(c->scratch + c->sl.amax, (int64_t)2 * B * 8, 0, st);
+    if (e == hipSuccess) e = river_launch_fill(a.amax, (int64_t)2 * B * 8, 0, st);
     if (e != hipSuccess) return hip_fail(e, "barrier/argmax reset");
     if (timed) timer_hook(c, TOP_PERSIST, 0);
     const bool long_ctx = (int64_t)c->pos_host[0] + s0 + n - 1 >= kPersistLongCtx;
@@ -581,7 +598,7 @@ static hipError_t step_layers(river_ctx* c, const DecodeArgs& a, int mode, hipSt
 
 static int run_steps(river_ctx* c, const DecodeArgs& a, int S, int mode, hipStream_t st) {
   if (c->persist_fn[mode] && (c->timer_op < 0 || c->timer_op == TOP_PERSIST))
-    return run_persist(c, a, S, mode, st);
+    return run_persist(c, a, S, mode, st, (unsigned*)(c->scratch + c->sl.bar));
   hipError_t e = river_launch_begin(a, st);
   if (e != hipSuccess) return hip_fail(e, "begin launch");
   if (c->timer_op >= 0) {  // timed: direct launches with events around the chosen op
@@ -726,6 +743,30 @@ int river_export_river(river_ctx* c, int32_t layer, int32_t which, uint8_t* pack
   const f16* s = (const f16*)(base + c->rl.off_s[m]) + (uint64_t)row0[which] * w4_row_scales(K, d.group);
   hipError_t e = river_launch_export(p, s, Ns[which], K, d.group, packed, scales, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "export launch");
+  return RIVER_OK;
+}
+
+int river_kv_write_counts(river_ctx* c, uint8_t* cnt, void* stream) {
+  if (!c || !cnt) return fail(RIVER_EINVAL, "NULL argument");
+#ifdef RIVER_DEBUG_KV_COUNT
+  const Dims& d = c->dm;
+  hipError_t e = river_launch_kv_slot_counts((const uint32_t*)(c->scratch + c->sl.kvcnt), d.L, d.B, d.Hkv,
+                                             d.Tmax, d.D, cnt, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv count launch");
+  return RIVER_OK;
+#else
+  (void)stream;
+  return fail(RIVER_EINVAL, "KV write counting needs the library built with RIVER_DEBUG_KV_COUNT");
+#endif
+}
+
+int river_kv_counting(int32_t* enabled) {
+  if (!enabled) return fail(RIVER_EINVAL, "NULL argument");
+#ifdef RIVER_DEBUG_KV_COUNT
+  *enabled = 1;
+#else
+  *enabled = 0;
+#endif
   return RIVER_OK;
 }
 

@@ -215,6 +215,8 @@ RIVER_DEV void attn_split(const DecodeArgs& a, int layer, int s, int kvh, int b,
           __hip_atomic_store((g_u64*)(Kb + (size_t)pos * D + d0) + j, k2[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store((g_u64*)(Vb + (size_t)pos * D + d0) + j, v2[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        kv_count(a.kvcnt, a.kv, Kb + (size_t)pos * D + d0, 8);
+        kv_count(a.kvcnt, a.kv, Vb + (size_t)pos * D + d0, 8);
       }
     }
     // scores are scaled by log2(e)/sqrt(D) after the fp32 dot (exact fp16 products)

@@ -313,14 +313,20 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
         }
         dst[i] = r0;
         dst[i + dm.D / 2] = r1;
+        if (head >= dm.H) {
+          kv_count(a.kvcnt, a.kv, dst + i, 1);
+          kv_count(a.kvcnt, a.kv, dst + i + dm.D / 2, 1);
+        }
       }
     } else {
       const int nn = logical_row(OP, tile, c, kBR, dm);
       if (nn < N) {
         const int vi = nn - qk_rows;
         const int kvh = vi / dm.D, i = vi % dm.D;
-        a.kv[((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * (size_t)dm.Tmax * dm.D +
-             (size_t)pos * dm.D + i] = f2h(yv);
+        f16* vd = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * (size_t)dm.Tmax * dm.D +
+                  (size_t)pos * dm.D + i;
+        *vd = f2h(yv);
+        kv_count(a.kvcnt, a.kv, vd, 1);
       }
     }
   } else if (OP == OP_GU) {

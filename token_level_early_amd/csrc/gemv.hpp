@@ -579,6 +579,10 @@ RIVER_DEV void gemv_tile(const DecodeArgs& a, const LayerDev* lwp, const TileIn&
         }
         sth<COH>(dst + i, r0);
         sth<COH>(dst + i + dm.D / 2, r1);
+        if (head >= dm.H) {
+          kv_count(a.kvcnt, a.kv, dst + i, 1);
+          kv_count(a.kvcnt, a.kv, dst + i + dm.D / 2, 1);
+        }
       }
     } else if (t < TR) {
       const int n = logical_row(OP, tile, t, TR, dm);
@@ -588,6 +592,7 @@ RIVER_DEV void gemv_tile(const DecodeArgs& a, const LayerDev* lwp, const TileIn&
         f16* vd = a.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) *
                              (size_t)dm.Tmax * dm.D + (size_t)pos * dm.D;
         sth<COH>(vd + i, f2h(y[t]));
+        kv_count(a.kvcnt, a.kv, vd + i, 1);
       }
     }
   } else if (OP == OP_GU) {

@@ -91,6 +91,7 @@ struct DecodeArgs {
   float* sim_out;        // [S][B][L] or null
   float* logits;         // [B][V] or null (single step only)
   float tau;
+  uint32_t* kvcnt;       // debug build only: per-element KV write counters (KV layout), else null
 };
 
 static constexpr int kMaxRed = 8192;
@@ -130,4 +131,17 @@ struct PfArgs {
   int* err;
   f16* kv;
   const float2* rope;
+  uint32_t* kvcnt;  // debug build only (see DecodeArgs::kvcnt)
 };
+
+// Debug build (RIVER_DEBUG_KV_COUNT): one 32-bit counter per element of the shared KV cache,
+// at the element's own index, incremented by every store of that element; river_kv_write_counts
+// reduces them to writes per (layer, row, position) slot. Release builds compile this away.
+#ifdef RIVER_DEBUG_KV_COUNT
+RIVER_DEV void kv_count(uint32_t* cnt, const f16* kv, const f16* dst, int n) {
+  for (int i = 0; i < n; ++i)
+    __hip_atomic_fetch_add(cnt + (dst - kv) + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#else
+RIVER_DEV void kv_count(uint32_t*, const f16*, const f16*, int) {}
+#endif

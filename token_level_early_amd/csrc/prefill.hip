@@ -220,6 +220,8 @@ __global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
                            (size_t)dm.Tmax * dm.D + (size_t)t * dm.D;
       kd[i] = r0;
       kd[i + half] = r1;
+      kv_count(p.kvcnt, p.kv, kd + i, 1);
+      kv_count(p.kvcnt, p.kv, kd + i + half, 1);
     }
   }
   const int nv = dm.Hkv * dm.D;
@@ -228,6 +230,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
     f16* vd = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) *
                          (size_t)dm.Tmax * dm.D + (size_t)t * dm.D;
     vd[i] = row[(dm.H + dm.Hkv) * dm.D + idx];
+    kv_count(p.kvcnt, p.kv, vd + i, 1);
   }
 }
 

@@ -115,3 +115,35 @@ hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st)
                      (uint32_t*)p, n, v);
   return hipGetLastError();
 }
+
+// Writes per KV slot from the debug build's per-element counters (same index as the cache
+// [L][2][B][Hkv][Tmax][D]): out[l][b][t] = the common count of the slot's 2*Hkv*D elements, or
+// 255 when they differ (part of the slot written more often than the rest). Counts cap at 254.
+__global__ __launch_bounds__(kBlock) void k_kv_slot_counts(const uint32_t* __restrict__ cnt, int L, int B,
+                                                           int Hkv, int Tmax, int D, uint8_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (idx >= (int64_t)L * B * Tmax) return;
+  const int t = (int)(idx % Tmax);
+  const int b = (int)((idx / Tmax) % B);
+  const int l = (int)(idx / ((int64_t)Tmax * B));
+  uint32_t first = 0;
+  bool same = true;
+  for (int kv = 0; kv < 2; ++kv)
+    for (int h = 0; h < Hkv; ++h) {
+      const uint32_t* p = cnt + (((((int64_t)l * 2 + kv) * B + b) * Hkv + h) * Tmax + t) * D;
+      for (int i = 0; i < D; ++i) {
+        if (kv == 0 && h == 0 && i == 0) first = p[0];
+        same &= (p[i] == first);
+      }
+    }
+  out[idx] = same ? (uint8_t)(first < 254u ? first : 254u) : (uint8_t)255;
+}
+
+hipError_t river_launch_kv_slot_counts(const uint32_t* cnt, int L, int B, int Hkv, int Tmax, int D,
+                                       uint8_t* out, hipStream_t st) {
+  const int64_t n = (int64_t)L * B * Tmax;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_kv_slot_counts, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                     cnt, L, B, Hkv, Tmax, D, out);
+  return hipGetLastError();
+}

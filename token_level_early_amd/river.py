@@ -12,6 +12,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libriver.so")
+# the same library built with per-element KV write counters (RIVER_DEBUG_KV_COUNT; tests only)
+LIB_KVCOUNT_PATH = os.path.join(_HERE, "libriver_kvcount.so")
 
 RIVER_OK, RIVER_EINVAL, RIVER_ENOMEM, RIVER_ERANGE, RIVER_EHIP, RIVER_EDEVICE = 0, -1, -2, -3, -4, -5
 
@@ -49,17 +51,17 @@ class KVDesc(ctypes.Structure):
                 ("elem_bytes", ctypes.c_int32), ("total_bytes", ctypes.c_uint64)]
 
 
-_lib = None
+_libs = {}
 
 
-def load():
-    """Open libriver.so (raises if it is missing: there is no fallback path)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
-    lib = ctypes.CDLL(LIB_PATH)
+def load(path=LIB_PATH):
+    """Open libriver.so, or another build of it (raises if it is missing: there is no
+    fallback path)."""
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
     P, I32, F32, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     sig = {
         "river_kv_layout": [P(Config), P(KVDesc)],
@@ -77,6 +79,8 @@ def load():
         "river_decode_backbone_steps": [VP, VP, I32, VP, VP],
         "river_timer_arm": [VP, I32, I32],
         "river_timer_read": [VP, P(F32), P(I32)],
+        "river_kv_write_counts": [VP, VP, VP],
+        "river_kv_counting": [P(I32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -84,13 +88,13 @@ def load():
         fn.restype = ctypes.c_int
     lib.river_last_error.argtypes = []
     lib.river_last_error.restype = ctypes.c_char_p
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
-def _check(rc):
+def _check(rc, lib=None):
     if rc != RIVER_OK:
-        raise RiverError(rc, load().river_last_error().decode())
+        raise RiverError(rc, (lib or load()).river_last_error().decode())
 
 
 def make_config(c, max_seq, max_prefill=None, batch=1):
@@ -126,14 +130,18 @@ class River:
     """One context: the borrowed fp16 backbone (torch tensors on the GPU), and torch-owned
     KV cache, river and scratch buffers sized by the library."""
 
-    def __init__(self, c, weights, max_seq, max_prefill=None, batch=1, device="cuda"):
-        self.lib = load()
+    def __init__(self, c, weights, max_seq, max_prefill=None, batch=1, device="cuda",
+                 lib_path=LIB_PATH):
+        self.lib = load(lib_path)
         self.c = dict(c)
         self.cfg = make_config(c, max_seq, max_prefill, batch)
         self.B = batch
         self.w = weights
         self.kvdesc = kv_layout(self.cfg)
-        rb, sb = workspace_bytes(self.cfg)
+        r_, s_ = ctypes.c_uint64(), ctypes.c_uint64()
+        self._chk(self.lib.river_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(r_),
+                                                 ctypes.byref(s_)))
+        rb, sb = r_.value, s_.value
         dev = torch.device(device)
         self.kv = torch.zeros(self.kvdesc.total_bytes // 2, dtype=torch.float16, device=dev)
         self.river_buf = torch.empty(rb, dtype=torch.uint8, device=dev)
@@ -150,14 +158,17 @@ class River:
                           final_norm=weights["final_norm"].data_ptr(),
                           layers=ctypes.cast(self._lw, ctypes.POINTER(LayerWeights)))
         ctx = ctypes.c_void_p()
-        _check(self.lib.river_init(ctypes.byref(self.cfg), ctypes.byref(self._w), _ptr(self.kv),
+        self._chk(self.lib.river_init(ctypes.byref(self.cfg), ctypes.byref(self._w), _ptr(self.kv),
                                    _ptr(self.river_buf), _ptr(self.scratch), _stream(),
                                    ctypes.byref(ctx)))
         self.ctx = ctx
 
+    def _chk(self, rc):
+        _check(rc, self.lib)
+
     def close(self):
         if self.ctx:
-            _check(self.lib.river_destroy(self.ctx))
+            self._chk(self.lib.river_destroy(self.ctx))
             self.ctx = None
 
     def __del__(self):
@@ -173,13 +184,13 @@ class River:
 
     def positions(self):
         arr = (ctypes.c_int32 * self.B)()
-        _check(self.lib.river_positions(self.ctx, arr))
+        self._chk(self.lib.river_positions(self.ctx, arr))
         return list(arr)
 
     def decode_path(self):
         """"persistent" or "per_op": the kernels that serve this context's decode calls."""
         v = ctypes.c_int32()
-        _check(self.lib.river_decode_path(self.ctx, ctypes.byref(v)))
+        self._chk(self.lib.river_decode_path(self.ctx, ctypes.byref(v)))
         return "persistent" if v.value else "per_op"
 
     def device_status(self):
@@ -194,7 +205,7 @@ class River:
         lg = torch.empty(B, self.c["V"], dtype=torch.float32, device=dev) if logits else None
         se = torch.empty(B, dtype=torch.int32, device=dev)
         ms = torch.empty(B, self.c["L"], dtype=torch.float32, device=dev) if min_sim else None
-        _check(self.lib.river_prefill(self.ctx, _ptr(tokens), P, int(prefill_exit), float(tau),
+        self._chk(self.lib.river_prefill(self.ctx, _ptr(tokens), P, int(prefill_exit), float(tau),
                                       _ptr(nt), _ptr(lg), _ptr(se), _ptr(ms), _stream()))
         return {"tokens": nt, "logits": lg, "seq_exit": se, "min_sim": ms}
 
@@ -206,7 +217,7 @@ class River:
         ex = torch.empty(self.B, dtype=torch.int32, device=dev)
         lg = torch.empty(self.B, self.c["V"], dtype=torch.float32, device=dev) if logits else None
         sm = torch.empty(self.B, self.c["L"], dtype=torch.float32, device=dev) if sim else None
-        _check(self.lib.river_decode_step(self.ctx, _ptr(tok_in), _ptr(fe), float(tau), _ptr(out),
+        self._chk(self.lib.river_decode_step(self.ctx, _ptr(tok_in), _ptr(fe), float(tau), _ptr(out),
                                           _ptr(lg), _ptr(ex), _ptr(sm), _stream()))
         return {"tokens": out, "logits": lg, "exit_layer": ex, "sim": sm}
 
@@ -218,7 +229,7 @@ class River:
             S = sched.shape[0]
         if tok_out is None:
             tok_out = torch.empty(S, self.B, dtype=torch.int32, device=dev)
-        _check(self.lib.river_decode_steps(self.ctx, _ptr(tok_in), _ptr(sched), int(S), float(tau),
+        self._chk(self.lib.river_decode_steps(self.ctx, _ptr(tok_in), _ptr(sched), int(S), float(tau),
                                            _ptr(tok_out), _ptr(exit_layer), _ptr(sim), _stream()))
         return tok_out
 
@@ -226,20 +237,20 @@ class River:
         """S full-depth fp16 steps (backbone only, no exit test)."""
         if tok_out is None:
             tok_out = torch.empty(S, self.B, dtype=torch.int32, device=tok_in.device)
-        _check(self.lib.river_decode_backbone_steps(self.ctx, _ptr(tok_in), int(S), _ptr(tok_out),
+        self._chk(self.lib.river_decode_backbone_steps(self.ctx, _ptr(tok_in), int(S), _ptr(tok_out),
                                                     _stream()))
         return tok_out
 
     TIMER_OPS = {"qkv": 0, "attn": 1, "o": 2, "gu": 3, "down": 4, "lm": 5, "persist": 6}
 
     def timer_arm(self, op, max_launches):
-        _check(self.lib.river_timer_arm(self.ctx, self.TIMER_OPS[op], int(max_launches)))
+        self._chk(self.lib.river_timer_arm(self.ctx, self.TIMER_OPS[op], int(max_launches)))
 
     def timer_read(self, max_launches):
         """Per-launch durations (ms) of the armed op, in launch order."""
         buf = (ctypes.c_float * max_launches)()
         n = ctypes.c_int32(max_launches)
-        _check(self.lib.river_timer_read(self.ctx, buf, ctypes.byref(n)))
+        self._chk(self.lib.river_timer_read(self.ctx, buf, ctypes.byref(n)))
         return list(buf[: n.value])
 
     def export_river(self, layer, which):
@@ -251,13 +262,22 @@ class River:
         N, K = shapes[MATS[which]]
         packed = torch.empty(N, (K + 1) // 2, dtype=torch.uint8, device=self.kv.device)
         scales = torch.empty(N, math.ceil(K / c["group"]), dtype=torch.int16, device=self.kv.device)
-        _check(self.lib.river_export_river(self.ctx, int(layer), int(which), _ptr(packed),
+        self._chk(self.lib.river_export_river(self.ctx, int(layer), int(which), _ptr(packed),
                                            _ptr(scales), _stream()))
         return packed, scales.view(torch.float16)
+
+    def kv_write_counts(self):
+        """Writes per shared-cache slot, uint8 [L][B][max_seq] (255: the slot's elements were
+        written unequal numbers of times). Needs the library built with RIVER_DEBUG_KV_COUNT."""
+        c = self.c
+        out = torch.empty(c["L"], self.B, int(self.kvdesc.dims[4]), dtype=torch.uint8,
+                          device=self.kv.device)
+        self._chk(self.lib.river_kv_write_counts(self.ctx, _ptr(out), _stream()))
+        return out
 
     def hidden(self):
         """Residual stream of the last decode step: [L+1][B][d] fp16."""
         c = self.c
         out = torch.empty(c["L"] + 1, self.B, c["d"], dtype=torch.float16, device=self.kv.device)
-        _check(self.lib.river_debug_hidden(self.ctx, _ptr(out), _stream()))
+        self._chk(self.lib.river_debug_hidden(self.ctx, _ptr(out), _stream()))
         return out
