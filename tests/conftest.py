@@ -32,14 +32,33 @@ def decode_path(request):
         os.environ["RIVER_PERSIST"] = old
 
 
+_NEAR = {"checked": 0, "near": 0}
+
+
 @pytest.fixture(autouse=True)
 def near_tie_budget():
-    """Counts the greedy-token comparisons a test makes (tests/_util.top1_checked) and fails the
-    test when more than MAX_NEAR_TIE_FRAC of them were near ties (not compared)."""
+    """Counts the greedy-token comparisons a test makes (tests/_util.top1_checked). A test fails
+    when more than max(2, MAX_NEAR_TIE_FRAC of them) were near ties (not compared: greedy decoding
+    of a random-weight model often repeats a token, so one near tie can recur on the next
+    steps); the session's totals are reported at the end and bounded by the same fraction."""
     from tests import _util
     _util.TOP1["checked"] = _util.TOP1["near"] = 0
     yield
     n, near = _util.TOP1["checked"], _util.TOP1["near"]
+    _NEAR["checked"] += n
+    _NEAR["near"] += near
     if n:
         print(f"top-1 comparisons: {n}, near ties (not compared): {near}")
-    assert near <= max(1, int(_util.MAX_NEAR_TIE_FRAC * n)), f"{near} near-tied steps of {n}"
+    assert near <= max(2, int(_util.MAX_NEAR_TIE_FRAC * n)), f"{near} near-tied steps of {n}"
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if _NEAR["checked"]:
+        terminalreporter.write_line(f"greedy top-1 comparisons: {_NEAR['checked']}, near ties not "
+                                    f"compared: {_NEAR['near']}")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    from tests import _util
+    if _NEAR["checked"] >= 20 and _NEAR["near"] > _util.MAX_NEAR_TIE_FRAC * _NEAR["checked"]:
+        session.exitstatus = 1
