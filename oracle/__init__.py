@@ -12,6 +12,9 @@ citations and the list of readings taken where the pages leave a step open.
 from .river_oracle import (  # noqa: F401
     to_f16,
     quantize_w4,
+    quantize_w4_zp,
+    dequantize_w4_zp,
+    pack_codes,
     pack_nibbles,
     unpack_nibbles,
     dequantize_w4,

@@ -43,6 +43,14 @@ Readings taken where the pages are silent:
       s = fp16(fp32(amax/7)); q = clamp(rint(fp32(w/s)), -8, 7) (round half to
       even); s == 0 gives q = 0; dequantised weight q*s is exact.  Stored nibble
       u = q + 8, element 2i in the low nibble of byte i.
+  R5z the zero-point river format (the pages' alternative backends, HQQ and AWQ, store a
+      scale and a zero point per group; their calibration is not reproduced): asymmetric
+      round-to-nearest int4 per group with the range widened to hold 0:
+      lo = min(min w, 0), hi = max(max w, 0) (fp16 values, so hi - lo is exact in fp64),
+      s = fp16(fp32((hi - lo) / 15)); s == 0 gives q = 0 and z = 0; else
+      z = clamp(rint(fp32(-lo / s)), 0, 15) and q = clamp(rint(fp32(w / s)) + z, 0, 15)
+      (round half to even); dequantised weight (q - z)*s is exact.  Stored nibble u = q,
+      element 2i in the low nibble of byte i; zero points one byte per group.
   R6  the seven linear maps of a block are quantised; RMSNorm gains, embedding and
       LM head stay fp16.
   R7  river layer l reads and writes the same KV[l] as backbone layer l.
@@ -112,6 +120,54 @@ def quantize_w4(W16, group):
         q[:, lo:hi] = np.clip(r, -8, 7).astype(np.int8)
         scales[:, j] = s16
     return q, scales
+
+
+def quantize_w4_zp(W16, group):
+    """Asymmetric int4 with an integer zero point per group (reading R5z): codes q[N][K] in
+    [0, 15] (uint8), fp16 scales s[N][ceil(K/group)], zero points z[N][ceil(K/group)] (uint8)."""
+    W = np.asarray(W16, dtype=F16).astype(F32)
+    N, K = W.shape
+    ng = (K + group - 1) // group
+    q = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, ng), dtype=F16)
+    zeros = np.zeros((N, ng), dtype=np.uint8)
+    for j in range(ng):
+        c0, c1 = j * group, min((j + 1) * group, K)
+        blk = W[:, c0:c1]
+        lo = np.minimum(blk.min(axis=1), F32(0.0)).astype(F64)
+        hi = np.maximum(blk.max(axis=1), F32(0.0)).astype(F64)
+        s16 = ((hi - lo) / 15.0).astype(F32).astype(F16)   # exact range, fp32 then fp16 rounding
+        s32 = s16.astype(F32)
+        zero = s32 == 0
+        denom = np.where(zero, F32(1.0), s32).astype(F32)
+        z = np.clip(np.rint((-lo).astype(F32) / denom), 0, 15).astype(F32)   # fp32 divide, RNE
+        r = np.rint(blk / denom[:, None]).astype(F32) + z[:, None]
+        r[zero, :] = 0
+        z[zero] = 0
+        q[:, c0:c1] = np.clip(r, 0, 15).astype(np.uint8)
+        scales[:, j] = s16
+        zeros[:, j] = z.astype(np.uint8)
+    return q, scales, zeros
+
+
+def dequantize_w4_zp(q, scales, zeros, group):
+    """Zero-point river weight W^[n][k] = (q[n][k] - z[n][k // group]) * s[n][k // group], exact
+    in fp64."""
+    q = np.asarray(q)
+    N, K = q.shape
+    s = np.repeat(np.asarray(scales).astype(F64), group, axis=1)[:, :K]
+    z = np.repeat(np.asarray(zeros).astype(F64), group, axis=1)[:, :K]
+    return (q.astype(F64) - z) * s
+
+
+def pack_codes(u):
+    """Unsigned 4-bit codes u[N][K] packed two per byte, element 2i in the low nibble of byte i
+    (odd K pads a 0 nibble): the zero-point format's code layout."""
+    u = np.asarray(u, dtype=np.uint8)
+    N, K = u.shape
+    if K % 2:
+        u = np.concatenate([u, np.zeros((N, 1), np.uint8)], axis=1)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
 
 
 def pack_nibbles(q):
@@ -329,7 +385,8 @@ class RiverOracle:
     weights: dict of fp16 numpy arrays: embed [V][d], lm_head [V][d] or None (tied to
     embed), final_norm [d], layers: list of L dicts with attn_norm, wq, wk, wv, wo,
     mlp_norm, w_gate, w_up, w_down.
-    cfg keys: L, d, H, Hkv, D, F, V, eps, theta, group, entry (E_min).
+    cfg keys: L, d, H, Hkv, D, F, V, eps, theta, group, entry (E_min), and optionally
+    zero_point (True: the river uses the zero-point format of reading R5z).
     ``layers`` restricts which layers are materialised (for per-layer slices of a
     large model); the others must not be run. ``river_layers`` (default: ``layers``)
     restricts the river copies separately, so a run whose exit layers are known ahead
@@ -349,14 +406,20 @@ class RiverOracle:
         for i in idx:
             lw = weights["layers"][i]
             self.bb[i] = {m: np.asarray(lw[m]).astype(F64) for m in _MATS}
+        zp = bool(self.cfg.get("zero_point", False))  # reading R5z instead of R5
         for i in ridx:
             lw = weights["layers"][i]
             self.rv[i] = {}
             self.qcodes[i] = {}
             for m in _MATS:
-                q, s = quantize_w4(lw[m], cfg["group"])
-                self.qcodes[i][m] = (q, s)
-                self.rv[i][m] = dequantize_w4(q, s, cfg["group"])
+                if zp:
+                    q, s, z = quantize_w4_zp(lw[m], cfg["group"])
+                    self.qcodes[i][m] = (q, s, z)
+                    self.rv[i][m] = dequantize_w4_zp(q, s, z, cfg["group"])
+                else:
+                    q, s = quantize_w4(lw[m], cfg["group"])
+                    self.qcodes[i][m] = (q, s)
+                    self.rv[i][m] = dequantize_w4(q, s, cfg["group"])
         self.embed16 = np.asarray(weights["embed"], dtype=F16)
         head = weights.get("lm_head")
         self.head16 = self.embed16 if head is None else np.asarray(head, dtype=F16)

@@ -125,3 +125,30 @@ def to_numpy(w):
     out["layers"] = [None if lw is None else {k: cv(v) for k, v in lw.items()}
                      for lw in w["layers"]]
     return out
+
+
+def representable_weights_zp(c, seed=0, device="cpu", exp=-8):
+    """Weights that zero-point int4 group quantisation reproduces exactly: in every group the
+    entries are (q - z0) * 2^exp with integer codes q in [0, 15], both q = 0 and q = 15 present,
+    and one zero point z0 in [0, 15] per group, so the widened range is 15 * 2^exp and the
+    group's scale is exactly 2^exp. Embedding/LM head/norms as in ``weights``."""
+    out = weights(c, seed=seed, device=device)
+    g = c["group"]
+    shapes = weight_shapes(c)
+    for l, lw in enumerate(out["layers"]):
+        for ti, m in enumerate(_MATS):
+            N, K = shapes[m]
+            gen = _gen(device, c.get("cfg_id", 0), 4, l, ti + 1, seed)
+            q = torch.randint(0, 16, (N, K), generator=gen, device=device, dtype=torch.int32)
+            ng = (K + g - 1) // g
+            z0 = torch.randint(0, 16, (N, ng), generator=gen, device=device, dtype=torch.int32)
+            rows = torch.arange(N, device=device)
+            for j in range(ng):
+                w = min(g, K - j * g)
+                c0 = j * g + torch.randint(0, w, (N,), generator=gen, device=device)
+                c1 = j * g + (c0 - j * g + 1 + torch.randint(0, w - 1, (N,), generator=gen, device=device)) % w
+                q[rows, c0] = 0
+                q[rows, c1] = 15
+            z = torch.repeat_interleave(z0, g, dim=1)[:, :K]
+            lw[m] = ((q - z).to(torch.float32) * (2.0 ** exp)).to(torch.float16)
+    return out
