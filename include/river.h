@@ -180,6 +180,23 @@ int river_decode_steps(river_ctx* ctx, const int32_t* tok_in, const int32_t* sch
                        float tau, int32_t* tok_out, int32_t* exit_layer, float* sim,
                        void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): river_decode_steps with the persistent kernel's
+ * cross-workgroup exchange buffers (tagged activations, attention split partials, tag counters,
+ * grid-barrier words, argmax keys) in a fixed device array of the library (4 MiB, one per GPU,
+ * held until the process ends) instead of the context's scratch. It calls no allocating
+ * routine. Same arguments, semantics and results (bit for bit) as river_decode_steps. Every
+ * call on a GPU shares that GPU's array and clears the part it uses before its launches, so
+ * calls that overlap on one GPU (any contexts, any streams) race and must be serialised by
+ * the caller. Errors: as river_decode_steps; RIVER_EINVAL when the context does not decode on
+ * the persistent kernel (batch 1, a supported shape, RIVER_PERSIST not "0") or a timer is
+ * armed; RIVER_ENOMEM when the model's exchange buffers exceed the array (the message gives
+ * both sizes; the 8B shape needs about 3.3 MB); RIVER_EHIP when the array's device address
+ * could not be looked up at river_init. */
+int river_decode_steps_static(river_ctx* ctx, const int32_t* tok_in, const int32_t* sched, int32_t S,
+                              float tau, int32_t* tok_out, int32_t* exit_layer, float* sim,
+                              void* stream);
+
 /* Full-depth fp16 decode of S steps: every layer on the backbone block, no exit test, no river
  * (the plain decoder the early exit is measured against). Same token I/O as river_decode_steps
  * with every forced exit = L; writes the same KV slots. Errors as river_decode_steps. */

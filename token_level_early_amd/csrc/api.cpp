@@ -31,6 +31,7 @@ const void* river_persist_fn(const Dims& dm, int mode, int long_ctx);
 int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
                                 unsigned* bar, hipStream_t st);
+hipError_t river_static_scratch(void** ptr, size_t* bytes);
 hipError_t river_decode_layers_batched(const DecodeArgs& a, f16* xn, int mode, hipStream_t st,
                                        void (*timer)(void*, int, int), void* tctx, int top);
 hipError_t river_launch_head_batched(const DecodeArgs& a, f16* xn, hipStream_t st,
@@ -214,6 +215,33 @@ ScratchLayout scratch_layout(const Dims& d) {
   return s;
 }
 
+// The persistent kernel's cross-workgroup exchange buffers, laid out from offset 0 (the
+// static-scratch decode puts them in the library's fixed device array).
+struct ExchangeLayout {
+  uint64_t amax, bar, t_qkv, t_o, t_a2, t_hmid, t_hs, t_part, tagc, total;
+};
+
+ExchangeLayout exchange_layout(const Dims& d, int smax) {
+  ExchangeLayout x{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  x.amax = take((uint64_t)2 * d.B * 8);
+  x.bar = take((uint64_t)kBarWords * 4);
+  x.t_qkv = take((uint64_t)d.nqkv * 4);
+  x.t_o = take((uint64_t)2 * d.hd * 4);
+  x.t_a2 = take((uint64_t)d.F * 4);
+  x.t_hmid = take((uint64_t)d.L * d.d * 4);
+  x.t_hs = take((uint64_t)(d.L + 1) * d.d * 4);
+  x.t_part = take((uint64_t)d.H * smax * (d.D + 2) * 8);
+  x.tagc = take(8);
+  x.total = off;
+  return x;
+}
+
 }  // namespace
 
 struct river_ctx {
@@ -248,6 +276,10 @@ struct river_ctx {
   const void* persist_fn_long[2] = {nullptr, nullptr};  // launches reaching kPersistLongCtx
   int persist_nwg[2] = {0, 0};
   int persist_chunk = 8;
+  // this GPU's fixed device scratch (river_decode_steps_static); null if the lookup failed
+  void* static_scratch = nullptr;
+  size_t static_bytes = 0;
+  std::string static_err;
 };
 
 static DecodeArgs base_args(const river_ctx* c) {
@@ -449,6 +481,12 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   }
   const char* pc = getenv("RIVER_PERSIST_CHUNK");
   if (pc && atoi(pc) > 0) c->persist_chunk = atoi(pc);
+  // device address of the fixed scratch of river_decode_steps_static (once per device)
+  e = river_static_scratch(&c->static_scratch, &c->static_bytes);
+  if (e != hipSuccess) {
+    c->static_scratch = nullptr;
+    c->static_err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+  }
   *out = c;
   return RIVER_OK;
 }
@@ -653,6 +691,50 @@ int river_decode_steps(river_ctx* c, const int32_t* tok_in, const int32_t* sched
   a.logits = nullptr;
   a.tau = sched ? 0.f : tau;
   int rc = run_steps(c, a, S, 0, (hipStream_t)stream);
+  if (rc) return rc;
+  for (auto& v : c->pos_host) v += S;
+  return RIVER_OK;
+}
+
+int river_decode_steps_static(river_ctx* c, const int32_t* tok_in, const int32_t* sched, int32_t S,
+                              float tau, int32_t* tok_out, int32_t* exit_layer, float* sim, void* stream) {
+  if (!c || !tok_in || !tok_out) return fail(RIVER_EINVAL, "NULL argument");
+  if (S < 1) return fail(RIVER_EINVAL, "S must be >= 1");
+  if (!sched && std::isnan(tau)) return fail(RIVER_EINVAL, "tau is NaN");
+  if (!c->persist_fn[0])
+    return fail(RIVER_EINVAL, "the static-scratch decode runs on the persistent kernel only (batch 1, "
+                              "supported shapes, RIVER_PERSIST not 0)");
+  if (c->timer_op >= 0) return fail(RIVER_EINVAL, "timer armed: use river_decode_steps");
+  if (!c->static_scratch) return fail(RIVER_EHIP, c->static_err);
+  for (int32_t p : c->pos_host)
+    if ((int64_t)p + S > c->dm.Tmax) return fail(RIVER_ERANGE, "position would pass max_seq");
+  const ExchangeLayout x = exchange_layout(c->dm, c->sl.smax);
+  if (x.total > c->static_bytes)
+    return fail(RIVER_ENOMEM, "this model's exchange buffers need " + std::to_string(x.total) +
+                                  " bytes; the static scratch holds " + std::to_string(c->static_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)c->static_scratch;
+  // the array keeps the last call's contents (possibly another context's): every tag, tag
+  // counter and barrier word starts from zero (tags are never 0, so no stale word matches)
+  hipError_t e = river_launch_fill(base, (int64_t)x.total, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "static scratch reset");
+  DecodeArgs a = base_args(c);
+  a.amax = (unsigned long long*)(base + x.amax);
+  a.t_qkv = (uint32_t*)(base + x.t_qkv);
+  a.t_o = (uint32_t*)(base + x.t_o);
+  a.t_a2 = (uint32_t*)(base + x.t_a2);
+  a.t_hmid = (uint32_t*)(base + x.t_hmid);
+  a.t_hs = (uint32_t*)(base + x.t_hs);
+  a.t_part = (unsigned long long*)(base + x.t_part);
+  a.tagc = (uint32_t*)(base + x.tagc);
+  a.tok_in = tok_in;
+  a.sched = sched;
+  a.tok_out = tok_out;
+  a.exit_out = exit_layer;
+  a.sim_out = sim;
+  a.logits = nullptr;
+  a.tau = sched ? 0.f : tau;
+  int rc = run_persist(c, a, S, 0, st, (unsigned*)(base + x.bar));
   if (rc) return rc;
   for (auto& v : c->pos_host) v += S;
   return RIVER_OK;

@@ -21,6 +21,7 @@
 // values); activations cross XCDs through write-through stores and coherent loads. The grid
 // barrier spins with a bound: a workgroup that waits too long raises an abort flag, after
 // which every barrier returns at once, so every wave reaches the end of the kernel.
+#include <mutex>
 #include <type_traits>
 
 #include "gemv.hpp"
@@ -845,4 +846,38 @@ hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int 
   unsigned* br = bar;
   void* args[] = {&aa, &SS, &sp, &br};
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kPB), args, 0, st);
+}
+
+// ---------------------------------------------------------------------------------------
+// Fixed device scratch of river_decode_steps_static, for callers that cannot allocate device
+// memory (code under graph capture, serving loops, harnesses that forbid it): the persistent
+// kernel's cross-workgroup exchange buffers (tagged activations, split partials, tag counters,
+// grid-barrier words, argmax keys) live in this file-scope array instead of the context's
+// scratch. Every GPU the library runs on holds its own copy until the process ends. In host
+// code the array's name is only a stand-in for the symbol: kernels get the device address
+// that river_static_scratch looks up.
+// ---------------------------------------------------------------------------------------
+static constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address and size of the current GPU's copy of `scratch`; looked up once per device
+// (with that device current) and remembered.
+hipError_t river_static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
 }

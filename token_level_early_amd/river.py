@@ -71,6 +71,7 @@ def load(path=LIB_PATH):
         "river_prefill": [VP, VP, I32, I32, F32, VP, VP, VP, VP, VP],
         "river_decode_step": [VP, VP, VP, F32, VP, VP, VP, VP, VP],
         "river_decode_steps": [VP, VP, VP, I32, F32, VP, VP, VP, VP],
+        "river_decode_steps_static": [VP, VP, VP, I32, F32, VP, VP, VP, VP],
         "river_positions": [VP, P(I32)],
         "river_decode_path": [VP, P(I32)],
         "river_device_status": [VP, VP],
@@ -231,6 +232,19 @@ class River:
             tok_out = torch.empty(S, self.B, dtype=torch.int32, device=dev)
         self._chk(self.lib.river_decode_steps(self.ctx, _ptr(tok_in), _ptr(sched), int(S), float(tau),
                                            _ptr(tok_out), _ptr(exit_layer), _ptr(sim), _stream()))
+        return tok_out
+
+    def decode_steps_static(self, tok_in, sched=None, S=None, tau=float("nan"), tok_out=None,
+                            exit_layer=None, sim=None):
+        """decode_steps with the exchange buffers in the library's fixed device array
+        (river_decode_steps_static: no allocation inside the call)."""
+        dev = tok_in.device
+        if sched is not None:
+            S = sched.shape[0]
+        if tok_out is None:
+            tok_out = torch.empty(S, self.B, dtype=torch.int32, device=dev)
+        self._chk(self.lib.river_decode_steps_static(self.ctx, _ptr(tok_in), _ptr(sched), int(S), float(tau),
+                                                     _ptr(tok_out), _ptr(exit_layer), _ptr(sim), _stream()))
         return tok_out
 
     def decode_backbone_steps(self, tok_in, S, tok_out=None):
