@@ -71,6 +71,13 @@ typedef struct river_config {
   int32_t max_seq;         /* Tmax: KV positions per row */
   int32_t max_prefill;     /* longest prompt river_prefill accepts (<= max_seq) */
   int32_t entry_layer;     /* E_min in [1, L]: first layer after which an exit is tested */
+  int32_t prefill_chunk;   /* positions per prefill chunk, >= 0 (0: 4096 / max_batch): the prompt
+                              runs layer by layer, each layer in chunks of this many positions of
+                              every row; scratch grows with max_batch * chunk, not max_prefill */
+  int32_t zero_point;      /* river format. 0: symmetric int4, one fp16 scale per group;
+                              1: asymmetric int4, one fp16 scale and one integer zero point per
+                              group (the scale-and-zero storage of the pages' other backends,
+                              HQQ and AWQ: paperlayer appendix A.1; without their calibration) */
 } river_config;
 
 /* Borrowed fp16 backbone weights of one block (device pointers, row-major [out][in]). */
@@ -213,6 +220,22 @@ int river_decode_backbone_steps(river_ctx* ctx, const int32_t* tok_in, int32_t S
 int river_timer_arm(river_ctx* ctx, int32_t op, int32_t max_launches);
 int river_timer_read(river_ctx* ctx, float* ms /* host */, int32_t* n /* host, in/out */);
 
+/* Backbone offloading (paperlayer summary, section 4 "Deployment Efficiency" and appendix A.3:
+ * under-used backbone blocks are moved out of device memory while the exit river stays, which
+ * cuts parameter memory toward that of a static 4-bit model; aitrends offloading paragraph).
+ * river_init accepts every borrowed weight pointer either in device memory or in page-locked
+ * host memory (hipHostMalloc, or a pinned torch tensor) and uses host memory through its
+ * mapped device address: a kernel then reads such a block over the host link, and only when a
+ * row runs that backbone block (the batched kernels skip a weight stream no row needs; the
+ * river, the embedding and the LM head stay wherever the caller put them). Any other pointer
+ * makes river_init fail with RIVER_EINVAL. river_weight_residency (host-only) reports the bytes
+ * of the borrowed weights in device memory and in host memory, and of the river buffer. */
+int river_weight_residency(const river_ctx* ctx, uint64_t* device_bytes /* host */,
+                           uint64_t* host_bytes /* host */, uint64_t* river_bytes /* host */);
+/* How river_init would take the weight pointer p: *placement = 0 device memory, 1 page-locked
+ * host memory; RIVER_EINVAL when river_init would reject it. Host-only (queries the runtime). */
+int river_weight_placement(const void* p, int32_t* placement /* host */);
+
 /* Which kernels serve the decode calls of this context: 1 the persistent decode kernel, 0 the
  * per-op kernels (see river_decode_steps). Host-only. Returns RIVER_EINVAL for NULL. */
 int river_decode_path(const river_ctx* ctx, int32_t* persistent /* host */);
@@ -226,11 +249,14 @@ int river_positions(const river_ctx* ctx, int32_t* pos /* host [B] */);
 int river_device_status(river_ctx* ctx, void* stream);
 
 /* Test support: the river copy of one matrix of one layer (0-based `layer`) in the canonical
- * layout -- packed [N][ceil(K/2)] bytes with element 2i in the low nibble of byte i, nibble =
- * q + 8, and fp16 scales [N][ceil(K/group)]. which: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up,
- * 6 w_down. `packed` and `scales` are device buffers. */
+ * layout -- packed [N][ceil(K/2)] bytes with element 2i in the low nibble of byte i, and fp16
+ * scales [N][ceil(K/group)]. Symmetric format: nibble = q + 8 (q in [-8, 7]), an odd K pads
+ * with 8. Zero-point format: nibble = q (q in [0, 15]), an odd K pads with 0, and `zeros`
+ * receives the zero points [N][ceil(K/group)] (one byte each; it must be NULL for the
+ * symmetric format and non-NULL for the zero-point format). which: 0 wq, 1 wk, 2 wv, 3 wo,
+ * 4 w_gate, 5 w_up, 6 w_down. `packed`, `scales` and `zeros` are device buffers. */
 int river_export_river(river_ctx* ctx, int32_t layer, int32_t which, uint8_t* packed,
-                       uint16_t* scales, void* stream);
+                       uint16_t* scales, uint8_t* zeros, void* stream);
 
 /* Test support: copies the residual stream of the last decode step, fp16 [L+1][B][d]
  * (index 0 = embedding row, index l = output of block l), into the device buffer `dst`. */

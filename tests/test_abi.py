@@ -72,6 +72,7 @@ def test_river_buffer_covers_int4_copy():
     ("max_batch", 17, "max_batch"),
     ("max_batch", 0, "max_batch"),
     ("rms_eps", 0.0, "rms_eps"),
+    ("zero_point", 2, "zero_point"),
 ])
 def test_bad_config_rejected(field, value, msg):
     c = configs.model_cfg(configs.LLAMA_8B)
@@ -109,3 +110,27 @@ def test_kv_write_counting_only_in_the_debug_build():
     assert dbg.river_kv_counting(ctypes.byref(flag)) == 0 and flag.value == 1
     for n in _declared():
         assert hasattr(dbg, n), n
+
+
+def test_prefill_scratch_is_bounded_by_the_chunk():
+    """Prefill keeps the residual stream of every prompt row (2 x B*P*d fp16 plus one fp64
+    similarity per row: the sequence-level exit needs all tokens of a layer before the next) and
+    every other activation only for one chunk of positions: at the 64K-prompt workload the
+    scratch is about 1.6 GB (1.07 GB of it the residual stream) instead of the 8.6 GB a
+    whole-prompt layout needs, and beyond the residual stream it grows with the chunk, not with
+    the prompt."""
+    c = configs.model_cfg(configs.LLAMA_8B)
+    d, hd, F, nqkv = c["d"], c["H"] * c["D"], c["F"], (c["H"] + 2 * c["Hkv"]) * c["D"]
+    P = 65536
+    per_row = 2 * (d + max(d, hd) + hd + nqkv + 2 * F + F)  # chunk activations, bytes per row
+    sizes = {}
+    for chunk in (1024, 4096):
+        cfg = river.make_config(dict(c, prefill_chunk=chunk), P + 64, P)
+        sizes[chunk] = river.workspace_bytes(cfg)[1]
+    resid = 2 * P * d * 2 + P * 8
+    assert abs((sizes[4096] - sizes[1024]) - 3072 * per_row) < 64 * 1024
+    assert resid < sizes[4096] < resid + 4096 * per_row + (64 << 20)
+    assert sizes[4096] < 1.7e9
+    # the default chunk is 4096 positions of one row (4096 / max_batch per row)
+    dflt = river.workspace_bytes(river.make_config(c, P + 64, P))[1]
+    assert dflt == sizes[4096]

@@ -33,3 +33,12 @@ def test_byte_model_matches_hand_derived_per_layer_figures():
     assert round(w16 / 1e6, 2) == 436.22
     assert round(w4 / 1e6, 2) == 112.48
     assert round(bm.op_bytes(c, "lm") / 1e9, 3) == 1.051
+
+
+def test_zero_point_format_adds_one_byte_per_group():
+    """The zero-point river reads one more byte per group: P_l/128 = 1.70 MB per 8B block."""
+    c = configs.model_cfg(configs.LLAMA_8B)
+    cz = configs.model_cfg(configs.LLAMA_8B_ZP)
+    P_l = 218_103_808
+    assert bm.token_bytes(cz, 0, 100) - bm.token_bytes(c, 0, 100) == c["L"] * P_l // 128
+    assert bm.token_bytes(cz, c["L"], 100) == bm.token_bytes(c, c["L"], 100)

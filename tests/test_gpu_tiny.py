@@ -387,3 +387,40 @@ def test_chained_launches_equal_single_steps(tiny, mode, decode_path):
         cur = int(ta[s])
     assert rel_err(ha[:, 0].float().numpy(), o["hs"][:, 0]) <= TOL
     assert rel_err(ka.float().numpy()[:, :, 0], np.stack([kvo.K[:, 0], kvo.V[:, 0]], axis=1)) <= TOL
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_chunked_prefill_matches_whole_prefill_and_oracle(tiny, batch):
+    """Prefill in chunks of 24 positions (64-token prompt: chunks 24, 24 and a ragged 16) gives
+    bit for bit the shared cache, exit layers, similarities and logits of a single-chunk prefill
+    (every output element is the same computation), and matches the oracle, in tau mode where
+    the sequence-level exit needs the similarities of every chunk's tokens."""
+    w, wn, orc = tiny
+    P = 64
+    tau = f32(0.95)
+    toks = synth.prompt(TINY, batch, P, seed=31, device="cuda")
+    runs = []
+    for chunk in (24, 0):
+        c = dict(TINY, prefill_chunk=chunk)
+        rv = river.River(c, w, max_seq=P + 2, max_prefill=P, batch=batch)
+        pre = rv.prefill(toks, prefill_exit=0, tau=tau, logits=True, min_sim=True)
+        torch.cuda.synchronize()
+        runs.append({k: (v.cpu() if v is not None else None) for k, v in pre.items()})
+        runs[-1]["kv"] = rv.kv_view().cpu()
+        rv.close()
+    a, b = runs
+    for k in ("tokens", "logits", "seq_exit", "kv"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(torch.isnan(a["min_sim"]), torch.isnan(b["min_sim"]))
+    kvo = orc.new_kv(batch, P + 2)
+    o = orc.prefill(kvo, toks.cpu().numpy(), tau=tau, gpu_seq_exit=a["seq_exit"].numpy())
+    assert np.array_equal(a["seq_exit"].numpy(), o["seq_exit"])
+    for r in range(batch):
+        assert rel_err(a["logits"][r].numpy(), o["logits"][r]) <= TOL
+        assert top1_checked(int(a["tokens"][r]), o["logits"][r]) is not False
+        fin = ~np.isnan(o["min_sim"][r])
+        assert np.allclose(a["min_sim"][r].numpy()[fin], o["min_sim"][r][fin], atol=2e-3)
+    kv = a["kv"].float().numpy()
+    for l in range(TINY["L"]):
+        assert rel_err(kv[l, 0, :, :, :P], kvo.K[l, :, :, :P]) <= TOL, l
+        assert rel_err(kv[l, 1, :, :, :P], kvo.V[l, :, :, :P]) <= TOL, l

@@ -6,7 +6,8 @@ the fp16 LM head:
 
     B_tok = sum_l [e >= l ? W16 : W4] + L*kv*(pos+1) + L*kv + 2d + 2d + 2*V*d
     W16 = 2*P_l + 4d          (fp16 matrices + two RMSNorm gain vectors)
-    W4  = P_l/2 + 2*P_l/g + 4d (int4 nibbles + one fp16 scale per group + gains)
+    W4  = P_l/2 + 2*P_l/g + 4d (int4 nibbles + one fp16 scale per group + gains), plus P_l/g
+                              (one zero-point byte per group) in the zero-point format
     kv  = 2*Hkv*D*2           (K and V of one position, fp16)
 
 Activation vectors (a few KB per kernel) are not counted.
@@ -19,9 +20,10 @@ def op_params(c):
     return {"qkv": ((H + 2 * Hkv) * D, d), "o": (d, H * D), "gu": (2 * F, d), "down": (d, F)}
 
 
-def matrix_bytes(N, K, river, group):
+def matrix_bytes(N, K, river, group, zero_point=False):
     if river:
-        return N * K // 2 + N * ((K + group - 1) // group) * 2
+        ng = N * ((K + group - 1) // group)
+        return N * K // 2 + ng * 2 + (ng if zero_point else 0)
     return 2 * N * K
 
 
@@ -36,7 +38,7 @@ def op_bytes(c, op, river=False, pos=0):
     if op == "lm":
         return 2 * c["V"] * d + 2 * d
     N, K = op_params(c)[op]
-    b = matrix_bytes(N, K, river, g)
+    b = matrix_bytes(N, K, river, g, c.get("zero_point", False))
     if op == "qkv":
         b += 2 * d + kv
     if op == "gu":
@@ -73,7 +75,8 @@ def batch_step_bytes(c, exits, positions):
     for l in range(1, L + 1):
         for river, used in ((False, any(e >= l for e in exits)), (True, any(e < l for e in exits))):
             if used:
-                total += sum(matrix_bytes(N, K, river, c["group"]) for N, K in op_params(c).values())
+                total += sum(matrix_bytes(N, K, river, c["group"], c.get("zero_point", False))
+                             for N, K in op_params(c).values())
                 total += 4 * d  # attention and MLP norm gains
     for p in positions:
         total += L * kv * (p + 1) + L * kv + 2 * d
@@ -95,7 +98,8 @@ def batch_op_bytes(c, op, exits, layer, positions):
     total = 0
     for river, used in ((False, any(e >= layer for e in exits)), (True, any(e < layer for e in exits))):
         if used:
-            total += matrix_bytes(N, K, river, c["group"]) + (2 * d if op in ("qkv", "gu") else 0)
+            total += (matrix_bytes(N, K, river, c["group"], c.get("zero_point", False))
+                      + (2 * d if op in ("qkv", "gu") else 0))
     if op == "qkv":
         total += kv * len(exits)
     return total

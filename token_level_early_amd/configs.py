@@ -39,10 +39,16 @@ LLAMA_8B_BS16 = dict(LLAMA_8B, name="llama3.1-8b-shape-bs16", cfg_id=3,
 LLAMA_8B_64K = dict(LLAMA_8B, name="llama3.1-8b-shape-64k", cfg_id=4,
                     batch=1, prompt=65536, steps=64, sched=("half", 8, 20))
 
-ALL = {c["name"]: c for c in (TINY, LLAMA_1B, LLAMA_8B, LLAMA_8B_BS16, LLAMA_8B_64K)}
+# The same workloads with the zero-point river format (scale and zero point per group).
+TINY_ZP = dict(TINY, name="tiny-zp", zero_point=True)
+LLAMA_8B_ZP = dict(LLAMA_8B, name="llama3.1-8b-shape-zp", zero_point=True)
+
+ALL = {c["name"]: c for c in (TINY, LLAMA_1B, LLAMA_8B, LLAMA_8B_BS16, LLAMA_8B_64K, TINY_ZP, LLAMA_8B_ZP)}
 
 
 def model_cfg(c):
     """The subset of fields that defines the model (what the oracle and the library need)."""
     keys = ("L", "d", "H", "Hkv", "D", "F", "V", "tied", "eps", "theta", "group", "entry")
-    return {k: c[k] for k in keys}
+    out = {k: c[k] for k in keys}
+    out["zero_point"] = bool(c.get("zero_point", False))
+    return out

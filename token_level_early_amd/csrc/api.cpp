@@ -20,9 +20,10 @@ hipError_t river_launch_head(const DecodeArgs& a, hipStream_t st, void (*timer)(
                              void* tctx, int top);
 int river_gemv_max_wg(const Dims& dm);
 hipError_t river_launch_quantize(const f16* W, int N, int K, int group, uint8_t* out, f16* scales,
-                                 hipStream_t st);
-hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K, int group,
-                               uint8_t* packed, uint16_t* scales, hipStream_t st);
+                                 uint8_t* zeros, hipStream_t st);
+hipError_t river_launch_export(const uint8_t* in, const f16* sin_, const uint8_t* zin, int N, int K,
+                               int group, uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                               hipStream_t st);
 hipError_t river_launch_rope_table(float2* tab, int Tmax, int D, double theta, hipStream_t st);
 hipError_t river_launch_fill(void* p, int64_t bytes, uint32_t v, hipStream_t st);
 hipError_t river_launch_kv_slot_counts(const uint32_t* cnt, int L, int B, int Hkv, int Tmax, int D,
@@ -81,6 +82,8 @@ int check_cfg(const river_config* c) {
     return fail(RIVER_EINVAL, "entry_layer must be in [1, n_layers]");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(RIVER_EINVAL, "rms_eps and rope_theta must be > 0");
   if (c->tied_embeddings != 0 && c->tied_embeddings != 1) return fail(RIVER_EINVAL, "tied_embeddings must be 0 or 1");
+  if (c->zero_point != 0 && c->zero_point != 1) return fail(RIVER_EINVAL, "zero_point must be 0 or 1");
+  if (c->prefill_chunk < 0) return fail(RIVER_EINVAL, "prefill_chunk must be >= 0");
   return RIVER_OK;
 }
 
@@ -99,6 +102,12 @@ Dims make_dims(const river_config* c) {
   d.entry = c->entry_layer;
   d.tied = c->tied_embeddings;
   d.max_prefill = c->max_prefill;
+  d.zp = c->zero_point;
+  {
+    const int def = 4096 / c->max_batch > 0 ? 4096 / c->max_batch : 1;
+    const int want = c->prefill_chunk > 0 ? c->prefill_chunk : def;
+    d.pf_chunk = want < c->max_prefill ? want : c->max_prefill;
+  }
   d.eps = c->rms_eps;
   d.theta = c->rope_theta;
   d.hd = c->n_heads * c->head_dim;
@@ -115,7 +124,7 @@ int attn_smax(const Dims& d) {
 
 // ---- river buffer layout: per layer qkv, o, gu, down (packed), then their scales
 struct RiverLayout {
-  uint64_t off_p[4], off_s[4];
+  uint64_t off_p[4], off_s[4], off_z[4];  // off_z: zero-point format only
   uint64_t layer_bytes;
   int N[4], K[4];
 };
@@ -135,6 +144,10 @@ RiverLayout river_layout(const Dims& d) {
     r.off_s[i] = off;
     off = align256(off + (uint64_t)N[i] * w4_row_scales(K[i], d.group) * 2);
   }
+  for (int i = 0; i < 4; ++i) {
+    r.off_z[i] = off;
+    if (d.zp) off = align256(off + (uint64_t)N[i] * w4_row_scales(K[i], d.group));
+  }
   r.layer_bytes = off;
   return r;
 }
@@ -144,7 +157,7 @@ struct ScratchLayout {
   uint64_t hs, hmid, q, o, a2, qkvr, gu, inv_attn, inv_mlp, route, pos, step, err, red, cnt, pml, pacc, amax,
       layers, rope, bar, xn;
   uint64_t t_qkv, t_o, t_a2, t_hmid, t_hs, t_part, tagc, t_end;  // tagged activations [t_qkv, t_end)
-  uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
+  uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_attn, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t kvcnt;  // debug build: per-element KV write counters (0 bytes otherwise)
   uint64_t total;
@@ -193,16 +206,19 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.xn = take(B * d.d * 2);                // batched decode: normalised block inputs
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
+  // prefill: the residual stream of every prompt row, the rest per chunk of positions
   const uint64_t M = B * d.max_prefill;
+  const uint64_t Mc = B * d.pf_chunk;
   const uint64_t wide = (uint64_t)(d.d > d.hd ? d.d : d.hd);
-  s.pf_hin = take(M * wide * 2);
-  s.pf_hout = take(M * wide * 2);
-  s.pf_hmid = take(M * wide * 2);
-  s.pf_act = take(M * wide * 2);
-  s.pf_qkv = take(M * d.nqkv * 2);
-  s.pf_gu = take(M * 2 * d.F * 2);
-  s.pf_a2 = take(M * d.F * 2);
+  s.pf_hin = take(M * d.d * 2);
+  s.pf_hout = take(M * d.d * 2);
   s.pf_cos = take(M * 8);
+  s.pf_hmid = take(Mc * d.d * 2);
+  s.pf_act = take(Mc * wide * 2);
+  s.pf_attn = take(Mc * d.hd * 2);
+  s.pf_qkv = take(Mc * d.nqkv * 2);
+  s.pf_gu = take(Mc * 2 * d.F * 2);
+  s.pf_a2 = take(Mc * d.F * 2);
   s.pf_route = take(B * 4);
   s.pf_exit = take(B * 4);
   s.pf_minsim = take(B * d.L * 4);
@@ -240,6 +256,38 @@ ExchangeLayout exchange_layout(const Dims& d, int smax) {
   x.tagc = take(8);
   x.total = off;
   return x;
+}
+
+// Device-visible address of a borrowed weight. The backbone may be partly offloaded (paperlayer
+// summary, section 4 "Deployment Efficiency" and appendix A.3: under-used backbone blocks leave
+// device memory while the river stays): device memory is used as is, page-locked host memory
+// (hipHostMalloc, or a pinned torch tensor) through its mapped device address, so a kernel reads
+// such a block over the host link only when some row runs it; any other pointer is rejected
+// here, before a kernel could fault on it.
+int weight_view(const void* p, const std::string& what, const void** out, bool* on_host) {
+  hipPointerAttribute_t at{};
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the query's error must not surface at the next launch check
+    return fail(RIVER_EINVAL, what + ": neither device memory nor page-locked host memory");
+  }
+  if (at.type == hipMemoryTypeDevice && !at.isManaged) {
+    *out = p;
+    *on_host = false;
+    return RIVER_OK;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    void* dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, const_cast<void*>(p), 0);
+    if (e != hipSuccess || !dp) {
+      (void)hipGetLastError();
+      return fail(RIVER_EINVAL, what + ": host memory without a device mapping");
+    }
+    *out = dp;
+    *on_host = true;
+    return RIVER_OK;
+  }
+  return fail(RIVER_EINVAL, what + ": neither device memory nor page-locked host memory");
 }
 
 }  // namespace
@@ -280,6 +328,8 @@ struct river_ctx {
   void* static_scratch = nullptr;
   size_t static_bytes = 0;
   std::string static_err;
+  // parameter bytes of the borrowed weights by placement (backbone offloading), and the river
+  uint64_t w_device_bytes = 0, w_host_bytes = 0, river_bytes = 0;
 };
 
 static DecodeArgs base_args(const river_ctx* c) {
@@ -378,10 +428,58 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   c->kv = (char*)kv;
   c->river = (char*)river_buf;
   c->scratch = (char*)scratch;
-  c->embed = (const f16*)w->embed;
-  c->lm_head = (const f16*)(cfg->tied_embeddings ? w->embed : w->lm_head);
-  c->final_norm = (const f16*)w->final_norm;
   c->pos_host.assign(cfg->max_batch, 0);
+  c->river_bytes = c->rl.layer_bytes * (uint64_t)cfg->n_layers;
+  {  // device-visible weight addresses (device memory, or page-locked host memory)
+    const uint64_t d = cfg->d_model, hd = (uint64_t)cfg->n_heads * cfg->head_dim,
+                   kvd = (uint64_t)cfg->n_kv_heads * cfg->head_dim, F = cfg->d_ffn, V = cfg->vocab;
+    auto view = [&](const void* p, const std::string& what, uint64_t elems, const void** out) {
+      bool host = false;
+      const int r = weight_view(p, what, out, &host);
+      if (r == RIVER_OK) (host ? c->w_host_bytes : c->w_device_bytes) += 2 * elems;
+      return r;
+    };
+    const void *emb = nullptr, *head = nullptr, *fin = nullptr;
+    int r = view(w->embed, "embed", V * d, &emb);
+    if (!r && !cfg->tied_embeddings) r = view(w->lm_head, "lm_head", V * d, &head);
+    if (!r) r = view(w->final_norm, "final_norm", d, &fin);
+    if (r) {
+      delete c;
+      return r;
+    }
+    c->embed = (const f16*)emb;
+    c->lm_head = (const f16*)(cfg->tied_embeddings ? emb : head);
+    c->final_norm = (const f16*)fin;
+    c->layers.resize(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers && !r; ++l) {
+      const river_layer_weights& lw = w->layers[l];
+      LayerDev& ld = c->layers[l];
+      const std::string L = "layer " + std::to_string(l) + " ";
+      const void* v[9] = {};
+      if (!r) r = view(lw.attn_norm, L + "attn_norm", d, &v[0]);
+      if (!r) r = view(lw.wq, L + "wq", hd * d, &v[1]);
+      if (!r) r = view(lw.wk, L + "wk", kvd * d, &v[2]);
+      if (!r) r = view(lw.wv, L + "wv", kvd * d, &v[3]);
+      if (!r) r = view(lw.wo, L + "wo", d * hd, &v[4]);
+      if (!r) r = view(lw.mlp_norm, L + "mlp_norm", d, &v[5]);
+      if (!r) r = view(lw.w_gate, L + "w_gate", F * d, &v[6]);
+      if (!r) r = view(lw.w_up, L + "w_up", F * d, &v[7]);
+      if (!r) r = view(lw.w_down, L + "w_down", d * F, &v[8]);
+      ld.attn_norm = (const f16*)v[0];
+      ld.wq = (const f16*)v[1];
+      ld.wk = (const f16*)v[2];
+      ld.wv = (const f16*)v[3];
+      ld.wo = (const f16*)v[4];
+      ld.mlp_norm = (const f16*)v[5];
+      ld.wg = (const f16*)v[6];
+      ld.wu = (const f16*)v[7];
+      ld.wd = (const f16*)v[8];
+    }
+    if (r) {
+      delete c;
+      return r;
+    }
+  }
   const char* ng = getenv("RIVER_NO_GRAPH");
   c->use_graph = !(ng && ng[0] == '1');
   hipError_t e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
@@ -390,19 +488,8 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
     return hip_fail(e, "hipStreamCreateWithFlags");
   }
   const Dims& d = c->dm;
-  c->layers.resize(d.L);
   for (int l = 0; l < d.L; ++l) {
-    const river_layer_weights& lw = w->layers[l];
     LayerDev& ld = c->layers[l];
-    ld.attn_norm = (const f16*)lw.attn_norm;
-    ld.wq = (const f16*)lw.wq;
-    ld.wk = (const f16*)lw.wk;
-    ld.wv = (const f16*)lw.wv;
-    ld.wo = (const f16*)lw.wo;
-    ld.mlp_norm = (const f16*)lw.mlp_norm;
-    ld.wg = (const f16*)lw.w_gate;
-    ld.wu = (const f16*)lw.w_up;
-    ld.wd = (const f16*)lw.w_down;
     char* base = c->river + (uint64_t)l * c->rl.layer_bytes;
     ld.r_qkv = (const uint8_t*)(base + c->rl.off_p[0]);
     ld.r_o = (const uint8_t*)(base + c->rl.off_p[1]);
@@ -412,21 +499,29 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
     ld.s_o = (const f16*)(base + c->rl.off_s[1]);
     ld.s_gu = (const f16*)(base + c->rl.off_s[2]);
     ld.s_d = (const f16*)(base + c->rl.off_s[3]);
+    if (d.zp) {
+      ld.z_qkv = (const uint8_t*)(base + c->rl.off_z[0]);
+      ld.z_o = (const uint8_t*)(base + c->rl.off_z[1]);
+      ld.z_gu = (const uint8_t*)(base + c->rl.off_z[2]);
+      ld.z_d = (const uint8_t*)(base + c->rl.off_z[3]);
+    }
     // quantise the seven matrices into the river copy
     struct Job {
       const void* W;
       int N, K, m, row0;
-    } jobs[7] = {{lw.wq, d.hd, d.d, 0, 0},
-                 {lw.wk, d.Hkv * d.D, d.d, 0, d.hd},
-                 {lw.wv, d.Hkv * d.D, d.d, 0, d.hd + d.Hkv * d.D},
-                 {lw.wo, d.d, d.hd, 1, 0},
-                 {lw.w_gate, d.F, d.d, 2, 0},
-                 {lw.w_up, d.F, d.d, 2, d.F},
-                 {lw.w_down, d.d, d.F, 3, 0}};
+    } jobs[7] = {{ld.wq, d.hd, d.d, 0, 0},
+                 {ld.wk, d.Hkv * d.D, d.d, 0, d.hd},
+                 {ld.wv, d.Hkv * d.D, d.d, 0, d.hd + d.Hkv * d.D},
+                 {ld.wo, d.d, d.hd, 1, 0},
+                 {ld.wg, d.F, d.d, 2, 0},
+                 {ld.wu, d.F, d.d, 2, d.F},
+                 {ld.wd, d.d, d.F, 3, 0}};
     for (const Job& j : jobs) {
       uint8_t* p = (uint8_t*)(base + c->rl.off_p[j.m]) + (uint64_t)j.row0 * w4_row_bytes(j.K);
       f16* s = (f16*)(base + c->rl.off_s[j.m]) + (uint64_t)j.row0 * w4_row_scales(j.K, d.group);
-      e = river_launch_quantize((const f16*)j.W, j.N, j.K, d.group, p, s, st);
+      uint8_t* z = d.zp ? (uint8_t*)(base + c->rl.off_z[j.m]) + (uint64_t)j.row0 * w4_row_scales(j.K, d.group)
+                        : nullptr;
+      e = river_launch_quantize((const f16*)j.W, j.N, j.K, d.group, p, s, z, st);
       if (e != hipSuccess) {
         river_destroy(c);
         return hip_fail(e, "quantize launch");
@@ -504,6 +599,25 @@ int river_destroy(river_ctx* c) {
   return RIVER_OK;
 }
 
+int river_weight_placement(const void* p, int32_t* placement) {
+  if (!p || !placement) return fail(RIVER_EINVAL, "NULL argument");
+  const void* dv = nullptr;
+  bool host = false;
+  const int r = weight_view(p, "pointer", &dv, &host);
+  if (r) return r;
+  *placement = host ? 1 : 0;
+  return RIVER_OK;
+}
+
+int river_weight_residency(const river_ctx* c, uint64_t* device_bytes, uint64_t* host_bytes,
+                           uint64_t* river_bytes) {
+  if (!c || !device_bytes || !host_bytes || !river_bytes) return fail(RIVER_EINVAL, "NULL argument");
+  *device_bytes = c->w_device_bytes;
+  *host_bytes = c->w_host_bytes;
+  *river_bytes = c->river_bytes;
+  return RIVER_OK;
+}
+
 int river_decode_path(const river_ctx* c, int32_t* persistent) {
   if (!c || !persistent) return fail(RIVER_EINVAL, "null argument");
   *persistent = (c->persist_fn[0] != nullptr) ? 1 : 0;
@@ -547,12 +661,14 @@ int river_prefill(river_ctx* c, const int32_t* tokens, int32_t P, int32_t prefil
   p.dm = d;
   p.M = d.B * P;
   p.P = P;
+  p.Ct = d.pf_chunk < P ? d.pf_chunk : P;
   p.tokens = tokens;
   p.embed = c->embed;
   p.hin = (f16*)(sc + s.pf_hin);
   p.hout = (f16*)(sc + s.pf_hout);
   p.hmid = (f16*)(sc + s.pf_hmid);
   p.act = (f16*)(sc + s.pf_act);
+  p.attn = (f16*)(sc + s.pf_attn);
   p.qkv = (f16*)(sc + s.pf_qkv);
   p.gu = (f16*)(sc + s.pf_gu);
   p.a2 = (f16*)(sc + s.pf_a2);
@@ -810,8 +926,10 @@ int river_decode_step(river_ctx* c, const int32_t* tok_in, const int32_t* forced
 }
 
 int river_export_river(river_ctx* c, int32_t layer, int32_t which, uint8_t* packed, uint16_t* scales,
-                       void* stream) {
+                       uint8_t* zeros, void* stream) {
   if (!c || !packed || !scales) return fail(RIVER_EINVAL, "NULL argument");
+  if ((zeros != nullptr) != (c->dm.zp != 0))
+    return fail(RIVER_EINVAL, "zeros must be non-NULL exactly for the zero-point format");
   const Dims& d = c->dm;
   if (layer < 0 || layer >= d.L) return fail(RIVER_ERANGE, "layer out of range");
   if (which < 0 || which > 6) return fail(RIVER_EINVAL, "which must be in [0, 6]");
@@ -823,7 +941,9 @@ int river_export_river(river_ctx* c, int32_t layer, int32_t which, uint8_t* pack
   const char* base = c->river + (uint64_t)layer * c->rl.layer_bytes;
   const uint8_t* p = (const uint8_t*)(base + c->rl.off_p[m]) + (uint64_t)row0[which] * w4_row_bytes(K);
   const f16* s = (const f16*)(base + c->rl.off_s[m]) + (uint64_t)row0[which] * w4_row_scales(K, d.group);
-  hipError_t e = river_launch_export(p, s, Ns[which], K, d.group, packed, scales, (hipStream_t)stream);
+  const uint8_t* z = d.zp ? (const uint8_t*)(base + c->rl.off_z[m]) + (uint64_t)row0[which] * w4_row_scales(K, d.group)
+                          : nullptr;
+  hipError_t e = river_launch_export(p, s, z, Ns[which], K, d.group, packed, scales, zeros, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "export launch");
   return RIVER_OK;
 }

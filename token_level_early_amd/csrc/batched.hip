@@ -208,13 +208,15 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
   } else {
     const uint8_t* rp[TW];
     const f16* sp[TW];
+    const uint8_t* zp[TW];  // zero-point format only (else null)
 #pragma unroll
-    for (int s = 0; s < TW; ++s) w4_row(OP, nok[s] ? n[s] : 0, *lw, dm, rp[s], sp[s]);
+    for (int s = 0; s < TW; ++s) w4_row(OP, nok[s] ? n[s] : 0, *lw, dm, rp[s], sp[s], zp[s]);
+    const bool zpf = dm.zp != 0;
     const int g = dm.group, wpg = g / 32;  // 32-wide windows per group (1, 2 or 4)
     const int ng = (K + g - 1) / g;
     const int g0 = w * ng / 4, g1 = (w + 1) * ng / 4;
     // one group's windows and scales per batch, double-buffered across groups
-    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4][TW], float (&sc)[TW]) {
+    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4][TW], float (&sc)[TW], float (&zc)[TW]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         xr[u] = make_uint4(0, 0, 0, 0);
@@ -231,10 +233,19 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
         }
       }
 #pragma unroll
-      for (int s = 0; s < TW; ++s) sc[s] = nok[s] ? h2f(sp[s][grp]) : 0.f;  // scale of (column, group)
+      for (int s = 0; s < TW; ++s) {
+        sc[s] = nok[s] ? h2f(sp[s][grp]) : 0.f;  // scale of (column, group)
+        zc[s] = (zpf && nok[s]) ? 8.f - (float)zp[s][grp] : 0.f;  // zero-point format: 8 - z
+      }
     };
-    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4][TW], const float (&sc)[TW]) {
+    // unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z): the group's
+    // input sums per batch row come from one more MFMA against a ones operand (they land in the
+    // accumulator layout, every column holding its row's sum)
+    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4][TW], const float (&sc)[TW],
+                    const float (&zc)[TW]) {
       bf4 tmp[TW];
+      bf4 xs = bf4{0.f, 0.f, 0.f, 0.f};
+      const bh4 ones = bh4{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
 #pragma unroll
       for (int s = 0; s < TW; ++s) tmp[s] = bf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,6 +256,10 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
           pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
           const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
           const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
+          if (zpf) {
+            xs = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, ones, xs, 0, 0, 0);
+            xs = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, ones, xs, 0, 0, 0);
+          }
 #pragma unroll
           for (int s = 0; s < TW; ++s) {
             h2 p0, p1, p2, p3;
@@ -259,18 +274,18 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
 #pragma unroll
       for (int s = 0; s < TW; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s], tmp[s][r], acc[s][r]);
+        for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s], zpf ? fmaf(zc[s], xs[r], tmp[s][r]) : tmp[s][r], acc[s][r]);
     };
     uint4 xr0[4], xr1[4];
     uint32_t wq0[4][TW], wq1[4][TW];
-    float sc0[TW], sc1[TW];
+    float sc0[TW], sc1[TW], zc0[TW], zc1[TW];
     int grp = g0;
-    if (grp < g1) loadg(grp, xr0, wq0, sc0);
+    if (grp < g1) loadg(grp, xr0, wq0, sc0, zc0);
     for (; grp < g1; grp += 2) {
-      if (grp + 1 < g1) loadg(grp + 1, xr1, wq1, sc1);
-      mmag(xr0, wq0, sc0);
-      if (grp + 2 < g1) loadg(grp + 2, xr0, wq0, sc0);
-      if (grp + 1 < g1) mmag(xr1, wq1, sc1);
+      if (grp + 1 < g1) loadg(grp + 1, xr1, wq1, sc1, zc1);
+      mmag(xr0, wq0, sc0, zc0);
+      if (grp + 2 < g1) loadg(grp + 2, xr0, wq0, sc0, zc0);
+      if (grp + 1 < g1) mmag(xr1, wq1, sc1, zc1);
     }
   }
   // lane holds Y[row 4*kq + r][col] of each tile; sum the four waves' K slices

@@ -74,20 +74,23 @@ RIVER_DEV const f16* f16_row(int op, int n, const LayerDev& lw, const DecodeArgs
   }
 }
 
+// Row n of the river copy of op: nibbles, scales and (zero-point format, else null) zero points.
 RIVER_DEV void w4_row(int op, int n, const LayerDev& lw, const Dims& dm, const uint8_t*& rp,
-                      const f16*& sp) {
+                      const f16*& sp, const uint8_t*& zp) {
   const int K = op_k(op, dm);
   const int64_t rb = w4_row_bytes(K), rs = w4_row_scales(K, dm.group);
   const uint8_t* base;
   const f16* sbase;
+  const uint8_t* zbase;
   switch (op) {
-    case OP_QKV: base = lw.r_qkv; sbase = lw.s_qkv; break;
-    case OP_O: base = lw.r_o; sbase = lw.s_o; break;
-    case OP_GU: base = lw.r_gu; sbase = lw.s_gu; break;
-    default: base = lw.r_d; sbase = lw.s_d; break;
+    case OP_QKV: base = lw.r_qkv; sbase = lw.s_qkv; zbase = lw.z_qkv; break;
+    case OP_O: base = lw.r_o; sbase = lw.s_o; zbase = lw.z_o; break;
+    case OP_GU: base = lw.r_gu; sbase = lw.s_gu; zbase = lw.z_gu; break;
+    default: base = lw.r_d; sbase = lw.s_d; zbase = lw.z_d; break;
   }
   rp = base + (size_t)n * rb;
   sp = sbase + (size_t)n * rs;
+  zp = zbase ? zbase + (size_t)n * rs : nullptr;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -302,10 +305,21 @@ RIVER_DEV void dot_rows_f16(const uint4 (&w)[RB][NCH], const h2 (&x)[NCH][4], fl
   }
 }
 
-// int4 rows: per chunk sum_k q_k x_k over the lane's 32 elements (one group), times its scale
+// int4 rows: per chunk sum_k q_k x_k over the lane's 32 elements (one group), times its scale.
+// unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z), so with `zp` the
+// lane's input sum X is added (8 - z) times per chunk.
 template <int NCH, int RB>
 RIVER_DEV void dot_rows_w4(const uint4 (&w)[RB][NCH], const f16 (&sc)[RB][NCH],
-                           const h2 (&x)[NCH][16], float (&acc)[RB]) {
+                           const uint8_t (&zz)[RB][NCH], bool zp, const h2 (&x)[NCH][16],
+                           float (&acc)[RB]) {
+  float xsum[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    xsum[c] = 0.f;
+    if (zp)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xsum[c] += h2f(x[c][j].x) + h2f(x[c][j].y);
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float tot = 0.f;
@@ -322,6 +336,7 @@ RIVER_DEV void dot_rows_w4(const uint4 (&w)[RB][NCH], const f16 (&sc)[RB][NCH],
         s = dot2(p2, x[c][m * 4 + 2], s);
         s = dot2(p3, x[c][m * 4 + 3], s);
       }
+      if (zp) s = fmaf(8.f - (float)zz[rb][c], xsum[c], s);
       tot = fmaf(h2f(sc[rb][c]), s, tot);
     }
     acc[rb] = tot;
@@ -408,13 +423,14 @@ RIVER_DEV void wave_gemv_f16(const f16* const (&rowp)[RB], const f16* xv, const 
 // One wave's share of a tile on the int4 stream: RB rows x NCH chunks of 2048 elements.
 template <int NCH, int RB, int WPR, bool HAS_GAIN, bool COH>
 RIVER_DEV void wave_gemv_w4(const uint8_t* const (&rowp)[RB], const f16* const (&sclp)[RB],
-                            const f16* xv, const f16* gain, int K, int group, int ws,
-                            bool want_norm, float inv, int dnorm, float eps, double* red,
-                            float (&acc)[RB]) {
+                            const uint8_t* const (&zrp)[RB], bool zp, const f16* xv,
+                            const f16* gain, int K, int group, int ws, bool want_norm, float inv,
+                            int dnorm, float eps, double* red, float (&acc)[RB]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nch = (K + kChunkW4 - 1) / kChunkW4;
   uint4 wv[RB][NCH];
   f16 sc[RB][NCH];
+  uint8_t zz[RB][NCH];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -423,6 +439,7 @@ RIVER_DEV void wave_gemv_w4(const uint8_t* const (&rowp)[RB], const f16* const (
       const bool ok = rowp[rb] != nullptr && cid < nch;
       wv[rb][c] = ldg16(ok ? (const void*)(rowp[rb] + (size_t)cid * 1024 + lane * 16) : (const void*)xv);
       sc[rb][c] = ldg2(ok ? sclp[rb] + (cid * kChunkW4 + lane * 32) / group : xv);
+      zz[rb][c] = (zp && ok) ? zrp[rb][(cid * kChunkW4 + lane * 32) / group] : (uint8_t)8;
     }
   uint4 xr[NCH][4], gr[NCH][4] = {};
 #pragma unroll
@@ -457,7 +474,7 @@ RIVER_DEV void wave_gemv_w4(const uint8_t* const (&rowp)[RB], const f16* const (
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[c][m * 4 + j] = o[j];
     }
-  dot_rows_w4<NCH, RB>(wv, sc, x, acc);
+  dot_rows_w4<NCH, RB>(wv, sc, zz, zp, x, acc);
 }
 
 
@@ -528,19 +545,21 @@ RIVER_DEV void gemv_tile(const DecodeArgs& a, const LayerDev* lwp, const TileIn&
     const int rg = w / WPR4, ws = w % WPR4;
     const uint8_t* rowp[RB];
     const f16* sclp[RB];
+    const uint8_t* zrp[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int n = logical_row(OP, tile, rg * RB + rb, T4::TR, dm);
       if (n < N) {
-        w4_row(OP, n, *lwp, dm, rowp[rb], sclp[rb]);
+        w4_row(OP, n, *lwp, dm, rowp[rb], sclp[rb], zrp[rb]);
       } else {
         rowp[rb] = nullptr;
         sclp[rb] = nullptr;
+        zrp[rb] = nullptr;
       }
     }
     float acc[RB];
-    wave_gemv_w4<NCH4, RB, WPR4, kHasGain, COH>(rowp, sclp, in.xv, in.gain, K, dm.group, ws,
-                                                in.want_norm, in.inv, dm.d, dm.eps, sm.dred, acc);
+    wave_gemv_w4<NCH4, RB, WPR4, kHasGain, COH>(rowp, sclp, zrp, dm.zp != 0, in.xv, in.gain, K, dm.group,
+                                                ws, in.want_norm, in.inv, dm.d, dm.eps, sm.dred, acc);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float v = wave_sum(acc[rb]);

@@ -31,10 +31,17 @@ struct LayerDev {
   const f16* s_o;
   const f16* s_gu;
   const f16* s_d;
+  // zero-point format only (else null): one zero point (uint8) per group, laid out like the scales
+  const uint8_t* z_qkv;
+  const uint8_t* z_o;
+  const uint8_t* z_gu;
+  const uint8_t* z_d;
 };
 
 struct Dims {
   int L, d, H, Hkv, D, F, V, group, B, Tmax, entry, tied, max_prefill;
+  int zp;    // river format: 0 symmetric int4, 1 zero-point int4
+  int pf_chunk;  // prefill positions per chunk
   float eps, theta;
   int hd;    // H*D
   int nqkv;  // H*D + 2*Hkv*D
@@ -112,18 +119,25 @@ enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
 enum { TOP_QKV = 0, TOP_ATTN = 1, TOP_O = 2, TOP_GU = 3, TOP_DOWN = 4, TOP_LM = 5, TOP_PERSIST = 6 };
 
 // Prefill activations and state (scratch), passed by value to the prefill kernels.
+// The prompt runs layer by layer (the sequence-level exit after layer l needs every token's
+// s_t(l)), each layer in chunks of Ct positions of every row: the residual stream hin/hout
+// holds all B*P rows, the other activations only the B*Ce rows of the current chunk
+// (chunk-local row mc <-> row b = mc / Ce, position t = t0 + mc % Ce, global row b*P + t).
 struct PfArgs {
   Dims dm;
   int M, P;            // M = B*P rows
+  int Ct;              // positions per chunk
+  int t0, Ce;          // current chunk: positions [t0, t0 + Ce)
   const int* tokens;   // [B][P]
   const f16* embed;
-  f16* hin;    // [M][max(d, H*D)] block input (residual stream)
-  f16* hout;   // [M][max(d, H*D)] attention output, then block output
-  f16* hmid;   // [M][max(d, H*D)]
-  f16* act;    // [M][max(d, H*D)] normed input / rotated q
-  f16* qkv;    // [M][nqkv]
-  f16* gu;     // [M][2F]
-  f16* a2;     // [M][F]
+  f16* hin;    // [M][d] block input (residual stream)
+  f16* hout;   // [M][d] block output
+  f16* hmid;   // [B*Ct][d]
+  f16* act;    // [B*Ct][max(d, H*D)] normed input / rotated q
+  f16* attn;   // [B*Ct][H*D] attention output
+  f16* qkv;    // [B*Ct][nqkv]
+  f16* gu;     // [B*Ct][2F]
+  f16* a2;     // [B*Ct][F]
   double* cosv;    // [M]
   int* seq_route;  // [B]
   int* seq_exit;   // [B]

@@ -114,6 +114,7 @@ struct PSmem {
     AttnLds<D, G, kPB, (RIVER_PATTN_GL < G ? RIVER_PATTN_GL : G)> at;
   };
   float xc[kMaxK / 32];  // int4 stream: per (chunk, lane) bias correction of the staged input
+  float xs[kMaxK / 32];  // zero-point format: per (chunk, lane) sum of the staged input
   double red[kPW];
   double c3[3];
   int flag;
@@ -136,9 +137,11 @@ RIVER_DEV int lds_group_index(int g) {  // g: group of 8 elements -> h2 index
 // Writes one group of 8 staged values into LDS in the stream's layout. For the int4 stream the
 // odd elements of each pair set are stored divided by 16 (exact) and the bias correction of
 // the (chunk, lane) the group belongs to is summed over its 4 groups (threads t..t+3 stage
-// them; the quad is always complete) -- see dot_seg4 for how both are used.
-template <bool IS4>
-RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
+// them; the quad is always complete) -- see dot_seg4 for how both are used. Zero-point format
+// (ZP): the correction leaves the zero point out (it is per group of weights), and xs gets the
+// plain sum of the lane's 32 inputs, which dot_seg4 scales by the group's zero point.
+template <bool IS4, bool ZP = false>
+RIVER_DEV void put_group(h2* xl, float* xc, float* xs, int g, uint4 u) {
   h2* dst = xl + lds_group_index<IS4>(g);
   if (IS4) {
     const uint32_t in[4] = {u.x, u.y, u.z, u.w};
@@ -151,10 +154,16 @@ RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
     dst[1] = o[1] * sixteenth;
     dst[2] = o[2];
     dst[3] = o[3] * sixteenth;
-    float c = -1032.f * xlo - 72.f * xhi;
+    float c = ZP ? -1024.f * xlo - 64.f * xhi : -1032.f * xlo - 72.f * xhi;
     c += dpp_f<0xB1>(c);
     c += dpp_f<0x4E>(c);
     if ((g & 3) == 0) xc[g >> 2] = c;
+    if (ZP) {
+      float xsum = xlo + xhi;
+      xsum += dpp_f<0xB1>(xsum);
+      xsum += dpp_f<0x4E>(xsum);
+      if ((g & 3) == 0) xs[g >> 2] = xsum;
+    }
   } else {
     dst[0] = as_h2(u.x);
     dst[1] = as_h2(u.y);
@@ -168,9 +177,9 @@ RIVER_DEV void put_group(h2* xl, float* xc, int g, uint4 u) {
 // during the launch (the embedding row). NORM: inv = 1/rms(src) computed here in a fixed
 // order (identical in every workgroup). Each thread reads its groups of 8 values two at a
 // time (both waits in one round trip), together with their gains.
-template <bool IS4, bool HAS_GAIN, bool NORM, bool TAG, int NG>
+template <bool IS4, bool HAS_GAIN, bool NORM, bool TAG, int NG, bool ZP = false>
 RIVER_DEV void stage_x(const void* src, uint32_t tag, int* abort, const f16* gain, int K, float inv,
-                       float eps, h2* xl, float* xc, double* red) {
+                       float eps, h2* xl, float* xc, float* xs, double* red) {
   const int t = threadIdx.x;
   const int nch = IS4 ? (K + kChunkW4 - 1) / kChunkW4 : (K + kChunkF16 - 1) / kChunkF16;
   const int ngp = nch * (IS4 ? kChunkW4 : kChunkF16) / 8;
@@ -208,9 +217,9 @@ RIVER_DEV void stage_x(const void* src, uint32_t tag, int* abort, const f16* gai
       if (g >= ngp) continue;
       uint4 u = v[i];
       if (HAS_GAIN && g * 8 < K) u = norm8(u, gv[i], inv, true);
-      put_group<IS4>(xl, xc, g, u);
+      put_group<IS4, ZP>(xl, xc, xs, g, u);
     }
-    for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4>(xl, xc, g, make_uint4(0, 0, 0, 0));
+    for (int g = t + NG * kPB; g < ngp; g += kPB) put_group<IS4, ZP>(xl, xc, xs, g, make_uint4(0, 0, 0, 0));
   } else {
     for (int g0 = t; g0 < ngp; g0 += 2 * kPB) {
       uint4 v[2];
@@ -221,7 +230,7 @@ RIVER_DEV void stage_x(const void* src, uint32_t tag, int* abort, const f16* gai
         if (g >= ngp) break;  // ngp is a multiple of 4: whole quads stay together
         uint4 u = v[i];
         if (HAS_GAIN && g * 8 < K) u = norm8(u, ldg16(gain + g * 8), inv, true);
-        put_group<IS4>(xl, xc, g, u);
+        put_group<IS4, ZP>(xl, xc, xs, g, u);
       }
     }
   }
@@ -323,6 +332,7 @@ template <int SEG>
 struct Seg {
   uint4 w[SEG];
   uint4 sr;  // int4: this lane's share of the item's group scales (fetched per chunk by shuffle)
+  uint2 zr;  // zero-point format: this lane's share of the item's zero points (bytes), likewise
 };
 
 // fp16: chunks [seg*SEG, seg*SEG+SEG) of `row`.
@@ -362,9 +372,9 @@ RIVER_DEV float dot_seg16(const Seg<SEG>& sg, const h2* xl, int nch, int seg, fl
 // item's group scales are contiguous too (spc = 2048/group per chunk); one load per lane
 // brings npl = SEG*spc/64 of them (lane L: scales [L*npl, L*npl + npl) of the item) instead of
 // one small load per chunk.
-template <int SEG, int GRP>
-RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const RowRange& rr, int nch, int q0,
-                         int qend, Seg<SEG>& sg) {
+template <int SEG, int GRP, bool ZP = false>
+RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const uint8_t* zbase, const RowRange& rr,
+                         int nch, int q0, int qend, Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int c = 0; c < SEG; ++c)
@@ -375,6 +385,7 @@ RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const RowRange& 
   static_assert(npl == 1 || npl == 2 || npl == 4 || npl == 8, "scales per lane");
   const int s0 = q0 * spc + lane * npl;  // virtual scale index; npl divides spc
   sg.sr = make_uint4(0, 0, 0, 0);
+  if (ZP) sg.zr = make_uint2(0, 0);
   if (s0 < qend * spc) {  // npl divides both: the lane's scales are all in range
     const f16* sp = sbase + (size_t)rr.chunk(s0 / spc, nch) * spc + s0 % spc;
     if (npl == 1) {
@@ -387,6 +398,17 @@ RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const RowRange& 
       sg.sr.y = (uint32_t)(v >> 32);
     } else {
       sg.sr = ldg16(sp);
+    }
+    if (ZP) {  // the same scale indices' zero points, one byte each
+      const uint8_t* zp = zbase + (size_t)rr.chunk(s0 / spc, nch) * spc + s0 % spc;
+      if (npl == 1) sg.zr.x = *(const __attribute__((address_space(1))) uint8_t*)zp;
+      else if (npl == 2) sg.zr.x = *(const __attribute__((address_space(1))) unsigned short*)zp;
+      else if (npl == 4) sg.zr.x = *(const __attribute__((address_space(1))) uint32_t*)zp;
+      else {
+        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+        const v2u v = *(const __attribute__((address_space(1))) v2u*)zp;
+        sg.zr = make_uint2(v.x, v.y);
+      }
     }
   }
 }
@@ -417,11 +439,26 @@ RIVER_DEV float item_scale(const Seg<SEG>& sg, int c) {
   return h2f(__builtin_bit_cast(f16, hv));
 }
 
+// Zero point of chunk c of an item for this lane's 32 elements (same index as item_scale).
+template <int SEG, int spc, int npl>
+RIVER_DEV float item_zero(const Seg<SEG>& sg, int c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = c * spc + (lane * spc) / kWave;
+  const int src = i / npl, e = i % npl;
+  const uint32_t wx = (uint32_t)__shfl((int)sg.zr.x, src, kWave);
+  uint32_t wv = wx;
+  if (npl == 8) {
+    const uint32_t wy = (uint32_t)__shfl((int)sg.zr.y, src, kWave);
+    wv = (e >> 2) ? wy : wx;
+  }
+  return (float)((wv >> (8 * (e & 3))) & 0xFFu);
+}
+
 // Reduces the int4 item starting at flat chunk q0 (chunk ch of row `row`); calls fin(row, lane
 // partial) at every row end and advances (row, ch).
-template <int SEG, int GRP, typename Fin>
-RIVER_DEV void dot_seg4(const Seg<SEG>& sg, const h2* xl, const float* xc, int nch, int q0,
-                        int qend, int& row, int& ch, float& acc, Fin&& fin) {
+template <int SEG, int GRP, bool ZP, typename Fin>
+RIVER_DEV void dot_seg4(const Seg<SEG>& sg, const h2* xl, const float* xc, const float* xs, int nch,
+                        int q0, int qend, int& row, int& ch, float& acc, Fin&& fin) {
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int spc = kChunkW4 / GRP, npl = SEG * spc / kWave;
 #pragma unroll
@@ -430,7 +467,9 @@ RIVER_DEV void dot_seg4(const Seg<SEG>& sg, const h2* xl, const float* xc, int n
     // nibbles OR-ed into fp16 1024.0 give 1024 + u (low nibble of each half) or 1024 + 16u
     // (high nibble); against x (resp. x/16) the dot is sum (u - 8) x + 1032 X_lo + 72 X_hi,
     // and the staged correction -1032 X_lo - 72 X_hi starts the sum
+    // zero-point format: sum (u - z) x = sum u x - z X, X the lane's input sum
     float sd = xc[ch * kWave + lane];
+    if (ZP) sd = fmaf(-item_zero<SEG, spc, npl>(sg, c), xs[ch * kWave + lane], sd);
     uint4 xv[4];  // all four 16-byte reads of this chunk's inputs first
 #pragma unroll
     for (int m = 0; m < 4; ++m) xv[m] = ((const uint4*)xl)[(ch * 4 + m) * kWave + lane];
@@ -454,11 +493,11 @@ RIVER_DEV void dot_seg4(const Seg<SEG>& sg, const h2* xl, const float* xc, int n
 
 // Base of the packed river matrix of OP and of its scales.
 template <int OP>
-RIVER_DEV void w4_base(const LayerDev* lw, const uint8_t*& base, const f16*& sbase) {
-  if (OP == OP_QKV) { base = lw->r_qkv; sbase = lw->s_qkv; }
-  else if (OP == OP_O) { base = lw->r_o; sbase = lw->s_o; }
-  else if (OP == OP_GU) { base = lw->r_gu; sbase = lw->s_gu; }
-  else { base = lw->r_d; sbase = lw->s_d; }
+RIVER_DEV void w4_base(const LayerDev* lw, const uint8_t*& base, const f16*& sbase, const uint8_t*& zbase) {
+  if (OP == OP_QKV) { base = lw->r_qkv; sbase = lw->s_qkv; zbase = lw->z_qkv; }
+  else if (OP == OP_O) { base = lw->r_o; sbase = lw->s_o; zbase = lw->z_o; }
+  else if (OP == OP_GU) { base = lw->r_gu; sbase = lw->s_gu; zbase = lw->z_gu; }
+  else { base = lw->r_d; sbase = lw->s_d; zbase = lw->z_d; }
 }
 
 // Epilogue inputs of a streamed phase.
@@ -481,9 +520,9 @@ RIVER_DEV int n_chunks(int K) {
 
 // Streams this wave's rows of an N-row phase; the input vector is staged in xl and the first
 // item is already in b0 (prefetch_first).
-template <int OP, bool IS4, int SEG, int GRP>
+template <int OP, bool IS4, int SEG, int GRP, bool ZP = false>
 RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K, const h2* xl,
-                           const float* xc, const StreamOut& so, Seg<SEG>& b0) {
+                           const float* xc, const float* xs, const StreamOut& so, Seg<SEG>& b0) {
   const int lane = threadIdx.x & (kWave - 1);
   const RowRange rr = wave_range<OP>(N);
   if (rr.nv <= 0) return;
@@ -558,17 +597,18 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
   } else {
     const uint8_t* base;
     const f16* sbase;
-    w4_base<OP>(lw, base, sbase);
+    const uint8_t* zbase;
+    w4_base<OP>(lw, base, sbase, zbase);
     const int qend = rr.nv * nch;  // virtual chunks
     int row = 0, ch = 0;
     int q = 0;
     for (; q + SEG < qend; q += 2 * SEG) {
-      load_seg4<SEG, GRP>(base, sbase, rr, nch, q + SEG, qend, b1);
-      dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
-      if (q + 2 * SEG < qend) load_seg4<SEG, GRP>(base, sbase, rr, nch, q + 2 * SEG, qend, b0);
-      dot_seg4<SEG, GRP>(b1, xl, xc, nch, q + SEG, qend, row, ch, acc, fin);
+      load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + SEG, qend, b1);
+      dot_seg4<SEG, GRP, ZP>(b0, xl, xc, xs, nch, q, qend, row, ch, acc, fin);
+      if (q + 2 * SEG < qend) load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + 2 * SEG, qend, b0);
+      dot_seg4<SEG, GRP, ZP>(b1, xl, xc, xs, nch, q + SEG, qend, row, ch, acc, fin);
     }
-    if (q < qend) dot_seg4<SEG, GRP>(b0, xl, xc, nch, q, qend, row, ch, acc, fin);
+    if (q < qend) dot_seg4<SEG, GRP, ZP>(b0, xl, xc, xs, nch, q, qend, row, ch, acc, fin);
   }
   if (OP == OP_LM && lane == 0 && bi != 0x7FFFFFFF) {
     const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
@@ -579,7 +619,7 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
 
 // Issues the first item of this wave's rows (weights only: allowed before the inputs of the
 // phase exist, e.g. before the grid barrier or while the input vector is staged).
-template <int OP, bool IS4, int SEG, int GRP>
+template <int OP, bool IS4, int SEG, int GRP, bool ZP = false>
 RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, int K, Seg<SEG>& pre) {
   const RowRange rr = wave_range<OP>(N);
   if (rr.nv <= 0) {  // no rows: still define the whole buffer
@@ -594,30 +634,31 @@ RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, in
   } else {
     const uint8_t* base;
     const f16* sbase;
-    w4_base<OP>(lw, base, sbase);
-    load_seg4<SEG, GRP>(base, sbase, rr, nch, 0, rr.nv * nch, pre);
+    const uint8_t* zbase;
+    w4_base<OP>(lw, base, sbase, zbase);
+    load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, 0, rr.nv * nch, pre);
   }
 }
 
 // One GEMV phase: stage the input (waiting for its tagged words), stream the rows. b0 holds the
 // phase's first item when `have` (issued at the end of the previous phase), else it is issued
 // here first.
-template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool TAG, int NG, int GRP>
+template <int OP, bool IS4, int SEG, bool HAS_GAIN, bool NORM, bool TAG, int NG, int GRP, bool ZP = false>
 RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K, const void* src,
                           uint32_t stag, const f16* gain, float inv, const StreamOut& so, h2* xl,
-                          float* xc, double* red, Seg<SEG>& b0, bool have) {
-  if (!have) prefetch_first<OP, IS4, SEG, GRP>(a, lw, N, K, b0);
-  stage_x<IS4, HAS_GAIN, NORM, TAG, NG>(src, stag, so.abort, gain, K, inv, a.dm.eps, xl, xc, red);
-  stream_rows<OP, IS4, SEG, GRP>(a, lw, N, K, xl, xc, so, b0);
+                          float* xc, float* xs, double* red, Seg<SEG>& b0, bool have) {
+  if (!have) prefetch_first<OP, IS4, SEG, GRP, ZP>(a, lw, N, K, b0);
+  stage_x<IS4, HAS_GAIN, NORM, TAG, NG, ZP>(src, stag, so.abort, gain, K, inv, a.dm.eps, xl, xc, xs, red);
+  stream_rows<OP, IS4, SEG, GRP, ZP>(a, lw, N, K, xl, xc, xs, so, b0);
   __syncthreads();  // LDS reuse by the next phase
 }
 
 // First item of the next phase on the route's weight stream; returns what `pre` now holds
 // (1: fp16 item, 2: int4 item).
-template <int OP, int SEG, int GRP>
+template <int OP, int SEG, int GRP, bool ZP = false>
 RIVER_DEV int prefetch_route(const DecodeArgs& a, const LayerDev* lw, int N, int K, bool r4, Seg<SEG>& pre) {
   if (r4) {
-    prefetch_first<OP, true, SEG, GRP>(a, lw, N, K, pre);
+    prefetch_first<OP, true, SEG, GRP, ZP>(a, lw, N, K, pre);
     return 2;
   }
   prefetch_first<OP, false, SEG, GRP>(a, lw, N, K, pre);
@@ -627,7 +668,7 @@ RIVER_DEV int prefetch_route(const DecodeArgs& a, const LayerDev* lw, int N, int
 // ---------------------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------------------
-template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP, int AU>
+template <int D, int G, int MODE, int SEG16, int SEG4, int NG, int GRP, int AU, bool ZP = false>
 __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits, unsigned* bar) {
   static_assert(SEG16 == SEG4, "one prefetch buffer serves both weight streams");
   constexpr int SEG = SEG16;
@@ -711,14 +752,14 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.out = a.t_qkv;
       so.tag = tg;
       if (l == 1) {
-        if (r4) gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (r4) gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
       } else if (r4) {
-        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
-        else gemv_phase<OP_QKV, true, SEG, true, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 2);
+        if (norm_known) gemv_phase<OP_QKV, true, SEG, true, false, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
+        else gemv_phase<OP_QKV, true, SEG, true, true, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
       } else {
-        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
-        else gemv_phase<OP_QKV, false, SEG, true, true, true, NG, GRP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.red, pre, pf == 1);
+        if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+        else gemv_phase<OP_QKV, false, SEG, true, true, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
       }
       // ---------------- attention (+ RoPE and the KV append of position pos); waits for q|k|v
       {
@@ -726,7 +767,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
         for (int it = wg; it < dm.Hkv * splits; it += nwg)
           attn_split<D, G, kPB, true, AU, AGL, true>(a, l, it % splits, it / splits, b, pos, splits, sm.at, at);
       }
-      pf = prefetch_route<OP_O, SEG, GRP>(a, lw, dm.d, dm.hd, r4, pre);
+      pf = prefetch_route<OP_O, SEG, GRP, ZP>(a, lw, dm.d, dm.hd, r4, pre);
       // ---------------- O + residual
       so = StreamOut{};
       so.abort = abort;
@@ -738,23 +779,23 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
         so.tres = hin_t;
         so.rtag = tgp;
       }
-      if (r4) gemv_phase<OP_O, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_O, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      if (r4) gemv_phase<OP_O, true, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
+      else gemv_phase<OP_O, false, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.hd, o_t, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
       // The argmax key of the next step is the one every workgroup read after the previous
       // step's barrier; having staged all of o, this workgroup knows every split (hence every
       // workgroup) has passed this step's layer-1 attention, so none still reads that key.
       if (l == 1 && wg == 0 && t == 0)
         __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      pf = prefetch_route<OP_GU, SEG, GRP>(a, lw, 2 * dm.F, dm.d, r4, pre);
+      pf = prefetch_route<OP_GU, SEG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, r4, pre);
       // ---------------- gate|up (+ SwiGLU in the epilogue)
       so = StreamOut{};
       so.abort = abort;
       so.out = a.t_a2;
       so.tag = tg;
-      if (r4) gemv_phase<OP_GU, true, SEG, true, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_GU, false, SEG, true, true, true, NG, GRP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
-      pf = prefetch_route<OP_DOWN, SEG, GRP>(a, lw, dm.d, dm.F, r4, pre);
+      if (r4) gemv_phase<OP_GU, true, SEG, true, true, true, NG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
+      else gemv_phase<OP_GU, false, SEG, true, true, true, NG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+      pf = prefetch_route<OP_DOWN, SEG, GRP, ZP>(a, lw, dm.d, dm.F, r4, pre);
       // ---------------- down (input: the SwiGLU vector) + residual -> h(l)
       so = StreamOut{};
       so.abort = abort;
@@ -763,13 +804,13 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.copy = a.hs + ((size_t)l * dm.B + b) * dm.d;
       so.tres = hmid_t;
       so.rtag = tg;
-      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 2);
-      else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
+      if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
+      else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
       // next phase: QKV of layer l+1 on its route (the exit test may still switch a backbone
       // guess to the river, which then loads its own first item) or the LM head
       const bool next_r4 = r4 || (MODE == 0 && a.sched && l == e_forced && l >= dm.entry);
       if (l < dm.L) {
-        pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[l], dm.nqkv, dm.d, next_r4, pre);
+        pf = prefetch_route<OP_QKV, SEG, GRP, ZP>(a, &a.layers[l], dm.nqkv, dm.d, next_r4, pre);
       } else {
         prefetch_first<OP_LM, false, SEG, GRP>(a, nullptr, dm.V, dm.d, pre);
         pf = 1;
@@ -782,9 +823,9 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.abort = abort;
       so.logits = a.logits ? a.logits + (size_t)b * dm.V : nullptr;
       so.key = a.amax + (step & 1) * dm.B + b;
-      gemv_phase<OP_LM, false, SEG, true, true, true, NG, GRP>(a, nullptr, dm.V, dm.d, a.t_hs + (size_t)dm.L * dm.d,
-                                                               tag_of(step, dm.L), a.final_norm, 1.f, so, xl, sm.xc, sm.red, pre, pf == 1);
-      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
+      gemv_phase<OP_LM, false, SEG, true, true, true, NG, GRP, ZP>(a, nullptr, dm.V, dm.d, a.t_hs + (size_t)dm.L * dm.d,
+                                                               tag_of(step, dm.L), a.final_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+      grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP, ZP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
       if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
@@ -815,13 +856,16 @@ const void* river_persist_fn(const Dims& dm, int mode, int long_ctx) {
   const int G = dm.H / dm.Hkv;
   if ((G & (G - 1)) || (dm.D & (dm.D - 1))) return nullptr;
   const int ng = (dm.d + 8 * kPB - 1) / (8 * kPB);  // groups of 8 per thread for K = d
+  // the zero-point format has its own early-exit kernels (the backbone-only decode reads no river)
 #define RIVER_PF(D_, G_, NG_, GRP_)                                                              \
   if (dm.D == D_ && G == G_ && ng == NG_ && dm.group == GRP_) {                                  \
     if (long_ctx)                                                                                \
       return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_, 4>                       \
-                  : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 4>;                      \
+             : dm.zp ? (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 4, true>              \
+                     : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 4>;                   \
     return mode ? (const void*)k_persist<D_, G_, 1, 8, 8, NG_, GRP_, 2>                         \
-                : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 2>;                        \
+           : dm.zp ? (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 2, true>                \
+                   : (const void*)k_persist<D_, G_, 0, 8, 8, NG_, GRP_, 2>;                     \
   }
   RIVER_PF(128, 4, 1, 128)
   RIVER_PF(64, 4, 1, 128)

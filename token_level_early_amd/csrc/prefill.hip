@@ -27,6 +27,7 @@ struct PfGemmArgs {
   // int4 weights (device layout)
   const uint8_t* w4;
   const f16* s4;
+  const uint8_t* z4;  // zero-point format: zero points (else null)
   int group;
   // per-row route filter: row m belongs to sequence m / P; computed only if route matches
   const int* seq_route;  // [B]
@@ -36,7 +37,13 @@ struct PfGemmArgs {
   f16* C;  // [M][N]
   const f16* R;  // residual [M][N] (EPI_RESID)
   int epi;
+  // C_GLOBAL / R_GLOBAL: C or R is the whole residual stream, whose row for chunk-local row m
+  // is (m / P) * Ptot + t0 + m % P
+  int c_global, r_global, Ptot, t0;
 };
+
+// Residual-stream row of chunk-local row m (chunks of Ce positions from t0, prompts of P).
+RIVER_DEV int64_t pf_row(int m, int Ce, int t0, int P) { return (int64_t)(m / Ce) * P + t0 + m % Ce; }
 
 static constexpr int GBM = 128, GBN = 128, GBK = 32, GLDK = GBK + 16;  // 96-byte rows: 16-byte aligned
 
@@ -76,6 +83,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
     }
     uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
     uint2 bq = make_uint2(0x88888888u, 0x88888888u);
+    f16 dz = (f16)0.0f;  // zero-point format: 8 - z of this row's group (unpack8 gives u - 8)
     {
       const int n = n0 + lr, k = k0 + lh * 16;
       if (n < g.N) {
@@ -87,6 +95,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
           if (k + 8 < g.K) b1 = *(const uint4*)(src + k + 8);
         } else {
           bq = *(const uint2*)(g.w4 + (size_t)n * rb4 + k / 2);
+          if (g.z4) dz = (f16)(8.0f - (float)g.z4[(size_t)n * rs4 + k0 / g.group]);
         }
       }
     }
@@ -102,6 +111,11 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
       for (int h = 0; h < 2; ++h) {
         h2 p0, p1, p2, p3;
         unpack8(wd[h], p0, p1, p2, p3);  // pairs (q0,q4),(q1,q5),(q2,q6),(q3,q7)
+        const h2 d2 = {dz, dz};  // exact: small integers
+        p0 += d2;
+        p1 += d2;
+        p2 += d2;
+        p3 += d2;
         f16* dst = &Bs[lr][lh * 16 + h * 8];
         dst[0] = p0.x; dst[4] = p0.y;
         dst[1] = p1.x; dst[5] = p1.y;
@@ -156,10 +170,13 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
         const int m = m0 + wm + i * 16 + 4 * (lane / 16) + r;
         if (m < g.M && n < g.N && g.seq_route[m / g.P] == g.want_route) {
           const f16 v = f2h(acc[i][j][r]);
-          if (g.epi == EPI_STORE)
-            g.C[(size_t)m * g.N + n] = v;
-          else
-            g.C[(size_t)m * g.N + n] = f2h(h2f(g.R[(size_t)m * g.N + n]) + h2f(v));
+          const int64_t cm = g.c_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
+          if (g.epi == EPI_STORE) {
+            g.C[cm * g.N + n] = v;
+          } else {
+            const int64_t rm = g.r_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
+            g.C[cm * g.N + n] = f2h(h2f(g.R[rm * g.N + n]) + h2f(v));
+          }
         }
       }
     }
@@ -180,12 +197,13 @@ __global__ __launch_bounds__(kBlock) void k_pf_embed(PfArgs p) {
   for (int i = threadIdx.x; i < p.dm.d; i += kBlock) p.hin[(size_t)m * p.dm.d + i] = src[i];
 }
 
-// out[m] = fp16(x[m] / sqrt(mean(x[m]^2) + eps) * w)
+// out[m] = fp16(x[m] / sqrt(mean(x[m]^2) + eps) * w); with gP > 0 x is the residual stream and
+// its row is the global row of chunk-local row m (chunks of gCe positions from gt0)
 __global__ __launch_bounds__(kBlock) void k_pf_rmsnorm(const f16* x, const f16* w, f16* out, int n,
-                                                       float eps) {
+                                                       float eps, int gP, int gCe, int gt0) {
   __shared__ double red[4];
   const int m = blockIdx.x;
-  const f16* xr = x + (size_t)m * n;
+  const f16* xr = x + (gP > 0 ? pf_row(m, gCe, gt0, gP) : (int64_t)m) * n;
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += kBlock) {
     const double v = (double)h2f(xr[i]);
@@ -200,8 +218,8 @@ __global__ __launch_bounds__(kBlock) void k_pf_rmsnorm(const f16* x, const f16* 
 // RoPE on q and k rows of qkv; q -> act [M][H*D]; k, v -> shared cache at (layer, b, kvh, t).
 __global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
   const Dims& dm = p.dm;
-  const int m = blockIdx.x;
-  const int b = m / p.P, t = m % p.P;
+  const int m = blockIdx.x;  // chunk-local row
+  const int b = m / p.Ce, t = p.t0 + m % p.Ce;
   const f16* row = p.qkv + (size_t)m * dm.nqkv;
   const int half = dm.D / 2;
   const int npairs = (dm.H + dm.Hkv) * half;
@@ -252,7 +270,8 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
   __shared__ f16 Vt[D][KT + 8];   // [dim][key]
   const Dims& dm = p.dm;
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int q0 = blockIdx.x * QW;
+  const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
+  const int tend = p.t0 + p.Ce;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int lr = lane % 16, lq = lane / 16;
   const int h = kvh * G + w;
@@ -266,11 +285,11 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int t = q0 + qb * 16 + lr;
-    const f16* qrow = p.act + ((size_t)b * p.P + (t < p.P ? t : 0)) * dm.hd + (size_t)h * D;
+    const f16* qrow = p.act + ((size_t)b * p.Ce + (t < tend ? t - p.t0 : 0)) * dm.hd + (size_t)h * D;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       h4 v = *(const h4*)(qrow + ks * 16 + 4 * lq);
-      if (t >= p.P) v = (h4){0, 0, 0, 0};
+      if (t >= tend) v = (h4){0, 0, 0, 0};
       qf[qb][ks] = v;
     }
   }
@@ -282,13 +301,13 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
   float mrow[2] = {-__builtin_inff(), -__builtin_inff()};
   float lsum[2] = {0.f, 0.f};  // this lane's share of the softmax denominator
 
-  const int kend = min(p.P, q0 + QW);  // keys [0, kend) can be visible to this block
+  const int kend = min(tend, q0 + QW);  // keys [0, kend) can be visible to this block
   for (int k0 = 0; k0 < kend; k0 += KT) {
     __syncthreads();
     for (int idx = tid; idx < KT * D / 8; idx += G * kWave) {
       const int r = idx / (D / 8), c = (idx % (D / 8)) * 8;
       uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (k0 + r < p.P) {
+      if (k0 + r < kend) {
         kv4 = *(const uint4*)(Kb + (size_t)(k0 + r) * D + c);
         vv4 = *(const uint4*)(Vb + (size_t)(k0 + r) * D + c);
       }
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + kb * 16 + 4 * lq + r;
-          const float v = (key <= t && key < p.P) ? sc[kb][qb][r] * qs : -__builtin_inff();
+          const float v = (key <= t && key < kend) ? sc[kb][qb][r] * qs : -__builtin_inff();
           sc[kb][qb][r] = v;
           mt = fmaxf(mt, v);
         }
@@ -370,8 +389,8 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     const int t = q0 + qb * 16 + lr;
-    if (t < p.P) {
-      f16* orow = p.hout + ((size_t)b * p.P + t) * dm.hd + (size_t)h * D;  // attention output -> hout
+    if (t < tend) {
+      f16* orow = p.attn + ((size_t)b * p.Ce + (t - p.t0)) * dm.hd + (size_t)h * D;
 #pragma unroll
       for (int db = 0; db < NK; ++db) {
         h4 v;
@@ -393,10 +412,10 @@ __global__ __launch_bounds__(kBlock) void k_pf_swiglu(PfArgs p) {
   }
 }
 
-// s_m = cos(hin[m], hout[m]) in fp64
+// s_m = cos(hin[m], hout[m]) in fp64, m the global row of chunk-local row blockIdx.x
 __global__ __launch_bounds__(kBlock) void k_pf_cos(PfArgs p) {
   __shared__ double red[4];
-  const int m = blockIdx.x;
+  const int64_t m = pf_row(blockIdx.x, p.Ce, p.t0, p.P);
   const int d = p.dm.d;
   double s0 = 0, s1 = 0, s2 = 0;
   for (int i = threadIdx.x; i < d; i += kBlock) {
@@ -491,96 +510,109 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
   PfArgs q = p;  // hin/hout swap per layer
   for (int l = 1; l <= dm.L; ++l) {
     const LayerDev& lw = host_layers[l - 1];
-    // attention half
-    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(M), dim3(kBlock), 0, st, (const f16*)q.hin, lw.attn_norm,
-                       q.act, dm.d, dm.eps);
-    PfGemmArgs g{};
-    g.M = M;
-    g.group = dm.group;
-    g.seq_route = q.seq_route;
-    g.P = q.P;
-    g.A = q.act;
-    g.N = dm.nqkv;
-    g.K = dm.d;
-    g.seg_ptr[0] = lw.wq;
-    g.seg_ptr[1] = lw.wk;
-    g.seg_ptr[2] = lw.wv;
-    g.seg_start[0] = 0;
-    g.seg_start[1] = dm.hd;
-    g.seg_start[2] = dm.hd + dm.Hkv * dm.D;
-    g.seg_start[3] = dm.nqkv;
-    g.w4 = lw.r_qkv;
-    g.s4 = lw.s_qkv;
-    g.C = q.qkv;
-    g.epi = EPI_STORE;
-    if ((e = gemm(g, lw, 0, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_rope_kv, dim3(M), dim3(kBlock), 0, st, q, l);
-    {
-      const int G = dm.H / dm.Hkv;
-      dim3 grid((q.P + 31) / 32, dm.Hkv, dm.B);
-      if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_fattn<128, 4>), grid, dim3(4 * kWave), 0, st, q, l);
-      else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_fattn<64, 4>), grid, dim3(4 * kWave), 0, st, q, l);
-      else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_fattn<64, 2>), grid, dim3(2 * kWave), 0, st, q, l);
-      else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_fattn<128, 2>), grid, dim3(2 * kWave), 0, st, q, l);
-      else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_fattn<128, 1>), grid, dim3(kWave), 0, st, q, l);
-      else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_fattn<64, 1>), grid, dim3(kWave), 0, st, q, l);
-      else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_fattn<128, 8>), grid, dim3(8 * kWave), 0, st, q, l);
-      else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_fattn<64, 8>), grid, dim3(8 * kWave), 0, st, q, l);
-      else return hipErrorInvalidValue;
+    for (int t0 = 0; t0 < q.P; t0 += q.Ct) {
+      q.t0 = t0;
+      q.Ce = min(q.Ct, q.P - t0);
+      const int Mc = dm.B * q.Ce;  // rows of this chunk
+      // attention half
+      hipLaunchKernelGGL(k_pf_rmsnorm, dim3(Mc), dim3(kBlock), 0, st, (const f16*)q.hin, lw.attn_norm,
+                         q.act, dm.d, dm.eps, q.P, q.Ce, q.t0);
+      PfGemmArgs g{};
+      g.M = Mc;
+      g.group = dm.group;
+      g.seq_route = q.seq_route;
+      g.P = q.Ce;
+      g.Ptot = q.P;
+      g.t0 = q.t0;
+      g.A = q.act;
+      g.N = dm.nqkv;
+      g.K = dm.d;
+      g.seg_ptr[0] = lw.wq;
+      g.seg_ptr[1] = lw.wk;
+      g.seg_ptr[2] = lw.wv;
+      g.seg_start[0] = 0;
+      g.seg_start[1] = dm.hd;
+      g.seg_start[2] = dm.hd + dm.Hkv * dm.D;
+      g.seg_start[3] = dm.nqkv;
+      g.w4 = lw.r_qkv;
+      g.s4 = lw.s_qkv;
+      g.z4 = lw.z_qkv;
+      g.C = q.qkv;
+      g.epi = EPI_STORE;
+      if ((e = gemm(g, lw, 0, st)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_pf_rope_kv, dim3(Mc), dim3(kBlock), 0, st, q, l);
+      {
+        const int G = dm.H / dm.Hkv;
+        dim3 grid((q.Ce + 31) / 32, dm.Hkv, dm.B);
+        if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_fattn<128, 4>), grid, dim3(4 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_fattn<64, 4>), grid, dim3(4 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_fattn<64, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+        else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_fattn<128, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+        else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_fattn<128, 1>), grid, dim3(kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_fattn<64, 1>), grid, dim3(kWave), 0, st, q, l);
+        else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_fattn<128, 8>), grid, dim3(8 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_fattn<64, 8>), grid, dim3(8 * kWave), 0, st, q, l);
+        else return hipErrorInvalidValue;
+      }
+      // O projection + residual (the residual stream rows of this chunk)
+      g.A = q.attn;
+      g.N = dm.d;
+      g.K = dm.hd;
+      g.seg_ptr[0] = lw.wo;
+      g.seg_start[0] = 0;
+      g.seg_start[1] = dm.d;
+      g.seg_start[2] = dm.d;
+      g.seg_start[3] = dm.d;
+      g.w4 = lw.r_o;
+      g.s4 = lw.s_o;
+      g.z4 = lw.z_o;
+      g.C = q.hmid;
+      g.R = q.hin;
+      g.r_global = 1;
+      g.epi = EPI_RESID;
+      if ((e = gemm(g, lw, 1, st)) != hipSuccess) return e;
+      g.r_global = 0;
+      // MLP half
+      hipLaunchKernelGGL(k_pf_rmsnorm, dim3(Mc), dim3(kBlock), 0, st, (const f16*)q.hmid, lw.mlp_norm,
+                         q.act, dm.d, dm.eps, 0, 0, 0);
+      g.A = q.act;
+      g.N = 2 * dm.F;
+      g.K = dm.d;
+      g.seg_ptr[0] = lw.wg;
+      g.seg_ptr[1] = lw.wu;
+      g.seg_start[0] = 0;
+      g.seg_start[1] = dm.F;
+      g.seg_start[2] = 2 * dm.F;
+      g.seg_start[3] = 2 * dm.F;
+      g.w4 = lw.r_gu;
+      g.s4 = lw.s_gu;
+      g.z4 = lw.z_gu;
+      g.C = q.gu;
+      g.R = nullptr;
+      g.epi = EPI_STORE;
+      if ((e = gemm(g, lw, 2, st)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_pf_swiglu, dim3(Mc), dim3(kBlock), 0, st, q);
+      g.A = q.a2;
+      g.N = dm.d;
+      g.K = dm.F;
+      g.seg_ptr[0] = lw.wd;
+      g.seg_start[0] = 0;
+      g.seg_start[1] = dm.d;
+      g.seg_start[2] = dm.d;
+      g.seg_start[3] = dm.d;
+      g.w4 = lw.r_d;
+      g.s4 = lw.s_d;
+      g.z4 = lw.z_d;
+      g.C = q.hout;
+      g.c_global = 1;
+      g.R = q.hmid;
+      g.epi = EPI_RESID;
+      if ((e = gemm(g, lw, 3, st)) != hipSuccess) return e;
+      // per-token similarity of this chunk's rows (the exit test needs all of them)
+      if (l < dm.L) hipLaunchKernelGGL(k_pf_cos, dim3(Mc), dim3(kBlock), 0, st, q);
     }
-    // O projection + residual: attention output sits in hout
-    g.A = q.hout;
-    g.N = dm.d;
-    g.K = dm.hd;
-    g.seg_ptr[0] = lw.wo;
-    g.seg_start[0] = 0;
-    g.seg_start[1] = dm.d;
-    g.seg_start[2] = dm.d;
-    g.seg_start[3] = dm.d;
-    g.w4 = lw.r_o;
-    g.s4 = lw.s_o;
-    g.C = q.hmid;
-    g.R = q.hin;
-    g.epi = EPI_RESID;
-    if ((e = gemm(g, lw, 1, st)) != hipSuccess) return e;
-    // MLP half
-    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(M), dim3(kBlock), 0, st, (const f16*)q.hmid, lw.mlp_norm,
-                       q.act, dm.d, dm.eps);
-    g.A = q.act;
-    g.N = 2 * dm.F;
-    g.K = dm.d;
-    g.seg_ptr[0] = lw.wg;
-    g.seg_ptr[1] = lw.wu;
-    g.seg_start[0] = 0;
-    g.seg_start[1] = dm.F;
-    g.seg_start[2] = 2 * dm.F;
-    g.seg_start[3] = 2 * dm.F;
-    g.w4 = lw.r_gu;
-    g.s4 = lw.s_gu;
-    g.C = q.gu;
-    g.R = nullptr;
-    g.epi = EPI_STORE;
-    if ((e = gemm(g, lw, 2, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_swiglu, dim3(M), dim3(kBlock), 0, st, q);
-    g.A = q.a2;
-    g.N = dm.d;
-    g.K = dm.F;
-    g.seg_ptr[0] = lw.wd;
-    g.seg_start[0] = 0;
-    g.seg_start[1] = dm.d;
-    g.seg_start[2] = dm.d;
-    g.seg_start[3] = dm.d;
-    g.w4 = lw.r_d;
-    g.s4 = lw.s_d;
-    g.C = q.hout;
-    g.R = q.hmid;
-    g.epi = EPI_RESID;
-    if ((e = gemm(g, lw, 3, st)) != hipSuccess) return e;
-    // sequence-level exit decision after this layer
-    if (l < dm.L) {
-      hipLaunchKernelGGL(k_pf_cos, dim3(M), dim3(kBlock), 0, st, q);
-      hipLaunchKernelGGL(k_pf_decide, dim3(dm.B), dim3(kBlock), 0, st, q, l, forced, tau);
-    }
+    // sequence-level exit decision after this layer (every chunk has run it)
+    if (l < dm.L) hipLaunchKernelGGL(k_pf_decide, dim3(dm.B), dim3(kBlock), 0, st, q, l, forced, tau);
     f16* t = q.hin;
     q.hin = q.hout;
     q.hout = t;

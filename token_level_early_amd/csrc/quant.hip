@@ -11,10 +11,18 @@
 // implementation of the same formula.
 #include "params.hpp"
 
-// One thread per (row, group) of the padded device layout.
+// Zero-point format (the scale-and-zero storage of the pages' other backends, HQQ and AWQ:
+// paperlayer.ai summary, appendix A.1; without their calibration): asymmetric round-to-nearest
+// int4 per group, the range widened to hold 0:
+//   lo = min(min w, 0), hi = max(max w, 0), s = fp16(fp32((hi - lo) / 15)) (hi - lo exact in
+//   fp64, fp64 quotient rounded to fp32, then to fp16), s == 0 -> q = 0 and z = 0, else
+//   z = clamp(rint(fp32(-lo / s)), 0, 15), q = clamp(rint(fp32(w / s)) + z, 0, 15); nibble u = q.
+
+// One thread per (row, group) of the padded device layout; `zeros` selects the format.
 __global__ __launch_bounds__(kBlock) void k_quantize(const f16* __restrict__ W, int N, int K,
                                                      int group, uint8_t* __restrict__ out,
-                                                     f16* __restrict__ scales) {
+                                                     f16* __restrict__ scales,
+                                                     uint8_t* __restrict__ zeros) {
   const int64_t rs = w4_row_scales(K, group);
   const int64_t rb = w4_row_bytes(K);
   const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -24,6 +32,35 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const f16* __restrict__ W, 
   const int lo = j * group;
   const int hi = min(lo + group, K);
   const f16* row = W + (size_t)n * K;
+  if (zeros) {
+    float wmin = 0.f, wmax = 0.f;  // the range always holds 0
+    for (int k = lo; k < hi; ++k) {
+      const float v = h2f(row[k]);
+      wmin = fminf(wmin, v);
+      wmax = fmaxf(wmax, v);
+    }
+    const f16 s16 = f2h((float)(((double)wmax - (double)wmin) / 15.0));
+    const float s = h2f(s16);
+    int z = 0;
+    if (s != 0.f) z = (int)fminf(fmaxf(rintf((float)((double)(-wmin) / (double)s)), 0.f), 15.f);
+    uint8_t* orow = out + (size_t)n * rb;
+    for (int k = lo; k < lo + group; k += 2) {
+      int u[2];
+      for (int h = 0; h < 2; ++h) {
+        const int kk = k + h;
+        int q = 0;
+        if (kk < hi && s != 0.f) {
+          const float r = rintf((float)((double)h2f(row[kk]) / (double)s)) + (float)z;
+          q = (int)fminf(fmaxf(r, 0.f), 15.f);
+        }
+        u[h] = q;
+      }
+      orow[k / 2] = (uint8_t)(u[0] | (u[1] << 4));
+    }
+    scales[(size_t)n * rs + j] = (lo < K) ? s16 : (f16)0.0f;
+    zeros[(size_t)n * rs + j] = (uint8_t)((lo < K) ? z : 0);
+    return;
+  }
   float amax = 0.f;
   for (int k = lo; k < hi; ++k) amax = fmaxf(amax, fabsf(h2f(row[k])));
   const float s32 = (float)((double)amax / 7.0);
@@ -46,11 +83,14 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const f16* __restrict__ W, 
   scales[(size_t)n * rs + j] = (lo < K) ? s16 : (f16)0.0f;
 }
 
-// Canonical export: packed [N][ceil(K/2)], scales [N][ceil(K/group)] (drops the padding).
+// Canonical export: packed [N][ceil(K/2)], scales [N][ceil(K/group)] and, for the zero-point
+// format, zero points [N][ceil(K/group)] (drops the padding).
 __global__ __launch_bounds__(kBlock) void k_export(const uint8_t* __restrict__ in,
-                                                   const f16* __restrict__ sin_, int N, int K,
+                                                   const f16* __restrict__ sin_,
+                                                   const uint8_t* __restrict__ zin, int N, int K,
                                                    int group, uint8_t* __restrict__ packed,
-                                                   uint16_t* __restrict__ scales) {
+                                                   uint16_t* __restrict__ scales,
+                                                   uint8_t* __restrict__ zeros) {
   const int64_t rb = w4_row_bytes(K), rs = w4_row_scales(K, group);
   const int kb = (K + 1) / 2, ng = (K + group - 1) / group;
   const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -58,12 +98,13 @@ __global__ __launch_bounds__(kBlock) void k_export(const uint8_t* __restrict__ i
   if (idx < nb) {
     const int n = (int)(idx / kb), i = (int)(idx % kb);
     uint8_t v = in[(size_t)n * rb + i];
-    if ((K & 1) && i == kb - 1) v = (uint8_t)((v & 0x0F) | 0x80);  // pad nibble of odd K
+    if ((K & 1) && i == kb - 1) v = (uint8_t)((v & 0x0F) | (zin ? 0x00 : 0x80));  // pad nibble of odd K
     packed[idx] = v;
   }
   if (idx < (int64_t)N * ng) {
     const int n = (int)(idx / ng), j = (int)(idx % ng);
     scales[idx] = __builtin_bit_cast(uint16_t, sin_[(size_t)n * rs + j]);
+    if (zin) zeros[idx] = zin[(size_t)n * rs + j];
   }
 }
 
@@ -84,19 +125,21 @@ __global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* p, int64_t n, uin
 }
 
 hipError_t river_launch_quantize(const f16* W, int N, int K, int group, uint8_t* out, f16* scales,
-                                 hipStream_t st) {
+                                 uint8_t* zeros, hipStream_t st) {
   const int64_t n = (int64_t)N * w4_row_scales(K, group);
   const int64_t g = (n + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)g), dim3(kBlock), 0, st, W, N, K, group, out, scales);
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)g), dim3(kBlock), 0, st, W, N, K, group, out, scales,
+                     zeros);
   return hipGetLastError();
 }
 
-hipError_t river_launch_export(const uint8_t* in, const f16* sin_, int N, int K, int group,
-                               uint8_t* packed, uint16_t* scales, hipStream_t st) {
+hipError_t river_launch_export(const uint8_t* in, const f16* sin_, const uint8_t* zin, int N, int K,
+                               int group, uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                               hipStream_t st) {
   const int64_t n1 = (int64_t)N * ((K + 1) / 2), n2 = (int64_t)N * ((K + group - 1) / group);
   const int64_t n = n1 > n2 ? n1 : n2;
   hipLaunchKernelGGL(k_export, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, in,
-                     sin_, N, K, group, packed, scales);
+                     sin_, zin, N, K, group, packed, scales, zeros);
   return hipGetLastError();
 }
 

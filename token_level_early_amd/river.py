@@ -33,6 +33,7 @@ class Config(ctypes.Structure):
         ("vocab", ctypes.c_int32), ("tied_embeddings", ctypes.c_int32), ("rms_eps", ctypes.c_float),
         ("rope_theta", ctypes.c_float), ("group", ctypes.c_int32), ("max_batch", ctypes.c_int32),
         ("max_seq", ctypes.c_int32), ("max_prefill", ctypes.c_int32), ("entry_layer", ctypes.c_int32),
+        ("prefill_chunk", ctypes.c_int32), ("zero_point", ctypes.c_int32),
     ]
 
 
@@ -75,12 +76,14 @@ def load(path=LIB_PATH):
         "river_positions": [VP, P(I32)],
         "river_decode_path": [VP, P(I32)],
         "river_device_status": [VP, VP],
-        "river_export_river": [VP, I32, I32, VP, VP, VP],
+        "river_export_river": [VP, I32, I32, VP, VP, VP, VP],
         "river_debug_hidden": [VP, VP, VP],
         "river_decode_backbone_steps": [VP, VP, I32, VP, VP],
         "river_timer_arm": [VP, I32, I32],
         "river_timer_read": [VP, P(F32), P(I32)],
         "river_kv_write_counts": [VP, VP, VP],
+        "river_weight_residency": [VP, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64)],
+        "river_weight_placement": [VP, P(I32)],
         "river_kv_counting": [P(I32)],
     }
     for name, args in sig.items():
@@ -104,7 +107,8 @@ def make_config(c, max_seq, max_prefill=None, batch=1):
                   head_dim=c["D"], d_ffn=c["F"], vocab=c["V"], tied_embeddings=int(c["tied"]),
                   rms_eps=c["eps"], rope_theta=c["theta"], group=c["group"], max_batch=batch,
                   max_seq=max_seq, max_prefill=max_prefill or max_seq,
-                  entry_layer=c.get("entry", 1))
+                  entry_layer=c.get("entry", 1), prefill_chunk=int(c.get("prefill_chunk", 0)),
+                  zero_point=int(bool(c.get("zero_point", False))))
 
 
 def kv_layout(cfg: Config) -> KVDesc:
@@ -132,7 +136,10 @@ class River:
     KV cache, river and scratch buffers sized by the library."""
 
     def __init__(self, c, weights, max_seq, max_prefill=None, batch=1, device="cuda",
-                 lib_path=LIB_PATH):
+                 lib_path=LIB_PATH, offload_from=None):
+        """offload_from: backbone blocks with 0-based index >= offload_from are copied to
+        page-locked host memory and handed to the library there (backbone offloading); the
+        caller's device copies are not touched."""
         self.lib = load(lib_path)
         self.c = dict(c)
         self.cfg = make_config(c, max_seq, max_prefill, batch)
@@ -149,10 +156,16 @@ class River:
         self.scratch = torch.empty(sb, dtype=torch.uint8, device=dev)
         L = c["L"]
         self._lw = (LayerWeights * L)()
+        self._host = []  # page-locked copies of offloaded backbone blocks (kept alive here)
         for i, lw in enumerate(weights["layers"]):
             for n in ("attn_norm", "mlp_norm") + MATS:
                 t = lw[n]
                 assert t.is_cuda and t.dtype == torch.float16 and t.is_contiguous(), n
+                if offload_from is not None and i >= offload_from and n in MATS:
+                    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+                    h.copy_(t)
+                    self._host.append(h)
+                    t = h
                 setattr(self._lw[i], n, t.data_ptr())
         self._w = Weights(embed=weights["embed"].data_ptr(),
                           lm_head=None if weights["lm_head"] is None else weights["lm_head"].data_ptr(),
@@ -187,6 +200,12 @@ class River:
         arr = (ctypes.c_int32 * self.B)()
         self._chk(self.lib.river_positions(self.ctx, arr))
         return list(arr)
+
+    def residency(self):
+        """Bytes of the borrowed weights in device and in host memory, and of the river."""
+        d, h, r = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        self._chk(self.lib.river_weight_residency(self.ctx, ctypes.byref(d), ctypes.byref(h), ctypes.byref(r)))
+        return {"device_bytes": d.value, "host_bytes": h.value, "river_bytes": r.value}
 
     def decode_path(self):
         """"persistent" or "per_op": the kernels that serve this context's decode calls."""
@@ -268,7 +287,8 @@ class River:
         return list(buf[: n.value])
 
     def export_river(self, layer, which):
-        """Canonical packed nibbles [N][ceil(K/2)] uint8 and scales [N][ceil(K/g)] fp16."""
+        """Canonical packed nibbles [N][ceil(K/2)] uint8 and scales [N][ceil(K/g)] fp16, plus the
+        zero points [N][ceil(K/g)] uint8 for the zero-point format (a third return value)."""
         c = self.c
         shapes = {"wq": (c["H"] * c["D"], c["d"]), "wk": (c["Hkv"] * c["D"], c["d"]),
                   "wv": (c["Hkv"] * c["D"], c["d"]), "wo": (c["d"], c["H"] * c["D"]),
@@ -276,8 +296,12 @@ class River:
         N, K = shapes[MATS[which]]
         packed = torch.empty(N, (K + 1) // 2, dtype=torch.uint8, device=self.kv.device)
         scales = torch.empty(N, math.ceil(K / c["group"]), dtype=torch.int16, device=self.kv.device)
+        zp = bool(c.get("zero_point", False))
+        zeros = torch.empty(N, math.ceil(K / c["group"]), dtype=torch.uint8, device=self.kv.device) if zp else None
         self._chk(self.lib.river_export_river(self.ctx, int(layer), int(which), _ptr(packed),
-                                           _ptr(scales), _stream()))
+                                              _ptr(scales), _ptr(zeros), _stream()))
+        if zp:
+            return packed, scales.view(torch.float16), zeros
         return packed, scales.view(torch.float16)
 
     def kv_write_counts(self):
