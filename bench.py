@@ -56,6 +56,10 @@ def main():
                     help="host only: write the HBM-traffic summary of k_persist from rocprofv3 "
                          "counter CSVs (FETCH_SIZE / WRITE_SIZE runs of this script, then the same "
                          "two counters on --calib-copy) and the bench output of the FETCH_SIZE run")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("RESULTS_DB", "BENCH_LOG", "OUT_MD"),
+                    help="host only: write a markdown summary of a rocprofv3 --kernel-trace --stats "
+                         "run of this script (its rocpd database and its log) with the persistent "
+                         "kernel's algorithmic bytes per launch and achieved bandwidth")
     ap.add_argument("--tau-sweep", type=int, default=0, metavar="N",
                     help="instead of the forced-schedule run: decode in tau mode at N values of tau "
                          "(quantiles of the similarities of a no-exit run) and report tokens/s "
@@ -63,6 +67,9 @@ def main():
     args = ap.parse_args()
     if args.pmc_summary:
         write_pmc_summary(*args.pmc_summary)
+        return
+    if args.trace_summary:
+        write_trace_summary(*args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -244,6 +251,11 @@ def main():
                 "speedup_over_full_depth": round(fms / zms, 4) if full else None}
         log(f"all river: {allr}")
 
+    # ---- prompt prefill at full depth (the step before decode): whole-prompt time and the
+    # arithmetic rate of its linear maps and causal attention
+    pf = prefill_rate(rv, toks, c, B, P, torch)
+    log(f"prefill: {pf}")
+
     # ---- achievable ceiling on this part: a plain device copy and a plain read of 1 GiB
     ceiling = hbm_ceiling(torch)
     log(f"measured HBM ceiling: {ceiling}")
@@ -306,6 +318,7 @@ def main():
         "full_depth_fp16": full,
         "all_river_int4": allr,
         "cpu_baseline": cpu,
+        "prefill_full_depth": pf,
     }
     print(json.dumps(out), flush=True)
 
@@ -442,6 +455,85 @@ def write_pmc_summary(f_csv, w_csv, cf_csv, cw_csv, bench_log):
         json.dump(summary, f, indent=1)
         f.write("\n")
     print(json.dumps({k: summary[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch_same_launches")}))
+
+
+def prefill_rate(rv, toks, c, B, P, torch, reps=2):
+    """Full-depth prefill of the bench prompt, best of `reps` after one untimed call (HIP
+    events on the current stream). FLOPs: 2 per weight per prompt row for the linear maps of
+    every block, 2*2*H*D per (query, visible key) pair for causal attention (QK^T and PV), the
+    LM head on the last position of each row."""
+    L, d, H, D, Hkv, F, V = c["L"], c["d"], c["H"], c["D"], c["Hkv"], c["F"], c["V"]
+    P_l = (H + 2 * Hkv) * D * d + d * H * D + 3 * F * d
+    lin = 2.0 * B * P * P_l * L + 2.0 * B * V * d
+    att = 2.0 * 2 * H * D * B * (P * (P + 1) / 2) * L
+    rv.prefill(toks, prefill_exit=L)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rv.prefill(toks, prefill_exit=L)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        best = t if best is None else min(best, t)
+    check_status(rv, "prefill timing")
+    return {"ms": round(best, 2), "tokens_per_s": round(B * P / (best / 1e3), 1),
+            "TFLOP/s": round((lin + att) / (best / 1e3) / 1e12, 1),
+            "frac_of_fp16_mfma_peak": round((lin + att) / (best / 1e3) / 2.5e15, 4),
+            "linear_TFLOP": round(lin / 1e12, 2), "attention_TFLOP": round(att / 1e12, 2),
+            "how": f"full-depth prefill of {B} x {P} tokens, best of {reps} after one untimed call"}
+
+
+def write_trace_summary(db, bench_log, out_md):
+    """Markdown summary of a kernel-trace run: the rocpd database's top_kernels view (torch's
+    own kernels, which only generate the synthetic inputs, left out) and, for the persistent
+    decode kernel, the bench's algorithmic bytes per launch against the traced average duration."""
+    import re
+    import sqlite3
+    rows = sqlite3.connect(db).execute(
+        "select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+    lines = [l for l in open(bench_log) if l.startswith("{") and '"metric"' in l]
+    out = json.loads(lines[-1]) if lines else None
+    cmd = [l for l in open(bench_log) if "[rocprofv3] '" in l]
+    md = ["# rocprofv3 kernel trace", ""]
+    if cmd:
+        md += ["Traced command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root):", "",
+               "```", "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/<dir> -o kt -- "
+               + re.sub(r"\S*/bench\.py", "$R/bench.py", cmd[0].split("'")[1]), "```", ""]
+    if out:
+        md += [f"Workload: {out['config']['workload']}; {out['steps']} timed steps after {out['warmup']} warm-up steps.", ""]
+    md += ["| kernel | calls | total us | avg us | % of GPU time |", "|---|---:|---:|---:|---:|"]
+    persist = None
+    for name, calls, tot, avg, pct in rows:
+        if name.startswith("void at::") or name.startswith("at::"):
+            continue
+        md.append(f"| `{name[:110]}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.2f} |")
+        if name.startswith("void k_persist") and persist is None:
+            persist = (name, calls, avg)
+    if out and out.get("roofline") and persist:
+        # the roofline pass is the run's last `launches` dispatches of the persistent kernel
+        r = out["roofline"]
+        n = int(r["launches"])
+        durs = [d for (d,) in sqlite3.connect(db).execute(
+            "select duration from kernels where name like 'void k_persist%' order by start")][-n:]
+        avg = sum(durs) / len(durs) / 1e3
+        gbs = r["bytes_per_launch"] / (avg * 1e-6) / 1e9
+        md += ["", f"Persistent decode kernel, roofline pass ({n} launches of {r['steps_per_launch']} steps, the "
+               f"run's last {n} dispatches of it): {r['bytes_per_launch'] / 1e9:.2f} GB algorithmic per launch "
+               f"(bytes model at the realised exit layers and positions: {out['config']['workload'].split('(')[-1].rstrip(')')}); "
+               f"traced average {avg:.1f} us per launch against {r['avg_launch_us']:.1f} us timed live with HIP "
+               f"events; {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s from the traced durations."]
+    if out and out.get("prefill_full_depth"):
+        pf = out["prefill_full_depth"]
+        md += ["", f"Full-depth prefill in the same run: {pf['ms']} ms, {pf['TFLOP/s']} TFLOP/s "
+               f"({pf['frac_of_fp16_mfma_peak']:.3f} of the 2.5 PF fp16 MFMA peak)."]
+    md += ["", "rocprofv3 wrote the database after the program's last line and then ended with a "
+           "segmentation fault in its exit handlers (the program launches cooperative kernels; the "
+           "figures come from the complete database)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(out_md)
 
 
 def hbm_ceiling(torch):

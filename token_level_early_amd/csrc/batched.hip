@@ -7,11 +7,11 @@
 // skips its stream entirely when no row needs it, so a layer reads both copies only when its
 // rows disagree.
 //
-// GEMM core: Y[16 rows][16 cols] = X[16][K] W[cols][K]^T on v_mfma_f32_16x16x16_f16 with fp32
-// accumulation; the batch is padded to 16 rows. Every lane loads 8 consecutive K elements of
-// one input row (A operand) and of one weight row (B operand) per 32-wide K window and feeds
-// them to two MFMAs; a dot product does not depend on which lane slot carries which K index as
-// long as both operands agree, so the two 4-element halves need no particular order. The int4
+// GEMM core: Y[16 rows][16 cols] = X[16][K] W[cols][K]^T on CDNA4's v_mfma_f32_16x16x32_f16 with
+// fp32 accumulation; the batch is padded to 16 rows. Every lane loads 8 consecutive K elements
+// of one input row (A operand) and of one weight row (B operand) per 32-wide K window: one MFMA
+// per window; a dot product does not depend on which lane slot carries which K index as long as
+// both operands agree. The int4
 // stream turns 8 nibbles into exact fp16 integers (the 0x6400 exponent trick, pairs (0,4),
 // (1,5), (2,6), (3,7)), permutes the input the same way, sums one quantisation group on the
 // MFMA and applies the fp32 group scale per output column. The four waves of a workgroup split
@@ -28,8 +28,11 @@ static constexpr int kBR = 16;  // rows of an MFMA tile (the batch, padded)
 typedef _Float16 bh4 __attribute__((ext_vector_type(4)));
 typedef float bf4 __attribute__((ext_vector_type(4)));
 
-RIVER_DEV bh4 lo4(uint4 u) { return __builtin_bit_cast(bh4, make_uint2(u.x, u.y)); }
-RIVER_DEV bh4 hi4(uint4 u) { return __builtin_bit_cast(bh4, make_uint2(u.z, u.w)); }
+typedef _Float16 bh8 __attribute__((ext_vector_type(8)));
+typedef uint32_t bu4 __attribute__((ext_vector_type(4)));
+
+// 8 fp16 values of a 16-byte load as one 16x16x32 MFMA operand
+RIVER_DEV bh8 as8(uint4 u) { return __builtin_bit_cast(bh8, (bu4){u.x, u.y, u.z, u.w}); }
 
 // ---------------------------------------------------------------------------------------
 // Per-row preparation: KIND 0 = exit test + attention RMSNorm of layer `layer`'s input,
@@ -192,8 +195,7 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
       for (int u = 0; u < WB; ++u)
 #pragma unroll
         for (int s = 0; s < TW; ++s) {
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(lo4(xa[u]), lo4(wb[u][s]), acc[s], 0, 0, 0);
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(hi4(xa[u]), hi4(wb[u][s]), acc[s], 0, 0, 0);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8(xa[u]), as8(wb[u][s]), acc[s], 0, 0, 0);
         }
     };
     uint4 xa0[WB], wb0[WB][TW], xa1[WB], wb1[WB][TW];
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
                     const float (&zc)[TW]) {
       bf4 tmp[TW];
       bf4 xs = bf4{0.f, 0.f, 0.f, 0.f};
-      const bh4 ones = bh4{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+      const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
 #pragma unroll
       for (int s = 0; s < TW; ++s) tmp[s] = bf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -254,20 +256,14 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
           const uint32_t in[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
           h2 xo[4];
           pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-          const bh4 alo = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[0]), as_u32(xo[1])));
-          const bh4 ahi = __builtin_bit_cast(bh4, make_uint2(as_u32(xo[2]), as_u32(xo[3])));
-          if (zpf) {
-            xs = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, ones, xs, 0, 0, 0);
-            xs = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, ones, xs, 0, 0, 0);
-          }
+          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
+          if (zpf) xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xs, 0, 0, 0);
 #pragma unroll
           for (int s = 0; s < TW; ++s) {
             h2 p0, p1, p2, p3;
             unpack8(wq[u][s], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-            const bh4 blo = __builtin_bit_cast(bh4, make_uint2(as_u32(p0), as_u32(p1)));
-            const bh4 bhi = __builtin_bit_cast(bh4, make_uint2(as_u32(p2), as_u32(p3)));
-            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, tmp[s], 0, 0, 0);
-            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, tmp[s], 0, 0, 0);
+            const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp[s], 0, 0, 0);
           }
         }
       }

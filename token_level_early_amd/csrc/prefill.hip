@@ -183,6 +183,186 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Prompt GEMM on CDNA4's 16x16x32 fp16 MFMA: 128 x 128 output tiles, K in steps of 64 staged
+// through a double-buffered LDS tile pair (the next step's global loads are in flight while the
+// current one runs on the matrix cores; one barrier per step; the global loads run two steps
+// ahead through two register sets). 4 waves of 64 x 64. The int4
+// river tile is unpacked into LDS as the exact fp16 integers u - z (z = 8 for the symmetric
+// format), and each step's product is scaled by the fp32 group scale of its column: a step of
+// SG = 64 positions (32 when group = 32) lies inside one quantisation group.
+// ---------------------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+static constexpr int QBM = 128, QBN = 128, QBK = 64, QLD = QBK + 8;
+
+template <int MODE, int SG>
+__global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmArgs g) {
+  __shared__ __attribute__((aligned(16))) f16 As[2][QBM][QLD];
+  __shared__ __attribute__((aligned(16))) f16 Bs[2][QBN][QLD];
+  const int m0 = blockIdx.y * QBM, n0 = blockIdx.x * QBN;
+  {  // skip tiles whose rows all belong to sequences on the other route
+    const int mlast = min(g.M, m0 + QBM) - 1;
+    bool any = false;
+    for (int sq = m0 / g.P; sq <= mlast / g.P; ++sq) any |= (g.seq_route[sq] == g.want_route);
+    if (!any) return;
+  }
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
+  const int64_t rb4 = w4_row_bytes(g.K), rs4 = w4_row_scales(g.K, g.group);
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  // loaders: A (and fp16 B) tiles are 128 rows x 64 halves = 1024 chunks of 16 B, thread t
+  // takes chunks t + 256 i (row c / 8, halves (c % 8) * 8); an int4 B tile is 128 rows x 32 B,
+  // thread t takes row t / 2, bytes (t % 2) * 16 (32 consecutive k)
+  const f16* brow[4];
+  if (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + (tid + 256 * i) / 8;
+      int si = 0;
+      while (si < 2 && n >= g.seg_start[si + 1]) ++si;
+      brow[i] = (n < g.N) ? g.seg_ptr[si] + (size_t)(n - g.seg_start[si]) * g.K : nullptr;
+    }
+  }
+  // one K step's global data of this thread, held in registers until it is stored to LDS
+  struct Regs {
+    uint4 a[4], b[4];
+    uint4 q;
+    f16 dz;
+  };
+  auto gload = [&](Regs& R, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / 8, k = k0 + (c % 8) * 8;
+      const int m = m0 + r;
+      R.a[i] = (m < g.M && k < g.K) ? *(const uint4*)(g.A + (size_t)m * g.K + k) : make_uint4(0, 0, 0, 0);
+      if (MODE == 0) R.b[i] = (brow[i] && k < g.K) ? *(const uint4*)(brow[i] + k) : make_uint4(0, 0, 0, 0);
+    }
+    if (MODE == 1) {
+      const int n = n0 + tid / 2, k = k0 + (tid % 2) * 32;
+      R.q = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+      R.dz = (f16)0.0f;
+      if (n < g.N && k < g.K) {
+        R.q = *(const uint4*)(g.w4 + (size_t)n * rb4 + k / 2);
+        if (g.z4) R.dz = (f16)(8.0f - (float)g.z4[(size_t)n * rs4 + k / g.group]);
+      }
+    }
+  };
+  auto lstore = [&](const Regs& R, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / 8, kc = (c % 8) * 8;
+      *(uint4*)&As[buf][r][kc] = R.a[i];
+      if (MODE == 0) *(uint4*)&Bs[buf][r][kc] = R.b[i];
+    }
+    if (MODE == 1) {
+      const uint32_t wd[4] = {R.q.x, R.q.y, R.q.z, R.q.w};
+      const h2 d2 = {R.dz, R.dz};  // zero-point format: u - 8 + (8 - z), exact small integers
+      f16* dst = &Bs[buf][tid / 2][(tid % 2) * 32];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        h2 p0, p1, p2, p3;
+        unpack8(wd[h], p0, p1, p2, p3);  // pairs (q0,q4),(q1,q5),(q2,q6),(q3,q7)
+        p0 += d2; p1 += d2; p2 += d2; p3 += d2;
+        h8 v;
+        v[0] = p0.x; v[1] = p1.x; v[2] = p2.x; v[3] = p3.x;
+        v[4] = p0.y; v[5] = p1.y; v[6] = p2.y; v[7] = p3.y;
+        *(h8*)(dst + h * 8) = v;
+      }
+    }
+  };
+  // column scales of this lane's 4 tiles for the step starting at k0 (MODE 1)
+  auto scales = [&](int k0, float (&sc)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + lane % 16;
+      sc[j] = (n < g.N) ? h2f(g.s4[(size_t)n * rs4 + k0 / g.group]) : 0.f;
+    }
+  };
+  auto compute = [&](int cur, int kt) {
+    float sc[2][4];
+    if (MODE == 1) {
+      scales(kt * QBK, sc[0]);
+      if (SG == 32) scales(kt * QBK + 32, sc[1]);
+    }
+    f4 tmp[4][4];
+#pragma unroll
+    for (int kk = 0; kk < QBK; kk += 32) {
+      h8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const h8*)&As[cur][wm + i * 16 + lane % 16][kk + 8 * (lane / 16)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *(const h8*)&Bs[cur][wn + j * 16 + lane % 16][kk + 8 * (lane / 16)];
+      if (MODE == 1 && (SG == 32 || kk == 0)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tmp[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (MODE == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          else
+            tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], tmp[i][j], 0, 0, 0);
+        }
+      if (MODE == 1 && (SG == 32 || kk == 32)) {
+        const float* s = sc[(SG == 32 && kk == 32) ? 1 : 0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] += s[j] * tmp[i][j];
+      }
+    }
+  };
+  // Two register sets alternate: step kt+1's data waits in one while step kt+2's loads land in
+  // the other, so every load has two steps of matrix work to arrive behind.
+  const int nk = (g.K + QBK - 1) / QBK;
+  Regs r0, r1;
+  gload(r0, 0);
+  lstore(r0, 0);
+  if (nk > 1) gload(r1, QBK);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) gload(r0, (kt + 2) * QBK);
+    compute(0, kt);
+    if (kt + 1 < nk) lstore(r1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) gload(r1, (kt + 3) * QBK);
+    compute(1, kt + 1);
+    if (kt + 2 < nk) lstore(r0, 0);
+    __syncthreads();
+  }
+  // epilogue: D[i][j] at row 4*(lane/16)+r, column lane%16 of each 16x16 block
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + j * 16 + lane % 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + i * 16 + 4 * (lane / 16) + r;
+        if (m < g.M && n < g.N && g.seq_route[m / g.P] == g.want_route) {
+          const f16 v = f2h(acc[i][j][r]);
+          const int64_t cm = g.c_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
+          if (g.epi == EPI_STORE) {
+            g.C[cm * g.N + n] = v;
+          } else {
+            const int64_t rm = g.r_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
+            g.C[cm * g.N + n] = f2h(h2f(g.R[rm * g.N + n]) + h2f(v));
+          }
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Elementwise prefill kernels (one workgroup per row unless stated)
 // ---------------------------------------------------------------------------------------
 
@@ -402,6 +582,196 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
   }
 }
 
+// The same prompt attention on CDNA4's 16x16x32 MFMA, with the K/V tiles double-buffered: the
+// next tile's global loads are issued before the current tile's products and stored to the
+// other LDS buffer after them (one barrier per tile). S^T = K Q^T takes 32 head dimensions per
+// instruction; O^T += V^T P^T takes 32 keys per instruction, the probabilities coming straight
+// from the score accumulators: lane group j holds keys 4j..4j+3 of two consecutive 16-key
+// blocks, and V^T is read from the transposed tile with the same key order (a dot product only
+// needs both operands to agree on it). NLD 16-byte K and V loads per thread per 64-key tile.
+// A workgroup takes 16*NQB queries (32): every K/V tile it stages serves them all, so the
+// causal prefix is re-read once per 32 queries of a KV head.
+template <int D, int G, int NQB>
+__global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
+  constexpr int KT = 64, QW = 16 * NQB, NT = G * kWave;
+  constexpr int NKS = D / 32;  // 32-wide steps over the head dimension
+  constexpr int NDB = D / 16;  // 16-row blocks of O^T
+  constexpr int NLD = KT * D / 8 / NT;
+  static_assert(NLD >= 1 && NLD * NT * 8 == KT * D, "tile loads");
+  __shared__ __attribute__((aligned(16))) f16 Ks[2][KT][D + 8];  // [key][dim]
+  __shared__ __attribute__((aligned(16))) f16 Vt[2][D][KT + 8];  // [dim][key]
+  const Dims& dm = p.dm;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
+  const int tend = p.t0 + p.Ce;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int lr = lane % 16, lq = lane / 16;
+  const int h = kvh * G + w;
+  const size_t hs = (size_t)dm.Tmax * D;
+  const f16* Kb = p.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + kvh) * hs;
+  const f16* Vb = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * hs;
+  const float qs = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
+
+  // Q^T operand: lane supplies Q[q = q0 + qb*16 + lr][dims ks*32 + 8*lq .. +8]
+  h8 qf[NQB][NKS];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int t = q0 + qb * 16 + lr;
+    const f16* qrow = p.act + ((size_t)b * p.Ce + (t < tend ? t - p.t0 : 0)) * dm.hd + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      h8 v = *(const h8*)(qrow + ks * 32 + 8 * lq);
+      if (t >= tend) v = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+      qf[qb][ks] = v;
+    }
+  }
+  f4 o[NDB][NQB];  // O^T: lane holds dims db*16 + 4*lq + r of query qb*16 + lr
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) o[db][qb] = (f4){0.f, 0.f, 0.f, 0.f};
+  float mrow[NQB], lsum[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    mrow[qb] = -__builtin_inff();
+    lsum[qb] = 0.f;  // this lane's share of the softmax denominator
+  }  // this lane's share of the softmax denominator
+
+  const int kend = min(tend, q0 + QW);  // keys [0, kend) can be visible to this block
+  struct Tile {
+    uint4 k[NLD], v[NLD];
+  };
+  auto gload = [&](Tile& T, int k0) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + NT * i, r = c / (D / 8), col = (c % (D / 8)) * 8;
+      const bool ok = k0 + r < kend;
+      T.k[i] = ok ? *(const uint4*)(Kb + (size_t)(k0 + r) * D + col) : make_uint4(0, 0, 0, 0);
+      T.v[i] = ok ? *(const uint4*)(Vb + (size_t)(k0 + r) * D + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](const Tile& T, int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + NT * i, r = c / (D / 8), col = (c % (D / 8)) * 8;
+      *(uint4*)&Ks[buf][r][col] = T.k[i];
+      const f16* vh = (const f16*)&T.v[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[buf][col + e][r] = vh[e];
+    }
+  };
+  auto compute = [&](int buf, int k0) {
+    f4 sc[4][NQB];  // S^T[key][q] for 4 key blocks x NQB query blocks
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) sc[kb][qb] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const h8 kf = *(const h8*)&Ks[buf][kb * 16 + lr][ks * 32 + 8 * lq];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
+      }
+    }
+    // mask, tile max per query column, online rescale
+    h4 pf[4][NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int t = q0 + qb * 16 + lr;
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kb * 16 + 4 * lq + r;
+          const float v = (key <= t && key < kend) ? sc[kb][qb][r] * qs : -__builtin_inff();
+          sc[kb][qb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const float mn = fmaxf(mrow[qb], mt);
+      const bool live = mn > -__builtin_inff();  // some visible key so far
+      const float cf = live ? exp2f(mrow[qb] - mn) : 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        h4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = live ? exp2f(sc[kb][qb][r] - mn) : 0.f;
+          pv[r] = (f16)e;
+          ps += e;
+        }
+        pf[kb][qb] = pv;
+      }
+      lsum[qb] = lsum[qb] * cf + ps;
+      mrow[qb] = mn;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db][qb] *= cf;
+    }
+    // O^T[dim][q] += V^T P^T, 32 keys (blocks 2s and 2s+1) per instruction
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      h8 pb[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const h4 a0 = pf[2 * s2][qb], a1 = pf[2 * s2 + 1][qb];
+        pb[qb] = (h8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const h4 v0 = *(const h4*)&Vt[buf][db * 16 + lr][(2 * s2) * 16 + 4 * lq];
+        const h4 v1 = *(const h4*)&Vt[buf][db * 16 + lr][(2 * s2 + 1) * 16 + 4 * lq];
+        const h8 vf = (h8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[qb], o[db][qb], 0, 0, 0);
+      }
+    }
+  };
+  const int nt = (kend + KT - 1) / KT;
+  Tile t0r, t1r;
+  if (nt > 0) {
+    gload(t0r, 0);
+    lstore(t0r, 0);
+  }
+  if (nt > 1) gload(t1r, KT);
+  __syncthreads();
+  for (int kt = 0; kt < nt; kt += 2) {
+    if (kt + 2 < nt) gload(t0r, (kt + 2) * KT);
+    compute(0, kt * KT);
+    if (kt + 1 < nt) lstore(t1r, 1);
+    __syncthreads();
+    if (kt + 1 >= nt) break;
+    if (kt + 3 < nt) gload(t1r, (kt + 3) * KT);
+    compute(1, (kt + 1) * KT);
+    if (kt + 2 < nt) lstore(t0r, 0);
+    __syncthreads();
+  }
+  // denominators (the four lanes of a query column hold disjoint keys), normalise, store
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float l = lsum[qb];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int t = q0 + qb * 16 + lr;
+    if (t < tend) {
+      f16* orow = p.attn + ((size_t)b * p.Ce + (t - p.t0)) * dm.hd + (size_t)h * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        h4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (f16)(o[db][qb][r] / l);
+        *(h4*)(orow + db * 16 + 4 * lq) = v;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void k_pf_swiglu(PfArgs p) {
   const int m = blockIdx.x;
   const int F = p.dm.F;
@@ -489,12 +859,13 @@ __global__ void k_pf_init_routes(PfArgs p) {
 static hipError_t gemm(const PfGemmArgs& g0, const LayerDev& lw, int which, hipStream_t st) {
   // which: 0 qkv, 1 o, 2 gu, 3 down. Launch the fp16 and the int4 variant; each skips the
   // tiles whose sequences are on the other route.
-  dim3 grid((g0.N + GBN - 1) / GBN, (g0.M + GBM - 1) / GBM);
+  dim3 grid((g0.N + QBN - 1) / QBN, (g0.M + QBM - 1) / QBM);
   PfGemmArgs g = g0;
   g.want_route = ROUTE_BACKBONE;
-  hipLaunchKernelGGL(k_pf_gemm<0>, grid, dim3(kBlock), 0, st, g);
+  hipLaunchKernelGGL((k_pf_gemm2<0, 64>), grid, dim3(kBlock), 0, st, g);
   g.want_route = ROUTE_RIVER;
-  hipLaunchKernelGGL(k_pf_gemm<1>, grid, dim3(kBlock), 0, st, g);
+  if (g.group >= 64) hipLaunchKernelGGL((k_pf_gemm2<1, 64>), grid, dim3(kBlock), 0, st, g);
+  else hipLaunchKernelGGL((k_pf_gemm2<1, 32>), grid, dim3(kBlock), 0, st, g);
   (void)lw;
   (void)which;
   return hipGetLastError();
@@ -544,14 +915,14 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       {
         const int G = dm.H / dm.Hkv;
         dim3 grid((q.Ce + 31) / 32, dm.Hkv, dm.B);
-        if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_fattn<128, 4>), grid, dim3(4 * kWave), 0, st, q, l);
-        else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_fattn<64, 4>), grid, dim3(4 * kWave), 0, st, q, l);
-        else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_fattn<64, 2>), grid, dim3(2 * kWave), 0, st, q, l);
-        else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_fattn<128, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+        if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_pf_fattn2<128, 4, 2>), grid, dim3(4 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_pf_fattn2<64, 4, 2>), grid, dim3(4 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_pf_fattn2<64, 2, 2>), grid, dim3(2 * kWave), 0, st, q, l);
+        else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_pf_fattn2<128, 2, 2>), grid, dim3(2 * kWave), 0, st, q, l);
         else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_pf_fattn<128, 1>), grid, dim3(kWave), 0, st, q, l);
         else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_pf_fattn<64, 1>), grid, dim3(kWave), 0, st, q, l);
-        else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_fattn<128, 8>), grid, dim3(8 * kWave), 0, st, q, l);
-        else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_fattn<64, 8>), grid, dim3(8 * kWave), 0, st, q, l);
+        else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_pf_fattn2<128, 8, 2>), grid, dim3(8 * kWave), 0, st, q, l);
+        else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_pf_fattn2<64, 8, 2>), grid, dim3(8 * kWave), 0, st, q, l);
         else return hipErrorInvalidValue;
       }
       // O projection + residual (the residual stream rows of this chunk)
