@@ -160,6 +160,7 @@ struct ScratchLayout {
   uint64_t pf_hin, pf_hout, pf_hmid, pf_act, pf_attn, pf_qkv, pf_gu, pf_a2, pf_cos, pf_route, pf_exit,
       pf_minsim;
   uint64_t kvcnt;  // debug build: per-element KV write counters (0 bytes otherwise)
+  uint64_t bpart, bcnt, bcnt_bytes;  // batched projections: partial tiles, per-tile slice counters
   uint64_t total;
   int smax;
   int ncnt;
@@ -204,6 +205,18 @@ ScratchLayout scratch_layout(const Dims& d) {
   s.tagc = take(8);
   s.t_end = off;
   s.xn = take(B * d.d * 2);                // batched decode: normalised block inputs
+  {  // batched projections split over K: partial tiles of both streams, slice counters
+    uint64_t parts = 0, tiles = 0;
+    for (int op = OP_QKV; op <= OP_LM; ++op) {
+      const int S = b_split(op, d), T = b_tiles(op, d);
+      if (S > 1 && (uint64_t)S * T > parts) parts = (uint64_t)S * T;
+      if (S > 1 && (uint64_t)T > tiles) tiles = T;
+    }
+    if (B < 2) parts = tiles = 0;
+    s.bpart = take(2 * parts * 256 * 4);
+    s.bcnt_bytes = align256(2 * tiles * 4);
+    s.bcnt = take(s.bcnt_bytes);
+  }
   s.layers = take((uint64_t)d.L * sizeof(LayerDev));
   s.rope = take((uint64_t)d.Tmax * (d.D / 2) * 8);
   // prefill: the residual stream of every prompt row, the rest per chunk of positions
@@ -369,6 +382,8 @@ static DecodeArgs base_args(const river_ctx* c) {
   a.t_part = (unsigned long long*)(sc + s.t_part);
   a.tagc = (uint32_t*)(sc + s.tagc);
   a.attn_smax = s.smax;
+  a.bpart = (float*)(sc + s.bpart);
+  a.bcnt = (uint32_t*)(sc + s.bcnt);
 #ifdef RIVER_DEBUG_KV_COUNT
   a.kvcnt = (uint32_t*)(sc + s.kvcnt);
 #endif
@@ -533,6 +548,7 @@ int river_init(const river_config* cfg, const river_weights* w, void* kv, void* 
   if ((e = river_launch_fill(c->scratch + c->sl.route, (uint64_t)(d.L + 2) * d.B * 4, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.pos, 256 * 3, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.cnt, align256((uint64_t)c->sl.ncnt * 4), 0, st)) ||
+      (c->sl.bcnt_bytes && (e = river_launch_fill(c->scratch + c->sl.bcnt, c->sl.bcnt_bytes, 0, st))) ||
       (e = river_launch_fill(c->scratch + c->sl.amax, align256((uint64_t)2 * d.B * 8), 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.t_qkv, c->sl.t_end - c->sl.t_qkv, 0, st)) ||
       (e = river_launch_fill(c->scratch + c->sl.kvcnt, c->sl.total - c->sl.kvcnt, 0, st)) ||

@@ -8,14 +8,12 @@
 // rows disagree.
 //
 // GEMM core: Y[16 rows][16 cols] = X[16][K] W[cols][K]^T on CDNA4's v_mfma_f32_16x16x32_f16 with
-// fp32 accumulation; the batch is padded to 16 rows. Every lane loads 8 consecutive K elements
-// of one input row (A operand) and of one weight row (B operand) per 32-wide K window: one MFMA
-// per window; a dot product does not depend on which lane slot carries which K index as long as
-// both operands agree. The int4
-// stream turns 8 nibbles into exact fp16 integers (the 0x6400 exponent trick, pairs (0,4),
+// fp32 accumulation; the batch is padded to 16 rows. Every lane feeds 8 K elements of one input
+// row (A operand) and of one weight row (B operand) to each MFMA (32 K per instruction). The
+// int4 stream turns 8 nibbles into exact fp16 integers (the 0x6400 exponent trick, pairs (0,4),
 // (1,5), (2,6), (3,7)), permutes the input the same way, sums one quantisation group on the
-// MFMA and applies the fp32 group scale per output column. The four waves of a workgroup split
-// K and meet in LDS.
+// MFMA and applies the fp32 group scale per output column. The waves of a workgroup split K
+// and meet in LDS.
 //
 // Per layer: k_b_prep (exit test per row, then the attention RMSNorm) -> QKV (RoPE, q and the
 // KV append at each row's position) -> attention (the split-K kernel shared with batch 1, one
@@ -120,185 +118,95 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
 }
 
 // ---------------------------------------------------------------------------------------
-// Batched projection: grid (tiles of 16 logical columns, stream), 4 waves splitting K.
-// ---------------------------------------------------------------------------------------
-// 16-column tiles per workgroup: four for gate|up (two weight streams, the int4 one reading
-// four times its own bytes of input per tile); one elsewhere, where fewer workgroups measured
-// slower
-static constexpr int kTW = 4;
-__host__ __device__ constexpr int b_tw(int op) { return op == OP_GU ? 4 : 1; }
-struct BSmem {
-  float part[4][kTW][kBR][kBR];  // per wave (K slice)
-  float y[kTW][kBR][kBR];
-  int need;
-};
+// Batched projection. Workgroup (g, s) of the grid (g < groups, s < S = b_split) stages slice s
+// of the input's K range, X[rows][k0 .. k0 + Ks), in LDS once, then computes that slice's part
+// of the 16-column tiles g, g + groups, ... of every stream a row runs at this layer. Its 8
+// waves split the slice and run one double-buffered weight-load pipeline across all of its
+// tiles (the next tile's weights are in flight while a tile's wave partials are summed in LDS
+// and its epilogue runs), reading the A operand from LDS: an input read through the caches by
+// every wave for every tile holds the weight stream to about half the bandwidth it reaches
+// alone. With S > 1, each workgroup stores its partial tile (written through to memory) and
+// counts it on the tile's counter; the one that completes the count sums the S partials in
+// slice order, so results do not depend on which finishes last, and resets the counter.
+// K slots inside one MFMA may be assigned freely as long as both operands agree: the fp16
+// stream gives lane (column c, quarter kq) K = base + 32 j + 8 kq + i for MFMA j (each load
+// instruction reads 64 contiguous bytes of every weight row), the int4 stream K = base +
+// kq * (group / 4) + 8 j + i (each lane reads its nibbles as one contiguous 16-, 8- or 4-byte
+// piece). LDS keeps piece p (8 values) of row r at p * 16 + r, so the 64 lanes of one A-operand
+// read take 4 consecutive pieces of 16 rows: 1 KB contiguous.
+#ifndef RIVER_BG_NB
+#define RIVER_BG_NB 1
+#endif
+#ifndef RIVER_BG_NG
+#define RIVER_BG_NG 2
+#endif
+static constexpr int kGB = 512;  // threads per projection workgroup
+static constexpr int kBMaxTiles = 64;  // tiles per workgroup when K is split (b_split keeps to it)
+static constexpr int kBMaxSplit = 8;   // K slices of one projection at most
+static constexpr int kGW = kGB / kWave;
 
-template <int OP>
-__global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, const f16* xin) {
-  __shared__ BSmem sm;
+// WPG: 32-wide K windows per int4 quantisation group (group / 32); SPLIT: b_split > 1. Without
+// a split the epilogue runs as each tile completes; with one, the loop only stores partial
+// tiles (an epilogue's dependent loads would wait for every weight load in flight).
+template <int OP, int WPG, bool SPLIT>
+__global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f16* xin, int streams) {
+  __shared__ uint4 xs[kBXs / 8 * kBR];  // the input slice, piece-interleaved
+  __shared__ float part[kGW][kBR][kBR];
+  __shared__ float ysm[kBR][kBR];
+  __shared__ int need[2], nlast, lastf[2 * kBMaxTiles];
   const Dims& dm = a.dm;
-  const int stream = blockIdx.y;  // stream 0 backbone fp16, 1 river int4
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
-  const int N = op_rows(OP, dm), K = op_k(OP, dm);
-  const LayerDev* lw = (OP == OP_LM) ? nullptr : &a.layers[layer - 1];
-  // does any row run this stream at this layer?
-  if (t == 0) sm.need = 0;
+  const int N = b_rows(OP, dm), K = b_k(OP, dm);
+  const int tiles = b_tiles(OP, dm), S = SPLIT ? b_split(OP, dm) : 1, Ks = b_slice(OP, dm);
+  const int groups = gridDim.x / S, g = blockIdx.x / S, sl = blockIdx.x % S;
+  const int k0 = sl * Ks;
+  // the layer's weight pointers, read once (left in the table, they would be reloaded inside
+  // the streaming loop behind the partial-tile stores, and each reload waits for every load)
+  LayerDev lwc{};
+  if (OP != OP_LM) lwc = a.layers[layer - 1];
+  const LayerDev* lw = &lwc;
+  // which streams does any row run at this layer?
+  if (t < 2) need[t] = 0;
   __syncthreads();
   if (t < dm.B) {
     const int r = (OP == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + t];
-    if (r == stream) atomicOr(&sm.need, 1);
+    if (r >= 0 && r < streams) atomicOr(&need[r], 1);
+  }
+  // stage the slice (rows past the batch and values past K are zero): every load is issued
+  // before the first LDS store (one round trip); workgroups start at different pieces so that
+  // they do not all read the same lines at once
+  {
+    constexpr int kPer = kBXs / 8 * kBR / kGB;
+    const int np = Ks / 8 * kBR;
+    const int rot = (int)((blockIdx.x * 613u * kBR) % (unsigned)np);
+    uint4 v[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      int i = t + m * kGB + rot;
+      i = i < np ? i : i - np;
+      const int pc = i / kBR, r = i % kBR, k = k0 + pc * 8;
+      const bool ok = t + m * kGB < np && r < dm.B && k < K;
+      const uint4 x = ldg16(xin + (ok ? (size_t)r * K + k : 0));
+      v[m] = ok ? x : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      int i = t + m * kGB + rot;
+      i = i < np ? i : i - np;
+      if (t + m * kGB < np) xs[i] = v[m];
+    }
   }
   __syncthreads();
-  if (!sm.need) return;
+  const bool need0 = need[0] != 0, need1 = need[1] != 0;
 
-  // TW 16-column tiles per workgroup: every wave reads each input window once for all of
-  // them (the inputs come from L2 for every tile, as many bytes as the fp16 weights)
-  constexpr int TW = b_tw(OP);
-  const int tile0 = blockIdx.x * TW;
   const int col = lane % 16, kq = lane / 16;
-  int n[TW];
-  bool nok[TW];
-#pragma unroll
-  for (int s = 0; s < TW; ++s) {  // this lane's weight column in tile s
-    n[s] = logical_row(OP, tile0 + s, col, kBR, dm);
-    nok[s] = n[s] < N;
-  }
-  const int xrow = lane % 16;  // batch row fed by this lane (A operand)
-  const bool xok = xrow < dm.B;
-  const f16* xp = xin + (size_t)(xok ? xrow : 0) * K;
-
-  bf4 acc[TW];
-#pragma unroll
-  for (int s = 0; s < TW; ++s) acc[s] = bf4{0.f, 0.f, 0.f, 0.f};
-  if (stream == 0) {
-    const f16* wrow[TW];
-#pragma unroll
-    for (int s = 0; s < TW; ++s)
-      wrow[s] = (OP == OP_LM) ? a.lm_head + (size_t)(nok[s] ? n[s] : 0) * dm.d : f16_row(OP, nok[s] ? n[s] : 0, *lw, a);
-    const int nwin = (K + 31) / 32;
-    const int w0 = w * nwin / 4, w1 = (w + 1) * nwin / 4;
-    // batches of two 32-wide windows, double-buffered: the next batch's loads are in flight
-    // while the current one runs on the MFMA
-    constexpr int WB = 2;
-    auto loadb = [&](int win, uint4 (&xa)[WB], uint4 (&wb)[WB][TW]) {
-#pragma unroll
-      for (int u = 0; u < WB; ++u) {
-        const int k = (win + u) * 32 + kq * 8;
-        const bool ok = win + u < w1 && k < K;
-        xa[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < TW; ++s) wb[u][s] = (ok && nok[s]) ? ldg16(wrow[s] + k) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto mmab = [&](const uint4 (&xa)[WB], const uint4 (&wb)[WB][TW]) {
-#pragma unroll
-      for (int u = 0; u < WB; ++u)
-#pragma unroll
-        for (int s = 0; s < TW; ++s) {
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8(xa[u]), as8(wb[u][s]), acc[s], 0, 0, 0);
-        }
-    };
-    uint4 xa0[WB], wb0[WB][TW], xa1[WB], wb1[WB][TW];
-    int win = w0;
-    if (win < w1) loadb(win, xa0, wb0);
-    for (; win < w1; win += 2 * WB) {
-      if (win + WB < w1) loadb(win + WB, xa1, wb1);
-      mmab(xa0, wb0);  // windows past w1 are zero: they add nothing
-      if (win + 2 * WB < w1) loadb(win + 2 * WB, xa0, wb0);
-      if (win + WB < w1) mmab(xa1, wb1);
-    }
-  } else {
-    const uint8_t* rp[TW];
-    const f16* sp[TW];
-    const uint8_t* zp[TW];  // zero-point format only (else null)
-#pragma unroll
-    for (int s = 0; s < TW; ++s) w4_row(OP, nok[s] ? n[s] : 0, *lw, dm, rp[s], sp[s], zp[s]);
-    const bool zpf = dm.zp != 0;
-    const int g = dm.group, wpg = g / 32;  // 32-wide windows per group (1, 2 or 4)
-    const int ng = (K + g - 1) / g;
-    const int g0 = w * ng / 4, g1 = (w + 1) * ng / 4;
-    // one group's windows and scales per batch, double-buffered across groups
-    auto loadg = [&](int grp, uint4 (&xr)[4], uint32_t (&wq)[4][TW], float (&sc)[TW], float (&zc)[TW]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xr[u] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < TW; ++s) wq[u][s] = 0x88888888u;
-        if (u < wpg) {
-          const int k = grp * g + u * 32 + kq * 8;
-          const bool ok = k < K;
-          xr[u] = (ok && xok) ? ldg16(xp + k) : make_uint4(0, 0, 0, 0);
-          // 8 nibbles of this lane's weight row: bytes k/2 .. k/2+3 (padding nibbles are q = 0)
-#pragma unroll
-          for (int s = 0; s < TW; ++s)
-            if (nok[s]) wq[u][s] = *(const __attribute__((address_space(1))) uint32_t*)(rp[s] + k / 2);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < TW; ++s) {
-        sc[s] = nok[s] ? h2f(sp[s][grp]) : 0.f;  // scale of (column, group)
-        zc[s] = (zpf && nok[s]) ? 8.f - (float)zp[s][grp] : 0.f;  // zero-point format: 8 - z
-      }
-    };
-    // unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z): the group's
-    // input sums per batch row come from one more MFMA against a ones operand (they land in the
-    // accumulator layout, every column holding its row's sum)
-    auto mmag = [&](const uint4 (&xr)[4], const uint32_t (&wq)[4][TW], const float (&sc)[TW],
-                    const float (&zc)[TW]) {
-      bf4 tmp[TW];
-      bf4 xs = bf4{0.f, 0.f, 0.f, 0.f};
-      const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
-#pragma unroll
-      for (int s = 0; s < TW; ++s) tmp[s] = bf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u < wpg) {
-          const uint32_t in[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
-          h2 xo[4];
-          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
-          if (zpf) xs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xs, 0, 0, 0);
-#pragma unroll
-          for (int s = 0; s < TW; ++s) {
-            h2 p0, p1, p2, p3;
-            unpack8(wq[u][s], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-            const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
-            tmp[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp[s], 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < TW; ++s)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][r] = fmaf(sc[s], zpf ? fmaf(zc[s], xs[r], tmp[s][r]) : tmp[s][r], acc[s][r]);
-    };
-    uint4 xr0[4], xr1[4];
-    uint32_t wq0[4][TW], wq1[4][TW];
-    float sc0[TW], sc1[TW], zc0[TW], zc1[TW];
-    int grp = g0;
-    if (grp < g1) loadg(grp, xr0, wq0, sc0, zc0);
-    for (; grp < g1; grp += 2) {
-      if (grp + 1 < g1) loadg(grp + 1, xr1, wq1, sc1, zc1);
-      mmag(xr0, wq0, sc0, zc0);
-      if (grp + 2 < g1) loadg(grp + 2, xr0, wq0, sc0, zc0);
-      if (grp + 1 < g1) mmag(xr1, wq1, sc1, zc1);
-    }
-  }
-  // lane holds Y[row 4*kq + r][col] of each tile; sum the four waves' K slices
-#pragma unroll
-  for (int s = 0; s < TW; ++s)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.part[w][s][4 * kq + r][col] = acc[s][r];
-  __syncthreads();
-  for (int i = t; i < TW * kBR * kBR; i += kBlock) {
-    const int s = i / (kBR * kBR), row = (i / kBR) % kBR, c = i % kBR;
-    sm.y[s][row][c] = (sm.part[0][s][row][c] + sm.part[1][s][row][c]) + (sm.part[2][s][row][c] + sm.part[3][s][row][c]);
-  }
-  __syncthreads();
+  // tiles of this workgroup: g + i * groups, i < my
+  const int my = g < tiles ? (tiles - 1 - g) / groups + 1 : 0;
+  bf4 acc = bf4{0.f, 0.f, 0.f, 0.f};
 
   // epilogue per 16-column tile: thread -> (row b, tile column c), rows on this stream only
-  auto epilogue = [&](int tile, const float (&y)[kBR][kBR]) {
-  const int b = t / kBR, c = t % kBR;
+  auto epilogue = [&](int stream, int tile, const float (&y)[kBR][kBR], int tt) {
+  const int b = tt / kBR, c = tt % kBR;
   if (b >= dm.B) return;
   if (OP != OP_LM && a.route[layer * dm.B + b] != stream) return;
   const float yv = y[b][c];
@@ -386,8 +294,249 @@ __global__ __launch_bounds__(kBlock) void k_b_gemm(DecodeArgs a, int layer, cons
     (void)v;
   }
   };
+
+  // sum the waves' parts of the tile in a fixed order; with one slice run the epilogue, else
+  // store the slice's partial tile (written through to memory; counted at the end)
+  auto finish = [&](int stream, int tile) {
 #pragma unroll
-  for (int s = 0; s < TW; ++s) epilogue(tile0 + s, sm.y[s]);
+    for (int r = 0; r < 4; ++r) part[w][4 * kq + r][col] = acc[r];
+    acc = bf4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    if (t < kBR * kBR) {
+      const int row = t / kBR, c = t % kBR;
+      float y = part[0][row][c];
+#pragma unroll
+      for (int j = 1; j < kGW; ++j) y += part[j][row][c];
+      if constexpr (!SPLIT) {
+        ysm[row][c] = y;
+      } else {
+        float* P = a.bpart + (((size_t)stream * tiles + tile) * S + sl) * (kBR * kBR);
+        __hip_atomic_store((g_f32*)P + t, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    if constexpr (!SPLIT) epilogue(stream, tile, ysm, t);
+  };
+
+  if (need0 && my > 0) {  // ---- fp16 backbone stream
+    // blocks of 128 K (four 32-wide windows); wave w takes blocks [b0, b1) of the slice in
+    // every tile. Its work is a sequence of upt units per tile (a unit is one block; waves
+    // with fewer blocks have empty units), loaded NB units per batch, batches double-buffered.
+    const int nb = Ks / 128;
+    const int b0 = w * nb / kGW, b1 = (w + 1) * nb / kGW;
+    constexpr int NB = RIVER_BG_NB;
+    const int upt = (nb + kGW - 1) / kGW;  // the same in every wave
+    const int U = my * upt, Qb = (U + NB - 1) / NB;
+    // loads are unconditional (an in-range address, the value zeroed afterwards): a load behind
+    // a branch leaves the compiler unable to count the loads in flight, and it then waits for
+    // all of them, the next batch's included
+    auto load = [&](int q, uint4 (&wb)[NB][4]) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int unit = q * NB + u;
+        const int tile = g + (unit / upt) * groups;
+        const int kb = b0 + unit % upt;
+        const int n = logical_row(OP, tile, col, kBR, dm);
+        const bool nok = unit < U && kb < b1 && n < N;
+        const f16* wrow = (OP == OP_LM) ? a.lm_head + (size_t)(nok ? n : 0) * dm.d : f16_row(OP, nok ? n : 0, *lw, a);
+        // the raw values stay in the buffer: a unit that is not this wave's reads an in-range
+        // address and is cancelled at use through a zero A operand (finite weights times zero)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = k0 + kb * 128 + j * 32 + kq * 8;
+          wb[u][j] = ldg16(wrow + ((nok && k < K) ? k : 0));
+        }
+      }
+    };
+    auto mma = [&](int q, const uint4 (&wb)[NB][4]) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int unit = q * NB + u;
+        if (unit >= U) break;  // the same in every wave
+        const int kb = b0 + unit % upt;
+        const bool kok = kb < b1;  // values past K are zero in the staged slice
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pc = (kok ? kb : 0) * 16 + 4 * j + kq;
+          const uint4 xv = xs[pc * kBR + col];
+          const uint4 xa = kok ? xv : make_uint4(0, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8(xa), as8(wb[u][j]), acc, 0, 0, 0);
+        }
+        if (unit % upt == upt - 1) finish(0, g + (unit / upt) * groups);
+      }
+    };
+    // Two register buffers in a ring: one batch's loads are in flight while the other is
+    // multiplied. No load sits behind a branch (batches past the end read an in-range address
+    // and are discarded), and the stages are fenced from the scheduler: hoisted above the
+    // MFMAs that read the buffer it refills, a load would overlap the buffer's old and new
+    // values and the loop would copy registers, waiting for every load in flight.
+    uint4 wb0[NB][4], wb1[NB][4];
+    load(0, wb0);
+    for (int q = 0; q < Qb; q += 2) {
+      load(q + 1, wb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q, wb0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(q + 2, wb0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q + 1, wb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (need1 && my > 0) {  // ---- int4 river stream
+    const bool zpf = dm.zp != 0;
+    // one quantisation group per unit: lane reads 8 * WPG contiguous K values, i.e. 4 * WPG
+    // bytes of nibbles (rows are padded to whole groups)
+    constexpr int G = 32 * WPG;
+    const int ng = Ks / G;  // groups of the slice (slices are whole 128-value blocks)
+    const int g0 = w * ng / kGW, g1 = (w + 1) * ng / kGW;
+    constexpr int NG = RIVER_BG_NG;  // units per batch
+    const int upt = (ng + kGW - 1) / kGW;
+    const int U = my * upt, Qb = (U + NG - 1) / NG;
+    const int grp0 = k0 / G;  // first group of the slice
+    auto load = [&](int q, uint32_t (&wq)[NG][WPG], f16 (&sc)[NG], uint8_t (&zc)[NG]) {
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int unit = q * NG + u;
+        const int tile = g + (unit / upt) * groups;
+        const int gs = g0 + unit % upt;  // group within the slice
+        const int grp = grp0 + gs;
+        const int n = logical_row(OP, tile, col, kBR, dm);
+        const bool gok = unit < U && gs < g1 && grp * G < K && n < N;
+        const uint8_t* rp;
+        const f16* sp;
+        const uint8_t* zp;  // zero-point format only (else null)
+        w4_row(OP, gok ? n : 0, *lw, dm, rp, sp, zp);
+        // raw values from in-range addresses (see the fp16 stream); a unit that is not this
+        // wave's is cancelled at use through a zero scale
+        const int gl = gok ? grp : 0;
+        const uint8_t* wp = rp + (gl * G + kq * 8 * WPG) / 2;
+        if (WPG == 4) {
+          const uint4 v = ldg16(wp);
+          wq[u][0] = v.x;
+          wq[u][WPG > 1 ? 1 : 0] = v.y;
+          wq[u][WPG > 2 ? 2 : 0] = v.z;
+          wq[u][WPG > 3 ? 3 : 0] = v.w;
+        } else if (WPG == 2) {
+          const unsigned long long v = *(const __attribute__((address_space(1))) unsigned long long*)wp;
+          wq[u][0] = (uint32_t)v;
+          wq[u][WPG > 1 ? 1 : 0] = (uint32_t)(v >> 32);
+        } else {
+          wq[u][0] = *(const __attribute__((address_space(1))) uint32_t*)wp;
+        }
+        sc[u] = ldg2(sp + gl);  // scale of (column, group), converted at use
+        // zero point (zero-point format; else any in-range byte, unused)
+        zc[u] = *(const __attribute__((address_space(1))) uint8_t*)(zpf ? zp + gl : (const uint8_t*)sp);
+      }
+    };
+    // unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z): the group's
+    // input sums per batch row come from one more MFMA against a ones operand (they land in the
+    // accumulator layout, every column holding its row's sum)
+    auto mma = [&](int q, const uint32_t (&wq)[NG][WPG], const f16 (&sc)[NG], const uint8_t (&zc)[NG]) {
+      const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int unit = q * NG + u;
+        if (unit >= U) break;  // the same in every wave
+        const int gs0 = g0 + unit % upt;
+        const bool gv = gs0 < g1 && (grp0 + gs0) * G < K;  // else not this wave's: cancelled
+        const int gs = gv ? gs0 : 0;
+        bf4 tmp = bf4{0.f, 0.f, 0.f, 0.f};
+        bf4 xsum = bf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < WPG; ++j) {
+          const uint4 xv = xs[(gs * 4 * WPG + kq * WPG + j) * kBR + col];
+          const uint32_t in[4] = {xv.x, xv.y, xv.z, xv.w};
+          h2 xo[4];
+          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
+          if (zpf) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xsum, 0, 0, 0);
+          h2 p0, p1, p2, p3;
+          unpack8(wq[u][j], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+          const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+          tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp, 0, 0, 0);
+        }
+        const float su = gv ? h2f(sc[u]) : 0.f;
+        const float zu = 8.f - (float)zc[u];  // zero-point format: 8 - z
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(su, zpf ? fmaf(zu, xsum[r], tmp[r]) : tmp[r], acc[r]);
+        if (unit % upt == upt - 1) finish(1, g + (unit / upt) * groups);
+      }
+    };
+    uint32_t wq0[NG][WPG], wq1[NG][WPG];
+    f16 sc0[NG], sc1[NG];
+    uint8_t zc0[NG], zc1[NG];
+    load(0, wq0, sc0, zc0);
+    for (int q = 0; q < Qb; q += 2) {  // the ring of the fp16 stream
+      load(q + 1, wq1, sc1, zc1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q, wq0, sc0, zc0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(q + 2, wq0, sc0, zc0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(q + 1, wq1, sc1, zc1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (!SPLIT || my == 0) return;
+  // ---- slices: every partial of this workgroup has been written through once its stores are
+  // acknowledged; then count them, and finish the tiles whose count this workgroup completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t < 2 * my) {
+    const int stream = t / my, tile = g + (t % my) * groups;
+    int mine = 0;
+    if (stream == 0 ? need0 : need1) {
+      uint32_t* cn = a.bcnt + (size_t)stream * tiles + tile;
+      const uint32_t done = __hip_atomic_fetch_add(cn, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mine = done == (uint32_t)(S - 1);
+      if (mine) __hip_atomic_store(cn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lastf[t] = mine;
+  }
+  __syncthreads();
+  if (t == 0) {  // compact the list of tiles to finish
+    int n = 0;
+    for (int i = 0; i < 2 * my; ++i)
+      if (lastf[i]) lastf[n++] = i;
+    nlast = n;
+  }
+  __syncthreads();
+  // wave w sums the slices of tiles w, w + 8, ... of the list into its own LDS tile (the input
+  // slice is no longer needed), then all waves run the epilogues
+  float(*yt)[kBR][kBR] = (float(*)[kBR][kBR])xs;
+  for (int r0 = 0; r0 < nlast; r0 += kGW) {
+    const int i = r0 + w;
+    if (i < nlast) {
+      const int stream = lastf[i] / my, tile = g + (lastf[i] % my) * groups;
+      const float* P = a.bpart + ((size_t)stream * tiles + tile) * S * (kBR * kBR);
+      // all S x 4 loads in flight at once, summed in slice order
+      float pv[kBMaxSplit][4];
+#pragma unroll
+      for (int j = 0; j < kBMaxSplit; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          pv[j][m] = __hip_atomic_load((g_f32*)P + (j < S ? j : 0) * (kBR * kBR) + lane + m * kWave,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = lane + m * kWave;
+        float v = pv[0][m];
+#pragma unroll
+        for (int j = 1; j < kBMaxSplit; ++j)
+          if (j < S) v += pv[j][m];
+        yt[w][e / kBR][e % kBR] = v;
+      }
+    }
+    __syncthreads();
+    if (i < nlast) {
+      const int stream = lastf[i] / my, tile = g + (lastf[i] % my) * groups;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) epilogue(stream, tile, yt[w], lane + m * kWave);
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -399,10 +548,20 @@ hipError_t river_launch_step_end(const DecodeArgs& a, hipStream_t st);
 template <int OP>
 static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const f16* xin, hipStream_t st) {
   const Dims& dm = a.dm;
-  const int N = (OP == OP_QKV) ? dm.nqkv : (OP == OP_GU) ? 2 * dm.F : (OP == OP_LM) ? dm.V : dm.d;
-  const int tiles = ((N + kBR - 1) / kBR + b_tw(OP) - 1) / b_tw(OP);  // workgroups of 16-column tiles
   const int streams = (OP == OP_LM || mode == 1) ? 1 : 2;
-  hipLaunchKernelGGL((k_b_gemm<OP>), dim3(tiles, streams), dim3(kBlock), 0, st, a, layer, xin);
+  const int S = b_split(OP, dm), groups = b_groups(OP, dm);
+  if (S > kBMaxSplit || (S > 1 && (b_tiles(OP, dm) + groups - 1) / groups > kBMaxTiles)) return hipErrorInvalidValue;
+  const dim3 grid(groups * S), block(kGB);
+  const int wpg = dm.group / 32;
+  if (S > 1) {
+    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, true>), grid, block, 0, st, a, layer, xin, streams);
+    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, true>), grid, block, 0, st, a, layer, xin, streams);
+    else hipLaunchKernelGGL((k_b_gemm<OP, 4, true>), grid, block, 0, st, a, layer, xin, streams);
+  } else {
+    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, false>), grid, block, 0, st, a, layer, xin, streams);
+    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, false>), grid, block, 0, st, a, layer, xin, streams);
+    else hipLaunchKernelGGL((k_b_gemm<OP, 4, false>), grid, block, 0, st, a, layer, xin, streams);
+  }
   return hipGetLastError();
 }
 

@@ -99,6 +99,8 @@ struct DecodeArgs {
   float* logits;         // [B][V] or null (single step only)
   float tau;
   uint32_t* kvcnt;       // debug build only: per-element KV write counters (KV layout), else null
+  float* bpart;          // batched projections: partial tiles [stream][tile][slice][16][16]
+  uint32_t* bcnt;        // batched projections: slices finished per [stream][tile] (back to 0 after each launch)
 };
 
 static constexpr int kMaxRed = 8192;
@@ -115,6 +117,39 @@ static constexpr int CNT_O = 0, CNT_DOWN = 1, CNT_LM = 2, CNT_ATTN = 8;  // attn
 
 // Decode GEMV operations (one launch each).
 enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
+
+// Batched projections (2..16 rows). A launch is a grid of at most kBGrid workgroups; workgroup
+// (g, s) holds slice s of the input's K range in LDS (at most kBXs values per row) and computes
+// that slice's contribution to the 16-column tiles g, g + groups, ...; the b_split(op) partial
+// tiles of a tile are summed, in slice order, by the workgroup that finishes it last.
+static constexpr int kBGrid = 256;
+static constexpr int kBXs = 4096;
+__host__ __device__ inline int b_rows(int op, const Dims& d) {
+  return op == OP_QKV ? d.nqkv : op == OP_GU ? 2 * d.F : op == OP_LM ? d.V : d.d;
+}
+__host__ __device__ inline int b_k(int op, const Dims& d) {
+  return op == OP_O ? d.hd : op == OP_DOWN ? d.F : d.d;
+}
+__host__ __device__ inline int b_tiles(int op, const Dims& d) { return (b_rows(op, d) + 15) / 16; }
+__host__ __device__ inline int b_split(int op, const Dims& d) {
+  const int K = b_k(op, d);
+  // more slices give each workgroup more tiles to share its staged input with; slices of at
+  // least 1024 values keep all 8 waves busy on every tile
+  int s = op == OP_LM ? 1 : op == OP_GU ? 2 : 4;
+  while (s > 1 && K / s < 1024) s /= 2;
+  const int lds = (K + kBXs - 1) / kBXs;
+  return s > lds ? s : lds;
+}
+// K values per slice: a whole number of 128-value blocks
+__host__ __device__ inline int b_slice(int op, const Dims& d) {
+  const int S = b_split(op, d), K = b_k(op, d);
+  return ((K + S - 1) / S + 127) / 128 * 128;
+}
+__host__ __device__ inline int b_groups(int op, const Dims& d) {
+  const int S = b_split(op, d), T = b_tiles(op, d);
+  const int g = kBGrid / S;
+  return T < g ? T : g;
+}
 // Timer op codes (public, see river_timer_arm): the launches of one decode step in order.
 enum { TOP_QKV = 0, TOP_ATTN = 1, TOP_O = 2, TOP_GU = 3, TOP_DOWN = 4, TOP_LM = 5, TOP_PERSIST = 6 };
 
