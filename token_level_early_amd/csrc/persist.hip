@@ -268,18 +268,42 @@ RIVER_DEV void block_cos(const f16* up, const uint32_t* ut, uint32_t utag, const
 // ---------------------------------------------------------------------------------------
 // Row streaming
 // ---------------------------------------------------------------------------------------
+// The fp16 matrices a phase reads (up to three: q, k, v), read from the layer table once per
+// phase and held wave-uniform; read per item, the table load (behind the phase's tagged
+// stores, so never hoisted by the compiler) stalls the row stream.
+template <typename T>
+RIVER_DEV const T* uniform_ptr(const T* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (const T*)(((unsigned long long)hi << 32) | lo);
+}
+struct W16 {
+  const f16* p0;
+  const f16* p1;
+  const f16* p2;
+};
 template <int OP>
-RIVER_DEV const f16* row16(const DecodeArgs& a, const LayerDev* lw, int n) {
-  const Dims& dm = a.dm;
+RIVER_DEV W16 w16_ptrs(const DecodeArgs& a, const LayerDev* lw) {
+  W16 w{nullptr, nullptr, nullptr};
+  if (OP == OP_QKV) w = W16{lw->wq, lw->wk, lw->wv};
+  else if (OP == OP_O) w.p0 = lw->wo;
+  else if (OP == OP_GU) w = W16{lw->wg, lw->wu, nullptr};
+  else if (OP == OP_DOWN) w.p0 = lw->wd;
+  else w.p0 = a.lm_head;
+  return W16{uniform_ptr(w.p0), uniform_ptr(w.p1), uniform_ptr(w.p2)};
+}
+template <int OP>
+RIVER_DEV const f16* row16(const W16& w, const Dims& dm, int n) {
   if (OP == OP_QKV) {
-    if (n < dm.hd) return lw->wq + (size_t)n * dm.d;
-    if (n < dm.hd + dm.Hkv * dm.D) return lw->wk + (size_t)(n - dm.hd) * dm.d;
-    return lw->wv + (size_t)(n - dm.hd - dm.Hkv * dm.D) * dm.d;
+    if (n < dm.hd) return w.p0 + (size_t)n * dm.d;
+    if (n < dm.hd + dm.Hkv * dm.D) return w.p1 + (size_t)(n - dm.hd) * dm.d;
+    return w.p2 + (size_t)(n - dm.hd - dm.Hkv * dm.D) * dm.d;
   }
-  if (OP == OP_O) return lw->wo + (size_t)n * dm.hd;
-  if (OP == OP_GU) return n < dm.F ? lw->wg + (size_t)n * dm.d : lw->wu + (size_t)(n - dm.F) * dm.d;
-  if (OP == OP_DOWN) return lw->wd + (size_t)n * dm.F;
-  return a.lm_head + (size_t)n * dm.d;
+  if (OP == OP_O) return w.p0 + (size_t)n * dm.hd;
+  if (OP == OP_GU) return n < dm.F ? w.p0 + (size_t)n * dm.d : w.p1 + (size_t)(n - dm.F) * dm.d;
+  if (OP == OP_DOWN) return w.p0 + (size_t)n * dm.F;
+  return w.p0 + (size_t)n * dm.d;
 }
 
 static constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
@@ -336,18 +360,18 @@ struct Seg {
 };
 
 // fp16: chunks [seg*SEG, seg*SEG+SEG) of `row`.
+// Every load is issued (a chunk past the row re-reads the row's last chunk: dot_seg16 stops at
+// nch), so that no load sits behind a branch: one there leaves the compiler unable to count the
+// loads in flight, and every later wait then drains them all, the next item's included.
 template <int OP, int SEG>
-RIVER_DEV void load_seg16(const DecodeArgs& a, const LayerDev* lw, int K, int nch, int row, int seg,
-                          Seg<SEG>& sg) {
+RIVER_DEV void load_seg16(const W16& w, const Dims& dm, int K, int nch, int row, int seg, Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
-  const f16* rp = row16<OP>(a, lw, row);
+  const f16* rp = row16<OP>(w, dm, row);
 #pragma unroll
   for (int c = 0; c < SEG; ++c) {
     const int ch = seg * SEG + c;
-    const int e = ch * kChunkF16 + lane * 8;
-    // chunks past the row are never reduced (dot_seg16 stops at nch); every slot is written so
-    // that a buffer is wholly redefined by each load
-    sg.w[c] = (ch < nch) ? ldg16(rp + (e < K ? e : 0)) : make_uint4(0, 0, 0, 0);  // past K meets x = 0
+    const int e = (ch < nch ? ch : nch - 1) * kChunkF16 + lane * 8;
+    sg.w[c] = ldg16(rp + (e < K ? e : 0));  // past K meets x = 0
   }
   sg.sr = make_uint4(0, 0, 0, 0);
 }
@@ -376,17 +400,19 @@ template <int SEG, int GRP, bool ZP = false>
 RIVER_DEV void load_seg4(const uint8_t* base, const f16* sbase, const uint8_t* zbase, const RowRange& rr,
                          int nch, int q0, int qend, Seg<SEG>& sg) {
   const int lane = threadIdx.x & (kWave - 1);
+  // every load is issued, from an in-range address (see load_seg16): chunks past the end
+  // re-read the last chunk and scales past the end the last scales; dot_seg4 uses neither
 #pragma unroll
   for (int c = 0; c < SEG; ++c)
-    sg.w[c] = (q0 + c < qend) ? ldg16(base + (size_t)rr.chunk(q0 + c, nch) * 1024 + lane * 16)
-                              : make_uint4(0, 0, 0, 0);
+    sg.w[c] = ldg16(base + (size_t)rr.chunk(q0 + c < qend ? q0 + c : qend - 1, nch) * 1024 + lane * 16);
   constexpr int spc = kChunkW4 / GRP;
   constexpr int npl = SEG * spc / kWave;
   static_assert(npl == 1 || npl == 2 || npl == 4 || npl == 8, "scales per lane");
-  const int s0 = q0 * spc + lane * npl;  // virtual scale index; npl divides spc
+  const int s00 = q0 * spc + lane * npl;  // virtual scale index; npl divides spc
+  const int s0 = s00 < qend * spc ? s00 : qend * spc - npl;  // npl divides both
   sg.sr = make_uint4(0, 0, 0, 0);
   if (ZP) sg.zr = make_uint2(0, 0);
-  if (s0 < qend * spc) {  // npl divides both: the lane's scales are all in range
+  {
     const f16* sp = sbase + (size_t)rr.chunk(s0 / spc, nch) * spc + s0 % spc;
     if (npl == 1) {
       sg.sr.x = __builtin_bit_cast(unsigned short, ldg2(sp));
@@ -576,6 +602,7 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
   Seg<SEG> b1;
   float acc = 0.f;
   if constexpr (!IS4) {
+    const W16 w = w16_ptrs<OP>(a, lw);
     const int nseg = (nch + SEG - 1) / SEG;
     const int nitems = rr.nv * nseg;
     auto step = [&](int it, const Seg<SEG>& sg) {
@@ -586,14 +613,20 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
         acc = 0.f;
       }
     };
+    auto load = [&](int it, Seg<SEG>& sg) { load_seg16<OP, SEG>(w, a.dm, K, nch, rr.row(it / nseg), it % nseg, sg); };
+    // Two buffers in a ring (b0 holds item 0). In the steady state no load is conditional, so
+    // each wait covers only the item it reduces; the last one or two items follow. (Fencing
+    // the stages from the scheduler as well measured slower here: more registers spilled.)
     int it = 0;
-    for (; it + 1 < nitems; it += 2) {
-      load_seg16<OP, SEG>(a, lw, K, nch, rr.row((it + 1) / nseg), (it + 1) % nseg, b1);
+    for (; it + 2 < nitems; it += 2) {
+      load(it + 1, b1);
       step(it, b0);
-      if (it + 2 < nitems) load_seg16<OP, SEG>(a, lw, K, nch, rr.row((it + 2) / nseg), (it + 2) % nseg, b0);
+      load(it + 2, b0);
       step(it + 1, b1);
     }
-    if (it < nitems) step(it, b0);
+    if (it + 1 < nitems) load(it + 1, b1);
+    step(it, b0);
+    if (it + 1 < nitems) step(it + 1, b1);
   } else {
     const uint8_t* base;
     const f16* sbase;
@@ -601,14 +634,19 @@ RIVER_DEV void stream_rows(const DecodeArgs& a, const LayerDev* lw, int N, int K
     w4_base<OP>(lw, base, sbase, zbase);
     const int qend = rr.nv * nch;  // virtual chunks
     int row = 0, ch = 0;
+    base = uniform_ptr(base);
+    sbase = uniform_ptr(sbase);
+    zbase = uniform_ptr(zbase);
     int q = 0;
-    for (; q + SEG < qend; q += 2 * SEG) {
+    for (; q + 2 * SEG < qend; q += 2 * SEG) {  // the ring of the fp16 stream
       load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + SEG, qend, b1);
       dot_seg4<SEG, GRP, ZP>(b0, xl, xc, xs, nch, q, qend, row, ch, acc, fin);
-      if (q + 2 * SEG < qend) load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + 2 * SEG, qend, b0);
+      load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + 2 * SEG, qend, b0);
       dot_seg4<SEG, GRP, ZP>(b1, xl, xc, xs, nch, q + SEG, qend, row, ch, acc, fin);
     }
-    if (q < qend) dot_seg4<SEG, GRP, ZP>(b0, xl, xc, xs, nch, q, qend, row, ch, acc, fin);
+    if (q + SEG < qend) load_seg4<SEG, GRP, ZP>(base, sbase, zbase, rr, nch, q + SEG, qend, b1);
+    dot_seg4<SEG, GRP, ZP>(b0, xl, xc, xs, nch, q, qend, row, ch, acc, fin);
+    if (q + SEG < qend) dot_seg4<SEG, GRP, ZP>(b1, xl, xc, xs, nch, q + SEG, qend, row, ch, acc, fin);
   }
   if (OP == OP_LM && lane == 0 && bi != 0x7FFFFFFF) {
     const unsigned long long key = ((unsigned long long)float_key(best) << 32) |
@@ -630,7 +668,7 @@ RIVER_DEV void prefetch_first(const DecodeArgs& a, const LayerDev* lw, int N, in
   }
   const int nch = n_chunks<IS4>(K);
   if constexpr (!IS4) {
-    load_seg16<OP, SEG>(a, lw, K, nch, rr.row(0), 0, pre);
+    load_seg16<OP, SEG>(w16_ptrs<OP>(a, lw), a.dm, K, nch, rr.row(0), 0, pre);
   } else {
     const uint8_t* base;
     const f16* sbase;
