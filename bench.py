@@ -60,6 +60,10 @@ def main():
                     help="host only: write a markdown summary of a rocprofv3 --kernel-trace --stats "
                          "run of this script (its rocpd database and its log) with the persistent "
                          "kernel's algorithmic bytes per launch and achieved bandwidth")
+    ap.add_argument("--phase-trace", metavar="OUT_MD",
+                    help="instead of the timed run: decode one 8-step launch on the library built "
+                         "with RIVER_PHASE_TRACE and write the per-phase timing of the persistent "
+                         "kernel (batch 1) to OUT_MD")
     ap.add_argument("--tau-sweep", type=int, default=0, metavar="N",
                     help="instead of the forced-schedule run: decode in tau mode at N values of tau "
                          "(quantiles of the similarities of a no-exit run) and report tokens/s "
@@ -95,6 +99,9 @@ def main():
     torch.cuda.synchronize()
     log(f"weights generated in {time.time() - t0:.1f}s")
     Tmax = P + W + S
+    if args.phase_trace:
+        phase_trace(args, c, cfgd, w, torch, bm, river, synth, log)
+        return
     rv = river.River(c, w, max_seq=Tmax, max_prefill=P, batch=B)
     rv_chunk = int(os.environ.get("RIVER_PERSIST_CHUNK", "8"))
     torch.cuda.synchronize()
@@ -483,6 +490,105 @@ def prefill_rate(rv, toks, c, B, P, torch, reps=2):
             "frac_of_fp16_mfma_peak": round((lin + att) / (best / 1e3) / 2.5e15, 4),
             "linear_TFLOP": round(lin / 1e12, 2), "attention_TFLOP": round(att / 1e12, 2),
             "how": f"full-depth prefill of {B} x {P} tokens, best of {reps} after one untimed call"}
+
+
+def phase_trace(args, c, cfgd, w, torch, bm, river, synth, log):
+    """Per-phase timing of the persistent kernel from the phase-trace library: one 8-step launch
+    of the bench workload (after its prefill and two warm launches), timestamps of every
+    workgroup at every phase boundary. Per phase: crit = growth of the last workgroup's finish
+    time over the previous phase's (the phase's share of the step), wait+stage = mean over
+    workgroups from finishing the previous phase to having the input staged, stream = mean from
+    staged to done; blocks split by route (backbone up to the exit layer, river after)."""
+    import numpy as np
+    B, P = cfgd["batch"], cfgd["prompt"]
+    if B != 1:
+        fail("--phase-trace measures the batch-1 persistent kernel")
+    L, S, W = c["L"], 8, 16
+    rv = river.River(c, w, max_seq=P + W + S + 8, max_prefill=P, batch=1, lib_path=river.LIB_PHASETRACE_PATH)
+    if rv.decode_path() != "persistent":
+        fail("the phase trace needs the persistent decode path")
+    toks = synth.prompt(c, 1, P, seed=args.seed, device="cuda")
+    sched_np = synth.schedule(cfgd, W + S, 1, seed=args.seed)
+    sched = torch.from_numpy(sched_np).to("cuda")
+    pre = rv.prefill(toks, prefill_exit=L)
+    out = rv.decode_steps(pre["tokens"], sched=sched[:W].contiguous())  # two warm launches
+    tok = out[-1].clone()
+    out = rv.decode_steps(tok, sched=sched[W:].contiguous())
+    torch.cuda.synchronize()
+    check_status(rv, "phase-trace launch")
+    t = rv.phase_trace().astype(np.float64) * 0.01  # 100 MHz ticks -> us
+    rv.close()
+    exits = [int(e) for e in sched_np[W:, 0]]
+    positions = [P + W + s for s in range(S)]
+    EV = {"start": 0, "qkv_st": 1, "qkv": 2, "att": 3, "o_st": 4, "o": 5, "gu_st": 6, "gu": 7, "dn_st": 8, "dn": 9}
+    phases = [("qkv", "start", "qkv_st", "qkv"), ("attn", "qkv", None, "att"), ("o", "att", "o_st", "o"),
+              ("gu", "o", "gu_st", "gu"), ("down", "gu", "dn_st", "dn")]
+    rows = {"backbone": {}, "river": {}}
+    layer_tot = {"backbone": [], "river": []}
+    head = {"lm": [], "barrier": []}
+    step_us = []
+    for s in range(S):
+        prev_end = None
+        if s > 0:
+            prev_end = t[s - 1, L, EV["att"]].max()
+        for l in range(1, L + 1):
+            T = t[s, l - 1]
+            kind = "backbone" if l <= exits[s] else "river"
+            start_max = prev_end if prev_end is not None else T[EV["start"]].max()
+            prev = start_max
+            for name, a0, st, a1 in phases:
+                end = T[EV[a1]].max()
+                r = rows[kind].setdefault(name, {"crit": [], "wait": [], "stream": [], "bytes": []})
+                r["crit"].append(end - prev)
+                if st is not None:
+                    r["wait"].append(float(np.mean(T[EV[st]] - T[EV[a0]])))
+                    r["stream"].append(float(np.mean(T[EV[a1]] - T[EV[st]])))
+                r["bytes"].append(bm.batch_op_bytes(c, name, [exits[s]], l, [positions[s]]))
+                prev = end
+            layer_tot[kind].append(T[EV["dn"]].max() - start_max)
+            prev_end = T[EV["dn"]].max()
+        H = t[s, L]
+        head["lm"].append(H[EV["qkv"]].max() - prev_end)
+        head["barrier"].append(H[EV["att"]].max() - H[EV["qkv"]].max())
+        if s > 0:
+            step_us.append(H[EV["att"]].max() - t[s - 1, L, EV["att"]].max())
+    lines = ["# k_persist per-phase timing (phase-trace build), " + cfgd["name"] + ", batch 1", "",
+             "Command: `python bench.py --config " + cfgd["name"] + " --phase-trace " + args.phase_trace + "`",
+             "(library `token_level_early_amd/libriver_phasetrace.so`: the same sources built with "
+             "`-DRIVER_PHASE_TRACE`; thread 0 of each of the 256 workgroups stores the 100 MHz realtime "
+             "counter at every phase boundary).", "",
+             f"Workload: {P}-token prompt, one persistent launch of {S} steps at positions "
+             f"{positions[0]}..{positions[-1]}, forced exit layers {exits} (blocks up to the exit layer run "
+             "the fp16 backbone, the rest the int4 river).", "",
+             "Per phase, means over the blocks of that route and the 8 steps: **crit** = growth of the last "
+             "workgroup's finish time over the previous phase's (the phase's share of the step); "
+             "**wait+stage** = mean over workgroups from finishing the previous phase to having this "
+             "phase's input staged in LDS; **stream** = mean from staged to done; **bytes** = algorithmic "
+             "bytes of the phase; **GB/s** = bytes / crit.", ""]
+    for kind in ("backbone", "river"):
+        n = len(layer_tot[kind])
+        if not n:
+            continue
+        lines += [f"## {kind} blocks ({n} block-steps): {np.mean(layer_tot[kind]):.1f} us per block", "",
+                  "| phase | crit us | wait+stage us | stream us | bytes MB | GB/s |", "|---|---|---|---|---|---|"]
+        for name, *_ in phases:
+            r = rows[kind][name]
+            crit = float(np.mean(r["crit"]))
+            wt = f"{np.mean(r['wait']):.2f}" if r["wait"] else "-"
+            stv = f"{np.mean(r['stream']):.2f}" if r["stream"] else "-"
+            byt = float(np.mean(r["bytes"]))
+            lines.append(f"| {name} | {crit:.2f} | {wt} | {stv} | {byt / 1e6:.2f} | {byt / (crit * 1e-6) / 1e9:.0f} |")
+        lines.append("")
+    lm_b = bm.batch_op_bytes(c, "lm", exits[:1], L + 1, positions[:1])
+    lines += ["## LM head and step", "",
+              f"LM head (final norm, {c['V']} rows): crit {np.mean(head['lm']):.1f} us "
+              f"({lm_b / (np.mean(head['lm']) * 1e-6) / 1e9:.0f} GB/s); grid barrier after it "
+              f"{np.mean(head['barrier']):.2f} us.", "",
+              f"Step time (barrier to barrier, steps 1..{S - 1}): {np.mean(step_us):.1f} us "
+              f"({1e6 / np.mean(step_us):.1f} tokens/s in this launch).", ""]
+    with open(args.phase_trace, "w") as f:
+        f.write("\n".join(lines))
+    log("\n".join(lines))
 
 
 def write_trace_summary(db, bench_log, out_md):

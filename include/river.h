@@ -276,6 +276,19 @@ int river_debug_hidden(river_ctx* ctx, void* dst, void* stream);
 int river_kv_write_counts(river_ctx* ctx, uint8_t* cnt, void* stream);
 int river_kv_counting(int32_t* enabled /* host */);
 
+/* Debug support: phase timestamps of the persistent batch-1 decode kernel, the measurement
+ * behind its per-phase timing (QKV, attention, O, gate|up and down of every block, the LM head
+ * and the step's grid barrier). Only a library built with RIVER_PHASE_TRACE
+ * (libriver_phasetrace.so) records them: thread 0 of every workgroup stores the 100 MHz
+ * realtime counter at each phase boundary of the last persistent launch, at
+ * [step][slot][event][workgroup] (slot l-1 for block l, slot L for the head; events: 0 start,
+ * 1 input staged, 2 rows done, 3 attention done / past the barrier, 4-5 O staged/done, 6-7
+ * gate|up staged/done, 8-9 down staged/done; 0 where nothing was recorded). river_phase_trace
+ * writes the array's shape {steps, slots, events, workgroups} to dims[4] (host) and copies its
+ * first min(n, size) words to the host buffer dst when dst is not NULL (synchronous; call after
+ * the launch has finished). A release library fills dims and returns RIVER_EINVAL. */
+int river_phase_trace(uint64_t* dst /* host */, uint64_t n, int32_t* dims /* host, 4 */);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* river_last_error(void);
 

@@ -112,6 +112,21 @@ def test_kv_write_counting_only_in_the_debug_build():
         assert hasattr(dbg, n), n
 
 
+def test_phase_trace_only_in_the_trace_build():
+    """river_phase_trace (host-only copy) reports the timestamp array's shape in both libraries,
+    refuses in the release one and copies in the one built with RIVER_PHASE_TRACE; both export
+    the same symbols."""
+    dims = (ctypes.c_int32 * 4)()
+    assert river.load().river_phase_trace(None, 0, dims) == river.RIVER_EINVAL
+    shape = tuple(dims)
+    assert shape[2] == 10 and shape[3] >= 256 and shape[0] >= 8
+    dbg = river.load(river.LIB_PHASETRACE_PATH)
+    dims2 = (ctypes.c_int32 * 4)()
+    assert dbg.river_phase_trace(None, 0, dims2) == 0 and tuple(dims2) == shape
+    for n in _declared():
+        assert hasattr(dbg, n), n
+
+
 def test_prefill_scratch_is_bounded_by_the_chunk():
     """Prefill keeps the residual stream of every prompt row (2 x B*P*d fp16 plus one fp64
     similarity per row: the sequence-level exit needs all tokens of a layer before the next) and

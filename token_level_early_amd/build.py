@@ -17,6 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libriver.so")
 # the same sources with -DRIVER_DEBUG_KV_COUNT: per-element KV write counters (tests only)
 OUT_KVCOUNT = os.path.join(HERE, "libriver_kvcount.so")
+# the same sources with -DRIVER_PHASE_TRACE: phase timestamps of the persistent kernel (profiling)
+OUT_PHASETRACE = os.path.join(HERE, "libriver_phasetrace.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,10 +33,16 @@ FLAGS = [
 SOURCES = ["api.cpp", "quant.hip", "decode.hip", "prefill.hip", "persist.hip", "batched.hip"]
 
 
+# debug variants: object suffix and define
+VARIANTS = {"": [], "kvcount": ["-DRIVER_DEBUG_KV_COUNT"], "phasetrace": ["-DRIVER_PHASE_TRACE"]}
+# the phase-trace library recompiles only what the define changes and links the rest as released
+PHASETRACE_SOURCES = ["api.cpp", "persist.hip"]
+
+
 def _compile(job):
-    src, debug = job
-    obj = os.path.join(BUILD, os.path.basename(src) + (".kvcount.o" if debug else ".o"))
-    extra = ["-DRIVER_DEBUG_KV_COUNT"] if debug else []
+    src, variant = job
+    obj = os.path.join(BUILD, os.path.basename(src) + (f".{variant}.o" if variant else ".o"))
+    extra = VARIANTS[variant]
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -51,10 +59,15 @@ def _link(objs, out):
     shutil.move(tmp, out)
 
 
-def build(verbose=False, kvcount=True):
-    """Builds libriver.so and (kvcount) libriver_kvcount.so; the slowest sources first."""
+def build(verbose=False, kvcount=True, phasetrace=True):
+    """Builds libriver.so, (kvcount) libriver_kvcount.so and (phasetrace)
+    libriver_phasetrace.so; the slowest sources first."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if kvcount else [])
+    jobs = [(s, "") for s in SOURCES]
+    if kvcount:
+        jobs += [(s, "kvcount") for s in SOURCES]
+    if phasetrace:
+        jobs += [(s, "phasetrace") for s in PHASETRACE_SOURCES]
     jobs.sort(key=lambda j: SOURCES.index(j[0]) < SOURCES.index("persist.hip"))
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
@@ -63,9 +76,11 @@ def build(verbose=False, kvcount=True):
         for _, err in results.values():
             if err.strip():
                 print(err, file=sys.stderr)
-    _link([results[(s, False)][0] for s in SOURCES], OUT)
+    _link([results[(s, "")][0] for s in SOURCES], OUT)
     if kvcount:
-        _link([results[(s, True)][0] for s in SOURCES], OUT_KVCOUNT)
+        _link([results[(s, "kvcount")][0] for s in SOURCES], OUT_KVCOUNT)
+    if phasetrace:
+        _link([results[(s, "phasetrace" if s in PHASETRACE_SOURCES else "")][0] for s in SOURCES], OUT_PHASETRACE)
     return OUT
 
 

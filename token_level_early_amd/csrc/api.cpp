@@ -33,6 +33,7 @@ int river_persist_grid(const void* fn);
 hipError_t river_launch_persist(const void* fn, const DecodeArgs& a, int S, int nwg, int splits,
                                 unsigned* bar, hipStream_t st);
 hipError_t river_static_scratch(void** ptr, size_t* bytes);
+hipError_t river_phase_trace_copy(unsigned long long* dst, size_t n, int* dims);
 hipError_t river_decode_layers_batched(const DecodeArgs& a, f16* xn, int mode, hipStream_t st,
                                        void (*timer)(void*, int, int), void* tctx, int top);
 hipError_t river_launch_head_batched(const DecodeArgs& a, f16* xn, hipStream_t st,
@@ -985,6 +986,17 @@ int river_kv_counting(int32_t* enabled) {
 #else
   *enabled = 0;
 #endif
+  return RIVER_OK;
+}
+
+int river_phase_trace(uint64_t* dst, uint64_t n, int32_t* dims) {
+  if (!dims) return fail(RIVER_EINVAL, "NULL argument");
+  int d4[4];
+  const hipError_t e = river_phase_trace_copy((unsigned long long*)dst, (size_t)n, d4);
+  for (int i = 0; i < 4; ++i) dims[i] = d4[i];
+  if (e == hipErrorNotSupported)
+    return fail(RIVER_EINVAL, "phase timestamps need the library built with RIVER_PHASE_TRACE");
+  if (e != hipSuccess) return hip_fail(e, "phase trace copy");
   return RIVER_OK;
 }
 

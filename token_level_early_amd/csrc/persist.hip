@@ -527,6 +527,38 @@ RIVER_DEV void w4_base(const LayerDev* lw, const uint8_t*& base, const f16*& sba
 }
 
 // Epilogue inputs of a streamed phase.
+// Phase timestamps (debug build with RIVER_PHASE_TRACE, libriver_phasetrace.so): thread 0 of
+// every workgroup records the 100 MHz realtime counter at the boundaries of each phase, at
+// [step][slot][event][workgroup] (slot l-1 for block l, slot L for the LM head; the events are
+// the RIVER_EV_* below). The release build records nothing.
+enum {
+  RIVER_EV_START = 0,      // block: before the exit test; head: before its staging
+  RIVER_EV_QKV_STAGED = 1, // head: LM input staged
+  RIVER_EV_QKV_END = 2,    // head: LM rows done
+  RIVER_EV_ATT_END = 3,    // head: past the step's grid barrier
+  RIVER_EV_O_STAGED = 4,
+  RIVER_EV_O_END = 5,
+  RIVER_EV_GU_STAGED = 6,
+  RIVER_EV_GU_END = 7,
+  RIVER_EV_DN_STAGED = 8,
+  RIVER_EV_DN_END = 9,
+  RIVER_EV_COUNT = 10
+};
+static constexpr int kTrSteps = 8, kTrSlots = 65, kTrWgs = 256;
+#ifdef RIVER_PHASE_TRACE
+static __device__ unsigned long long g_phase_ts[kTrSteps * kTrSlots * RIVER_EV_COUNT * kTrWgs];
+#define RIVER_TS(step, slot, ev)                                                                   \
+  do {                                                                                             \
+    if (threadIdx.x == 0 && (step) < kTrSteps && (slot) < kTrSlots && blockIdx.x < kTrWgs)        \
+      g_phase_ts[(((size_t)(step) * kTrSlots + (slot)) * RIVER_EV_COUNT + (ev)) * kTrWgs + blockIdx.x] = \
+          __builtin_amdgcn_s_memrealtime();                                                        \
+  } while (0)
+#else
+#define RIVER_TS(step, slot, ev) \
+  do {                           \
+  } while (0)
+#endif
+
 struct StreamOut {
   uint32_t* out;      // tagged output: QKV -> q|k|v, O -> h_mid, GU -> SwiGLU vector, DOWN -> h(l)
   uint32_t tag;       // its tag
@@ -537,6 +569,7 @@ struct StreamOut {
   int* abort;
   float* logits;      // LM (optional)
   unsigned long long* key;  // LM argmax key
+  int tr_step, tr_slot, tr_ev;  // phase trace: where the staged-input timestamp goes
 };
 
 template <bool IS4>
@@ -687,6 +720,7 @@ RIVER_DEV void gemv_phase(const DecodeArgs& a, const LayerDev* lw, int N, int K,
                           float* xc, float* xs, double* red, Seg<SEG>& b0, bool have) {
   if (!have) prefetch_first<OP, IS4, SEG, GRP, ZP>(a, lw, N, K, b0);
   stage_x<IS4, HAS_GAIN, NORM, TAG, NG, ZP>(src, stag, so.abort, gain, K, inv, a.dm.eps, xl, xc, xs, red);
+  RIVER_TS(so.tr_step, so.tr_slot, so.tr_ev);
   stream_rows<OP, IS4, SEG, GRP, ZP>(a, lw, N, K, xl, xc, xs, so, b0);
   __syncthreads();  // LDS reuse by the next phase
 }
@@ -753,6 +787,7 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       uint32_t* hmid_t = a.t_hmid + (size_t)(l - 1) * dm.d;
       uint32_t* o_t = a.t_o + (size_t)(l & 1) * dm.hd;  // two buffers by layer parity
       // ---------------- QKV (exit test after block l-1 first)
+      RIVER_TS(step, l - 1, RIVER_EV_START);
       bool norm_known = false;
       float inv = 1.f;
       if (l == 1) {
@@ -789,6 +824,9 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       so.abort = abort;
       so.out = a.t_qkv;
       so.tag = tg;
+      so.tr_step = step;
+      so.tr_slot = l - 1;
+      so.tr_ev = RIVER_EV_QKV_STAGED;
       if (l == 1) {
         if (r4) gemv_phase<OP_QKV, true, SEG, true, true, false, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
         else gemv_phase<OP_QKV, false, SEG, true, true, false, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, emb, 0, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
@@ -799,18 +837,23 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
         if (norm_known) gemv_phase<OP_QKV, false, SEG, true, false, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
         else gemv_phase<OP_QKV, false, SEG, true, true, true, NG, GRP, ZP>(a, lw, dm.nqkv, dm.d, hin_t, tgp, lw->attn_norm, inv, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
       }
+      RIVER_TS(step, l - 1, RIVER_EV_QKV_END);
       // ---------------- attention (+ RoPE and the KV append of position pos); waits for q|k|v
       {
         const AttnTag at{a.t_qkv, o_t, tg, a.t_part, tbase32 + (uint32_t)(step * (dm.L + 1) + l), abort};
         for (int it = wg; it < dm.Hkv * splits; it += nwg)
           attn_split<D, G, kPB, true, AU, AGL, true>(a, l, it % splits, it / splits, b, pos, splits, sm.at, at);
       }
+      RIVER_TS(step, l - 1, RIVER_EV_ATT_END);
       pf = prefetch_route<OP_O, SEG, GRP, ZP>(a, lw, dm.d, dm.hd, r4, pre);
       // ---------------- O + residual
       so = StreamOut{};
       so.abort = abort;
       so.out = hmid_t;
       so.tag = tg;
+      so.tr_step = step;
+      so.tr_slot = l - 1;
+      so.tr_ev = RIVER_EV_O_STAGED;
       if (l == 1) {
         so.pres = emb;
       } else {
@@ -825,25 +868,34 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
       if (l == 1 && wg == 0 && t == 0)
         __hip_atomic_store(a.amax + ((step + 1) & 1) * dm.B + b, 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+      RIVER_TS(step, l - 1, RIVER_EV_O_END);
       pf = prefetch_route<OP_GU, SEG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, r4, pre);
       // ---------------- gate|up (+ SwiGLU in the epilogue)
       so = StreamOut{};
       so.abort = abort;
       so.out = a.t_a2;
       so.tag = tg;
+      so.tr_step = step;
+      so.tr_slot = l - 1;
+      so.tr_ev = RIVER_EV_GU_STAGED;
       if (r4) gemv_phase<OP_GU, true, SEG, true, true, true, NG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
       else gemv_phase<OP_GU, false, SEG, true, true, true, NG, GRP, ZP>(a, lw, 2 * dm.F, dm.d, hmid_t, tg, lw->mlp_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+      RIVER_TS(step, l - 1, RIVER_EV_GU_END);
       pf = prefetch_route<OP_DOWN, SEG, GRP, ZP>(a, lw, dm.d, dm.F, r4, pre);
       // ---------------- down (input: the SwiGLU vector) + residual -> h(l)
       so = StreamOut{};
       so.abort = abort;
       so.out = a.t_hs + (size_t)l * dm.d;
       so.tag = tg;
+      so.tr_step = step;
+      so.tr_slot = l - 1;
+      so.tr_ev = RIVER_EV_DN_STAGED;
       so.copy = a.hs + ((size_t)l * dm.B + b) * dm.d;
       so.tres = hmid_t;
       so.rtag = tg;
       if (r4) gemv_phase<OP_DOWN, true, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 2);
       else gemv_phase<OP_DOWN, false, SEG, false, false, true, NG, GRP, ZP>(a, lw, dm.d, dm.F, a.t_a2, tg, nullptr, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+      RIVER_TS(step, l - 1, RIVER_EV_DN_END);
       // next phase: QKV of layer l+1 on its route (the exit test may still switch a backbone
       // guess to the river, which then loads its own first item) or the LM head
       const bool next_r4 = r4 || (MODE == 0 && a.sched && l == e_forced && l >= dm.entry);
@@ -857,13 +909,19 @@ __global__ __launch_bounds__(kPB) void k_persist(DecodeArgs a, int S, int splits
     // ---------------- LM head (final RMSNorm while staging) + argmax; the one grid barrier of
     // a step (every workgroup needs the whole argmax)
     {
+      RIVER_TS(step, dm.L, RIVER_EV_START);
       StreamOut so{};
       so.abort = abort;
       so.logits = a.logits ? a.logits + (size_t)b * dm.V : nullptr;
       so.key = a.amax + (step & 1) * dm.B + b;
+      so.tr_step = step;
+      so.tr_slot = dm.L;
+      so.tr_ev = RIVER_EV_QKV_STAGED;
       gemv_phase<OP_LM, false, SEG, true, true, true, NG, GRP, ZP>(a, nullptr, dm.V, dm.d, a.t_hs + (size_t)dm.L * dm.d,
                                                                tag_of(step, dm.L), a.final_norm, 1.f, so, xl, sm.xc, sm.xs, sm.red, pre, pf == 1);
+      RIVER_TS(step, dm.L, RIVER_EV_QKV_END);
       grid_sync(bar, epoch, nwg, [&] { pf = prefetch_route<OP_QKV, SEG, GRP, ZP>(a, &a.layers[0], dm.nqkv, dm.d, false, pre); });
+      RIVER_TS(step, dm.L, RIVER_EV_ATT_END);
       const unsigned long long k = __hip_atomic_load(so.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
       if (wg == 0 && t == 0) a.tok_out[step * dm.B + b] = tok;
@@ -944,6 +1002,24 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 // Device address and size of the current GPU's copy of `scratch`; looked up once per device
 // (with that device current) and remembered.
+// Phase trace (debug build): copies the timestamp array to host memory; its shape goes to
+// dims[4] = {steps, slots, events, workgroups}. The release build reports hipErrorNotSupported.
+hipError_t river_phase_trace_copy(unsigned long long* dst, size_t n, int* dims) {
+  dims[0] = kTrSteps;
+  dims[1] = kTrSlots;
+  dims[2] = RIVER_EV_COUNT;
+  dims[3] = kTrWgs;
+#ifdef RIVER_PHASE_TRACE
+  const size_t total = (size_t)kTrSteps * kTrSlots * RIVER_EV_COUNT * kTrWgs;
+  if (!dst) return hipSuccess;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_phase_ts), (n < total ? n : total) * 8, 0, hipMemcpyDeviceToHost);
+#else
+  (void)dst;
+  (void)n;
+  return hipErrorNotSupported;
+#endif
+}
+
 hipError_t river_static_scratch(void** ptr, size_t* bytes) {
   constexpr int kMaxDevices = 64;
   static std::mutex mu;

@@ -14,6 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libriver.so")
 # the same library built with per-element KV write counters (RIVER_DEBUG_KV_COUNT; tests only)
 LIB_KVCOUNT_PATH = os.path.join(_HERE, "libriver_kvcount.so")
+# the same library with the persistent kernel recording phase timestamps (profiling only)
+LIB_PHASETRACE_PATH = os.path.join(_HERE, "libriver_phasetrace.so")
 
 RIVER_OK, RIVER_EINVAL, RIVER_ENOMEM, RIVER_ERANGE, RIVER_EHIP, RIVER_EDEVICE = 0, -1, -2, -3, -4, -5
 
@@ -85,6 +87,7 @@ def load(path=LIB_PATH):
         "river_weight_residency": [VP, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64)],
         "river_weight_placement": [VP, P(I32)],
         "river_kv_counting": [P(I32)],
+        "river_phase_trace": [VP, ctypes.c_uint64, P(I32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -311,6 +314,17 @@ class River:
         out = torch.empty(c["L"], self.B, int(self.kvdesc.dims[4]), dtype=torch.uint8,
                           device=self.kv.device)
         self._chk(self.lib.river_kv_write_counts(self.ctx, _ptr(out), _stream()))
+        return out
+
+    def phase_trace(self):
+        """Phase timestamps of the last persistent launch, uint64 [steps][slots][events][workgroups]
+        (100 MHz ticks). Needs the library built with RIVER_PHASE_TRACE."""
+        import numpy as np
+        dims = (ctypes.c_int32 * 4)()
+        self._chk(self.lib.river_phase_trace(None, 0, dims))
+        shape = tuple(int(x) for x in dims)
+        out = np.zeros(shape, dtype=np.uint64)
+        self._chk(self.lib.river_phase_trace(out.ctypes.data_as(ctypes.c_void_p), out.size, dims))
         return out
 
     def hidden(self):
