@@ -145,15 +145,21 @@ static constexpr int kBMaxTiles = 64;  // tiles per workgroup when K is split (b
 static constexpr int kBMaxSplit = 8;   // K slices of one projection at most
 static constexpr int kGW = kGB / kWave;
 
-// WPG: 32-wide K windows per int4 quantisation group (group / 32); SPLIT: b_split > 1. Without
-// a split the epilogue runs as each tile completes; with one, the loop only stores partial
-// tiles (an epilogue's dependent loads would wait for every weight load in flight).
-template <int OP, int WPG, bool SPLIT>
+// WPG: 32-wide K windows per int4 quantisation group (group / 32). EPI, where a tile's epilogue
+// runs: EPI_LOOP as the tile completes (the LM head, whose epilogue loads nothing), EPI_LDS after
+// the stream, from tile results kept in LDS (an epilogue's dependent loads inside the loop would
+// wait for every weight load in flight), EPI_SPLIT after the stream, by the workgroup that
+// completes the tile's slices (b_split > 1).
+enum { EPI_LOOP = 0, EPI_LDS = 1, EPI_SPLIT = 2 };
+static constexpr int kBDefer = 16;  // tile results a workgroup can keep for EPI_LDS (both streams)
+template <int OP, int WPG, int EPI>
 __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f16* xin, int streams) {
+  constexpr bool SPLIT = EPI == EPI_SPLIT;
   __shared__ uint4 xs[kBXs / 8 * kBR];  // the input slice, piece-interleaved
   __shared__ float part[kGW][kBR][kBR];
   __shared__ float ysm[kBR][kBR];
-  __shared__ int need[2], nlast, lastf[2 * kBMaxTiles];
+  __shared__ float ytl[EPI == EPI_LDS ? kBDefer : 1][kBR][kBR];
+  __shared__ int need[2], nlast, lastf[2 * kBMaxTiles], sroute[kBR];
   const Dims& dm = a.dm;
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
   const int N = b_rows(OP, dm), K = b_k(OP, dm);
@@ -170,6 +176,7 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
   __syncthreads();
   if (t < dm.B) {
     const int r = (OP == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + t];
+    sroute[t] = r;  // the epilogues read the routes here
     if (r >= 0 && r < streams) atomicOr(&need[r], 1);
   }
   // stage the slice (rows past the batch and values past K are zero): every load is issued
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
   auto epilogue = [&](int stream, int tile, const float (&y)[kBR][kBR], int tt) {
   const int b = tt / kBR, c = tt % kBR;
   if (b >= dm.B) return;
-  if (OP != OP_LM && a.route[layer * dm.B + b] != stream) return;
+  if (OP != OP_LM && sroute[b] != stream) return;
   const float yv = y[b][c];
   if (OP == OP_QKV) {
     const int pos = a.pos[b];
@@ -307,15 +314,17 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
       float y = part[0][row][c];
 #pragma unroll
       for (int j = 1; j < kGW; ++j) y += part[j][row][c];
-      if constexpr (!SPLIT) {
+      if constexpr (EPI == EPI_LOOP) {
         ysm[row][c] = y;
+      } else if constexpr (EPI == EPI_LDS) {
+        ytl[stream * my + (tile - g) / groups][row][c] = y;
       } else {
         float* P = a.bpart + (((size_t)stream * tiles + tile) * S + sl) * (kBR * kBR);
         __hip_atomic_store((g_f32*)P + t, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
-    if constexpr (!SPLIT) epilogue(stream, tile, ysm, t);
+    if constexpr (EPI == EPI_LOOP) epilogue(stream, tile, ysm, t);
   };
 
   if (need0 && my > 0) {  // ---- fp16 backbone stream
@@ -479,7 +488,17 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     }
   }
 
-  if (!SPLIT || my == 0) return;
+  if (EPI == EPI_LOOP || my == 0) return;
+  if constexpr (EPI == EPI_LDS) {  // wave w runs the epilogues of kept tiles w, w + 8, ...
+    for (int i = w; i < 2 * my; i += kGW) {
+      const int stream = i / my;
+      if (stream == 0 ? need0 : need1) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) epilogue(stream, g + (i % my) * groups, ytl[i], lane + m * kWave);
+      }
+    }
+    return;
+  }
   // ---- slices: every partial of this workgroup has been written through once its stores are
   // acknowledged; then count them, and finish the tiles whose count this workgroup completed
   __builtin_amdgcn_s_waitcnt(0);
@@ -553,15 +572,18 @@ static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const 
   if (S > kBMaxSplit || (S > 1 && (b_tiles(OP, dm) + groups - 1) / groups > kBMaxTiles)) return hipErrorInvalidValue;
   const dim3 grid(groups * S), block(kGB);
   const int wpg = dm.group / 32;
-  if (S > 1) {
-    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, true>), grid, block, 0, st, a, layer, xin, streams);
-    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, true>), grid, block, 0, st, a, layer, xin, streams);
-    else hipLaunchKernelGGL((k_b_gemm<OP, 4, true>), grid, block, 0, st, a, layer, xin, streams);
-  } else {
-    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, false>), grid, block, 0, st, a, layer, xin, streams);
-    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, false>), grid, block, 0, st, a, layer, xin, streams);
-    else hipLaunchKernelGGL((k_b_gemm<OP, 4, false>), grid, block, 0, st, a, layer, xin, streams);
-  }
+  const int my = (b_tiles(OP, dm) + groups - 1) / groups;  // tiles per workgroup at most
+  const int epi = S > 1 ? EPI_SPLIT : (OP == OP_LM || 2 * my > kBDefer) ? EPI_LOOP : EPI_LDS;
+#define RIVER_B_LAUNCH(E)                                                                              \
+  do {                                                                                               \
+    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, E>), grid, block, 0, st, a, layer, xin, streams); \
+    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, E>), grid, block, 0, st, a, layer, xin, streams); \
+    else hipLaunchKernelGGL((k_b_gemm<OP, 4, E>), grid, block, 0, st, a, layer, xin, streams);       \
+  } while (0)
+  if (epi == EPI_SPLIT) RIVER_B_LAUNCH(EPI_SPLIT);
+  else if (epi == EPI_LDS) RIVER_B_LAUNCH(EPI_LDS);
+  else RIVER_B_LAUNCH(EPI_LOOP);
+#undef RIVER_B_LAUNCH
   return hipGetLastError();
 }
 

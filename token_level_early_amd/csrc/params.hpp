@@ -123,6 +123,18 @@ enum { OP_QKV = 0, OP_O = 1, OP_GU = 2, OP_DOWN = 3, OP_LM = 4 };
 // that slice's contribution to the 16-column tiles g, g + groups, ...; the b_split(op) partial
 // tiles of a tile are summed, in slice order, by the workgroup that finishes it last.
 static constexpr int kBGrid = 256;
+#ifndef RIVER_BS_QKV  // preferred K slices per projection
+#define RIVER_BS_QKV 1
+#endif
+#ifndef RIVER_BS_O
+#define RIVER_BS_O 1
+#endif
+#ifndef RIVER_BS_GU
+#define RIVER_BS_GU 1
+#endif
+#ifndef RIVER_BS_DOWN
+#define RIVER_BS_DOWN 4
+#endif
 static constexpr int kBXs = 4096;
 __host__ __device__ inline int b_rows(int op, const Dims& d) {
   return op == OP_QKV ? d.nqkv : op == OP_GU ? 2 * d.F : op == OP_LM ? d.V : d.d;
@@ -135,7 +147,7 @@ __host__ __device__ inline int b_split(int op, const Dims& d) {
   const int K = b_k(op, d);
   // more slices give each workgroup more tiles to share its staged input with; slices of at
   // least 1024 values keep all 8 waves busy on every tile
-  int s = op == OP_LM ? 1 : op == OP_GU ? 2 : 4;
+  int s = op == OP_LM ? 1 : op == OP_GU ? RIVER_BS_GU : op == OP_DOWN ? RIVER_BS_DOWN : op == OP_O ? RIVER_BS_O : RIVER_BS_QKV;
   while (s > 1 && K / s < 1024) s /= 2;
   const int lds = (K + kBXs - 1) / kBXs;
   return s > lds ? s : lds;
