@@ -60,6 +60,8 @@ def main():
                     help="host only: write a markdown summary of a rocprofv3 --kernel-trace --stats "
                          "run of this script (its rocpd database and its log) with the persistent "
                          "kernel's algorithmic bytes per launch and achieved bandwidth")
+    ap.add_argument("--pmc-table", nargs=4, metavar=("CSV", "OUT_MD", "TITLE", "COMMAND"),
+                    help="host only: per-kernel means of every counter in a rocprofv3 --pmc CSV")
     ap.add_argument("--phase-trace", metavar="OUT_MD",
                     help="instead of the timed run: decode one 8-step launch on the library built "
                          "with RIVER_PHASE_TRACE and write the per-phase timing of the persistent "
@@ -74,6 +76,9 @@ def main():
         return
     if args.trace_summary:
         write_trace_summary(*args.trace_summary)
+        return
+    if args.pmc_table:
+        write_pmc_table(*args.pmc_table)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -591,6 +596,32 @@ def phase_trace(args, c, cfgd, w, torch, bm, river, synth, log):
     log("\n".join(lines))
 
 
+def write_pmc_table(csv_path, out_md, title, command):
+    """Markdown table of a rocprofv3 --pmc CSV: per kernel, the dispatch count and the mean of
+    every collected counter (derived counters such as MfmaUtil included as rocprofv3 computed
+    them)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            if k.startswith("void at::") or k.startswith("at::"):
+                continue
+            d = per.setdefault(k, {})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for d in per.values() for c in d})
+    md = [f"# {title}", "", "Command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root):", "", "```",
+          command, "```", "", "| kernel | dispatches | " + " | ".join(f"mean {c}" for c in names) + " |",
+          "|---|---:|" + "---:|" * len(names)]
+    for k, d in sorted(per.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
+        n = len(next(iter(d.values())))
+        md.append(f"| `{k[:100]}` | {n} | " + " | ".join(
+            f"{sum(d[c]) / len(d[c]):.4g}" if c in d else "-" for c in names) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(out_md)
+
+
 def write_trace_summary(db, bench_log, out_md):
     """Markdown summary of a kernel-trace run: the rocpd database's top_kernels view (torch's
     own kernels, which only generate the synthetic inputs, left out) and, for the persistent
@@ -618,15 +649,19 @@ def write_trace_summary(db, bench_log, out_md):
         if name.startswith("void k_persist") and persist is None:
             persist = (name, calls, avg)
     if out and out.get("roofline") and persist:
-        # the roofline pass is the run's last `launches` dispatches of the persistent kernel
+        # the roofline pass: of the early-exit kernel's dispatches (its warm-up launches, the timed
+        # pass, the roofline pass and, when run, the all-river pass, in that order), the window of
+        # `launches` consecutive ones whose mean is closest to the live HIP-event average
         r = out["roofline"]
         n = int(r["launches"])
-        durs = [d for (d,) in sqlite3.connect(db).execute(
-            "select duration from kernels where name like 'void k_persist%' order by start")][-n:]
-        avg = sum(durs) / len(durs) / 1e3
+        seq = [d / 1e3 for (d,) in sqlite3.connect(db).execute(
+            "select duration from kernels where name = ? order by start", (persist[0],))]
+        best = min(range(len(seq) - n + 1), key=lambda i: abs(sum(seq[i:i + n]) / n - r["avg_launch_us"]))
+        avg = sum(seq[best:best + n]) / n
         gbs = r["bytes_per_launch"] / (avg * 1e-6) / 1e9
-        md += ["", f"Persistent decode kernel, roofline pass ({n} launches of {r['steps_per_launch']} steps, the "
-               f"run's last {n} dispatches of it): {r['bytes_per_launch'] / 1e9:.2f} GB algorithmic per launch "
+        md += ["", f"Persistent decode kernel, roofline pass ({n} launches of {r['steps_per_launch']} steps: "
+               f"dispatches {best + 1}..{best + n} of the {len(seq)} of `{persist[0].split('(')[0]}`, the window of {n} "
+               f"consecutive ones closest to the live average): {r['bytes_per_launch'] / 1e9:.2f} GB algorithmic per launch "
                f"(bytes model at the realised exit layers and positions: {out['config']['workload'].split('(')[-1].rstrip(')')}); "
                f"traced average {avg:.1f} us per launch against {r['avg_launch_us']:.1f} us timed live with HIP "
                f"events; {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s from the traced durations."]
@@ -634,9 +669,11 @@ def write_trace_summary(db, bench_log, out_md):
         pf = out["prefill_full_depth"]
         md += ["", f"Full-depth prefill in the same run: {pf['ms']} ms, {pf['TFLOP/s']} TFLOP/s "
                f"({pf['frac_of_fp16_mfma_peak']:.3f} of the 2.5 PF fp16 MFMA peak)."]
-    md += ["", "rocprofv3 wrote the database after the program's last line and then ended with a "
-           "segmentation fault in its exit handlers (the program launches cooperative kernels; the "
-           "figures come from the complete database)."]
+    st = [l.strip() for l in open(bench_log) if l.startswith("rocprofv3 exit status")]
+    if st:
+        coop = "launches" if persist else "does not launch"
+        md += ["", f"{st[-1]} (the program {coop} cooperative kernels; the database was complete and "
+               "the program's last line printed before rocprofv3 ended)."]
     with open(out_md, "w") as f:
         f.write("\n".join(md) + "\n")
     print(out_md)
