@@ -152,8 +152,12 @@ static constexpr int kGW = kGB / kWave;
 // completes the tile's slices (b_split > 1).
 enum { EPI_LOOP = 0, EPI_LDS = 1, EPI_SPLIT = 2 };
 static constexpr int kBDefer = 16;  // tile results a workgroup can keep for EPI_LDS (both streams)
+// normin: the input is the raw residual stream after attention (h_mid of this layer) and is
+// staged RMS-normalised with the layer's MLP gain, each row's 1/rms computed by every workgroup
+// from the whole row in one fixed order (needs an unsplit K: the whole row in LDS).
 template <int OP, int WPG, int EPI>
-__global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f16* xin, int streams) {
+__global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f16* xin, int streams,
+                                                int normin) {
   constexpr bool SPLIT = EPI == EPI_SPLIT;
   __shared__ uint4 xs[kBXs / 8 * kBR];  // the input slice, piece-interleaved
   __shared__ float part[kGW][kBR][kBR];
@@ -204,6 +208,36 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     }
   }
   __syncthreads();
+  if (normin) {  // RMSNorm in LDS: fp64 sum of squares per row, thread t of row t % 16 summing
+               // pieces t / 16, t / 16 + 32, ... in that order, then the 32 partials in order
+    __shared__ double rs[kBR][kGB / kBR];
+    __shared__ float rinv[kBR];
+    const int r = t % kBR, j0 = t / kBR, np = Ks / 8;
+    // this thread's gain pieces, all in flight while the sums are formed
+    constexpr int kPer = kBXs / 8 * kBR / kGB;
+    uint4 gv[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int pc = (t + m * kGB) / kBR;
+      gv[m] = ldg16(lwc.mlp_norm + (pc * 8 < K ? pc * 8 : 0));
+    }
+    double ss = 0.0;
+    for (int pc = j0; pc < np; pc += kGB / kBR) ss += sq8(xs[pc * kBR + r]);
+    rs[r][j0] = ss;
+    __syncthreads();
+    if (t < kBR) {
+      double tot = 0.0;
+      for (int j = 0; j < kGB / kBR; ++j) tot += rs[t][j];
+      rinv[t] = inv_rms(tot, K, dm.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int i = t + m * kGB, pc = i / kBR, row = i % kBR;
+      if (i < np * kBR && row < dm.B && pc * 8 < K) xs[i] = norm8(xs[i], gv[m], rinv[row], true);
+    }
+    __syncthreads();
+  }
   const bool need0 = need[0] != 0, need1 = need[1] != 0;
 
   const int col = lane % 16, kq = lane / 16;
@@ -565,20 +599,22 @@ hipError_t river_launch_attn(const DecodeArgs& a, int layer, hipStream_t st);
 hipError_t river_launch_step_end(const DecodeArgs& a, hipStream_t st);
 
 template <int OP>
-static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const f16* xin, hipStream_t st) {
+static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const f16* xin, hipStream_t st,
+                                int normin = 0) {
   const Dims& dm = a.dm;
   const int streams = (OP == OP_LM || mode == 1) ? 1 : 2;
   const int S = b_split(OP, dm), groups = b_groups(OP, dm);
   if (S > kBMaxSplit || (S > 1 && (b_tiles(OP, dm) + groups - 1) / groups > kBMaxTiles)) return hipErrorInvalidValue;
+  if (normin && S > 1) return hipErrorInvalidValue;  // normalising while staging needs whole rows
   const dim3 grid(groups * S), block(kGB);
   const int wpg = dm.group / 32;
   const int my = (b_tiles(OP, dm) + groups - 1) / groups;  // tiles per workgroup at most
   const int epi = S > 1 ? EPI_SPLIT : (OP == OP_LM || 2 * my > kBDefer) ? EPI_LOOP : EPI_LDS;
 #define RIVER_B_LAUNCH(E)                                                                              \
   do {                                                                                               \
-    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, E>), grid, block, 0, st, a, layer, xin, streams); \
-    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, E>), grid, block, 0, st, a, layer, xin, streams); \
-    else hipLaunchKernelGGL((k_b_gemm<OP, 4, E>), grid, block, 0, st, a, layer, xin, streams);       \
+    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, E>), grid, block, 0, st, a, layer, xin, streams, normin); \
+    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, E>), grid, block, 0, st, a, layer, xin, streams, normin); \
+    else hipLaunchKernelGGL((k_b_gemm<OP, 4, E>), grid, block, 0, st, a, layer, xin, streams, normin);       \
   } while (0)
   if (epi == EPI_SPLIT) RIVER_B_LAUNCH(EPI_SPLIT);
   else if (epi == EPI_LDS) RIVER_B_LAUNCH(EPI_LDS);
@@ -616,9 +652,13 @@ hipError_t river_decode_layers_batched(const DecodeArgs& a, f16* xn, int mode, h
     T(TOP_O, 0);
     if ((e = launch_b_gemm<OP_O>(a, l, mode, a.o, st)) != hipSuccess) return e;
     T(TOP_O, 1);
-    hipLaunchKernelGGL((k_b_prep<1>), dim3(dm.B), dim3(kBlock), 0, st, a, l, mode, xn);
+    // the MLP RMSNorm runs in gate|up's staging when its K is not split, else as its own kernel
+    const bool fuse = b_split(OP_GU, dm) == 1;
+    if (!fuse) hipLaunchKernelGGL((k_b_prep<1>), dim3(dm.B), dim3(kBlock), 0, st, a, l, mode, xn);
     T(TOP_GU, 0);
-    if ((e = launch_b_gemm<OP_GU>(a, l, mode, xn, st)) != hipSuccess) return e;
+    if (fuse) e = launch_b_gemm<OP_GU>(a, l, mode, a.hmid + (size_t)(l - 1) * dm.B * dm.d, st, 1);
+    else e = launch_b_gemm<OP_GU>(a, l, mode, xn, st);
+    if (e != hipSuccess) return e;
     T(TOP_GU, 1);
     T(TOP_DOWN, 0);
     if ((e = launch_b_gemm<OP_DOWN>(a, l, mode, a.a2, st)) != hipSuccess) return e;
