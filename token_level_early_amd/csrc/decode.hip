@@ -178,10 +178,20 @@ __global__ void k_step_end(DecodeArgs a) {
 
 // GQA split-K decode attention over the shared cache (attn.hpp). Grid (smax, Hkv, B).
 template <int D, int G>
+#ifndef RIVER_DATTN_UP
+#define RIVER_DATTN_UP 2  // positions per lane per block
+#endif
+#ifndef RIVER_DATTN_GL
+#define RIVER_DATTN_GL 2  // query heads per lane (at least what fits a wave)
+#endif
 __global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
-  __shared__ AttnLds<D, G, kBlock> sm;
+  // query heads per lane: as requested, but enough that one slot's lanes fit a wave
+  constexpr int GLmin = (G * (D / 8) + kWave - 1) / kWave;
+  constexpr int GLr = RIVER_DATTN_GL < G ? RIVER_DATTN_GL : G;
+  constexpr int GLP = GLr > GLmin ? GLr : GLmin;
+  __shared__ AttnLds<D, G, kBlock, GLP> sm;
   const int b = blockIdx.z;
-  attn_split<D, G, kBlock, false>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b], a.attn_smax, sm);
+  attn_split<D, G, kBlock, false, RIVER_DATTN_UP, GLP>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b], a.attn_smax, sm);
 }
 
 // ---------------------------------------------------------------------------------------
