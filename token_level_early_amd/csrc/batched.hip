@@ -35,19 +35,26 @@ RIVER_DEV bh8 as8(uint4 u) { return __builtin_bit_cast(bh8, (bu4){u.x, u.y, u.z,
 // ---------------------------------------------------------------------------------------
 // Per-row preparation: KIND 0 = exit test + attention RMSNorm of layer `layer`'s input,
 // KIND 1 = MLP RMSNorm of h_mid, KIND 2 = final RMSNorm of h(L). Writes xn[b][d].
+// Every load of a row (input, gain, and h(l-2) for the exit test) is issued at once, 16 bytes
+// per load, kPP pieces of 8 values per thread held in registers for the norm (rows longer than
+// kPP * 8 * kBlock values stream the rest). The fp64 sums run per thread over its pieces in
+// order, then over the block in a fixed order.
 // ---------------------------------------------------------------------------------------
 template <int KIND>
 __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int mode, f16* xn) {
-  __shared__ double red[4];
+  constexpr int kPP = 4;
+  constexpr int kW = kBlock / kWave;
+  __shared__ double red[3][kW];
   const Dims& dm = a.dm;
   const int b = blockIdx.x, t = threadIdx.x;
+  const int np = dm.d / 8;
   const int step = *a.step;
   const f16* hin;
   const f16* gain;
+  const f16* hprev = nullptr;  // KIND 0: h(l-2) when the exit test may run
+  int route = ROUTE_BACKBONE, prev = ROUTE_BACKBONE;
   if (KIND == 0) {
-    const LayerDev& lw = a.layers[layer - 1];
-    gain = lw.attn_norm;
-    int route = ROUTE_BACKBONE;
+    gain = a.layers[layer - 1].attn_norm;
     if (layer == 1) {
       int tok = (step == 0) ? a.tok_in[b] : a.tok_out[(step - 1) * dm.B + b];
       if (tok < 0 || tok >= dm.V) {
@@ -55,8 +62,6 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
         tok = 0;
       }
       hin = a.embed + (size_t)tok * dm.d;
-      f16* h0 = a.hs + (size_t)b * dm.d;
-      for (int i = t; i < dm.d; i += kBlock) h0[i] = hin[i];
       if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = dm.L;
       if (a.sim_out)
         for (int i = t; i < dm.L; i += kBlock) a.sim_out[((size_t)step * dm.B + b) * dm.L + i] = __builtin_nanf("");
@@ -65,39 +70,13 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
         if (t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = 0;
       }
     } else {
-      hin = a.hs + ((size_t)(layer - 1) * dm.B + b) * dm.d;
+      const int lp = layer - 1;
+      hin = a.hs + ((size_t)lp * dm.B + b) * dm.d;
       if (mode == 0) {
-        const int lp = layer - 1;
-        const int prev = a.route[lp * dm.B + b];
-        if (prev == ROUTE_RIVER) {
-          route = ROUTE_RIVER;
-        } else if (lp >= dm.entry) {
-          if (a.sched) {
-            int e = a.sched[step * dm.B + b];
-            if ((e < dm.entry && e != 0) || e > dm.L) {
-              if (t == 0) atomicOr(a.err, ERR_FORCED);
-              e = dm.L;
-            }
-            if (lp == e) route = ROUTE_RIVER;
-          } else {
-            const f16* hprev = a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d;
-            double s0 = 0.0, s1 = 0.0, s2 = 0.0;
-            for (int i = t; i < dm.d; i += kBlock) {
-              const double x = (double)h2f(hprev[i]), y = (double)h2f(hin[i]);
-              s0 += x * y;
-              s1 += x * x;
-              s2 += y * y;
-            }
-            const double dot = block_sum_d(s0, red), n1 = block_sum_d(s1, red), n2 = block_sum_d(s2, red);
-            const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
-            if (t == 0 && a.sim_out) a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
-            if (sim > (double)a.tau) route = ROUTE_RIVER;
-          }
-          if (route == ROUTE_RIVER && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = lp;
-        }
+        prev = a.route[lp * dm.B + b];
+        if (lp >= dm.entry && !a.sched) hprev = a.hs + ((size_t)(lp - 1) * dm.B + b) * dm.d;
       }
     }
-    if (t == 0) a.route[layer * dm.B + b] = route;
   } else if (KIND == 1) {
     hin = a.hmid + ((size_t)(layer - 1) * dm.B + b) * dm.d;
     gain = a.layers[layer - 1].mlp_norm;
@@ -105,16 +84,94 @@ __global__ __launch_bounds__(kBlock) void k_b_prep(DecodeArgs a, int layer, int 
     hin = a.hs + ((size_t)dm.L * dm.B + b) * dm.d;
     gain = a.final_norm;
   }
-  // RMSNorm (fp64 sum of squares), rounded to fp16 like every other path's staging
-  double ss = 0.0;
-  for (int i = t; i < dm.d; i += kBlock) {
-    const double x = (double)h2f(hin[i]);
-    ss += x * x;
+  // s2 = |h|^2 (the norm), s0 = h(l-2).h, s1 = |h(l-2)|^2 (the exit test)
+  uint4 hv[kPP], gv[kPP], pv[kPP];
+#pragma unroll
+  for (int m = 0; m < kPP; ++m) {
+    const int i = t + m * kBlock, ic = (i < np ? i : 0) * 8;
+    hv[m] = ldg16(hin + ic);
+    gv[m] = ldg16(gain + ic);
+    if (KIND == 0 && hprev) pv[m] = ldg16(hprev + ic);
   }
-  const float inv = inv_rms(block_sum_d(ss, red), dm.d, dm.eps);
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+  auto add = [&](uint4 y, uint4 x, bool both) {
+    const f16* hy = (const f16*)&y;
+    const f16* hx = (const f16*)&x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double yv = (double)h2f(hy[e]);
+      s2 += yv * yv;
+      if (both) {
+        const double xv = (double)h2f(hx[e]);
+        s0 += xv * yv;
+        s1 += xv * xv;
+      }
+    }
+  };
+  const bool both = KIND == 0 && hprev != nullptr;
+#pragma unroll
+  for (int m = 0; m < kPP; ++m)
+    if (t + m * kBlock < np) add(hv[m], both ? pv[m] : hv[m], both);
+  for (int i = t + kPP * kBlock; i < np; i += kBlock)
+    add(ldg16(hin + i * 8), both ? ldg16(hprev + i * 8) : make_uint4(0, 0, 0, 0), both);
+  // the three sums over the block at once: waves, then the kW wave totals in order
+  s0 = wave_sum_d(s0);
+  s1 = wave_sum_d(s1);
+  s2 = wave_sum_d(s2);
+  if (t % kWave == 0) {
+    red[0][t / kWave] = s2;
+    red[1][t / kWave] = s0;
+    red[2][t / kWave] = s1;
+  }
+  __syncthreads();
+  double n2 = 0.0, dot = 0.0, n1 = 0.0;
+#pragma unroll
+  for (int j = 0; j < kW; ++j) {
+    n2 += red[0][j];
+    dot += red[1][j];
+    n1 += red[2][j];
+  }
+  if (KIND == 0) {
+    if (layer > 1 && mode == 0) {
+      const int lp = layer - 1;
+      if (prev == ROUTE_RIVER) {
+        route = ROUTE_RIVER;
+      } else if (lp >= dm.entry) {
+        if (a.sched) {
+          int e = a.sched[step * dm.B + b];
+          if ((e < dm.entry && e != 0) || e > dm.L) {
+            if (t == 0) atomicOr(a.err, ERR_FORCED);
+            e = dm.L;
+          }
+          if (lp == e) route = ROUTE_RIVER;
+        } else {  // cos(h(l-2), h(l-1)) > tau: exit after block l - 1
+          const double sim = (n1 > 0.0 && n2 > 0.0) ? dot / sqrt(n1 * n2) : 0.0;
+          if (t == 0 && a.sim_out) a.sim_out[((size_t)step * dm.B + b) * dm.L + lp - 1] = (float)sim;
+          if (sim > (double)a.tau) route = ROUTE_RIVER;
+        }
+        if (route == ROUTE_RIVER && t == 0 && a.exit_out) a.exit_out[step * dm.B + b] = lp;
+      }
+    }
+    if (t == 0) a.route[layer * dm.B + b] = route;
+  }
+  // RMSNorm (1/rms from the fp64 sum of squares), rounded to fp16 like every other path's staging
+  const float inv = inv_rms(n2, dm.d, dm.eps);
   f16* out = xn + (size_t)b * dm.d;
-  for (int g = t; g * 8 < dm.d; g += kBlock)
-    *(uint4*)(out + g * 8) = norm8(*(const uint4*)(hin + g * 8), *(const uint4*)(gain + g * 8), inv, true);
+  f16* h0 = a.hs + (size_t)b * dm.d;  // KIND 0, first layer: h(0) is the embedding row
+  const bool first = KIND == 0 && layer == 1;
+#pragma unroll
+  for (int m = 0; m < kPP; ++m) {
+    const int i = t + m * kBlock;
+    if (i < np) {
+      *(uint4*)(out + i * 8) = norm8(hv[m], gv[m], inv, true);
+      if (first) *(uint4*)(h0 + i * 8) = hv[m];
+    }
+  }
+  for (int i = t + kPP * kBlock; i < np; i += kBlock) {
+    const uint4 x = ldg16(hin + i * 8);
+    *(uint4*)(out + i * 8) = norm8(x, ldg16(gain + i * 8), inv, true);
+    if (first) *(uint4*)(h0 + i * 8) = x;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -175,14 +232,11 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
   LayerDev lwc{};
   if (OP != OP_LM) lwc = a.layers[layer - 1];
   const LayerDev* lw = &lwc;
-  // which streams does any row run at this layer?
+  // which streams does any row run at this layer? The routes' load is issued before the
+  // staging loads and consumed after them, so that it adds no round trip of its own. need[] is
+  // cleared and set by wave 0 alone (in program order), before the barrier that ends staging.
   if (t < 2) need[t] = 0;
-  __syncthreads();
-  if (t < dm.B) {
-    const int r = (OP == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + t];
-    sroute[t] = r;  // the epilogues read the routes here
-    if (r >= 0 && r < streams) atomicOr(&need[r], 1);
-  }
+  const int rt = (OP == OP_LM) ? ROUTE_BACKBONE : a.route[layer * dm.B + (t < dm.B ? t : 0)];
   // stage the slice (rows past the batch and values past K are zero): every load is issued
   // before the first LDS store (one round trip); workgroups start at different pieces so that
   // they do not all read the same lines at once
@@ -206,6 +260,10 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
       i = i < np ? i : i - np;
       if (t + m * kGB < np) xs[i] = v[m];
     }
+  }
+  if (t < dm.B) {
+    sroute[t] = rt;  // the epilogues read the routes here
+    if (rt >= 0 && rt < streams) atomicOr(&need[rt], 1);
   }
   __syncthreads();
   if (normin) {  // RMSNorm in LDS: fp64 sum of squares per row, thread t of row t % 16 summing
