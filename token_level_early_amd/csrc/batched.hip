@@ -202,7 +202,8 @@ static constexpr int kBMaxTiles = 64;  // tiles per workgroup when K is split (b
 static constexpr int kBMaxSplit = 8;   // K slices of one projection at most
 static constexpr int kGW = kGB / kWave;
 
-// WPG: 32-wide K windows per int4 quantisation group (group / 32). EPI, where a tile's epilogue
+// WPG: 32-wide K windows per int4 quantisation group (group / 32). ZP: the river copy is in the
+// zero-point format (else symmetric: no zero-point loads or input sums). EPI, where a tile's epilogue
 // runs: EPI_LOOP as the tile completes (the LM head, whose epilogue loads nothing), EPI_LDS after
 // the stream, from tile results kept in LDS (an epilogue's dependent loads inside the loop would
 // wait for every weight load in flight), EPI_SPLIT after the stream, by the workgroup that
@@ -212,7 +213,7 @@ static constexpr int kBDefer = 16;  // tile results a workgroup can keep for EPI
 // normin: the input is the raw residual stream after attention (h_mid of this layer) and is
 // staged RMS-normalised with the layer's MLP gain, each row's 1/rms computed by every workgroup
 // from the whole row in one fixed order (needs an unsplit K: the whole row in LDS).
-template <int OP, int WPG, int EPI>
+template <int OP, int WPG, int EPI, bool ZP>
 __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f16* xin, int streams,
                                                 int normin) {
   constexpr bool SPLIT = EPI == EPI_SPLIT;
@@ -485,7 +486,6 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     }
   }
   if (need1 && my > 0) {  // ---- int4 river stream
-    const bool zpf = dm.zp != 0;
     // one quantisation group per unit: lane reads 8 * WPG contiguous K values, i.e. 4 * WPG
     // bytes of nibbles (rows are padded to whole groups)
     constexpr int G = 32 * WPG;
@@ -526,41 +526,55 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
           wq[u][0] = *(const __attribute__((address_space(1))) uint32_t*)wp;
         }
         sc[u] = ldg2(sp + gl);  // scale of (column, group), converted at use
-        // zero point (zero-point format; else any in-range byte, unused)
-        zc[u] = *(const __attribute__((address_space(1))) uint8_t*)(zpf ? zp + gl : (const uint8_t*)sp);
+        if constexpr (ZP) zc[u] = *(const __attribute__((address_space(1))) uint8_t*)(zp + gl);
+        else zc[u] = 8;
       }
     };
     // unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z): the group's
     // input sums per batch row come from one more MFMA against a ones operand (they land in the
     // accumulator layout, every column holding its row's sum)
+    // A batch in two passes: first the products of all its units, on accumulators of their own
+    // with no branch in between (the LDS reads, unpacking and matrix work of different units can
+    // then overlap; a unit past the end reads in-range LDS and is dropped), then the scaled
+    // accumulation and the tile ends in unit order.
     auto mma = [&](int q, const uint32_t (&wq)[NG][WPG], const f16 (&sc)[NG], const uint8_t (&zc)[NG]) {
       const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+      bf4 tmp[NG], xsum[NG];
+      uint4 xv[NG][WPG];
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int gs0 = g0 + (q * NG + u) % upt;
+        const int gs = gs0 < g1 ? gs0 : 0;
+#pragma unroll
+        for (int j = 0; j < WPG; ++j) xv[u][j] = xs[(gs * 4 * WPG + kq * WPG + j) * kBR + col];
+      }
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        tmp[u] = bf4{0.f, 0.f, 0.f, 0.f};
+        xsum[u] = bf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < WPG; ++j) {
+          const uint32_t in[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
+          h2 xo[4];
+          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
+          if constexpr (ZP) xsum[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xsum[u], 0, 0, 0);
+          h2 p0, p1, p2, p3;
+          unpack8(wq[u][j], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+          const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+          tmp[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp[u], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
         const int unit = q * NG + u;
         if (unit >= U) break;  // the same in every wave
         const int gs0 = g0 + unit % upt;
         const bool gv = gs0 < g1 && (grp0 + gs0) * G < K;  // else not this wave's: cancelled
-        const int gs = gv ? gs0 : 0;
-        bf4 tmp = bf4{0.f, 0.f, 0.f, 0.f};
-        bf4 xsum = bf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < WPG; ++j) {
-          const uint4 xv = xs[(gs * 4 * WPG + kq * WPG + j) * kBR + col];
-          const uint32_t in[4] = {xv.x, xv.y, xv.z, xv.w};
-          h2 xo[4];
-          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
-          if (zpf) xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xsum, 0, 0, 0);
-          h2 p0, p1, p2, p3;
-          unpack8(wq[u][j], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-          const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
-          tmp = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp, 0, 0, 0);
-        }
         const float su = gv ? h2f(sc[u]) : 0.f;
         const float zu = 8.f - (float)zc[u];  // zero-point format: 8 - z
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = fmaf(su, zpf ? fmaf(zu, xsum[r], tmp[r]) : tmp[r], acc[r]);
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(su, ZP ? fmaf(zu, xsum[u][r], tmp[u][r]) : tmp[u][r], acc[r]);
         if (unit % upt == upt - 1) finish(1, g + (unit / upt) * groups);
       }
     };
@@ -668,16 +682,22 @@ static hipError_t launch_b_gemm(const DecodeArgs& a, int layer, int mode, const 
   const int wpg = dm.group / 32;
   const int my = (b_tiles(OP, dm) + groups - 1) / groups;  // tiles per workgroup at most
   const int epi = S > 1 ? EPI_SPLIT : (OP == OP_LM || 2 * my > kBDefer) ? EPI_LOOP : EPI_LDS;
-#define RIVER_B_LAUNCH(E)                                                                              \
+#define RIVER_B_LAUNCH2(E, Z)                                                                          \
   do {                                                                                               \
-    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, E>), grid, block, 0, st, a, layer, xin, streams, normin); \
-    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, E>), grid, block, 0, st, a, layer, xin, streams, normin); \
-    else hipLaunchKernelGGL((k_b_gemm<OP, 4, E>), grid, block, 0, st, a, layer, xin, streams, normin);       \
+    if (wpg == 1) hipLaunchKernelGGL((k_b_gemm<OP, 1, E, Z>), grid, block, 0, st, a, layer, xin, streams, normin); \
+    else if (wpg == 2) hipLaunchKernelGGL((k_b_gemm<OP, 2, E, Z>), grid, block, 0, st, a, layer, xin, streams, normin); \
+    else hipLaunchKernelGGL((k_b_gemm<OP, 4, E, Z>), grid, block, 0, st, a, layer, xin, streams, normin);       \
+  } while (0)
+#define RIVER_B_LAUNCH(E)                  \
+  do {                                     \
+    if (dm.zp) RIVER_B_LAUNCH2(E, true);   \
+    else RIVER_B_LAUNCH2(E, false);        \
   } while (0)
   if (epi == EPI_SPLIT) RIVER_B_LAUNCH(EPI_SPLIT);
   else if (epi == EPI_LDS) RIVER_B_LAUNCH(EPI_LDS);
   else RIVER_B_LAUNCH(EPI_LOOP);
 #undef RIVER_B_LAUNCH
+#undef RIVER_B_LAUNCH2
   return hipGetLastError();
 }
 
