@@ -32,6 +32,13 @@ typedef uint32_t bu4 __attribute__((ext_vector_type(4)));
 // 8 fp16 values of a 16-byte load as one 16x16x32 MFMA operand
 RIVER_DEV bh8 as8(uint4 u) { return __builtin_bit_cast(bh8, (bu4){u.x, u.y, u.z, u.w}); }
 
+// (w & m) | c in one instruction (v_and_or_b32)
+RIVER_DEV uint32_t b_and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------
 // Per-row preparation: KIND 0 = exit test + attention RMSNorm of layer `layer`'s input,
 // KIND 1 = MLP RMSNorm of h_mid, KIND 2 = final RMSNorm of h(L). Writes xn[b][d].
@@ -222,6 +229,12 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
   __shared__ float ysm[kBR][kBR];
   __shared__ float ytl[EPI == EPI_LDS ? kBDefer : 1][kBR][kBR];
   __shared__ int need[2], nlast, lastf[2 * kBMaxTiles], sroute[kBR];
+  // symmetric group-128 river copy, gate|up and down: the int4 stream multiplies biased codes
+  // (see below) and starts each group's accumulator from minus its input correction,
+  // [group][row / 4][row % 4]. The input is transformed once per workgroup, which pays off only
+  // with several tiles per workgroup (QKV and O have one or two).
+  constexpr bool BIAS = WPG == 4 && !ZP && (OP == OP_GU || OP == OP_DOWN);
+  __shared__ float4 corr[BIAS ? kBXs / 128 : 1][kBR / 4];
   const Dims& dm = a.dm;
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
   const int N = b_rows(OP, dm), K = b_k(OP, dm);
@@ -537,32 +550,50 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     // with no branch in between (the LDS reads, unpacking and matrix work of different units can
     // then overlap; a unit past the end reads in-range LDS and is dropped), then the scaled
     // accumulation and the tile ends in unit order.
+    // BIAS: a nibble u OR-ed into fp16 1024.0 is 1024 + u (low nibble of a byte) or 1024 + 16 u
+    // (high nibble) exactly; the staged input was reordered to the same pairs once, its
+    // high-nibble elements divided by 16, so a group's product is sum x (u - 8) + C with the
+    // per-row constant C = 1032 sum(even x) + 1152 sum(odd x / 16), taken off at the start.
+    // Otherwise the codes are unpacked to u - 8 (u - z) and the input reordered per window.
     auto mma = [&](int q, const uint32_t (&wq)[NG][WPG], const f16 (&sc)[NG], const uint8_t (&zc)[NG]) {
       const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
       bf4 tmp[NG], xsum[NG];
       uint4 xv[NG][WPG];
+      float4 cv[NG];
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
         const int gs0 = g0 + (q * NG + u) % upt;
         const int gs = gs0 < g1 ? gs0 : 0;
 #pragma unroll
         for (int j = 0; j < WPG; ++j) xv[u][j] = xs[(gs * 4 * WPG + kq * WPG + j) * kBR + col];
+        if constexpr (BIAS) cv[u] = corr[gs][kq];
       }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        tmp[u] = bf4{0.f, 0.f, 0.f, 0.f};
-        xsum[u] = bf4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BIAS) {
+          tmp[u] = bf4{-cv[u].x, -cv[u].y, -cv[u].z, -cv[u].w};
+        } else {
+          tmp[u] = bf4{0.f, 0.f, 0.f, 0.f};
+          xsum[u] = bf4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int j = 0; j < WPG; ++j) {
-          const uint32_t in[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
-          h2 xo[4];
-          pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-          const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
-          if constexpr (ZP) xsum[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xsum[u], 0, 0, 0);
-          h2 p0, p1, p2, p3;
-          unpack8(wq[u][j], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
-          const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
-          tmp[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp[u], 0, 0, 0);
+          if constexpr (BIAS) {
+            const uint32_t w = wq[u][j], w8 = w >> 8, mg = 0x64006400u;
+            const uint4 b = make_uint4(b_and_or(w, 0x000F000Fu, mg), b_and_or(w, 0x00F000F0u, mg),
+                                       b_and_or(w8, 0x000F000Fu, mg), b_and_or(w8, 0x00F000F0u, mg));
+            tmp[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as8(xv[u][j]), as8(b), tmp[u], 0, 0, 0);
+          } else {
+            const uint32_t in[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
+            h2 xo[4];
+            pair_for_unpack(in, xo);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+            const bh8 a8 = __builtin_bit_cast(bh8, (bu4){as_u32(xo[0]), as_u32(xo[1]), as_u32(xo[2]), as_u32(xo[3])});
+            if constexpr (ZP) xsum[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ones, xsum[u], 0, 0, 0);
+            h2 p0, p1, p2, p3;
+            unpack8(wq[u][j], p0, p1, p2, p3);  // (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+            const bh8 b8 = __builtin_bit_cast(bh8, (bu4){as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+            tmp[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, b8, tmp[u], 0, 0, 0);
+          }
         }
       }
 #pragma unroll
@@ -582,6 +613,30 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     f16 sc0[NG], sc1[NG];
     uint8_t zc0[NG], zc1[NG];
     load(0, wq0, sc0, zc0);
+    if constexpr (BIAS) {
+      // the staged slice, in place (the fp16 stream, if any, is done with it: its last tile
+      // ended at a barrier): thread (row r, group gg) reorders the group's 16 pieces of row r to
+      // the code pairs, divides its high-nibble elements by 16 and sums both kinds
+      for (int pg = t; pg < ng * kBR; pg += kGB) {
+        const int r = pg % kBR, gg = pg / kBR;
+        float se = 0.f, so = 0.f;
+        const h2 s16 = {(f16)0.0625f, (f16)0.0625f};
+#pragma unroll 4
+        for (int i = 0; i < G / 8; ++i) {
+          uint4& x = xs[(gg * (G / 8) + i) * kBR + r];
+          const uint4 v = x;
+          const h2 e0 = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u));  // x0 | x4<<16
+          const h2 o0 = as_h2(__builtin_amdgcn_perm(v.z, v.x, 0x07060302u)) * s16;  // x1, x5
+          const h2 e1 = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x05040100u));  // x2, x6
+          const h2 o1 = as_h2(__builtin_amdgcn_perm(v.w, v.y, 0x07060302u)) * s16;  // x3, x7
+          se += (h2f(e0.x) + h2f(e0.y)) + (h2f(e1.x) + h2f(e1.y));
+          so += (h2f(o0.x) + h2f(o0.y)) + (h2f(o1.x) + h2f(o1.y));
+          x = make_uint4(as_u32(e0), as_u32(o0), as_u32(e1), as_u32(o1));
+        }
+        ((float*)&corr[gg][0])[r] = 1032.f * se + 1152.f * so;
+      }
+      __syncthreads();
+    }
     for (int q = 0; q < Qb; q += 2) {  // the ring of the fp16 stream
       load(q + 1, wq1, sc1, zc1);
       __builtin_amdgcn_sched_barrier(0);
