@@ -508,19 +508,27 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     const int upt = (ng + kGW - 1) / kGW;
     const int U = my * upt, Qb = (U + NG - 1) / NG;
     const int grp0 = k0 / G;  // first group of the slice
+    // The loader and the multiplier each walk the units in order (every batch is loaded once
+    // and multiplied once, both in increasing order): unit (tile index t, unit u of the tile),
+    // advanced by counting instead of dividing. The lane's row pointers change once per tile.
+    int lt = 0, lu = 0;  // next unit to load
+    const uint8_t* rp;
+    const f16* sp;
+    const uint8_t* zp;  // zero-point format only (else null)
+    bool nok;
+    auto tile_rows = [&](int ti) {
+      const int n = logical_row(OP, g + ti * groups, col, kBR, dm);
+      nok = ti < my && n < N;
+      w4_row(OP, nok ? n : 0, *lw, dm, rp, sp, zp);
+    };
+    tile_rows(0);
     auto load = [&](int q, uint32_t (&wq)[NG][WPG], f16 (&sc)[NG], uint8_t (&zc)[NG]) {
+      (void)q;
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int unit = q * NG + u;
-        const int tile = g + (unit / upt) * groups;
-        const int gs = g0 + unit % upt;  // group within the slice
+        const int gs = g0 + lu;  // group within the slice
         const int grp = grp0 + gs;
-        const int n = logical_row(OP, tile, col, kBR, dm);
-        const bool gok = unit < U && gs < g1 && grp * G < K && n < N;
-        const uint8_t* rp;
-        const f16* sp;
-        const uint8_t* zp;  // zero-point format only (else null)
-        w4_row(OP, gok ? n : 0, *lw, dm, rp, sp, zp);
+        const bool gok = nok && gs < g1 && grp * G < K;
         // raw values from in-range addresses (see the fp16 stream); a unit that is not this
         // wave's is cancelled at use through a zero scale
         const int gl = gok ? grp : 0;
@@ -541,6 +549,10 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
         sc[u] = ldg2(sp + gl);  // scale of (column, group), converted at use
         if constexpr (ZP) zc[u] = *(const __attribute__((address_space(1))) uint8_t*)(zp + gl);
         else zc[u] = 8;
+        if (++lu == upt) {
+          lu = 0;
+          tile_rows(++lt);
+        }
       }
     };
     // unpack8 gives q = u - 8; the zero-point format needs u - z = (u - 8) + (8 - z): the group's
@@ -555,14 +567,18 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
     // high-nibble elements divided by 16, so a group's product is sum x (u - 8) + C with the
     // per-row constant C = 1032 sum(even x) + 1152 sum(odd x / 16), taken off at the start.
     // Otherwise the codes are unpacked to u - 8 (u - z) and the input reordered per window.
+    int mt = 0, mu = 0;  // next unit to multiply
     auto mma = [&](int q, const uint32_t (&wq)[NG][WPG], const f16 (&sc)[NG], const uint8_t (&zc)[NG]) {
+      (void)q;
       const bh8 ones = bh8{(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
       bf4 tmp[NG], xsum[NG];
       uint4 xv[NG][WPG];
       float4 cv[NG];
+      int pu = mu;  // the batch's units, without advancing the walk yet
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int gs0 = g0 + (q * NG + u) % upt;
+        const int gs0 = g0 + pu;
+        pu = pu + 1 == upt ? 0 : pu + 1;
         const int gs = gs0 < g1 ? gs0 : 0;
 #pragma unroll
         for (int j = 0; j < WPG; ++j) xv[u][j] = xs[(gs * 4 * WPG + kq * WPG + j) * kBR + col];
@@ -598,15 +614,18 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
       }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int unit = q * NG + u;
-        if (unit >= U) break;  // the same in every wave
-        const int gs0 = g0 + unit % upt;
+        if (mt >= my) break;  // past the last unit (the same in every wave)
+        const int gs0 = g0 + mu;
         const bool gv = gs0 < g1 && (grp0 + gs0) * G < K;  // else not this wave's: cancelled
         const float su = gv ? h2f(sc[u]) : 0.f;
         const float zu = 8.f - (float)zc[u];  // zero-point format: 8 - z
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = fmaf(su, ZP ? fmaf(zu, xsum[u][r], tmp[u][r]) : tmp[u][r], acc[r]);
-        if (unit % upt == upt - 1) finish(1, g + (unit / upt) * groups);
+        if (mu == upt - 1) finish(1, g + mt * groups);
+        if (++mu == upt) {
+          mu = 0;
+          ++mt;
+        }
       }
     };
     uint32_t wq0[NG][WPG], wq1[NG][WPG];
