@@ -592,8 +592,12 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
           tmp[u] = bf4{0.f, 0.f, 0.f, 0.f};
           xsum[u] = bf4{0.f, 0.f, 0.f, 0.f};
         }
+      }
+      // windows outer, units inner: consecutive matrix instructions are independent
 #pragma unroll
-        for (int j = 0; j < WPG; ++j) {
+      for (int j = 0; j < WPG; ++j) {
+#pragma unroll
+        for (int u = 0; u < NG; ++u) {
           if constexpr (BIAS) {
             const uint32_t w = wq[u][j], w8 = w >> 8, mg = 0x64006400u;
             const uint4 b = make_uint4(b_and_or(w, 0x000F000Fu, mg), b_and_or(w, 0x00F000F0u, mg),
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kGB) void k_b_gemm(DecodeArgs a, int layer, const f
       }
       __syncthreads();
     }
-    for (int q = 0; q < Qb; q += 2) {  // the ring of the fp16 stream
+    for (int q = 0; q < Qb; q += 2) {  // the ring, as in the fp16 stream
       load(q + 1, wq1, sc1, zc1);
       __builtin_amdgcn_sched_barrier(0);
       mma(q, wq0, sc0, zc0);
