@@ -192,7 +192,13 @@ __global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
 // SG = 64 positions (32 when group = 32) lies inside one quantisation group.
 // ---------------------------------------------------------------------------------------
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-static constexpr int QBM = 128, QBN = 128, QBK = 64, QLD = QBK + 8;
+static constexpr int QBM = 128, QBN = 128, QBK = 64, QLD = QBK;
+// LDS tiles are 128-byte rows with no padding; 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7). A fragment read (16 rows, the same chunk, then the next chunk for the next
+// 16 lanes) and a tile store (8 chunks of consecutive rows) then touch every bank once per
+// 16 lanes on 64 banks and per 32 lanes on 128 banks (with the plain padded row, the stores and
+// the wider read groups collided).
+RIVER_DEV int qsw(int r, int k) { return ((((k >> 3) ^ (r >> 1)) & 7) << 3) | (k & 7); }
 
 template <int MODE, int SG>
 __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmArgs g) {
@@ -255,13 +261,13 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, r = c / 8, kc = (c % 8) * 8;
-      *(uint4*)&As[buf][r][kc] = R.a[i];
-      if (MODE == 0) *(uint4*)&Bs[buf][r][kc] = R.b[i];
+      *(uint4*)&As[buf][r][qsw(r, kc)] = R.a[i];
+      if (MODE == 0) *(uint4*)&Bs[buf][r][qsw(r, kc)] = R.b[i];
     }
     if (MODE == 1) {
       const uint32_t wd[4] = {R.q.x, R.q.y, R.q.z, R.q.w};
       const h2 d2 = {R.dz, R.dz};  // zero-point format: u - 8 + (8 - z), exact small integers
-      f16* dst = &Bs[buf][tid / 2][(tid % 2) * 32];
+      const int br = tid / 2;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         h2 p0, p1, p2, p3;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
         h8 v;
         v[0] = p0.x; v[1] = p1.x; v[2] = p2.x; v[3] = p3.x;
         v[4] = p0.y; v[5] = p1.y; v[6] = p2.y; v[7] = p3.y;
-        *(h8*)(dst + h * 8) = v;
+        *(h8*)&Bs[buf][br][qsw(br, (tid % 2) * 32 + h * 8)] = v;
       }
     }
   };
@@ -293,9 +299,15 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
     for (int kk = 0; kk < QBK; kk += 32) {
       h8 af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const h8*)&As[cur][wm + i * 16 + lane % 16][kk + 8 * (lane / 16)];
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + i * 16 + lane % 16;
+        af[i] = *(const h8*)&As[cur][r][qsw(r, kk + 8 * (lane / 16))];
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *(const h8*)&Bs[cur][wn + j * 16 + lane % 16][kk + 8 * (lane / 16)];
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn + j * 16 + lane % 16;
+        bf[j] = *(const h8*)&Bs[cur][r][qsw(r, kk + 8 * (lane / 16))];
+      }
       if (MODE == 1 && (SG == 32 || kk == 0)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -588,9 +600,21 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
 // instruction; O^T += V^T P^T takes 32 keys per instruction, the probabilities coming straight
 // from the score accumulators: lane group j holds keys 4j..4j+3 of two consecutive 16-key
 // blocks, and V^T is read from the transposed tile with the same key order (a dot product only
-// needs both operands to agree on it). NLD 16-byte K and V loads per thread per 64-key tile.
+// needs both operands to agree on it); V stays key-major in LDS and is read transposed.
+// NLD 16-byte K and V loads per thread per 64-key tile.
 // A workgroup takes 16*NQB queries (32): every K/V tile it stages serves them all, so the
 // causal prefix is re-read once per 32 queries of a KV head.
+// V^T fragments from the key-major V tile with CDNA4's transposing LDS read (ds_read_b64_tr_b16):
+// in each group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces that lanes
+// 4j + i / 4 address (j = 0..3). Lane r pointing at V[k0 + r / 4][d0 + 4 (r % 4)] therefore
+// receives V[k0 + j][d0 + r] for j = 0..3: four consecutive keys of dimension d0 + r, the A
+// operand layout of the V^T P^T product.
+typedef short vt_s4 __attribute__((ext_vector_type(4)));
+RIVER_DEV h4 vt_read(const f16* p) {
+  const vt_s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) vt_s4*)p);
+  return __builtin_bit_cast(h4, v);
+}
+
 template <int D, int G, int NQB>
 __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
   constexpr int KT = 64, QW = 16 * NQB, NT = G * kWave;
@@ -599,7 +623,9 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
   constexpr int NLD = KT * D / 8 / NT;
   static_assert(NLD >= 1 && NLD * NT * 8 == KT * D, "tile loads");
   __shared__ __attribute__((aligned(16))) f16 Ks[2][KT][D + 8];  // [key][dim]
-  __shared__ __attribute__((aligned(16))) f16 Vt[2][D][KT + 8];  // [dim][key]
+  // [key][dim] like K; rows of D + 16 values (288 bytes at D = 128), so that the eight keys
+  // a half-wave's transposed reads take start 8 banks apart and cover all 64 banks
+  __shared__ __attribute__((aligned(16))) f16 Vs[2][KT][D + 16];
   const Dims& dm = p.dm;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
@@ -655,9 +681,7 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
     for (int i = 0; i < NLD; ++i) {
       const int c = tid + NT * i, r = c / (D / 8), col = (c % (D / 8)) * 8;
       *(uint4*)&Ks[buf][r][col] = T.k[i];
-      const f16* vh = (const f16*)&T.v[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[buf][col + e][r] = vh[e];
+      *(uint4*)&Vs[buf][r][col] = T.v[i];
     }
   };
   auto compute = [&](int buf, int k0) {
@@ -724,8 +748,8 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const h4 v0 = *(const h4*)&Vt[buf][db * 16 + lr][(2 * s2) * 16 + 4 * lq];
-        const h4 v1 = *(const h4*)&Vt[buf][db * 16 + lr][(2 * s2 + 1) * 16 + 4 * lq];
+        const h4 v0 = vt_read(&Vs[buf][(2 * s2) * 16 + 4 * lq + lr / 4][db * 16 + 4 * (lr % 4)]);
+        const h4 v1 = vt_read(&Vs[buf][(2 * s2 + 1) * 16 + 4 * lq + lr / 4][db * 16 + 4 * (lr % 4)]);
         const h8 vf = (h8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
