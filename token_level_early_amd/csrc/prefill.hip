@@ -295,19 +295,27 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
       if (SG == 32) scales(kt * QBK + 32, sc[1]);
     }
     f4 tmp[4][4];
+    // both 32-wide halves' fragments are read first: the second half's LDS reads overlap the
+    // first half's matrix work
+    h8 afs[2][4], bfs[2][4];
 #pragma unroll
-    for (int kk = 0; kk < QBK; kk += 32) {
-      h8 af[4], bf[4];
+    for (int hk = 0; hk < 2; ++hk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm + i * 16 + lane % 16;
-        af[i] = *(const h8*)&As[cur][r][qsw(r, kk + 8 * (lane / 16))];
+        afs[hk][i] = *(const h8*)&As[cur][r][qsw(r, hk * 32 + 8 * (lane / 16))];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = wn + j * 16 + lane % 16;
-        bf[j] = *(const h8*)&Bs[cur][r][qsw(r, kk + 8 * (lane / 16))];
+        bfs[hk][j] = *(const h8*)&Bs[cur][r][qsw(r, hk * 32 + 8 * (lane / 16))];
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of the products
+#pragma unroll
+    for (int kk = 0; kk < QBK; kk += 32) {
+      const h8(&af)[4] = afs[kk / 32];
+      const h8(&bf)[4] = bfs[kk / 32];
       if (MODE == 1 && (SG == 32 || kk == 0)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
