@@ -12,13 +12,15 @@
 // row (A operand) and of one weight row (B operand) to each MFMA (32 K per instruction). The
 // int4 stream turns 8 nibbles into exact fp16 integers (the 0x6400 exponent trick, pairs (0,4),
 // (1,5), (2,6), (3,7)), permutes the input the same way, sums one quantisation group on the
-// MFMA and applies the fp32 group scale per output column. The waves of a workgroup split K
-// and meet in LDS.
+// MFMA and applies the fp32 group scale per output column (gate|up and down, symmetric
+// group-128: biased codes against an input reordered once per workgroup, see k_b_gemm). The
+// waves of a workgroup split K and meet in LDS.
 //
 // Per layer: k_b_prep (exit test per row, then the attention RMSNorm) -> QKV (RoPE, q and the
 // KV append at each row's position) -> attention (the split-K kernel shared with batch 1, one
-// grid slice per row) -> O + residual -> k_b_prep (MLP RMSNorm) -> gate|up + SwiGLU -> down +
-// residual. Head: final RMSNorm, fp16 LM head with a per-row 64-bit atomic-max argmax, step end.
+// grid slice per row) -> O + residual -> gate|up (the MLP RMSNorm in its input staging; a
+// k_b_prep kernel where its K is split) + SwiGLU -> down + residual. Head: final RMSNorm, fp16
+// LM head with a per-row 64-bit atomic-max argmax, step end.
 #include "gemv.hpp"
 
 static constexpr int kBR = 16;  // rows of an MFMA tile (the batch, padded)
