@@ -610,7 +610,7 @@ def write_pmc_table(csv_path, out_md, title, command):
             d = per.setdefault(k, {})
             d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     names = sorted({c for d in per.values() for c in d})
-    md = [f"# {title}", "", "Command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root):", "", "```",
+    md = [f"# {title}", "", "Command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root, `OUT` = an output directory):", "", "```",
           command, "```", "", "| kernel | dispatches | " + " | ".join(f"mean {c}" for c in names) + " |",
           "|---|---:|" + "---:|" * len(names)]
     for k, d in sorted(per.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
@@ -635,8 +635,8 @@ def write_trace_summary(db, bench_log, out_md):
     cmd = [l for l in open(bench_log) if "[rocprofv3] '" in l]
     md = ["# rocprofv3 kernel trace", ""]
     if cmd:
-        md += ["Traced command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root):", "",
-               "```", "rocprofv3 --kernel-trace --stats -d $R/gpurun_out/<dir> -o kt -- "
+        md += ["Traced command (run from /tmp with `TMPDIR=/tmp`, `R` = repository root, `OUT` = an output directory):", "",
+               "```", "rocprofv3 --kernel-trace --stats -d $OUT -o kt -- "
                + re.sub(r"\S*/bench\.py", "$R/bench.py", cmd[0].split("'")[1]), "```", ""]
     if out:
         md += [f"Workload: {out['config']['workload']}; {out['steps']} timed steps after {out['warmup']} warm-up steps.", ""]
