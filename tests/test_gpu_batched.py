@@ -1,6 +1,7 @@
 """GPU parity of batched decode (several rows per step, each with its own exit layer) against
 the CPU oracle: the tiny decoder with 4 rows end to end, and the Llama-3.1-8B shape with 16
-rows and 4096-token prompts (the batch-16 configuration) on sampled rows and layers."""
+rows and 4096-token prompts (the batch-16 configuration): sampled rows in depth, every row at its
+last block and head."""
 
 import numpy as np
 import pytest
@@ -120,7 +121,7 @@ def test_llama8b_batch16_decode_slices_match_oracle():
     toks = synth.prompt(c, B, P, seed=0, device="cuda")
     sched = torch.from_numpy(synth.schedule(cfg, S, B, seed=0)).to("cuda")  # U{8..32} per row
     pre = rv.prefill(toks, prefill_exit=L)
-    rows = [0, 7, 15]
+    rows = [0, 5, 10, 15]  # checked at the first layer, around the exit and at the last
     es_rows = {b: [int(sched[s, b]) for s in range(S)] for b in rows}
     layers = sorted({1, L} | {e for v in es_rows.values() for e in v} |
                     {min(e + 1, L) for v in es_rows.values() for e in v})
@@ -147,6 +148,19 @@ def test_llama8b_batch16_decode_slices_match_oracle():
                 assert rel_err(hs[l], out) <= TOL, (s, b, l)
                 assert rel_err(k_gpu, Kl[:, pos]) <= TOL, (s, b, l)
                 assert rel_err(v_gpu, Vl[:, pos]) <= TOL, (s, b, l)
+            lg = orc.head_logits(hs[L])
+            assert rel_err(r["logits"][b].cpu().numpy(), lg) <= TOL, (s, b)
+            assert top1_checked(int(r["tokens"][b]), lg) is not False, (s, b)
+        # every other row: the last block (on the route its exit gives it), the head, the token
+        for b in range(B):
+            if b in rows:
+                continue
+            e = int(sched[s, b])
+            hs = hs_all[:, b]
+            Kl = kv[L - 1, 0, b, :, : pos + 1].cpu().numpy().copy()
+            Vl = kv[L - 1, 1, b, :, : pos + 1].cpu().numpy().copy()
+            out = O.block_decode(c, orc.weights_for(L - 1, L > e), orc.norms(L - 1), hs[L - 1], pos, Kl, Vl)
+            assert rel_err(hs[L], out) <= TOL, (s, b, L)
             lg = orc.head_logits(hs[L])
             assert rel_err(r["logits"][b].cpu().numpy(), lg) <= TOL, (s, b)
             assert top1_checked(int(r["tokens"][b]), lg) is not False, (s, b)
