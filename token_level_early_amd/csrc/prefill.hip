@@ -602,14 +602,18 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
   }
 }
 
-// The same prompt attention on CDNA4's 16x16x32 MFMA, with the K/V tiles double-buffered: the
-// next tile's global loads are issued before the current tile's products and stored to the
-// other LDS buffer after them (one barrier per tile). S^T = K Q^T takes 32 head dimensions per
+// The same prompt attention on CDNA4's 16x16x32 MFMA. K/V tiles of 64 keys flow through a ring
+// of three LDS stages filled by LDS DMA (global_load_lds_dwordx4: no registers held in flight),
+// two tiles ahead of the one being multiplied (one barrier per tile). S^T = K Q^T takes 32 head dimensions per
 // instruction; O^T += V^T P^T takes 32 keys per instruction, the probabilities coming straight
 // from the score accumulators: lane group j holds keys 4j..4j+3 of two consecutive 16-key
 // blocks, and V^T is read from the transposed tile with the same key order (a dot product only
 // needs both operands to agree on it); V stays key-major in LDS and is read transposed.
-// NLD 16-byte K and V loads per thread per 64-key tile.
+// Both tiles are 16-byte chunks with no padding, chunk c of key row k stored at c ^ fK(k)
+// (K) or c ^ fV(k) (V): a K fragment read (16 keys, one chunk) and a half-wave's transposing V
+// reads (8 keys, one chunk pair) then touch every bank once. A DMA instruction writes 64
+// consecutive chunks (lane i at M0 + 16 i), so each lane loads the global chunk that belongs
+// at its slot. Keys past the causal end load the last visible key (finite, masked).
 // A workgroup takes 16*NQB queries (32): every K/V tile it stages serves them all, so the
 // causal prefix is re-read once per 32 queries of a KV head.
 // V^T fragments from the key-major V tile with CDNA4's transposing LDS read (ds_read_b64_tr_b16):
@@ -618,6 +622,12 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
 // receives V[k0 + j][d0 + r] for j = 0..3: four consecutive keys of dimension d0 + r, the A
 // operand layout of the V^T P^T product.
 typedef short vt_s4 __attribute__((ext_vector_type(4)));
+// s_waitcnt for vector memory only (at most N outstanding; expcnt and lgkmcnt left free)
+template <int N>
+RIVER_DEV void pf_vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
 RIVER_DEV h4 vt_read(const f16* p) {
   const vt_s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) vt_s4*)p);
   return __builtin_bit_cast(h4, v);
@@ -628,12 +638,22 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
   constexpr int KT = 64, QW = 16 * NQB, NT = G * kWave;
   constexpr int NKS = D / 32;  // 32-wide steps over the head dimension
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
-  constexpr int NLD = KT * D / 8 / NT;
-  static_assert(NLD >= 1 && NLD * NT * 8 == KT * D, "tile loads");
-  __shared__ __attribute__((aligned(16))) f16 Ks[2][KT][D + 8];  // [key][dim]
-  // [key][dim] like K; rows of D + 16 values (288 bytes at D = 128), so that the eight keys
-  // a half-wave's transposed reads take start 8 banks apart and cover all 64 banks
-  __shared__ __attribute__((aligned(16))) f16 Vs[2][KT][D + 16];
+  constexpr int NS = 3;        // LDS stages
+  constexpr int CPR = D / 8;   // 16-byte chunks per key row
+  constexpr int NI = KT * CPR / kWave / G;  // DMA instructions per wave per tile and matrix
+  static_assert(NI >= 1 && NI * kWave * G == KT * CPR, "tile loads");
+  static_assert(D == 128 || D == 64, "swizzles");
+  // [key][chunk ^ fK(key)][8] and [key][chunk ^ fV(key)][8], one array per stage: the compiler
+  // then sees that a stage being read is not the one the DMA in flight writes (with one array it
+  // waits for every DMA before any LDS read)
+  __shared__ __attribute__((aligned(16))) f16 Ks0[KT * D];
+  __shared__ __attribute__((aligned(16))) f16 Ks1[KT * D];
+  __shared__ __attribute__((aligned(16))) f16 Ks2[KT * D];
+  __shared__ __attribute__((aligned(16))) f16 Vs0[KT * D];
+  __shared__ __attribute__((aligned(16))) f16 Vs1[KT * D];
+  __shared__ __attribute__((aligned(16))) f16 Vs2[KT * D];
+  auto kst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Ks0 : decltype(S)::value == 1 ? Ks1 : Ks2; };
+  auto vst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Vs0 : decltype(S)::value == 1 ? Vs1 : Vs2; };
   const Dims& dm = p.dm;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
@@ -672,27 +692,26 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
   }  // this lane's share of the softmax denominator
 
   const int kend = min(tend, q0 + QW);  // keys [0, kend) can be visible to this block
-  struct Tile {
-    uint4 k[NLD], v[NLD];
-  };
-  auto gload = [&](Tile& T, int k0) {
+  auto fK = [](int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); };
+  auto fV = [](int key) { return D == 128 ? ((key & 7) << 1) : (((key >> 1) & 3) << 1); };
+  // tile at keys k0.. into stage st: instruction j of wave w fills chunks (w NI + j) 64 + lane
+  auto issue = [&](auto S, int k0) {
+    f16* const Kd = kst(S);
+    f16* const Vd = vst(S);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = tid + NT * i, r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const bool ok = k0 + r < kend;
-      T.k[i] = ok ? *(const uint4*)(Kb + (size_t)(k0 + r) * D + col) : make_uint4(0, 0, 0, 0);
-      T.v[i] = ok ? *(const uint4*)(Vb + (size_t)(k0 + r) * D + col) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int slot = (w * NI + j) * kWave;  // first chunk of this instruction
+      const int P = slot + lane, key = P / CPR, pc = P % CPR;
+      const size_t kr = (size_t)min(k0 + key, kend - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kb + kr * D + (pc ^ fK(key)) * 8),
+                                       (__attribute__((address_space(3))) void*)(Kd + slot * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vb + kr * D + (pc ^ fV(key)) * 8),
+                                       (__attribute__((address_space(3))) void*)(Vd + slot * 8), 16, 0, 0);
     }
   };
-  auto lstore = [&](const Tile& T, int buf) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int c = tid + NT * i, r = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(uint4*)&Ks[buf][r][col] = T.k[i];
-      *(uint4*)&Vs[buf][r][col] = T.v[i];
-    }
-  };
-  auto compute = [&](int buf, int k0) {
+  auto compute = [&](auto S, int k0) {
+    const f16* const Kc = kst(S);
+    const f16* const Vc = vst(S);
     f4 sc[4][NQB];  // S^T[key][q] for 4 key blocks x NQB query blocks
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -702,7 +721,8 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const h8 kf = *(const h8*)&Ks[buf][kb * 16 + lr][ks * 32 + 8 * lq];
+        const int key = kb * 16 + lr;
+        const h8 kf = *(const h8*)&Kc[key * D + ((ks * 4 + lq) ^ fK(key)) * 8];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
@@ -756,8 +776,11 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const h4 v0 = vt_read(&Vs[buf][(2 * s2) * 16 + 4 * lq + lr / 4][db * 16 + 4 * (lr % 4)]);
-        const h4 v1 = vt_read(&Vs[buf][(2 * s2 + 1) * 16 + 4 * lq + lr / 4][db * 16 + 4 * (lr % 4)]);
+        // lane r: key kb0 + r / 4, dims 16 db + 4 (r % 4): chunk 2 db + (r % 4) / 2, half (r % 2)
+        const int c = 2 * db + (lr % 4) / 2, hoff = 4 * (lr % 2);
+        const int key0 = (2 * s2) * 16 + 4 * lq + lr / 4, key1 = key0 + 16;
+        const h4 v0 = vt_read(&Vc[key0 * D + (c ^ fV(key0)) * 8 + hoff]);
+        const h4 v1 = vt_read(&Vc[key1 * D + (c ^ fV(key1)) * 8 + hoff]);
         const h8 vf = (h8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -766,23 +789,33 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
     }
   };
   const int nt = (kend + KT - 1) / KT;
-  Tile t0r, t1r;
-  if (nt > 0) {
-    gload(t0r, 0);
-    lstore(t0r, 0);
-  }
-  if (nt > 1) gload(t1r, KT);
-  __syncthreads();
-  for (int kt = 0; kt < nt; kt += 2) {
-    if (kt + 2 < nt) gload(t0r, (kt + 2) * KT);
-    compute(0, kt * KT);
-    if (kt + 1 < nt) lstore(t1r, 1);
-    __syncthreads();
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  // tile kt sits in stage kt % 3; the loop runs three tiles per iteration so that every stage
+  // is known at compile time
+  auto step = [&](auto S, auto SN, int kt) {
+    // this wave's DMA of tile kt is complete once at most the next tile's is in flight
+    if (kt + 1 < nt) pf_vm_wait<2 * NI>();
+    else pf_vm_wait<0>();
+    // every wave's part of tile kt landed; every wave is done with tile kt - 1 (its LDS reads
+    // returned before the products that used them). A plain barrier: the workgroup fence of
+    // __syncthreads would wait for every DMA in flight, the next tile's too. The empty asm
+    // statements keep the compiler from moving memory accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nt) issue(SN, (kt + 2) * KT);
+    compute(S, kt * KT);
+  };
+  if (nt > 0) issue(S0{}, 0);
+  if (nt > 1) issue(S1{}, KT);
+  for (int kt = 0; kt < nt; kt += 3) {
+    step(S0{}, S2{}, kt);
     if (kt + 1 >= nt) break;
-    if (kt + 3 < nt) gload(t1r, (kt + 3) * KT);
-    compute(1, (kt + 1) * KT);
-    if (kt + 2 < nt) lstore(t0r, 0);
-    __syncthreads();
+    step(S1{}, S0{}, kt + 1);
+    if (kt + 2 >= nt) break;
+    step(S2{}, S1{}, kt + 2);
   }
   // denominators (the four lanes of a query column hold disjoint keys), normalise, store
 #pragma unroll
