@@ -602,9 +602,11 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn(PfArgs p, int layer) {
   }
 }
 
-// The same prompt attention on CDNA4's 16x16x32 MFMA. K/V tiles of 64 keys flow through a ring
-// of three LDS stages filled by LDS DMA (global_load_lds_dwordx4: no registers held in flight),
-// two tiles ahead of the one being multiplied (one barrier per tile). S^T = K Q^T takes 32 head dimensions per
+// The same prompt attention on CDNA4's 16x16x32 MFMA. K/V tiles of 64 keys flow through two LDS
+// stages filled by LDS DMA (global_load_lds_dwordx4: no registers held in flight), one tile
+// ahead of the one being multiplied (one barrier per tile). Without registers for staging, the
+// kernel fits two waves per SIMD (two workgroups per CU: 64 KB of LDS each at D = 128), and
+// the other workgroup's products cover a tile's load. S^T = K Q^T takes 32 head dimensions per
 // instruction; O^T += V^T P^T takes 32 keys per instruction, the probabilities coming straight
 // from the score accumulators: lane group j holds keys 4j..4j+3 of two consecutive 16-key
 // blocks, and V^T is read from the transposed tile with the same key order (a dot product only
@@ -634,26 +636,25 @@ RIVER_DEV h4 vt_read(const f16* p) {
 }
 
 template <int D, int G, int NQB>
-__global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
+__global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_pf_fattn2(PfArgs p, int layer) {
+  // (two waves per SIMD: at D = 128 the register allocator spills 20 bytes per lane, which
+  // costs far less than the latency a second wave hides)
   constexpr int KT = 64, QW = 16 * NQB, NT = G * kWave;
   constexpr int NKS = D / 32;  // 32-wide steps over the head dimension
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
-  constexpr int NS = 3;        // LDS stages
   constexpr int CPR = D / 8;   // 16-byte chunks per key row
   constexpr int NI = KT * CPR / kWave / G;  // DMA instructions per wave per tile and matrix
   static_assert(NI >= 1 && NI * kWave * G == KT * CPR, "tile loads");
   static_assert(D == 128 || D == 64, "swizzles");
   // [key][chunk ^ fK(key)][8] and [key][chunk ^ fV(key)][8], one array per stage: the compiler
-  // then sees that a stage being read is not the one the DMA in flight writes (with one array it
-  // waits for every DMA before any LDS read)
+  // then sees that the stage being read is not the one the DMA in flight writes (with one array
+  // it waits for every DMA before any LDS read)
   __shared__ __attribute__((aligned(16))) f16 Ks0[KT * D];
   __shared__ __attribute__((aligned(16))) f16 Ks1[KT * D];
-  __shared__ __attribute__((aligned(16))) f16 Ks2[KT * D];
   __shared__ __attribute__((aligned(16))) f16 Vs0[KT * D];
   __shared__ __attribute__((aligned(16))) f16 Vs1[KT * D];
-  __shared__ __attribute__((aligned(16))) f16 Vs2[KT * D];
-  auto kst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Ks0 : decltype(S)::value == 1 ? Ks1 : Ks2; };
-  auto vst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Vs0 : decltype(S)::value == 1 ? Vs1 : Vs2; };
+  auto kst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Ks0 : Ks1; };
+  auto vst = [&](auto S) -> f16* { return decltype(S)::value == 0 ? Vs0 : Vs1; };
   const Dims& dm = p.dm;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
@@ -791,31 +792,25 @@ __global__ __launch_bounds__(G * kWave) void k_pf_fattn2(PfArgs p, int layer) {
   const int nt = (kend + KT - 1) / KT;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  // tile kt sits in stage kt % 3; the loop runs three tiles per iteration so that every stage
-  // is known at compile time
+  // tile kt sits in stage kt % 2; the loop runs two tiles per iteration so that every stage is
+  // known at compile time
   auto step = [&](auto S, auto SN, int kt) {
-    // this wave's DMA of tile kt is complete once at most the next tile's is in flight
-    if (kt + 1 < nt) pf_vm_wait<2 * NI>();
-    else pf_vm_wait<0>();
+    pf_vm_wait<0>();  // this wave's DMA of tile kt (the only one in flight) is complete
     // every wave's part of tile kt landed; every wave is done with tile kt - 1 (its LDS reads
     // returned before the products that used them). A plain barrier: the workgroup fence of
-    // __syncthreads would wait for every DMA in flight, the next tile's too. The empty asm
-    // statements keep the compiler from moving memory accesses across it.
+    // __syncthreads would wait for the DMA issued after it as well. The empty asm statements
+    // keep the compiler from moving memory accesses across it.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 2 < nt) issue(SN, (kt + 2) * KT);
+    if (kt + 1 < nt) issue(SN, (kt + 1) * KT);
     compute(S, kt * KT);
   };
   if (nt > 0) issue(S0{}, 0);
-  if (nt > 1) issue(S1{}, KT);
-  for (int kt = 0; kt < nt; kt += 3) {
-    step(S0{}, S2{}, kt);
+  for (int kt = 0; kt < nt; kt += 2) {
+    step(S0{}, S1{}, kt);
     if (kt + 1 >= nt) break;
     step(S1{}, S0{}, kt + 1);
-    if (kt + 2 >= nt) break;
-    step(S2{}, S1{}, kt + 2);
   }
   // denominators (the four lanes of a query column hold disjoint keys), normalise, store
 #pragma unroll
