@@ -45,143 +45,6 @@ struct PfGemmArgs {
 // Residual-stream row of chunk-local row m (chunks of Ce positions from t0, prompts of P).
 RIVER_DEV int64_t pf_row(int m, int Ce, int t0, int P) { return (int64_t)(m / Ce) * P + t0 + m % Ce; }
 
-static constexpr int GBM = 128, GBN = 128, GBK = 32, GLDK = GBK + 16;  // 96-byte rows: 16-byte aligned
-
-template <int MODE>
-__global__ __launch_bounds__(kBlock) void k_pf_gemm(PfGemmArgs g) {
-  __shared__ f16 As[GBM][GLDK];
-  __shared__ f16 Bs[GBN][GLDK];
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-  // skip tiles whose rows all belong to sequences on the other route
-  {
-    const int mlast = min(g.M, m0 + GBM) - 1;
-    bool any = false;
-    for (int sq = m0 / g.P; sq <= mlast / g.P; ++sq) any |= (g.seq_route[sq] == g.want_route);
-    if (!any) return;
-  }
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  const int wm = (w / 2) * 64, wn = (w % 2) * 64;
-  f4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  const int64_t rb4 = w4_row_bytes(g.K), rs4 = w4_row_scales(g.K, g.group);
-  const int lr = tid / 2, lh = tid % 2;  // loader: row lr, half lh of the k-tile
-
-  for (int k0 = 0; k0 < g.K; k0 += GBK) {
-    // ---- global -> registers
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-    {
-      const int m = m0 + lr, k = k0 + lh * 16;
-      if (m < g.M) {
-        const f16* src = g.A + (size_t)m * g.K;
-        if (k < g.K) a0 = *(const uint4*)(src + k);
-        if (k + 8 < g.K) a1 = *(const uint4*)(src + k + 8);
-      }
-    }
-    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-    uint2 bq = make_uint2(0x88888888u, 0x88888888u);
-    f16 dz = (f16)0.0f;  // zero-point format: 8 - z of this row's group (unpack8 gives u - 8)
-    {
-      const int n = n0 + lr, k = k0 + lh * 16;
-      if (n < g.N) {
-        if (MODE == 0) {
-          int si = 0;
-          while (si < 2 && n >= g.seg_start[si + 1]) ++si;
-          const f16* src = g.seg_ptr[si] + (size_t)(n - g.seg_start[si]) * g.K;
-          if (k < g.K) b0 = *(const uint4*)(src + k);
-          if (k + 8 < g.K) b1 = *(const uint4*)(src + k + 8);
-        } else {
-          bq = *(const uint2*)(g.w4 + (size_t)n * rb4 + k / 2);
-          if (g.z4) dz = (f16)(8.0f - (float)g.z4[(size_t)n * rs4 + k0 / g.group]);
-        }
-      }
-    }
-    __syncthreads();
-    *(uint4*)&As[lr][lh * 16] = a0;
-    *(uint4*)&As[lr][lh * 16 + 8] = a1;
-    if (MODE == 0) {
-      *(uint4*)&Bs[lr][lh * 16] = b0;
-      *(uint4*)&Bs[lr][lh * 16 + 8] = b1;
-    } else {
-      const uint32_t wd[2] = {bq.x, bq.y};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        h2 p0, p1, p2, p3;
-        unpack8(wd[h], p0, p1, p2, p3);  // pairs (q0,q4),(q1,q5),(q2,q6),(q3,q7)
-        const h2 d2 = {dz, dz};  // exact: small integers
-        p0 += d2;
-        p1 += d2;
-        p2 += d2;
-        p3 += d2;
-        f16* dst = &Bs[lr][lh * 16 + h * 8];
-        dst[0] = p0.x; dst[4] = p0.y;
-        dst[1] = p1.x; dst[5] = p1.y;
-        dst[2] = p2.x; dst[6] = p2.y;
-        dst[3] = p3.x; dst[7] = p3.y;
-      }
-    }
-    __syncthreads();
-    // ---- MFMA over the k-tile
-    f4 tmp[4][4];
-    if (MODE == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tmp[i][j] = (f4){0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kk = 0; kk < GBK; kk += 16) {
-      h4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const h4*)&As[wm + i * 16 + lane % 16][kk + 4 * (lane / 16)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *(const h4*)&Bs[wn + j * 16 + lane % 16][kk + 4 * (lane / 16)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (MODE == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-          else
-            tmp[i][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(af[i], bf[j], tmp[i][j], 0, 0, 0);
-        }
-    }
-    if (MODE == 1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn + j * 16 + lane % 16;
-        const float s = (n < g.N) ? h2f(g.s4[(size_t)n * rs4 + k0 / g.group]) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] += s * tmp[i][j];
-      }
-    }
-  }
-  // ---- epilogue: D[i][j] at row 4*(lane/16)+r, column lane%16 of each 16x16 block
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + j * 16 + lane % 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + i * 16 + 4 * (lane / 16) + r;
-        if (m < g.M && n < g.N && g.seq_route[m / g.P] == g.want_route) {
-          const f16 v = f2h(acc[i][j][r]);
-          const int64_t cm = g.c_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
-          if (g.epi == EPI_STORE) {
-            g.C[cm * g.N + n] = v;
-          } else {
-            const int64_t rm = g.r_global ? pf_row(m, g.P, g.t0, g.Ptot) : m;
-            g.C[cm * g.N + n] = f2h(h2f(g.R[rm * g.N + n]) + h2f(v));
-          }
-        }
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // Prompt GEMM on CDNA4's 16x16x32 fp16 MFMA: 128 x 128 output tiles, K in steps of 64 staged
 // through a double-buffered LDS tile pair (the next step's global loads are in flight while the
