@@ -179,19 +179,22 @@ __global__ void k_step_end(DecodeArgs a) {
 // GQA split-K decode attention over the shared cache (attn.hpp). Grid (smax, Hkv, B).
 template <int D, int G>
 #ifndef RIVER_DATTN_UP
-#define RIVER_DATTN_UP 2  // positions per lane per block
+#define RIVER_DATTN_UP 4  // positions per lane per block
 #endif
 #ifndef RIVER_DATTN_GL
 #define RIVER_DATTN_GL 2  // query heads per lane (at least what fits a wave)
 #endif
-__global__ __launch_bounds__(kBlock) void k_dec_attn(DecodeArgs a, int layer) {
+#ifndef RIVER_DATTN_NT
+#define RIVER_DATTN_NT kBlock  // threads per workgroup
+#endif
+__global__ __launch_bounds__(RIVER_DATTN_NT) void k_dec_attn(DecodeArgs a, int layer) {
   // query heads per lane: as requested, but enough that one slot's lanes fit a wave
   constexpr int GLmin = (G * (D / 8) + kWave - 1) / kWave;
   constexpr int GLr = RIVER_DATTN_GL < G ? RIVER_DATTN_GL : G;
   constexpr int GLP = GLr > GLmin ? GLr : GLmin;
-  __shared__ AttnLds<D, G, kBlock, GLP> sm;
+  __shared__ AttnLds<D, G, RIVER_DATTN_NT, GLP> sm;
   const int b = blockIdx.z;
-  attn_split<D, G, kBlock, false, RIVER_DATTN_UP, GLP>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b], a.attn_smax, sm);
+  attn_split<D, G, RIVER_DATTN_NT, false, RIVER_DATTN_UP, GLP>(a, layer, blockIdx.x, blockIdx.y, b, a.pos[b], a.attn_smax, sm);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -263,14 +266,14 @@ hipError_t river_launch_attn(const DecodeArgs& a, int layer, hipStream_t st) {
   const Dims& dm = a.dm;
   const int G = dm.H / dm.Hkv;
   dim3 grid(a.attn_smax, dm.Hkv, dm.B);
-  if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_dec_attn<128, 4>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_dec_attn<64, 4>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_dec_attn<64, 2>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_dec_attn<128, 2>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_dec_attn<128, 1>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_dec_attn<64, 1>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_dec_attn<128, 8>), grid, dim3(kBlock), 0, st, a, layer);
-  else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_dec_attn<64, 8>), grid, dim3(kBlock), 0, st, a, layer);
+  if (dm.D == 128 && G == 4) hipLaunchKernelGGL((k_dec_attn<128, 4>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 64 && G == 4) hipLaunchKernelGGL((k_dec_attn<64, 4>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 64 && G == 2) hipLaunchKernelGGL((k_dec_attn<64, 2>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 128 && G == 2) hipLaunchKernelGGL((k_dec_attn<128, 2>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 128 && G == 1) hipLaunchKernelGGL((k_dec_attn<128, 1>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 64 && G == 1) hipLaunchKernelGGL((k_dec_attn<64, 1>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 128 && G == 8) hipLaunchKernelGGL((k_dec_attn<128, 8>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
+  else if (dm.D == 64 && G == 8) hipLaunchKernelGGL((k_dec_attn<64, 8>), grid, dim3(RIVER_DATTN_NT), 0, st, a, layer);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
