@@ -24,8 +24,18 @@ def tiny():
 
 @pytest.mark.parametrize("mode", ["forced", "tau"])
 def test_tiny_batch4_matches_oracle(tiny, mode):
+    _tiny_batch_vs_oracle(tiny, mode, B=4, P=24, S=8)
+
+
+# Longer prompts split each row's attention over several 64-position chunks, the last one
+# ragged (203 + s and 77 + s are not multiples of 64), at 3 rows and at the 16-row maximum.
+@pytest.mark.parametrize("B,P", [(3, 203), (16, 77)])
+def test_tiny_batch_ragged_attention_splits_match_oracle(tiny, B, P):
+    _tiny_batch_vs_oracle(tiny, "forced", B=B, P=P, S=4)
+
+
+def _tiny_batch_vs_oracle(tiny, mode, B, P, S):
     w, orc = tiny
-    B, P, S = 4, 24, 8
     L = TINY["L"]
     Tmax = P + S + 4
     rv = river.River(TINY, w, max_seq=Tmax, max_prefill=P, batch=B)
