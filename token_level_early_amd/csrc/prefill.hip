@@ -592,43 +592,59 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
       }
     }
-    // mask, tile max per query column, online rescale
+    // mask, tile max per query column, online rescale. A tile wholly at or below the first
+    // query of the block (k0 + KT - 1 <= q0 < kend) is visible to every query of it: it takes
+    // no mask, and every column then has a visible key.
     h4 pf[4][NQB];
+    auto softmax = [&](auto EDGE) {
+      constexpr bool E = decltype(EDGE)::value;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int t = q0 + qb * 16 + lr;
-      float mt = -__builtin_inff();
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int t = q0 + qb * 16 + lr;
+        float mt = -__builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + kb * 16 + 4 * lq + r;
-          const float v = (key <= t && key < kend) ? sc[kb][qb][r] * qs : -__builtin_inff();
-          sc[kb][qb][r] = v;
-          mt = fmaxf(mt, v);
+          for (int r = 0; r < 4; ++r) {
+            float v = sc[kb][qb][r] * qs;
+            if (E) {
+              const int key = k0 + kb * 16 + 4 * lq + r;
+              v = (key <= t && key < kend) ? v : -__builtin_inff();
+            }
+            sc[kb][qb][r] = v;
+            mt = fmaxf(mt, v);
+          }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+        const float mn = fmaxf(mrow[qb], mt);
+        const bool live = !E || mn > -__builtin_inff();  // some visible key so far
+        // v_exp_f32 itself: arguments below -126 give 0 instead of a subnormal, which the fp16
+        // probabilities and the sums (at least 1 once a key is visible) cannot hold anyway
+        const float cf = live ? __builtin_amdgcn_exp2f(mrow[qb] - mn) : 1.f;
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          h4 pv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = live ? __builtin_amdgcn_exp2f(sc[kb][qb][r] - mn) : 0.f;
+            pv[r] = (f16)e;
+            ps += e;
+          }
+          pf[kb][qb] = pv;
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      const float mn = fmaxf(mrow[qb], mt);
-      const bool live = mn > -__builtin_inff();  // some visible key so far
-      const float cf = live ? exp2f(mrow[qb] - mn) : 1.f;
-      float ps = 0.f;
+        lsum[qb] = lsum[qb] * cf + ps;
+        mrow[qb] = mn;
+        // cf is exactly 1 in a column whose running max did not grow: the rescale is skipped
+        // when that holds in every column of the wave
+        if (__ballot(cf != 1.f)) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        h4 pv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = live ? exp2f(sc[kb][qb][r] - mn) : 0.f;
-          pv[r] = (f16)e;
-          ps += e;
+          for (int db = 0; db < NDB; ++db) o[db][qb] *= cf;
         }
-        pf[kb][qb] = pv;
       }
-      lsum[qb] = lsum[qb] * cf + ps;
-      mrow[qb] = mn;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db][qb] *= cf;
-    }
+    };
+    if (k0 + KT - 1 > q0) softmax(std::true_type{});
+    else softmax(std::false_type{});
     // O^T[dim][q] += V^T P^T, 32 keys (blocks 2s and 2s+1) per instruction
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
