@@ -522,7 +522,8 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int q0 = p.t0 + blockIdx.x * QW;  // queries: positions of the current chunk
   const int tend = p.t0 + p.Ce;
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  // the wave index as a scalar: the DMA's LDS addresses (M0) and the head are then scalar
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int lr = lane % 16, lq = lane / 16;
   const int h = kvh * G + w;
   const size_t hs = (size_t)dm.Tmax * D;
@@ -559,17 +560,22 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
   auto fK = [](int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); };
   auto fV = [](int key) { return D == 128 ? ((key & 7) << 1) : (((key >> 1) & 3) << 1); };
   // tile at keys k0.. into stage st: instruction j of wave w fills chunks (w NI + j) 64 + lane
+  // (scalar tile base + a 32-bit per-lane byte offset: rows past kend - 1 read row kend - 1)
   auto issue = [&](auto S, int k0) {
     f16* const Kd = kst(S);
     f16* const Vd = vst(S);
+    const char* const Kt = (const char*)(Kb + (size_t)k0 * D);
+    const char* const Vt = (const char*)(Vb + (size_t)k0 * D);
+    const int lim = kend - 1 - k0;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int slot = (w * NI + j) * kWave;  // first chunk of this instruction
       const int P = slot + lane, key = P / CPR, pc = P % CPR;
-      const size_t kr = (size_t)min(k0 + key, kend - 1);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kb + kr * D + (pc ^ fK(key)) * 8),
+      const uint32_t kr = (uint32_t)min(key, lim);
+      const uint32_t ok = (kr * D + (pc ^ fK(key)) * 8) * 2, ov = (kr * D + (pc ^ fV(key)) * 8) * 2;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kt + ok),
                                        (__attribute__((address_space(3))) void*)(Kd + slot * 8), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vb + kr * D + (pc ^ fV(key)) * 8),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vt + ov),
                                        (__attribute__((address_space(3))) void*)(Vd + slot * 8), 16, 0, 0);
     }
   };
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float v = sc[kb][qb][r] * qs;
+            float v = sc[kb][qb][r];  // unscaled: the scale is applied with the max below
             if (E) {
               const int key = k0 + kb * 16 + 4 * lq + r;
               v = (key <= t && key < kend) ? v : -__builtin_inff();
@@ -616,7 +622,9 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
           }
         mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
         mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-        const float mn = fmaxf(mrow[qb], mt);
+        // qs > 0 and rounding is monotonic, so mt * qs is the largest of the rounded scaled
+        // scores; each exponent is then one fused s * qs - mn
+        const float mn = fmaxf(mrow[qb], mt * qs);
         const bool live = !E || mn > -__builtin_inff();  // some visible key so far
         // v_exp_f32 itself: arguments below -126 give 0 instead of a subnormal, which the fp16
         // probabilities and the sums (at least 1 once a key is visible) cannot hold anyway
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(G * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
           h4 pv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = live ? __builtin_amdgcn_exp2f(sc[kb][qb][r] - mn) : 0.f;
+            const float e = live ? __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r], qs, -mn)) : 0.f;
             pv[r] = (f16)e;
             ps += e;
           }
