@@ -63,7 +63,7 @@ static constexpr int QBM = 128, QBN = 128, QBK = 64, QLD = QBK;
 // the wider read groups collided).
 RIVER_DEV int qsw(int r, int k) { return ((((k >> 3) ^ (r >> 1)) & 7) << 3) | (k & 7); }
 
-template <int MODE, int SG>
+template <int MODE, int SG, bool IN = false>
 __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmArgs g) {
   __shared__ __attribute__((aligned(16))) f16 As[2][QBM][QLD];
   __shared__ __attribute__((aligned(16))) f16 Bs[2][QBN][QLD];
@@ -118,6 +118,35 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
         R.q = *(const uint4*)(g.w4 + (size_t)n * rb4 + k / 2);
         if (g.z4) R.dz = (f16)(8.0f - (float)g.z4[(size_t)n * rs4 + k / g.group]);
       }
+    }
+  };
+  // IN (fp16 weights; M, N and K multiples of the tile and step, so every tile is in range):
+  // no bounds tests, hence no branches around the loads, and the wait before a step's LDS
+  // stores then covers only that step's loads (the next step's stay in flight)
+  static_assert(!IN || MODE == 0, "in-range variant: fp16 weights only");
+  // Operands as scalar tile bases plus one 32-bit lane offset shared by A and B (a tile never
+  // straddles two weight segments: their starts are multiples of the tile), so the addresses
+  // hold one vector register; native vectors (arrays of HIP's uint4 wrapper were left in
+  // private memory here).
+  int si0 = 0;
+  while (si0 < 2 && n0 >= g.seg_start[si0 + 1]) ++si0;
+  const char* const At = (const char*)(g.A + (size_t)m0 * g.K);
+  const char* const Bt = (const char*)(g.seg_ptr[si0] + (size_t)(n0 - g.seg_start[si0]) * g.K);
+  const uint32_t loff = (uint32_t)((tid / 8) * g.K + (tid % 8) * 8) * 2u;
+  auto gload_in = [&](h8 (&a)[4], h8 (&b)[4], int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t u = ((size_t)32 * i * g.K + k0) * 2;  // rows 32 i.., columns k0..
+      a[i] = *(const h8*)(At + u + loff);
+      b[i] = *(const h8*)(Bt + u + loff);
+    }
+  };
+  auto lstore_in = [&](const h8 (&a)[4], const h8 (&b)[4], int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / 8, kc = (c % 8) * 8;
+      *(h8*)&As[buf][r][qsw(r, kc)] = a[i];
+      *(h8*)&Bs[buf][r][qsw(r, kc)] = b[i];
     }
   };
   auto lstore = [&](const Regs& R, int buf) {
@@ -207,20 +236,41 @@ __global__ __launch_bounds__(kBlock, MODE == 0 ? 2 : 1) void k_pf_gemm2(PfGemmAr
   // the other, so every load has two steps of matrix work to arrive behind.
   const int nk = (g.K + QBK - 1) / QBK;
   Regs r0, r1;
-  gload(r0, 0);
-  lstore(r0, 0);
-  if (nk > 1) gload(r1, QBK);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) gload(r0, (kt + 2) * QBK);
-    compute(0, kt);
-    if (kt + 1 < nk) lstore(r1, 1);
+  if constexpr (IN) {
+    // the last two steps reload the final K step instead of skipping their loads (the values
+    // are never stored), so every iteration issues the same loads
+    h8 a0[4], b0[4], a1[4], b1[4];
+    gload_in(a0, b0, 0);
+    lstore_in(a0, b0, 0);
+    gload_in(a1, b1, min(1, nk - 1) * QBK);
     __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) gload(r1, (kt + 3) * QBK);
-    compute(1, kt + 1);
-    if (kt + 2 < nk) lstore(r0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      gload_in(a0, b0, min(kt + 2, nk - 1) * QBK);
+      compute(0, kt);
+      if (kt + 1 < nk) lstore_in(a1, b1, 1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      gload_in(a1, b1, min(kt + 3, nk - 1) * QBK);
+      compute(1, kt + 1);
+      if (kt + 2 < nk) lstore_in(a0, b0, 0);
+      __syncthreads();
+    }
+  } else {
+    gload(r0, 0);
+    lstore(r0, 0);
+    if (nk > 1) gload(r1, QBK);
     __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) gload(r0, (kt + 2) * QBK);
+      compute(0, kt);
+      if (kt + 1 < nk) lstore(r1, 1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      if (kt + 3 < nk) gload(r1, (kt + 3) * QBK);
+      compute(1, kt + 1);
+      if (kt + 2 < nk) lstore(r0, 0);
+      __syncthreads();
+    }
   }
   // epilogue: D[i][j] at row 4*(lane/16)+r, column lane%16 of each 16x16 block
 #pragma unroll
@@ -809,7 +859,11 @@ static hipError_t gemm(const PfGemmArgs& g0, const LayerDev& lw, int which, hipS
   dim3 grid((g0.N + QBN - 1) / QBN, (g0.M + QBM - 1) / QBM);
   PfGemmArgs g = g0;
   g.want_route = ROUTE_BACKBONE;
-  hipLaunchKernelGGL((k_pf_gemm2<0, 64>), grid, dim3(kBlock), 0, st, g);
+  if (g.M % QBM == 0 && g.N % QBN == 0 && g.K % QBK == 0 && g.seg_start[1] % QBN == 0 &&
+      g.seg_start[2] % QBN == 0)
+    hipLaunchKernelGGL((k_pf_gemm2<0, 64, true>), grid, dim3(kBlock), 0, st, g);
+  else
+    hipLaunchKernelGGL((k_pf_gemm2<0, 64>), grid, dim3(kBlock), 0, st, g);
   g.want_route = ROUTE_RIVER;
   if (g.group >= 64) hipLaunchKernelGGL((k_pf_gemm2<1, 64>), grid, dim3(kBlock), 0, st, g);
   else hipLaunchKernelGGL((k_pf_gemm2<1, 32>), grid, dim3(kBlock), 0, st, g);
