@@ -317,6 +317,32 @@ __global__ __launch_bounds__(kBlock) void k_pf_rmsnorm(const f16* x, const f16* 
   __shared__ double red[4];
   const int m = blockIdx.x;
   const f16* xr = x + (gP > 0 ? pf_row(m, gCe, gt0, gP) : (int64_t)m) * n;
+  f16* orow = out + (size_t)m * n;
+  if ((n & 7) == 0) {  // 16-byte pieces (rows start 16-byte aligned)
+    double s = 0.0;
+    for (int i = threadIdx.x * 8; i < n; i += kBlock * 8) {
+      const uint4 v = *(const uint4*)(xr + i);
+      const f16* v8 = (const f16*)&v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double d = (double)h2f(v8[j]);
+        s += d * d;
+      }
+    }
+    s = block_sum_d(s, red);
+    const float inv = (float)(1.0 / sqrt(s / n + (double)eps));
+    for (int i = threadIdx.x * 8; i < n; i += kBlock * 8) {
+      const uint4 v = *(const uint4*)(xr + i), g = *(const uint4*)(w + i);
+      const f16* v8 = (const f16*)&v;
+      const f16* g8 = (const f16*)&g;
+      uint4 o;
+      f16* o8 = (f16*)&o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o8[j] = f2h(h2f(v8[j]) * inv * h2f(g8[j]));
+      *(uint4*)(orow + i) = o;
+    }
+    return;
+  }
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += kBlock) {
     const double v = (double)h2f(xr[i]);
@@ -324,8 +350,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_rmsnorm(const f16* x, const f16* 
   }
   s = block_sum_d(s, red);
   const float inv = (float)(1.0 / sqrt(s / n + (double)eps));
-  for (int i = threadIdx.x; i < n; i += kBlock)
-    out[(size_t)m * n + i] = f2h(h2f(xr[i]) * inv * h2f(w[i]));
+  for (int i = threadIdx.x; i < n; i += kBlock) orow[i] = f2h(h2f(xr[i]) * inv * h2f(w[i]));
 }
 
 // RoPE on q and k rows of qkv; q -> act [M][H*D]; k, v -> shared cache at (layer, b, kvh, t).
@@ -773,9 +798,24 @@ __global__ __launch_bounds__(kBlock) void k_pf_swiglu(PfArgs p) {
   const int m = blockIdx.x;
   const int F = p.dm.F;
   const f16* row = p.gu + (size_t)m * 2 * F;
-  for (int f = threadIdx.x; f < F; f += kBlock) {
-    const float g = h2f(row[f]), u = h2f(row[F + f]);
-    p.a2[(size_t)m * F + f] = f2h(g / (1.f + __expf(-g)) * u);
+  f16* out = p.a2 + (size_t)m * F;
+  auto act = [](f16 gh, f16 uh) {
+    const float g = h2f(gh), u = h2f(uh);
+    return f2h(g / (1.f + __expf(-g)) * u);
+  };
+  if ((F & 7) == 0) {  // 16-byte pieces: the rows of both buffers then start 16-byte aligned
+    for (int f = threadIdx.x * 8; f < F; f += kBlock * 8) {
+      const uint4 gv = *(const uint4*)(row + f), uv = *(const uint4*)(row + F + f);
+      const f16* g8 = (const f16*)&gv;
+      const f16* u8 = (const f16*)&uv;
+      uint4 o;
+      f16* o8 = (f16*)&o;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[i] = act(g8[i], u8[i]);
+      *(uint4*)(out + f) = o;
+    }
+  } else {
+    for (int f = threadIdx.x; f < F; f += kBlock) out[f] = act(row[f], row[F + f]);
   }
 }
 
