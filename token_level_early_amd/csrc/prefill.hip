@@ -360,6 +360,47 @@ __global__ __launch_bounds__(kBlock) void k_pf_rope_kv(PfArgs p, int layer) {
   const int b = m / p.Ce, t = p.t0 + m % p.Ce;
   const f16* row = p.qkv + (size_t)m * dm.nqkv;
   const int half = dm.D / 2;
+  const size_t cache_row = (size_t)dm.Tmax * dm.D;
+  if ((half & 7) == 0 && (dm.nqkv & 7) == 0) {
+    // 8 consecutive pairs (i, i + half) per thread, 16-byte pieces (the same arithmetic)
+    const int pw = half / 8;
+    for (int idx = threadIdx.x; idx < (dm.H + dm.Hkv) * pw; idx += kBlock) {
+      const int head = idx / pw, i0 = (idx % pw) * 8;
+      const uint4 av = *(const uint4*)(row + head * dm.D + i0);
+      const uint4 bv = *(const uint4*)(row + head * dm.D + i0 + half);
+      const f16* a8 = (const f16*)&av;
+      const f16* b8 = (const f16*)&bv;
+      const float2* cs = p.rope + (size_t)t * half + i0;
+      uint4 o0, o1;
+      f16* r0 = (f16*)&o0;
+      f16* r1 = (f16*)&o1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = h2f(a8[j]), x1 = h2f(b8[j]);
+        const float2 c = cs[j];
+        r0[j] = f2h(x0 * c.x - x1 * c.y);
+        r1[j] = f2h(x1 * c.x + x0 * c.y);
+      }
+      f16* dst;
+      if (head < dm.H) {
+        dst = p.act + (size_t)m * dm.hd + head * dm.D;
+      } else {
+        dst = p.kv + ((((size_t)(layer - 1) * 2 + 0) * dm.B + b) * dm.Hkv + (head - dm.H)) * cache_row +
+              (size_t)t * dm.D;
+        kv_count(p.kvcnt, p.kv, dst + i0, 8);
+        kv_count(p.kvcnt, p.kv, dst + i0 + half, 8);
+      }
+      *(uint4*)(dst + i0) = o0;
+      *(uint4*)(dst + i0 + half) = o1;
+    }
+    for (int idx = threadIdx.x; idx < dm.Hkv * dm.D / 8; idx += kBlock) {
+      const int kvh = idx / (dm.D / 8), i0 = (idx % (dm.D / 8)) * 8;
+      f16* vd = p.kv + ((((size_t)(layer - 1) * 2 + 1) * dm.B + b) * dm.Hkv + kvh) * cache_row + (size_t)t * dm.D;
+      *(uint4*)(vd + i0) = *(const uint4*)(row + (dm.H + dm.Hkv) * dm.D + kvh * dm.D + i0);
+      kv_count(p.kvcnt, p.kv, vd + i0, 8);
+    }
+    return;
+  }
   const int npairs = (dm.H + dm.Hkv) * half;
   for (int idx = threadIdx.x; idx < npairs; idx += kBlock) {
     const int head = idx / half, i = idx % half;
