@@ -934,20 +934,25 @@ __global__ void k_pf_init_routes(PfArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------
-static hipError_t gemm(const PfGemmArgs& g0, const LayerDev& lw, int which, hipStream_t st) {
+static hipError_t gemm(const PfGemmArgs& g0, const LayerDev& lw, int which, int routes, hipStream_t st) {
   // which: 0 qkv, 1 o, 2 gu, 3 down. Launch the fp16 and the int4 variant; each skips the
-  // tiles whose sequences are on the other route.
+  // tiles whose sequences are on the other route. routes: bit 0 / bit 1 = some sequence may be
+  // on the backbone / on the river at this layer (a variant no sequence can use is not launched)
   dim3 grid((g0.N + QBN - 1) / QBN, (g0.M + QBM - 1) / QBM);
   PfGemmArgs g = g0;
   g.want_route = ROUTE_BACKBONE;
-  if (g.M % QBM == 0 && g.N % QBN == 0 && g.K % QBK == 0 && g.seg_start[1] % QBN == 0 &&
-      g.seg_start[2] % QBN == 0)
-    hipLaunchKernelGGL((k_pf_gemm2<0, 64, true>), grid, dim3(kBlock), 0, st, g);
-  else
-    hipLaunchKernelGGL((k_pf_gemm2<0, 64>), grid, dim3(kBlock), 0, st, g);
+  if (routes & 1) {
+    if (g.M % QBM == 0 && g.N % QBN == 0 && g.K % QBK == 0 && g.seg_start[1] % QBN == 0 &&
+        g.seg_start[2] % QBN == 0)
+      hipLaunchKernelGGL((k_pf_gemm2<0, 64, true>), grid, dim3(kBlock), 0, st, g);
+    else
+      hipLaunchKernelGGL((k_pf_gemm2<0, 64>), grid, dim3(kBlock), 0, st, g);
+  }
   g.want_route = ROUTE_RIVER;
-  if (g.group >= 64) hipLaunchKernelGGL((k_pf_gemm2<1, 64>), grid, dim3(kBlock), 0, st, g);
-  else hipLaunchKernelGGL((k_pf_gemm2<1, 32>), grid, dim3(kBlock), 0, st, g);
+  if (routes & 2) {
+    if (g.group >= 64) hipLaunchKernelGGL((k_pf_gemm2<1, 64>), grid, dim3(kBlock), 0, st, g);
+    else hipLaunchKernelGGL((k_pf_gemm2<1, 32>), grid, dim3(kBlock), 0, st, g);
+  }
   (void)lw;
   (void)which;
   return hipGetLastError();
@@ -963,6 +968,8 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
   PfArgs q = p;  // hin/hout swap per layer
   for (int l = 1; l <= dm.L; ++l) {
     const LayerDev& lw = host_layers[l - 1];
+    // a forced exit layer fixes every sequence's route: the backbone up to it, the river after
+    const int routes = forced > 0 ? (l <= forced ? 1 : 2) : 3;
     for (int t0 = 0; t0 < q.P; t0 += q.Ct) {
       q.t0 = t0;
       q.Ce = min(q.Ct, q.P - t0);
@@ -992,7 +999,7 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       g.z4 = lw.z_qkv;
       g.C = q.qkv;
       g.epi = EPI_STORE;
-      if ((e = gemm(g, lw, 0, st)) != hipSuccess) return e;
+      if ((e = gemm(g, lw, 0, routes, st)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_pf_rope_kv, dim3(Mc), dim3(kBlock), 0, st, q, l);
       {
         const int G = dm.H / dm.Hkv;
@@ -1023,7 +1030,7 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       g.R = q.hin;
       g.r_global = 1;
       g.epi = EPI_RESID;
-      if ((e = gemm(g, lw, 1, st)) != hipSuccess) return e;
+      if ((e = gemm(g, lw, 1, routes, st)) != hipSuccess) return e;
       g.r_global = 0;
       // MLP half
       hipLaunchKernelGGL(k_pf_rmsnorm, dim3(Mc), dim3(kBlock), 0, st, (const f16*)q.hmid, lw.mlp_norm,
@@ -1043,7 +1050,7 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       g.C = q.gu;
       g.R = nullptr;
       g.epi = EPI_STORE;
-      if ((e = gemm(g, lw, 2, st)) != hipSuccess) return e;
+      if ((e = gemm(g, lw, 2, routes, st)) != hipSuccess) return e;
       hipLaunchKernelGGL(k_pf_swiglu, dim3(Mc), dim3(kBlock), 0, st, q);
       g.A = q.a2;
       g.N = dm.d;
@@ -1060,7 +1067,7 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       g.c_global = 1;
       g.R = q.hmid;
       g.epi = EPI_RESID;
-      if ((e = gemm(g, lw, 3, st)) != hipSuccess) return e;
+      if ((e = gemm(g, lw, 3, routes, st)) != hipSuccess) return e;
       // per-token similarity of this chunk's rows (the exit test needs all of them)
       if (l < dm.L) hipLaunchKernelGGL(k_pf_cos, dim3(Mc), dim3(kBlock), 0, st, q);
     }
