@@ -891,6 +891,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_decide(PfArgs p, int layer, int f
     if (threadIdx.x < s) red[threadIdx.x] = fmin(red[threadIdx.x], red[threadIdx.x + s]);
     __syncthreads();
   }
+  // (with a forced exit layer, or before the entry layer, cosv is not written and not used)
   if (threadIdx.x == 0 && layer < dm.L && p.seq_route[b] == ROUTE_BACKBONE) {
     bool ex;
     if (forced > 0) {
@@ -1068,8 +1069,9 @@ hipError_t river_launch_prefill(const PfArgs& p, const DecodeArgs& a, const Laye
       g.R = q.hmid;
       g.epi = EPI_RESID;
       if ((e = gemm(g, lw, 3, routes, st)) != hipSuccess) return e;
-      // per-token similarity of this chunk's rows (the exit test needs all of them)
-      if (l < dm.L) hipLaunchKernelGGL(k_pf_cos, dim3(Mc), dim3(kBlock), 0, st, q);
+      // per-token similarity of this chunk's rows (the exit test needs all of them; a forced
+      // exit layer, or a layer before the entry layer, decides without them)
+      if (l < dm.L && forced <= 0 && l >= dm.entry) hipLaunchKernelGGL(k_pf_cos, dim3(Mc), dim3(kBlock), 0, st, q);
     }
     // sequence-level exit decision after this layer (every chunk has run it)
     if (l < dm.L) hipLaunchKernelGGL(k_pf_decide, dim3(dm.B), dim3(kBlock), 0, st, q, l, forced, tau);
